@@ -1,0 +1,297 @@
+"""Float64 NumPy oracle of one DSpark speculative-decoding round.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by ``__graft_entry__.smoke()``
+and by the ``cpu_baseline`` leg of bench.py, never by the HIP library.
+
+Sources (cited by page title and section; the pages quote the DSpark paper):
+  [HADA]  "DSpark: Aceleração da inferência de LLM com speculative decoding"
+          (pt.news.hada.io), sections "Definição do problema", "Arquitetura"
+          (decode cycle, Semi-Autoregressive Generation, Markov head,
+          Confidence-Scheduled Verification, Hardware-Aware Prefix Scheduler)
+          and "Treinamento" (per-step acceptance 1 - TV/2).
+  [AITALK] "DSpark: la apuesta de DeepSeek por la velocidad que no traiciona la
+          calidad" (aitalk.it), sections "El cuello de botella de la
+          inferencia" and "Verificar solo lo que importa".
+  [JDON]  "DeepSpec发布：让大模型生成提速6倍，输出质量却一点没变差" (jdon.com),
+          the scheduler sections (global candidate pool, early stop).
+
+What the round computes, in the pages' order:
+  1. Markov head (sequential stage): for k = 1..gamma, the prefix-dependent
+     bias B_k = W1[x_{k-1}] . W2 is added to the parallel stage's base logits
+     of position k, and x_k is sampled from the resulting distribution
+     ([HADA] Arquitetura, Semi-Autoregressive Generation and Markov head;
+     the anchor is the first prediction position, so x_0 is the anchor).
+  2. Scheduler: survival probabilities a_{r,j} are cumulative products of
+     the confidences c; all R*gamma candidates are pooled, sorted by a and
+     admitted greedily while the expected throughput tau*SPS(B) rises; the
+     walk stops at the first drop ([HADA] Hardware-Aware Prefix Scheduler;
+     [JDON] global pool; [AITALK] Verificar solo lo que importa).
+  3. Lossless verification: accept x_k with probability min(1, p/q), stop at
+     the first rejection and emit one corrected token from the normalised
+     residual max(0, p - q), or a bonus token from the next target row when
+     the whole verified block is accepted ([HADA] Definição do problema and
+     the decode cycle in Arquitetura; [AITALK] first section).
+
+Readings where the pages are silent (each also listed in the design doc):
+  * sampling is inverse-CDF over ascending token index with one uniform per
+    event: x = min{v : u < F[v]}; if rounding leaves no such v, x is the last
+    token with nonzero probability;
+  * accept iff u < p/q (strict), so the acceptance probability is min(1, p/q);
+  * draft and target share the temperature T; T = 0 means greedy: argmax with
+    the lowest index on ties, accept iff the draft token equals the target
+    argmax, emit the target argmax;
+  * one final uniform per request serves the residual or the bonus sample;
+    the bonus is drawn from target row L_r;
+  * the residual falls back to p when its mass is zero;
+  * the scheduler's a is an fp32 sequential product; the sort key is
+    (a descending, flat index r*gamma + j ascending); sums of a are exact
+    2^-36 fixed point; Theta_n = T_n * SPS(R + n) in fp64, SPS beyond the
+    table is 0; the walk stops at the first strict drop.
+
+All floating point is float64 on the exact input values (bf16 and fp32
+inputs widen exactly), except the scheduler's fp32 cumulative product.
+"""
+
+import numpy as np
+
+FLAG_EPS = 1e-6          # events closer than this to a decision boundary flag the row
+FIX_SHIFT = 36           # fixed-point scale 2^36 for survival-probability sums
+
+
+# ---------------------------------------------------------------------------
+# inputs
+
+
+def widen_weights(w, w_dtype):
+    """Return a float64 copy of a Markov factor stored as fp32 or as bf16 bits."""
+    if w_dtype == "bf16":
+        bits = np.ascontiguousarray(w, dtype=np.uint16).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64)
+    return np.asarray(w, dtype=np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# 1. Markov head and draft sampling  ([HADA] Arquitetura, Markov head)
+
+
+def markov_bias(W1_64, W2_64, prev):
+    """Transition bias rows W1[prev] @ W2 for an array of previous tokens.
+
+    Row index of W1 is the previous token, column index of W2 the next token:
+    after sampling "of" the bias raises "course" ([HADA] Markov head).
+    """
+    return W1_64[np.asarray(prev)] @ W2_64
+
+
+def inverse_cdf(w, u):
+    """Sample index from non-negative weights ``w`` (1-D) with uniform ``u``.
+
+    Returns (index, margin, F) where F is the normalised cumulative sum,
+    index = min{v : u < F[v]} (falls back to the last v with w[v] > 0), and
+    margin = min(u - F[index-1], F[index] - u) is the distance of u to the
+    nearest edge of the chosen interval.
+    """
+    total = w.sum()
+    F = np.cumsum(w) / total
+    idx = int(np.searchsorted(F, u, side="right"))
+    if idx >= len(w):
+        idx = int(np.flatnonzero(w > 0)[-1])
+    lo = F[idx - 1] if idx > 0 else 0.0
+    margin = min(u - lo, F[idx] - u)
+    return idx, margin, F
+
+
+def draft_distribution(z, T):
+    """Softmax of logits z / T over the last axis (T > 0), in float64.
+
+    Returns (pi, m, Z) with m = max z and Z = sum exp((z - m) / T), so that
+    pi = exp((z - m) / T) / Z.
+    """
+    m = z.max(axis=-1, keepdims=True)
+    e = np.exp((z - m) / T)
+    Z = e.sum(axis=-1, keepdims=True)
+    return e / Z, m[..., 0], Z[..., 0]
+
+
+def _greedy(z):
+    """Argmax (lowest index on ties) and top-1 minus top-2 gap, per row."""
+    idx = np.argmax(z, axis=-1)
+    top2 = np.partition(z, -2, axis=-1)[..., -2:] if z.shape[-1] > 1 else None
+    top1 = z.max(axis=-1)
+    gap = (top2[..., 1] - top2[..., 0]) if top2 is not None else np.full(top1.shape, np.inf)
+    return idx, top1, gap
+
+
+def draft(base, W1, W2, w_dtype, anchor, u_draft, T):
+    """Sequential Markov-head drafting of gamma tokens for every request.
+
+    base [R, gamma, V] fp32, W1 [V, r], W2 [r, V], anchor [R], u_draft [R, gamma].
+    Returns dict(tokens int32 [R, gamma], probs [R, gamma] (q_k(x_k)),
+    stats [R, gamma, 2] (max z, sum exp((z - max)/T)), margin [R, gamma]).
+    For T = 0 (greedy) probs are 1, stats are (max z, 1) and margin is the
+    top-1 minus top-2 logit gap.
+    """
+    R, g, V = base.shape
+    W1_64, W2_64 = widen_weights(W1, w_dtype), widen_weights(W2, w_dtype)
+    tokens = np.zeros((R, g), dtype=np.int32)
+    probs = np.zeros((R, g))
+    stats = np.zeros((R, g, 2))
+    margin = np.zeros((R, g))
+    prev = np.asarray(anchor, dtype=np.int64)
+    for k in range(g):
+        z = base[:, k, :].astype(np.float64) + markov_bias(W1_64, W2_64, prev)
+        if T == 0:
+            idx, top1, gap = _greedy(z)
+            tokens[:, k] = idx
+            probs[:, k] = 1.0
+            stats[:, k, 0], stats[:, k, 1] = top1, 1.0
+            margin[:, k] = gap / np.maximum(1.0, np.abs(top1))
+        else:
+            pi, m, Z = draft_distribution(z, T)
+            stats[:, k, 0], stats[:, k, 1] = m, Z
+            for i in range(R):
+                x, mg, _ = inverse_cdf(pi[i], float(u_draft[i, k]))
+                tokens[i, k], probs[i, k], margin[i, k] = x, pi[i, x], mg
+        prev = tokens[:, k].astype(np.int64)
+    return dict(tokens=tokens, probs=probs, stats=stats, margin=margin)
+
+
+# ---------------------------------------------------------------------------
+# 2. Hardware-aware prefix scheduler  ([HADA] Hardware-Aware Prefix Scheduler)
+
+
+def schedule(conf, sps):
+    """Confidence scheduler: per-request verify lengths from confidences only.
+
+    conf [R, gamma] fp32 conditional confidences c_{r,j} in (0, 1];
+    sps [N] fp32 cost table, sps[i] = throughput at verify batch B = i + 1.
+    Never reads a drafted token (the non-anticipation requirement).
+    Returns dict(verify_len int32 [R], n_admitted, cum_conf fp32 [R, gamma],
+    theta float64 [R*gamma + 1], order int64 [R*gamma]).
+    """
+    c = np.asarray(conf, dtype=np.float32)
+    R, g = c.shape
+    # survival probability a_{r,j}: fp32 running product of the conditionals
+    a = np.empty_like(c)
+    a[:, 0] = c[:, 0]
+    for j in range(1, g):
+        a[:, j] = a[:, j - 1] * c[:, j]          # float32 * float32 -> float32
+    flat = np.arange(R * g, dtype=np.int64)
+    af = a.reshape(-1)
+    # global pool sorted by a descending, ties by flat index ascending
+    order = np.lexsort((flat, -af.astype(np.float64)))
+    # expected emitted tokens tau_n = R + sum of the n best a, in 2^-36 units
+    a_fx = np.floor(af[order].astype(np.float64) * float(1 << FIX_SHIFT)).astype(np.int64)
+    T_n = np.concatenate([[0], np.cumsum(a_fx)]) + np.int64(R) * (np.int64(1) << FIX_SHIFT)
+    n = np.arange(R * g + 1)
+    B = R + n
+    S = np.zeros(R * g + 1)
+    ok = B <= len(sps)
+    S[ok] = np.asarray(sps, dtype=np.float32)[B[ok] - 1].astype(np.float64)
+    theta = T_n.astype(np.float64) * S
+    drops = np.flatnonzero(theta[1:] < theta[:-1])
+    n_star = int(drops[0]) if len(drops) else R * g
+    L = np.bincount(order[:n_star] // g, minlength=R).astype(np.int32)
+    return dict(verify_len=L, n_admitted=n_star, cum_conf=a, theta=theta, order=order)
+
+
+# ---------------------------------------------------------------------------
+# 3. Lossless verification  ([HADA] Definição do problema; decode cycle)
+
+
+def verify(target, base, W1, W2, w_dtype, anchor, draft_tokens, draft_probs,
+           verify_len, u_accept, u_final, T):
+    """Rejection-sampling verification of the drafted blocks.
+
+    target [R, gamma+1, V]: row k-1 scores draft position k, row L_r scores the
+    bonus.  draft_probs are the q_k(x_k) the draft reported.  verify_len [R]
+    (None means gamma for every request).
+    Returns dict(out_tokens int32 [R, gamma+1] (-1 padded), accept_len int32 [R],
+    target_probs [R, gamma] (p_k(x_k) for every evaluated position, -1 for the
+    rest), accept_margin [R, gamma] (inf where not evaluated), final_margin [R],
+    residual_mass [R] (NaN for bonus rows)).
+    """
+    R, g1, V = target.shape
+    g = g1 - 1
+    L = np.full(R, g, dtype=np.int64) if verify_len is None else np.asarray(verify_len, np.int64)
+    W1_64, W2_64 = widen_weights(W1, w_dtype), widen_weights(W2, w_dtype)
+    x = np.asarray(draft_tokens, dtype=np.int64)
+    q = np.asarray(draft_probs, dtype=np.float64)
+    out = np.full((R, g + 1), -1, dtype=np.int32)
+    A = np.zeros(R, dtype=np.int32)
+    tp = np.full((R, g), -1.0)
+    acc_m = np.full((R, g), np.inf)
+    fin_m = np.full(R, np.inf)
+    res_mass = np.full(R, np.nan)
+    for i in range(R):
+        kstar = None
+        for k in range(1, L[i] + 1):
+            t = target[i, k - 1].astype(np.float64)
+            if T == 0:
+                idx, top1, gap = _greedy(t)
+                ok = int(idx) == x[i, k - 1]
+                tp[i, k - 1] = 1.0 if ok else 0.0
+                acc_m[i, k - 1] = gap / max(1.0, abs(top1))
+            else:
+                p, _, _ = draft_distribution(t, T)
+                rho = p[x[i, k - 1]] / q[i, k - 1]
+                ok = float(u_accept[i, k - 1]) < rho
+                tp[i, k - 1] = p[x[i, k - 1]]
+                acc_m[i, k - 1] = abs(float(u_accept[i, k - 1]) - rho)
+            if not ok:
+                kstar = k
+                break
+        A[i] = L[i] if kstar is None else kstar - 1
+        out[i, :A[i]] = x[i, :A[i]]
+        row = target[i, A[i]].astype(np.float64)       # rejected row k*-1, or bonus row L_r
+        if T == 0:
+            idx, top1, gap = _greedy(row)
+            y = int(idx)
+            fin_m[i] = gap / max(1.0, abs(top1))
+        else:
+            p, _, _ = draft_distribution(row, T)
+            w = p
+            if kstar is not None:
+                prev = anchor[i] if kstar == 1 else x[i, kstar - 2]
+                z = base[i, kstar - 1].astype(np.float64) + markov_bias(W1_64, W2_64, [prev])[0]
+                pi, _, _ = draft_distribution(z, T)
+                d = np.maximum(0.0, p - pi)
+                res_mass[i] = d.sum()
+                if res_mass[i] > 0:
+                    w = d
+            y, fin_m[i], _ = inverse_cdf(w, float(u_final[i]))
+        out[i, A[i]] = y
+    return dict(out_tokens=out, accept_len=A, target_probs=tp, accept_margin=acc_m,
+                final_margin=fin_m, residual_mass=res_mass)
+
+
+# ---------------------------------------------------------------------------
+# whole round and boundary flags
+
+
+def run_round(inp, T=1.0, use_scheduler=None):
+    """Draft -> schedule -> verify on one input dict from ``gen.make_inputs``."""
+    sched = None
+    if use_scheduler is None:
+        use_scheduler = inp.get("conf") is not None
+    d = draft(inp["base"], inp["W1"], inp["W2"], inp["w_dtype"], inp["anchor"], inp["u_draft"], T)
+    L = None
+    if use_scheduler:
+        sched = schedule(inp["conf"], inp["sps"])
+        L = sched["verify_len"][inp["rows"]] if "rows" in inp else sched["verify_len"]
+    v = verify(inp["target"], inp["base"], inp["W1"], inp["W2"], inp["w_dtype"], inp["anchor"],
+               d["tokens"], d["probs"], L, inp["u_accept"], inp["u_final"], T)
+    flags = row_flags(d, v)
+    return dict(draft=d, schedule=sched, verify=v, flags=flags,
+                verify_len=(np.full(len(inp["anchor"]), inp["base"].shape[1], np.int32)
+                            if L is None else np.asarray(L, np.int32)))
+
+
+def row_flags(d, v, eps=FLAG_EPS):
+    """Rows whose outcome lies within ``eps`` of a decision boundary.
+
+    Covers every draft event, the accept tests that were evaluated, and the
+    final sample.  Such rows are excluded from bit-exact comparison and counted.
+    """
+    return ((d["margin"] < eps).any(axis=1) | (v["accept_margin"] < eps).any(axis=1)
+            | (v["final_margin"] < eps))

@@ -1,0 +1,503 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: each test checks a worked
+example, a closed form, an invariant, a special case that reduces to a library
+routine, or exact enumeration by bisection over the uniforms.
+"""
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy import special, stats
+
+import oracle as O
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _softmax(x):
+    return special.softmax(np.asarray(x, dtype=np.float64))
+
+
+# ---------------------------------------------------------------------------
+# worked trace of the decode cycle
+
+
+def _trace_inputs(T):
+    g = json.load(open(os.path.join(GOLD, "worked_trace.json")))
+    V, t, peak = g["V"], g["tokens"], g["peak"]
+    base = np.zeros((1, 4, V), np.float32)
+    for k, name in enumerate("EFGH"):
+        base[0, k, t[name]] = peak
+    target = np.zeros((1, 5, V), np.float32)
+    target[0, 0], target[0, 1] = base[0, 0], base[0, 1]
+    target[0, 2, t["K"]] = peak
+    target[0, 3, t["H"]] = peak
+    target[0, 4, 0] = peak
+    W1 = np.zeros((V, 2), np.float32)
+    W2 = np.zeros((2, V), np.float32)
+    inp = dict(base=base, target=target, W1=W1, W2=W2, w_dtype="f32",
+               anchor=np.array([t["D"]], np.int32), rows=np.array([0]),
+               u_draft=np.full((1, 4), g["u"], np.float32),
+               u_accept=np.full((1, 4), g["u"], np.float32),
+               u_final=np.full(1, g["u"], np.float32),
+               conf=np.array([g["conf"]], np.float32),
+               sps=np.array(g["sps_B_1_to_5"], np.float32))
+    return g, inp
+
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_worked_trace(T):
+    g, inp = _trace_inputs(T)
+    e = g["expected"]
+    res = O.run_round(inp, T=T)
+    assert res["draft"]["tokens"][0].tolist() == e["draft_tokens"]
+    s = res["schedule"]
+    np.testing.assert_allclose(s["cum_conf"][0], e["cum_conf"], rtol=1e-6)
+    np.testing.assert_allclose(s["theta"] / 2.0 ** 36, e["theta_scaled"], rtol=1e-6)
+    assert s["n_admitted"] == e["n_admitted"]
+    assert res["verify_len"][0] == e["verify_len"]
+    assert res["verify"]["accept_len"][0] == e["accept_len"]
+    assert res["verify"]["out_tokens"][0].tolist() == e["out_tokens"]
+    assert not res["flags"][0]
+
+
+# ---------------------------------------------------------------------------
+# draft: softmax normalisation, exact bias, Markov direction, special cases
+
+
+def _rand_case(rng, R=3, g=3, V=24, r=4, wsig=0.5):
+    base = (rng.standard_normal((R, g, V)) * 2).astype(np.float32)
+    W1 = (rng.standard_normal((V, r)) * wsig).astype(np.float32)
+    W2 = (rng.standard_normal((r, V)) * wsig).astype(np.float32)
+    anchor = rng.integers(0, V, R).astype(np.int32)
+    return base, W1, W2, anchor
+
+
+def test_softmax_normalisation_and_logsumexp():
+    rng = np.random.default_rng(1)
+    z = rng.standard_normal((5, 300)) * 4
+    for T in (1.0, 0.7, 2.5):
+        pi, m, Z = O.draft_distribution(z, T)
+        np.testing.assert_allclose(pi.sum(axis=1), 1.0, atol=1e-13)
+        np.testing.assert_allclose(np.log(Z) + m / T, special.logsumexp(z / T, axis=1), rtol=1e-13)
+        np.testing.assert_allclose(pi, special.softmax(z / T, axis=1), atol=1e-15)
+
+
+def test_bias_is_exact_sum_of_bf16_products():
+    from gen.inputs import bf16_bits_from_f32
+    rng = np.random.default_rng(2)
+    V, r = 40, 16
+    w1 = bf16_bits_from_f32(rng.standard_normal((V, r)).astype(np.float32) * 0.05)
+    w2 = bf16_bits_from_f32(rng.standard_normal((r, V)).astype(np.float32) * 0.05)
+    W1 = O.widen_weights(w1, "bf16")
+    W2 = O.widen_weights(w2, "bf16")
+    prev = [3, 17, 39]
+    bias = O.markov_bias(W1, W2, prev)
+
+    def exact(bits):   # bf16 pattern -> exact rational
+        sign = -1 if bits >> 15 else 1
+        ex = (bits >> 7) & 0xFF
+        man = bits & 0x7F
+        return sign * Fraction(128 + man, 128) * Fraction(2) ** (ex - 127)
+
+    for i, pv in enumerate(prev):
+        for v in (0, 7, 21, 39):
+            s = sum(exact(int(w1[pv, k])) * exact(int(w2[k, v])) for k in range(r))
+            assert abs(float(s) - bias[i, v]) <= 1e-15 * max(1.0, abs(float(s)))
+
+
+def test_markov_direction_of_course():
+    # vocabulary: 0 "of", 1 "course", 2 "problem", 3 "no", 4.. filler
+    V, r = 8, 2
+    W1 = np.zeros((V, r), np.float32)
+    W2 = np.zeros((r, V), np.float32)
+    W1[0, 0] = 1.0            # previous token "of" -> latent 0
+    W2[0, 1], W2[0, 2] = 3.0, -3.0   # latent 0 raises "course", lowers "problem"
+    base = np.zeros((1, 1, V), np.float32)
+    base[0, 0, [1, 2]] = 2.0   # parallel stage is bimodal between the two
+    res = O.draft(base, W1, W2, "f32", np.array([0], np.int32), np.array([[0.5]], np.float32), 1.0)
+    z = base[0, 0].astype(np.float64).copy()
+    z[1] += 3.0
+    z[2] -= 3.0
+    # index direction: row of W1 = previous token, column of W2 = next token
+    assert res["tokens"][0, 0] == 1
+    np.testing.assert_allclose(res["probs"][0, 0], _softmax(z)[1], rtol=1e-14)
+    # after any other previous token the bias vanishes
+    res2 = O.draft(base, W1, W2, "f32", np.array([5], np.int32), np.array([[0.5]], np.float32), 1.0)
+    np.testing.assert_allclose(res2["probs"][0, 0], _softmax(base[0, 0])[res2["tokens"][0, 0]],
+                               rtol=1e-14)
+    # transposing the factors (a plausible bug) would bias the wrong pair
+    assert O.markov_bias(W1.astype(np.float64), W2.astype(np.float64), [0])[0, 1] == 3.0
+    assert O.markov_bias(W1.astype(np.float64), W2.astype(np.float64), [1])[0, 0] == 0.0
+
+
+def test_zero_factors_give_independent_parallel_drafter():
+    rng = np.random.default_rng(3)
+    base, W1, W2, anchor = _rand_case(rng, R=4, g=5, V=30)
+    W1[:] = 0
+    W2[:] = 0
+    u = rng.random((4, 5)).astype(np.float32)
+    res = O.draft(base, W1, W2, "f32", anchor, u, 1.0)
+    for i in range(4):
+        for k in range(5):
+            p = _softmax(base[i, k])
+            x = int(np.searchsorted(np.cumsum(p), u[i, k], side="right"))
+            assert res["tokens"][i, k] == x
+            np.testing.assert_allclose(res["probs"][i, k], p[x], rtol=1e-13)
+            np.testing.assert_allclose(res["stats"][i, k, 0], base[i, k].max())
+
+
+def test_rank_one_bias_is_outer_product():
+    rng = np.random.default_rng(4)
+    base, W1, W2, anchor = _rand_case(rng, R=2, g=3, V=20, r=1)
+    u = rng.random((2, 3)).astype(np.float32)
+    res = O.draft(base, W1, W2, "f32", anchor, u, 1.0)
+    prev = anchor.copy()
+    for k in range(3):
+        for i in range(2):
+            z = base[i, k].astype(np.float64) + float(W1[prev[i], 0]) * W2[0].astype(np.float64)
+            p = _softmax(z)
+            np.testing.assert_allclose(res["probs"][i, k], p[res["tokens"][i, k]], rtol=1e-13)
+            np.testing.assert_allclose(res["stats"][i, k, 1], np.exp(z - z.max()).sum(), rtol=1e-13)
+        prev = res["tokens"][:, k]
+
+
+def test_greedy_draft_is_argmax():
+    rng = np.random.default_rng(5)
+    base, W1, W2, anchor = _rand_case(rng)
+    res = O.draft(base, W1, W2, "f32", anchor, np.zeros((3, 3), np.float32), 0.0)
+    prev = anchor
+    for k in range(3):
+        z = base[:, k].astype(np.float64) + W1[prev].astype(np.float64) @ W2.astype(np.float64)
+        assert (res["tokens"][:, k] == z.argmax(axis=1)).all()
+        prev = res["tokens"][:, k]
+    assert (res["probs"] == 1).all()
+
+
+# ---------------------------------------------------------------------------
+# exact enumeration by bisection over the uniforms
+
+
+def _bisect_first(pred, iters=64):
+    """Smallest u in [0, 1) (to ~2^-64) where the monotone predicate turns True."""
+    lo, hi = 0.0, 1.0
+    if pred(lo):
+        return 0.0
+    for _ in range(iters):
+        mid = 0.5 * (lo + hi)
+        if pred(mid):
+            hi = mid
+        else:
+            lo = mid
+    return hi
+
+
+def _interval_masses(f, n):
+    """Measures of {u : f(u) = v} for a monotone non-decreasing f: [0,1) -> {0..n-1}."""
+    edges = [0.0] + [_bisect_first(lambda u, v=v: f(u) >= v) for v in range(1, n)] + [1.0]
+    return np.diff(edges), edges
+
+
+class _Tiny:
+    """A V = 4, gamma = 2 single-request round with x1-dependent target rows."""
+
+    def __init__(self, seed, T=1.0):
+        rng = np.random.default_rng(seed)
+        self.V, self.T = 4, T
+        self.base = (rng.standard_normal((1, 2, 4)) * 1.5).astype(np.float32)
+        self.W1 = (rng.standard_normal((4, 2)) * 0.8).astype(np.float32)
+        self.W2 = (rng.standard_normal((2, 4)) * 0.8).astype(np.float32)
+        self.anchor = np.array([1], np.int32)
+        self.T1 = (rng.standard_normal(4) * 1.5).astype(np.float32)          # target row 0
+        self.T2 = (rng.standard_normal((4, 4)) * 1.5).astype(np.float32)     # row 1 given x1
+        self.T3 = (rng.standard_normal(4) * 1.5).astype(np.float32)          # bonus row 2
+
+    def draft(self, u1, u2):
+        r = O.draft(self.base, self.W1, self.W2, "f32", self.anchor,
+                    np.array([[u1, u2]]), self.T)
+        return r["tokens"][0], r["probs"][0]
+
+    def verify(self, x, q, L, ua1, ua2, uf):
+        tgt = np.stack([self.T1, self.T2[x[0]], self.T3])[None]
+        return O.verify(tgt, self.base, self.W1, self.W2, "f32", self.anchor, x[None], q[None],
+                        np.array([L]), np.array([[ua1, ua2]]), np.array([uf]), self.T)
+
+    def mid_u1(self, a):
+        m, e = _interval_masses(lambda u: self.draft(u, 0.5)[0][0], 4)
+        return 0.5 * (e[a] + e[a + 1]), m
+
+    def first_token_law(self, L_of_x1):
+        """Exact law of the first emitted token; L may depend on x1 (a control)."""
+        P = np.zeros(4)
+        _, m1 = self.mid_u1(0)
+        for a in range(4):
+            if m1[a] == 0:
+                continue
+            u1, _ = self.mid_u1(a)
+            x, q = self.draft(u1, 0.5)
+            L = L_of_x1(a)
+            if L == 0:
+                law, _ = _interval_masses(lambda uf: self.verify(x, q, 0, .5, .5, uf)["out_tokens"][0, 0], 4)
+                P += m1[a] * law
+                continue
+            p_acc = _bisect_first(lambda ua: self.verify(x, q, L, ua, 0.0, 0.5)["accept_len"][0] == 0)
+            P[a] += m1[a] * p_acc
+            if p_acc < 1:
+                law, _ = _interval_masses(
+                    lambda uf: self.verify(x, q, L, 1 - 1e-17, 0.0, uf)["out_tokens"][0, 0], 4)
+                P += m1[a] * (1 - p_acc) * law
+        return P
+
+    def second_token_law(self, a, L):
+        """Exact law of the second emitted token given x1 = a was accepted."""
+        u1, _ = self.mid_u1(a)
+        P = np.zeros(4)
+        if L == 1:
+            x, q = self.draft(u1, 0.5)
+            law, _ = _interval_masses(lambda uf: self.verify(x, q, 1, 0.0, .5, uf)["out_tokens"][0, 1], 4)
+            return law
+        m2, _ = _interval_masses(lambda u: self.draft(u1, u)[0][1], 4)
+        e2 = np.concatenate([[0.0], np.cumsum(m2)])
+        for b in range(4):
+            if m2[b] == 0:
+                continue
+            x, q = self.draft(u1, 0.5 * (e2[b] + e2[b + 1]))
+            assert x[0] == a and x[1] == b
+            p_acc = _bisect_first(lambda ua: self.verify(x, q, 2, 0.0, ua, 0.5)["accept_len"][0] == 1)
+            P[b] += m2[b] * p_acc
+            if p_acc < 1:
+                law, _ = _interval_masses(
+                    lambda uf: self.verify(x, q, 2, 0.0, 1 - 1e-17, uf)["out_tokens"][0, 1], 4)
+                P += m2[b] * (1 - p_acc) * law
+        return P
+
+
+@pytest.mark.parametrize("seed", [11, 12])
+@pytest.mark.parametrize("L", [0, 1, 2])
+def test_lossless_first_token_exact(seed, L):
+    t = _Tiny(seed)
+    P = t.first_token_law(lambda a: L)
+    np.testing.assert_allclose(P, _softmax(t.T1), atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [11, 13])
+@pytest.mark.parametrize("L", [1, 2])
+def test_lossless_second_token_exact(seed, L):
+    t = _Tiny(seed)
+    for a in range(4):
+        np.testing.assert_allclose(t.second_token_law(a, L), _softmax(t.T2[a]), atol=1e-12)
+
+
+def test_lossless_with_scheduler_lengths():
+    t = _Tiny(14)
+    sched = O.schedule(np.array([[0.9, 0.6]], np.float32),
+                       np.array([1.0, 0.8, 0.5], np.float32))
+    L = int(sched["verify_len"][0])
+    P = t.first_token_law(lambda a: L)
+    np.testing.assert_allclose(P, _softmax(t.T1), atol=1e-12)
+
+
+def test_negative_control_anticipating_scheduler_is_biased():
+    """Verify length chosen from the drafted token breaks losslessness."""
+    t = _Tiny(11)
+    _, m1 = t.mid_u1(0)
+    fav = int(np.argmax(m1))
+    P = t.first_token_law(lambda a: 1 if a == fav else 0)
+    assert np.abs(P - _softmax(t.T1)).max() > 1e-3
+
+
+def test_accept_probability_closed_form():
+    """P(accept at position 1) = sum min(p, q) = 1 - TV(p, q)."""
+    t = _Tiny(15)
+    p = _softmax(t.T1)
+    q = _softmax(t.base[0, 0].astype(np.float64) + t.W1[1].astype(np.float64) @ t.W2.astype(np.float64))
+    _, m1 = t.mid_u1(0)
+    P = 0.0
+    for a in range(4):
+        if m1[a] == 0:
+            continue
+        u1, _ = t.mid_u1(a)
+        x, qq = t.draft(u1, 0.5)
+        P += m1[a] * _bisect_first(lambda ua: t.verify(x, qq, 1, ua, 0.0, 0.5)["accept_len"][0] == 0)
+    np.testing.assert_allclose(P, np.minimum(p, q).sum(), atol=1e-12)
+    np.testing.assert_allclose(P, 1 - 0.5 * np.abs(p - q).sum(), atol=1e-12)
+
+
+def test_residual_mass_is_half_l1_distance():
+    rng = np.random.default_rng(16)
+    R, g, V = 6, 3, 50
+    base, W1, W2, anchor = _rand_case(rng, R=R, g=g, V=V)
+    target = (rng.standard_normal((R, g + 1, V)) * 2).astype(np.float32)
+    u = rng.random((R, g)).astype(np.float32)
+    d = O.draft(base, W1, W2, "f32", anchor, u, 1.0)
+    v = O.verify(target, base, W1, W2, "f32", anchor, d["tokens"], d["probs"], None,
+                 np.full((R, g), 0.999999, np.float32), rng.random(R).astype(np.float32), 1.0)
+    for i in range(R):
+        A = v["accept_len"][i]
+        if A == g:
+            continue
+        prev = anchor[i] if A == 0 else d["tokens"][i, A - 1]
+        pi = _softmax(base[i, A].astype(np.float64) + W1[prev].astype(np.float64) @ W2.astype(np.float64))
+        p = _softmax(target[i, A])
+        np.testing.assert_allclose(v["residual_mass"][i], 0.5 * np.abs(p - pi).sum(), rtol=1e-12)
+
+
+def test_chi_square_first_emitted_token():
+    rng = np.random.default_rng(17)
+    R, g, V = 100000, 2, 16
+    base1 = (rng.standard_normal((g, V)) * 1.5).astype(np.float32)
+    W1 = (rng.standard_normal((V, 2)) * 0.5).astype(np.float32)
+    W2 = (rng.standard_normal((2, V)) * 0.5).astype(np.float32)
+    tgt1 = (base1[0] + rng.standard_normal(V) * 0.8).astype(np.float32)
+    base = np.broadcast_to(base1, (R, g, V))
+    target = np.broadcast_to(np.stack([tgt1, base1[1], base1[0]]), (R, g + 1, V))
+    anchor = np.full(R, 3, np.int32)
+    ur = np.random.default_rng(18)
+    d = O.draft(base, W1, W2, "f32", anchor, ur.random((R, g), np.float32), 1.0)
+    v = O.verify(target, base, W1, W2, "f32", anchor, d["tokens"], d["probs"], np.ones(R, np.int64),
+                 ur.random((R, g), np.float32), ur.random(R, np.float32), 1.0)
+    y = v["out_tokens"][:, 0]
+    exp = _softmax(tgt1) * R
+    obs = np.bincount(y, minlength=V).astype(np.float64)
+    keep = exp >= 5
+    o = np.concatenate([obs[keep], [obs[~keep].sum()]]) if (~keep).any() else obs
+    e = np.concatenate([exp[keep], [exp[~keep].sum()]]) if (~keep).any() else exp
+    assert stats.chisquare(o, e).pvalue >= 1e-3
+
+
+def test_equal_draft_and_target_always_accepts():
+    rng = np.random.default_rng(19)
+    R, g, V = 5, 4, 40
+    base, W1, W2, anchor = _rand_case(rng, R=R, g=g, V=V)
+    W1[:] = 0
+    target = np.concatenate([base, base[:, :1]], axis=1)
+    u = rng.random((R, g)).astype(np.float32)
+    d = O.draft(base, W1, W2, "f32", anchor, u, 1.0)
+    L = np.array([0, 1, 2, 3, 4])
+    v = O.verify(target, base, W1, W2, "f32", anchor, d["tokens"], d["probs"], L,
+                 np.full((R, g), 0.99999994, np.float32), u[:, 0], 1.0)
+    assert (v["accept_len"] == L).all()
+
+
+def test_greedy_verify():
+    rng = np.random.default_rng(20)
+    R, g, V = 6, 3, 30
+    base, W1, W2, anchor = _rand_case(rng, R=R, g=g, V=V)
+    target = (rng.standard_normal((R, g + 1, V))).astype(np.float32)
+    d = O.draft(base, W1, W2, "f32", anchor, np.zeros((R, g)), 0.0)
+    # make row 0 accept everything, row 1 reject at 2
+    for k in range(g):
+        target[0, k, d["tokens"][0, k]] = 50
+    target[1, 0, d["tokens"][1, 0]] = 50
+    target[1, 1, d["tokens"][1, 1]] = -50
+    v = O.verify(target, base, W1, W2, "f32", anchor, d["tokens"], d["probs"], None,
+                 np.zeros((R, g)), np.zeros(R), 0.0)
+    assert v["accept_len"][0] == g
+    assert v["out_tokens"][0, g] == int(np.argmax(target[0, g]))
+    assert v["accept_len"][1] == 1
+    assert v["out_tokens"][1, 1] == int(np.argmax(target[1, 1]))
+    for i in range(R):
+        A = v["accept_len"][i]
+        assert (v["out_tokens"][i, :A] == d["tokens"][i, :A]).all()
+        assert v["out_tokens"][i, A] == int(np.argmax(target[i, A]))
+
+
+def test_boundary_uniform_is_flagged():
+    rng = np.random.default_rng(21)
+    base, W1, W2, anchor = _rand_case(rng, R=1, g=1, V=10)
+    z = base[0, 0].astype(np.float64) + W1[anchor[0]].astype(np.float64) @ W2.astype(np.float64)
+    F = np.cumsum(_softmax(z))
+    for u, flagged in ((F[3] - 3e-7, True), (F[3] + 3e-7, True), (0.5 * (F[3] + F[4]), False)):
+        d = O.draft(base, W1, W2, "f32", anchor, np.array([[u]]), 1.0)
+        assert (d["margin"][0, 0] < O.FLAG_EPS) == flagged
+
+
+# ---------------------------------------------------------------------------
+# scheduler
+
+
+def _sched_case(seed, R=8, g=5, ties=False):
+    rng = np.random.default_rng(seed)
+    c = rng.uniform(0.3, 1.0, (R, g)).astype(np.float32)
+    if ties:
+        c[rng.random((R, g)) < 0.3] = 1.0
+    return c
+
+
+@pytest.mark.parametrize("ties", [False, True])
+def test_schedule_invariants(ties):
+    c = _sched_case(30, R=16, g=6, ties=ties)
+    sps = (1.0 / (1.0 + 0.02 * np.arange(1, 200))).astype(np.float32)
+    s = O.schedule(c, sps)
+    a = s["cum_conf"]
+    assert (a[:, 1:] <= a[:, :-1]).all()                       # survival is non-increasing
+    L, n = s["verify_len"], s["n_admitted"]
+    assert L.sum() == n
+    admitted = set(int(f) for f in s["order"][:n])
+    for r in range(16):
+        assert admitted & set(range(r * 6, r * 6 + 6)) == set(range(r * 6, r * 6 + L[r]))
+    assert 0 <= n <= 16 * 6
+
+
+def test_constant_table_admits_everything():
+    c = _sched_case(31)
+    s = O.schedule(c, np.ones(100, np.float32))
+    assert s["n_admitted"] == c.size and (s["verify_len"] == c.shape[1]).all()
+
+
+def test_table_end_is_a_wall():
+    c = np.ones((4, 5), np.float32)
+    s = O.schedule(c, np.ones(10, np.float32))       # B = 4 + n must stay <= 10
+    assert s["n_admitted"] == 6
+
+
+def test_early_stop_is_global_optimum_on_unimodal_objective():
+    import itertools
+    for seed in range(40, 60):
+        rng = np.random.default_rng(seed)
+        R, g = 3, 3
+        c = rng.uniform(0.2, 1.0, (R, g)).astype(np.float32)
+        slope = rng.uniform(0.05, 0.6)
+        sps = (1.0 / (1.0 + slope * np.arange(1, 30))).astype(np.float32)
+        s = O.schedule(c, sps)
+        th = s["theta"]
+        k = int(np.argmax(th))
+        if not ((np.diff(th[: k + 1]) >= 0).all() and (np.diff(th[k:]) <= 0).all()):
+            continue                               # precondition: unimodal along the pool order
+        a = s["cum_conf"].astype(np.float64)
+        best, bestL = -1.0, None
+        for Lv in itertools.product(range(g + 1), repeat=R):
+            tau = R + sum(a[r, :Lv[r]].sum() for r in range(R))
+            val = tau * float(sps[R + sum(Lv) - 1])
+            if val > best:
+                best, bestL = val, Lv
+        assert tuple(s["verify_len"]) == bestL
+
+
+def test_stair_table_cut_lands_on_a_stair_edge():
+    from gen.inputs import cost_table
+    rng = np.random.default_rng(32)
+    R, g = 128, 7
+    c = rng.beta(8, 2, (R, g)).astype(np.float32)
+    s = O.schedule(c, cost_table("stairs64", R, g))
+    n = s["n_admitted"]
+    assert 0 < n < R * g
+    assert (R + n) % 64 == 0
+
+
+def test_verify_length_ignores_drafted_tokens():
+    """Non-anticipation: L depends on confidences only, never on tokens or uniforms."""
+    from gen import make_inputs
+    a = make_inputs(1)
+    b = make_inputs(1, seed_u=99)
+    ra, rb = O.run_round(a), O.run_round(b)
+    assert (ra["draft"]["tokens"] != rb["draft"]["tokens"]).any()
+    assert (ra["verify_len"] == rb["verify_len"]).all()
+    # relabelling the vocabulary leaves the schedule alone as well
+    perm = np.random.default_rng(5).permutation(a["base"].shape[2])
+    c = dict(a, base=a["base"][:, :, perm], target=a["target"][:, :, perm], W2=a["W2"][:, perm])
+    assert (O.run_round(c)["verify_len"] == ra["verify_len"]).all()

@@ -1,0 +1,309 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSpark draft -> schedule -> verify round on one MI355X.
+
+One step = one whole round (dspark_draft, dspark_schedule, dspark_verify) over
+one batch of seeded synthetic inputs already resident in HBM.  Default
+workload: R = 128 requests, block gamma = 7, vocabulary V = 131072, Markov
+rank r = 256, bf16 factors, fp32 logits, scheduler on, temperature 1.
+
+The round is captured once into a HIP graph and replayed; W untimed replays,
+then K timed replays between device synchronisations (ms_per_step).  A second
+timed pass of K rounds launches eagerly with the library's launch hook armed:
+HIP events recorded around every launch of the dominant kernel (the per-step
+bias GEMM + softmax partials) on its stream give its average duration.
+
+Prints ONE JSON line.  The CPU baseline is the float64 oracle, run in a child
+process on a bounded sample (whole rounds until --cpu-seconds elapse).
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "draft+verify tokens/s at R=128,γ=7,V=131k; % of MI355X HBM roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
+PROFILE_KERNEL = "k_draft_partials"
+KID_DRAFT_PARTIALS = 1   # dspark_kernel_id of the dominant kernel
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="3", help="workload key (default 3: R=128, gamma=7, V=131072)")
+    ap.add_argument("--temperature", type=float, default=1.0)
+    ap.add_argument("--eager", action="store_true", help="launch kernels eagerly instead of a graph")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-baseline-worker", action="store_true", help=argparse.SUPPRESS)
+    return ap.parse_args()
+
+
+def cfg_key(s):
+    return int(s) if s.isdigit() else s
+
+
+def source_digest():
+    """sha256 of the HIP sources: ties stored counter readings to this build."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "draft_sampling_verify_markov_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None.
+
+    The summary is used only if it was taken on the current kernel sources.
+    """
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, timed in a child process
+
+
+def cpu_worker(a):
+    from threadpoolctl import threadpool_info
+    from gen import make_inputs
+    import oracle as O
+    inp = make_inputs(cfg_key(a.config))
+    t0 = time.perf_counter()
+    n, toks = 0, 0
+    while True:
+        res = O.run_round(inp, T=a.temperature)
+        n += 1
+        toks += int((res["verify"]["accept_len"] + 1).sum())
+        if time.perf_counter() - t0 >= a.cpu_seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    print(json.dumps(dict(rounds=n, seconds=dt, tokens=toks, threads=threads)))
+
+
+def cpu_baseline(a):
+    ncpu = len(os.sched_getaffinity(0))
+    env = dict(os.environ)
+    for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        env.setdefault(k, str(ncpu))
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-worker", "--config", a.config,
+           "--cpu-seconds", str(a.cpu_seconds), "--temperature", str(a.temperature)]
+    out = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=600)
+    if out.returncode != 0:
+        return dict(error=out.stderr[-400:])
+    r = json.loads(out.stdout.strip().splitlines()[-1])
+    return dict(value=r["tokens"] / r["seconds"], unit="tokens/s", cores=r["threads"], kind="oracle",
+                rounds_per_s=r["rounds"] / r["seconds"],
+                sample=f"{r['rounds']} whole round(s) of the same workload (all requests), "
+                       f"float64 NumPy oracle, {r['seconds']:.1f} s")
+
+
+# ---------------------------------------------------------------------------
+# GPU measurement
+
+
+def gpu_bench(a):
+    import numpy as np
+    import torch
+    import draft_sampling_verify_markov_amd as D
+    from gen import make_inputs, config
+    from gen.inputs import algorithmic_bytes
+
+    key = cfg_key(a.config)
+    d = config(key)
+    R, g, V, r = d["R"], d["gamma"], d["V"], d["r"]
+    inp = make_inputs(key)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def t(x, dt):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=dt)).to(dev)
+
+    def w(x):
+        if inp["w_dtype"] == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).to(dev).view(torch.bfloat16)
+        return t(x, np.float32)
+
+    dd = dict(base=t(inp["base"], np.float32), target=t(inp["target"], np.float32),
+              W1=w(inp["W1"]), W2=w(inp["W2"]), anchor=t(inp["anchor"], np.int32),
+              u_draft=t(inp["u_draft"], np.float32), u_accept=t(inp["u_accept"], np.float32),
+              u_final=t(inp["u_final"], np.float32),
+              conf=None if inp["conf"] is None else t(inp["conf"], np.float32),
+              sps=None if inp["sps"] is None else t(inp["sps"], np.float32))
+    del inp
+    ws = D.new_workspace(R, g, V, r, dev)
+    T = a.temperature
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+
+    # one eager round: reference outputs and workload statistics
+    with torch.cuda.stream(stream):
+        ref = D.run_round(dd, T, ws)
+    torch.cuda.synchronize()
+    if D.device_error(ws) != 0:
+        raise RuntimeError("device-side data error in the benchmark inputs")
+    ref = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in ref.items()}
+
+    lib = D.load_library()
+    use_graph = not a.eager
+    graph = None
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            out = D.run_round(dd, T, ws)
+        torch.cuda.synchronize()
+        # replays must reproduce the eager round exactly, replay after replay
+        for _ in range(3):
+            graph.replay()
+            torch.cuda.synchronize()
+            for k in ("draft_tokens", "out_tokens", "accept_len", "verify_len"):
+                if ref[k] is not None and not torch.equal(out[k], ref[k]):
+                    raise RuntimeError(f"graph replay differs from the eager round in {k}")
+
+    def one_round():
+        if use_graph:
+            graph.replay()
+        else:
+            D.run_round(dd, T, ws)
+
+    def timed(fn, n):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            t0.record()
+            for _ in range(n):
+                fn()
+            t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n
+
+    with torch.cuda.stream(stream):
+        for _ in range(a.warmup):
+            one_round()
+    ms = timed(one_round, a.steps)
+
+    # Second timed pass, eager launches: HIP events recorded by the library's
+    # launch hook around every launch of the dominant kernel, on its stream.
+    n_prof = g * a.steps
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(n_prof)]
+    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(n_prof)]
+    with torch.cuda.stream(stream):
+        for e in ev_s + ev_e:
+            e.record()
+    torch.cuda.synchronize()
+    ArrT = ctypes.c_void_p * n_prof
+    starts = ArrT(*[e.cuda_event for e in ev_s])
+    stops = ArrT(*[e.cuda_event for e in ev_e])
+    lib.dspark_profile_arm(KID_DRAFT_PARTIALS, starts, stops, n_prof)
+    with torch.cuda.stream(stream):
+        ms_eager = timed(lambda: D.run_round(dd, T, ws), a.steps)
+    used = lib.dspark_profile_disarm()
+    k1_ms = sum(s.elapsed_time(e) for s, e in zip(ev_s[:used], ev_e[:used])) / max(used, 1)
+
+    A = ref["accept_len"].cpu().numpy().astype(np.int64)
+    L = (ref["verify_len"].cpu().numpy() if ref["verify_len"] is not None else np.full(R, g))
+    tokens = int((A + 1).sum())
+    b_min, b_sched = algorithmic_bytes(d, tokens, int((L + 1).sum()))
+    wb = 2 if d["w_dtype"] == "bf16" else 4
+    k1_bytes = 4 * R * V + wb * r * V          # base slice + W2, one draft step
+    k1_flops = 2 * R * r * V
+    traffic = stored_traffic(PROFILE_KERNEL, f"R{R}_g{g}_V{V}_r{r}")
+    return dict(
+        ms=ms, tokens=tokens, A=A, L=L, n_admitted=(int(ref["n_admitted"].cpu()[0])
+                                                    if ref["n_admitted"] is not None else None),
+        b_min=b_min, b_sched=b_sched, k1_ms=k1_ms, k1_bytes=k1_bytes, k1_flops=k1_flops,
+        traffic=traffic, graph=use_graph, cfg=d, ms_eager=ms_eager, n_k1=used)
+
+
+def main():
+    a = parse()
+    if a.cpu_baseline_worker:
+        cpu_worker(a)
+        return 0
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU: this build runs on a single MI355X and has no "
+              f"multi-GPU path (asked for --gpus {a.gpus}).", file=sys.stderr)
+        return 2
+    rank = int(os.environ.get("RANK", "0"))
+    gb = gpu_bench(a)
+    d = gb["cfg"]
+    ms = gb["ms"]
+    achieved = gb["k1_bytes"] / (gb["k1_ms"] * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": gb["tokens"] / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 x bf16 -> f32 (MFMA), f32 softmax, f64 cross-tile scans",
+        "data": "synthetic (seeded NumPy; stands in for the pages' benchmark suites)",
+        "config": {"workload": f"{d['name']}: R={d['R']} gamma={d['gamma']} V={d['V']} r={d['r']} "
+                               f"{d['w_dtype']} factors, base {d['base']}, target {d['target']}, "
+                               f"conf {d['conf']}, table {d['table']}",
+                   "R": d["R"], "gamma": d["gamma"], "V": d["V"], "r": d["r"],
+                   "temperature": a.temperature, "launch": "hip graph" if gb["graph"] else "eager"},
+        "ms_per_step_eager": gb["ms_eager"],
+        "rounds_per_s": 1e3 / ms,
+        "tokens_per_round": gb["tokens"],
+        "mean_accept_len": float(gb["A"].mean()),
+        "mean_verify_len": float(gb["L"].mean()),
+        "n_admitted": gb["n_admitted"],
+        "round_hbm": {
+            "bytes_min": gb["b_min"], "bytes_scheduled": gb["b_sched"],
+            "achieved_min_GBs": gb["b_min"] / (ms * 1e-3) / 1e9,
+            "frac_min": gb["b_min"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "frac_scheduled": gb["b_sched"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": PROFILE_KERNEL, "achieved": achieved, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+            "traffic": gb["traffic"], "launch_us": gb["k1_ms"] * 1e3, "launches_timed": gb["n_k1"],
+            "algorithmic_bytes_per_launch": gb["k1_bytes"],
+        },
+        "mfma": {
+            "kernel": PROFILE_KERNEL,
+            "achieved": gb["k1_flops"] / (gb["k1_ms"] * 1e-3) / 1e12,
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": gb["k1_flops"] / (gb["k1_ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        },
+    }
+    if not a.no_cpu_baseline and rank == 0:
+        res["cpu_baseline"] = cpu_baseline(a)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,31 @@
+"""DSpark draft -> schedule -> verify round on AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libdspark.so`` (include/dspark.h).
+It only marshals arguments: it checks dtypes, devices, shapes and contiguity
+of torch tensors, passes raw device pointers and the current HIP stream, and
+turns negative status codes into exceptions.  Every step of the round runs in
+the HIP kernels of the library; there is no fallback path.
+"""
+
+from ._binding import (  # noqa: F401
+    DSPARK_W_BF16,
+    DSPARK_W_F32,
+    DERR_BITS,
+    DSparkError,
+    lib_path,
+    load_library,
+    workspace_size,
+    new_workspace,
+    workspace_init,
+    device_error,
+    draft,
+    schedule,
+    verify,
+    run_round,
+)
+
+__all__ = [
+    "DSPARK_W_BF16", "DSPARK_W_F32", "DERR_BITS", "DSparkError", "lib_path", "load_library",
+    "workspace_size", "new_workspace", "workspace_init", "device_error", "draft", "schedule",
+    "verify", "run_round",
+]

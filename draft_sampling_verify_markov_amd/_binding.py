@@ -1,0 +1,206 @@
+"""ctypes marshalling for libdspark.so (see include/dspark.h for the contract)."""
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+DSPARK_W_BF16, DSPARK_W_F32 = 0, 1
+STATUS = {0: "DSPARK_OK", -1: "DSPARK_EINVAL", -2: "DSPARK_ENOSPC", -3: "DSPARK_EHIP"}
+DERR_BITS = {1: "NONFINITE", 2: "UNIFORM", 4: "CONF", 8: "TOKEN", 16: "PROB", 32: "LENGTH"}
+
+_lib = None
+
+
+class DSparkError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} returned {status} ({STATUS.get(status, 'unknown')})")
+        self.status = status
+
+
+def lib_path():
+    return os.environ.get("DSPARK_LIB", os.path.join(HERE, "libdspark.so"))
+
+
+def load_library():
+    """Load libdspark.so once.  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m draft_sampling_verify_markov_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I, Z, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    lib.dspark_workspace_size.argtypes = [I, I, I, I]
+    lib.dspark_workspace_size.restype = Z
+    lib.dspark_workspace_init.argtypes = [P, Z, P]
+    lib.dspark_workspace_init.restype = I
+    lib.dspark_device_error.argtypes = [P, Z, ctypes.POINTER(ctypes.c_int32), P]
+    lib.dspark_device_error.restype = I
+    lib.dspark_status_string.argtypes = [I]
+    lib.dspark_status_string.restype = ctypes.c_char_p
+    lib.dspark_draft.argtypes = [P, P, P, I, P, P, I, I, I, I, F, P, P, P, P, Z, P]
+    lib.dspark_draft.restype = I
+    lib.dspark_schedule.argtypes = [P, P, I, I, I, P, P, P, P, Z, P]
+    lib.dspark_schedule.restype = I
+    lib.dspark_verify.argtypes = [P, P, P, P, I, P, P, P, P, P, P, P, I, I, I, I, F, P, P, P, P, Z, P]
+    lib.dspark_verify.restype = I
+    lib.dspark_profile_arm.argtypes = [I, P, P, I]
+    lib.dspark_profile_arm.restype = I
+    lib.dspark_profile_disarm.argtypes = []
+    lib.dspark_profile_disarm.restype = I
+    _lib = lib
+    return lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise DSparkError(fn, status)
+
+
+def _ptr(t, dtype, shape, name, device):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _wtype(W):
+    if W.dtype == torch.bfloat16 or W.dtype in (torch.int16, torch.uint16):
+        return DSPARK_W_BF16
+    if W.dtype == torch.float32:
+        return DSPARK_W_F32
+    raise TypeError(f"W1/W2 dtype {W.dtype}: expected bfloat16 (or its uint16 bits) or float32")
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def workspace_size(R, gamma, V, r):
+    n = load_library().dspark_workspace_size(R, gamma, V, r)
+    if n == 0:
+        raise ValueError(f"sizes outside the library limits: R={R} gamma={gamma} V={V} r={r}")
+    return n
+
+
+def new_workspace(R, gamma, V, r, device):
+    """Allocate (torch) and clear a workspace for these sizes."""
+    ws = torch.empty(workspace_size(R, gamma, V, r), dtype=torch.uint8, device=device)
+    workspace_init(ws)
+    return ws
+
+
+def workspace_init(ws):
+    _check("dspark_workspace_init",
+           load_library().dspark_workspace_init(ws.data_ptr(), ws.numel(), _stream(ws.device)))
+
+
+def device_error(ws):
+    """Return (and clear) the device-side data error bits of a workspace."""
+    v = ctypes.c_int32(0)
+    _check("dspark_device_error", load_library().dspark_device_error(
+        ws.data_ptr(), ws.numel(), ctypes.byref(v), _stream(ws.device)))
+    return int(v.value)
+
+
+def draft(base, W1, W2, anchor, u_draft, temperature, ws, out=None):
+    """dspark_draft.  Returns (draft_tokens, draft_probs, draft_stats)."""
+    R, g, V = base.shape
+    r = W1.shape[1]
+    dev = base.device
+    wt = _wtype(W1)
+    wdt = W1.dtype
+    if out is None:
+        out = (torch.empty((R, g), dtype=torch.int32, device=dev),
+               torch.empty((R, g), dtype=torch.float32, device=dev),
+               torch.empty((R, g, 2), dtype=torch.float32, device=dev))
+    tok, prob, stats = out
+    args = (_ptr(base, torch.float32, (R, g, V), "base", dev),
+            _ptr(W1, wdt, (V, r), "W1", dev), _ptr(W2, wdt, (r, V), "W2", dev), wt,
+            _ptr(anchor, torch.int32, (R,), "anchor", dev),
+            _ptr(u_draft, torch.float32, (R, g), "u_draft", dev),
+            R, g, V, r, float(temperature),
+            _ptr(tok, torch.int32, (R, g), "draft_tokens", dev),
+            _ptr(prob, torch.float32, (R, g), "draft_probs", dev),
+            _ptr(stats, torch.float32, (R, g, 2), "draft_stats", dev),
+            ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("dspark_draft", load_library().dspark_draft(*args))
+    return tok, prob, stats
+
+
+def schedule(conf, sps, ws, out=None, with_cum=True):
+    """dspark_schedule.  Returns (verify_len, n_admitted[1], cum_conf or None)."""
+    R, g = conf.shape
+    dev = conf.device
+    if out is None:
+        out = (torch.empty(R, dtype=torch.int32, device=dev),
+               torch.empty(1, dtype=torch.int32, device=dev),
+               torch.empty((R, g), dtype=torch.float32, device=dev) if with_cum else None)
+    L, n, a = out
+    args = (_ptr(conf, torch.float32, (R, g), "conf", dev),
+            _ptr(sps, torch.float32, (sps.numel(),), "sps", dev), R, g, sps.numel(),
+            _ptr(L, torch.int32, (R,), "verify_len", dev), _ptr(n, torch.int32, (1,), "n_admitted", dev),
+            _ptr(a, torch.float32, (R, g), "cum_conf", dev),
+            ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("dspark_schedule", load_library().dspark_schedule(*args))
+    return L, n, a
+
+
+def verify(target, base, W1, W2, anchor, draft_tokens, draft_probs, draft_stats, verify_len,
+           u_accept, u_final, temperature, ws, out=None, with_probs=True):
+    """dspark_verify.  Returns (out_tokens, accept_len, target_probs or None)."""
+    R, g1, V = target.shape
+    g = g1 - 1
+    r = W1.shape[1]
+    dev = target.device
+    wt = _wtype(W1)
+    wdt = W1.dtype
+    if out is None:
+        out = (torch.empty((R, g + 1), dtype=torch.int32, device=dev),
+               torch.empty(R, dtype=torch.int32, device=dev),
+               torch.empty((R, g), dtype=torch.float32, device=dev) if with_probs else None)
+    ot, al, tp = out
+    args = (_ptr(target, torch.float32, (R, g + 1, V), "target", dev),
+            _ptr(base, torch.float32, (R, g, V), "base", dev),
+            _ptr(W1, wdt, (V, r), "W1", dev), _ptr(W2, wdt, (r, V), "W2", dev), wt,
+            _ptr(anchor, torch.int32, (R,), "anchor", dev),
+            _ptr(draft_tokens, torch.int32, (R, g), "draft_tokens", dev),
+            _ptr(draft_probs, torch.float32, (R, g), "draft_probs", dev),
+            _ptr(draft_stats, torch.float32, (R, g, 2), "draft_stats", dev),
+            _ptr(verify_len, torch.int32, (R,), "verify_len", dev),
+            _ptr(u_accept, torch.float32, (R, g), "u_accept", dev),
+            _ptr(u_final, torch.float32, (R,), "u_final", dev),
+            R, g, V, r, float(temperature),
+            _ptr(ot, torch.int32, (R, g + 1), "out_tokens", dev),
+            _ptr(al, torch.int32, (R,), "accept_len", dev),
+            _ptr(tp, torch.float32, (R, g), "target_probs", dev),
+            ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("dspark_verify", load_library().dspark_verify(*args))
+    return ot, al, tp
+
+
+def run_round(dev_inputs, temperature, ws, use_scheduler=True):
+    """draft -> schedule -> verify on a dict of device tensors (see bench.py)."""
+    d = dev_inputs
+    tok, prob, stats = draft(d["base"], d["W1"], d["W2"], d["anchor"], d["u_draft"], temperature, ws)
+    L = None
+    n = None
+    if use_scheduler and d.get("conf") is not None:
+        L, n, _ = schedule(d["conf"], d["sps"], ws, with_cum=False)
+    ot, al, tp = verify(d["target"], d["base"], d["W1"], d["W2"], d["anchor"], tok, prob, stats, L,
+                        d["u_accept"], d["u_final"], temperature, ws)
+    return dict(draft_tokens=tok, draft_probs=prob, draft_stats=stats, verify_len=L, n_admitted=n,
+                out_tokens=ot, accept_len=al, target_probs=tp)

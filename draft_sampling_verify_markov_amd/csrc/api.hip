@@ -1,0 +1,167 @@
+// C ABI entry points: host-side argument checks, workspace queries and
+// dispatch to the draft / schedule / verify launchers.
+#include "select.h"
+
+namespace dspark {
+int draft_impl(const float* base, const void* W1, const void* W2, dspark_wtype w_type,
+               const int32_t* anchor, const float* u_draft, int R, int gamma, int V, int r, float T,
+               int32_t* tokens, float* probs, float* stats, void* ws, hipStream_t stream);
+int schedule_impl(const float* conf, const float* sps, int R, int gamma, int n_table,
+                  int32_t* verify_len, int32_t* n_admitted, float* cum_conf, void* ws,
+                  hipStream_t stream);
+int verify_impl(const float* target, const float* base, const void* W1, const void* W2,
+                dspark_wtype w_type, const int32_t* anchor, const int32_t* dtok, const float* dprob,
+                const float* dstats, const int32_t* vlen, const float* u_acc, const float* u_fin,
+                int R, int gamma, int V, int r, float T, int32_t* out_tokens, int32_t* accept_len,
+                float* target_probs, void* ws, hipStream_t stream);
+
+__global__ void k_fill_i32(int32_t* p, int n, int32_t v) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// Largest element count any kernel indexes with 32-bit products.
+constexpr long long MAX_ELEMS = (1LL << 31) - 1;
+
+static bool sizes_ok(int R, int gamma, int V, int r) {
+  if (R < 1 || gamma < 1 || gamma > DSPARK_MAX_GAMMA) return false;
+  if (V < 8 || (V % 8) != 0 || V > MAX_V) return false;
+  if (r < 16 || r > DSPARK_MAX_RANK || (r % 16) != 0) return false;
+  if ((long long)R * (gamma + 1) * ceil_div(V, VSEG) > MAX_ELEMS) return false;
+  return true;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct ProfState {
+  int kid = 0;
+  hipEvent_t* starts = nullptr;
+  hipEvent_t* stops = nullptr;
+  int n = 0, used = 0;
+};
+static thread_local ProfState prof;
+
+void prof_before(int kid, hipStream_t stream) {
+  if (prof.kid == kid && prof.used < prof.n) (void)hipEventRecord(prof.starts[prof.used], stream);
+}
+void prof_after(int kid, hipStream_t stream) {
+  if (prof.kid == kid && prof.used < prof.n) (void)hipEventRecord(prof.stops[prof.used++], stream);
+}
+
+static int check_ws(void* ws, size_t bytes, int R, int gamma, int V) {
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return DSPARK_EINVAL;
+  if (bytes < ws_layout(R, gamma, V).total) return DSPARK_ENOSPC;
+  return DSPARK_OK;
+}
+
+}  // namespace dspark
+
+using namespace dspark;
+
+extern "C" {
+
+size_t dspark_workspace_size(int R, int gamma, int V, int r) {
+  if (!sizes_ok(R, gamma, V, r)) return 0;
+  return ws_layout(R, gamma, V).total;
+}
+
+int dspark_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!workspace || workspace_bytes < 256) return DSPARK_EINVAL;
+  hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, stream, static_cast<int32_t*>(workspace), 64,
+                     0);
+  return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
+}
+
+int dspark_device_error(void* workspace, size_t workspace_bytes, int32_t* host_bits,
+                        hipStream_t stream) {
+  if (!workspace || !host_bits || workspace_bytes < 256) return DSPARK_EINVAL;
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, workspace, sizeof(v), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return DSPARK_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return DSPARK_EHIP;
+  *host_bits = v;
+  hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, stream, static_cast<int32_t*>(workspace), 1,
+                     0);
+  if (hipGetLastError() != hipSuccess) return DSPARK_EHIP;
+  return hipStreamSynchronize(stream) == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
+}
+
+int dspark_profile_arm(int kid, hipEvent_t* starts, hipEvent_t* stops, int n) {
+  if (kid < DSPARK_KID_DRAFT_PARTIALS || kid > DSPARK_KID_VERIFY_FINALIZE || !starts || !stops ||
+      n < 1)
+    return DSPARK_EINVAL;
+  prof.kid = kid;
+  prof.starts = starts;
+  prof.stops = stops;
+  prof.n = n;
+  prof.used = 0;
+  return DSPARK_OK;
+}
+
+int dspark_profile_disarm(void) {
+  const int used = prof.used;
+  prof = ProfState();
+  return used;
+}
+
+const char* dspark_status_string(int status) {
+  switch (status) {
+    case DSPARK_OK: return "DSPARK_OK";
+    case DSPARK_EINVAL: return "DSPARK_EINVAL: invalid argument";
+    case DSPARK_ENOSPC: return "DSPARK_ENOSPC: workspace too small";
+    case DSPARK_EHIP: return "DSPARK_EHIP: HIP runtime or launch failure";
+    default: return "unknown dspark status";
+  }
+}
+
+int dspark_draft(const float* base, const void* W1, const void* W2, dspark_wtype w_type,
+                 const int32_t* anchor, const float* u_draft, int R, int gamma, int V, int r,
+                 float temperature, int32_t* draft_tokens, float* draft_probs, float* draft_stats,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!sizes_ok(R, gamma, V, r)) return DSPARK_EINVAL;
+  if (w_type != DSPARK_W_BF16 && w_type != DSPARK_W_F32) return DSPARK_EINVAL;
+  if (!base || !W1 || !W2 || !anchor || !u_draft || !draft_tokens || !draft_probs || !draft_stats)
+    return DSPARK_EINVAL;
+  if (!aligned16(base) || !aligned16(W1) || !aligned16(W2)) return DSPARK_EINVAL;
+  if (!(temperature >= 0.f) || __builtin_isinf(temperature)) return DSPARK_EINVAL;
+  const int wsr = check_ws(workspace, workspace_bytes, R, gamma, V);
+  if (wsr != DSPARK_OK) return wsr;
+  return draft_impl(base, W1, W2, w_type, anchor, u_draft, R, gamma, V, r, temperature,
+                    draft_tokens, draft_probs, draft_stats, workspace, stream);
+}
+
+int dspark_schedule(const float* conf, const float* sps, int R, int gamma, int n_table,
+                    int32_t* verify_len, int32_t* n_admitted, float* cum_conf, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  if (R < 1 || gamma < 1 || gamma > DSPARK_MAX_GAMMA || (long long)R * gamma > DSPARK_MAX_POOL)
+    return DSPARK_EINVAL;
+  if (n_table < 1) return DSPARK_EINVAL;
+  if (!conf || !sps || !verify_len || !n_admitted) return DSPARK_EINVAL;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DSPARK_EINVAL;
+  if (workspace_bytes < 256) return DSPARK_ENOSPC;
+  return schedule_impl(conf, sps, R, gamma, n_table, verify_len, n_admitted, cum_conf, workspace,
+                       stream);
+}
+
+int dspark_verify(const float* target, const float* base, const void* W1, const void* W2,
+                  dspark_wtype w_type, const int32_t* anchor, const int32_t* draft_tokens,
+                  const float* draft_probs, const float* draft_stats, const int32_t* verify_len,
+                  const float* u_accept, const float* u_final, int R, int gamma, int V, int r,
+                  float temperature, int32_t* out_tokens, int32_t* accept_len, float* target_probs,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!sizes_ok(R, gamma, V, r)) return DSPARK_EINVAL;
+  if (w_type != DSPARK_W_BF16 && w_type != DSPARK_W_F32) return DSPARK_EINVAL;
+  if (!target || !base || !W1 || !W2 || !anchor || !draft_tokens || !draft_probs || !draft_stats ||
+      !u_accept || !u_final || !out_tokens || !accept_len)
+    return DSPARK_EINVAL;
+  if (!aligned16(target) || !aligned16(base) || !aligned16(W1) || !aligned16(W2))
+    return DSPARK_EINVAL;
+  if (!(temperature >= 0.f) || __builtin_isinf(temperature)) return DSPARK_EINVAL;
+  const int wsr = check_ws(workspace, workspace_bytes, R, gamma, V);
+  if (wsr != DSPARK_OK) return wsr;
+  return verify_impl(target, base, W1, W2, w_type, anchor, draft_tokens, draft_probs, draft_stats,
+                     verify_len, u_accept, u_final, R, gamma, V, r, temperature, out_tokens,
+                     accept_len, target_probs, workspace, stream);
+}
+
+}  // extern "C"

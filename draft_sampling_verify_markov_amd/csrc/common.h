@@ -1,0 +1,474 @@
+// Shared device helpers of the DSpark round kernels (gfx950 / CDNA4, wave64).
+//
+// Contents: vector types, an accurate fp32 exp, wave/block reductions, the
+// Markov bias block (bf16 MFMA or fp32 FMA), and the workspace layout shared
+// by the host entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dspark.h"
+
+namespace dspark {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Column tile of the draft/residual partials: one workgroup of 4 waves, each
+// wave owns 64 consecutive columns.
+constexpr int TILE = 256;
+constexpr int WCOLS = 64;
+// Rows of the gathered W1 block held in LDS per pass (4 MFMA row blocks of 32).
+constexpr int RCH = 128;
+// Column tile of the target-row partials (one wave, 16 floats per lane) and
+// the column segment one verify-stream workgroup covers (4 such tiles).
+constexpr int VTILE = 1024;
+constexpr int VSEG = 4 * VTILE;
+// Sentinel "no rejection" position in the per-request rejection slot.
+constexpr int NO_REJECT = 1 << 30;
+
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// exp(x) for the softmax weights.  2^(x log2 e) with the rounding error of the
+// product x*log2(e) carried separately (split-constant method), so the result
+// keeps v_exp_f32's ~1 ulp accuracy for the arguments used here (x <= ~0).
+// Arguments below -100 return 0 (also -inf); NaN propagates.
+__device__ __forceinline__ float exp_acc(float x) {
+  const float L2E = 1.44269502162933349609375f;  // fp32 nearest to log2(e)
+  const float L2E_LO = 1.925963033500011e-8f;    // log2(e) - L2E
+  const float LN2 = 0.693147180559945309f;
+  float t = x * L2E;
+  float err = fmaf(x, L2E, -t) + x * L2E_LO;
+  float e = __builtin_amdgcn_exp2f(t);
+  float r = fmaf(e, err * LN2, e);
+  return (x < -100.f) ? 0.f : r;
+}
+
+__device__ __forceinline__ bool is_bad(float x) { return !(x == x) || __builtin_isinf(x); }
+
+// ---------------------------------------------------------------------------
+// cross-lane helpers (wave64)
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+// (value, index) maximum with the lowest index on ties.
+__device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
+  if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    float v2 = __shfl_xor(v, o);
+    int i2 = __shfl_xor(i, o);
+    argmax_merge(v, i, v2, i2);
+  }
+}
+
+// Block-wide exclusive scan of one value per thread (blockDim.x == 256):
+// thread t gets the sum of the values of threads 0..t-1, computed by a fixed
+// tree (deterministic).  `tmp` is __shared__ T[256].
+template <typename T>
+__device__ inline T block_exscan_256(T v, T* tmp) {
+  const int t = threadIdx.x;
+  tmp[t] = v;
+  __syncthreads();
+  const T shifted = (t > 0) ? tmp[t - 1] : T(0);
+  __syncthreads();
+  tmp[t] = shifted;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const T add = (t >= o) ? tmp[t - o] : T(0);
+    __syncthreads();
+    tmp[t] += add;
+    __syncthreads();
+  }
+  const T ex = tmp[t];
+  __syncthreads();
+  return ex;
+}
+
+__device__ __forceinline__ void raise_err(int32_t* err, int bits) { atomicOr(err, bits); }
+
+__device__ __forceinline__ int checked_token(int tok, int V, int32_t* err) {
+  if (tok < 0 || tok >= V) {
+    raise_err(err, DSPARK_DERR_TOKEN);
+    return 0;
+  }
+  return tok;
+}
+__device__ __forceinline__ float checked_uniform(float u, int32_t* err) {
+  if (!(u >= 0.f && u < 1.f)) {
+    raise_err(err, DSPARK_DERR_UNIFORM);
+    return 0.f;
+  }
+  return u;
+}
+
+// Streaming loads (non-temporal: logit rows and W2 are read once per pass).
+__device__ __forceinline__ f32x4 ld_stream4(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+__device__ __forceinline__ uint32_t ld_stream_u32(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+
+// Raw buffer loads: a uniform (SGPR) resource, one 32-bit per-lane byte offset
+// and a uniform byte offset per load, so long unrolled load sequences cost one
+// VGPR of address instead of a 64-bit address pair each.  Offsets at or past
+// num_records read 0.  AUX_NT marks the load non-temporal.
+constexpr int AUX_NT = 2;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, size_t bytes) {
+  const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ uint32_t buf_u32(rsrc_t rs, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(rs, (int)voff, (int)soff, AUX_NT);
+}
+template <int AUX = AUX_NT>
+__device__ __forceinline__ u32x4 buf_u32x4(rsrc_t rs, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff, (int)soff, AUX);
+}
+
+// ---------------------------------------------------------------------------
+// Markov bias block.
+//
+// Computes, for up to 4 row blocks of 32 requests (rows of the LDS block A,
+// which holds the gathered W1 rows) and the 64 columns [cbase, cbase + 64) a
+// wave owns, bias[row][col] = sum_k A[row][k] * W2[k][col] with fp32
+// accumulation, in the MFMA 32x32x16 output layout:
+//
+//   acc[rb][p][t], lane l = 32 h + j:
+//     row = 32 rb + j,   col = cbase + 16 (t / 4) + 8 h + 2 (t % 4) + p
+//
+// The W2 operand is loaded as dwords (columns col, col+1 of one k row), which
+// gives two MFMA operands per load (p = 0: even columns, p = 1: odd columns):
+// each load instruction reads 2 x 128 contiguous bytes.  Columns >= V (V is a
+// multiple of 8) contribute zeros.
+//
+// load() issues the loads of the whole k range at once (one memory round trip;
+// 8 KS dwords per lane) and mma() consumes them, so a caller can put other
+// loads in flight between the two.  KS (a power of two >= r/16) is a template
+// parameter so the fragment stays in registers; loads are branch-free (invalid
+// addresses are clamped to valid memory and the value masked).
+constexpr int MAX_KS = DSPARK_MAX_RANK / 16;
+
+template <typename WT>
+struct BiasBlock;
+
+template <>
+struct BiasBlock<uint16_t> {
+  static constexpr int APAD = 8;  // bf16 elements of LDS row padding
+  template <int KS>
+  struct Frag {
+    uint32_t w[KS][8];
+  };
+  template <int KS>
+  __device__ static __forceinline__ void load(Frag<KS>& F, const uint16_t* __restrict__ W2, int V,
+                                              int r, int cbase) {
+    const int lane = threadIdx.x & 63, j = lane & 31, h = lane >> 5;
+    const int col = cbase + 2 * j;
+    const bool cv = col < V;
+    const rsrc_t rs = make_rsrc(W2, (size_t)r * V * 2);
+    const uint32_t voff = (uint32_t)(8 * h * V + (cv ? col : 0)) * 2u;
+    const int nks = r / 16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+      const int kk = min(ks, nks - 1);
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const uint32_t x = buf_u32(rs, voff, (uint32_t)((kk * 16 + e) * V) * 2u);
+        F.w[ks][e] = cv ? x : 0u;
+      }
+    }
+  }
+  template <int KS>
+  __device__ static __forceinline__ void operands(const Frag<KS>& F, int ks, bf16x8& a0, bf16x8& a1) {
+    u32x4 lo, hi;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      lo[e] = (F.w[ks][2 * e] & 0xFFFFu) | (F.w[ks][2 * e + 1] << 16);
+      hi[e] = (F.w[ks][2 * e] >> 16) | (F.w[ks][2 * e + 1] & 0xFFFF0000u);
+    }
+    a0 = __builtin_bit_cast(bf16x8, lo);
+    a1 = __builtin_bit_cast(bf16x8, hi);
+  }
+  // B operand row block: rows (rb*32 + j) of A_lds.
+  template <int KS>
+  __device__ static __forceinline__ void mma(const Frag<KS>& F, int r, const uint16_t* A_lds,
+                                             int a_stride, int nrb, f32x16 (&acc)[4][2]) {
+    const int lane = threadIdx.x & 63, j = lane & 31, h = lane >> 5;
+    const int nks = r / 16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+      if (ks < nks) {
+        bf16x8 a0, a1;
+        operands(F, ks, a0, a1);
+#pragma unroll
+        for (int rb = 0; rb < 4; rb++) {
+          if (rb < nrb) {
+            const u32x4 bb =
+                *reinterpret_cast<const u32x4*>(A_lds + (rb * 32 + j) * a_stride + ks * 16 + 8 * h);
+            const bf16x8 b = __builtin_bit_cast(bf16x8, bb);
+            acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc[rb][0], 0, 0, 0);
+            acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[rb][1], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+  // W1 row fragments of one request (lanes with j == 0 hold W1[tok][ks*16 + 8h .. +8],
+  // the others zero) for mma_row.
+  template <int KS>
+  struct Row {
+    u32x4 b[KS];
+  };
+  template <int KS>
+  __device__ static __forceinline__ void load_row(Row<KS>& B, const uint16_t* __restrict__ W1, int r,
+                                                  int tok) {
+    const int lane = threadIdx.x & 63, j = lane & 31, h = lane >> 5;
+    const int nks = r / 16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+      const int kk = min(ks, nks - 1);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(W1 + (size_t)tok * r + kk * 16 + 8 * h);
+      B.b[ks] = (j == 0 && ks < nks) ? x : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  // Output row 0 of row block 0 (the request whose W1 row is in B).
+  template <int KS>
+  __device__ static __forceinline__ void mma_row(const Frag<KS>& F, int r, const Row<KS>& B,
+                                                 f32x16 (&acc)[2]) {
+    const int nks = r / 16;
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+      if (ks < nks) {
+        bf16x8 a0, a1;
+        operands(F, ks, a0, a1);
+        const bf16x8 bb = __builtin_bit_cast(bf16x8, B.b[ks]);
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bb, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bb, acc[1], 0, 0, 0);
+      }
+    }
+  }
+};
+
+// fp32 factors: same lane/element mapping, scalar FMA in ascending k.  W2 is
+// read inside mma (the fp32 path is the small-workload path).
+template <>
+struct BiasBlock<float> {
+  static constexpr int APAD = 4;
+  template <int KS>
+  struct Frag {
+    const float* W2;
+    int V, cbase;
+  };
+  template <int KS>
+  __device__ static __forceinline__ void load(Frag<KS>& F, const float* __restrict__ W2, int V, int,
+                                              int cbase) {
+    F.W2 = W2;
+    F.V = V;
+    F.cbase = cbase;
+  }
+  template <int KS>
+  __device__ static __forceinline__ void w2_at(const Frag<KS>& F, int k, float (&w)[4][2][4]) {
+    const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+      const int c0 = F.cbase + 16 * g + 8 * h;
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+#pragma unroll
+        for (int p = 0; p < 2; p++) {
+          const int c = c0 + 2 * q + p;
+          w[g][p][q] = (c < F.V) ? F.W2[(size_t)k * F.V + c] : 0.f;
+        }
+    }
+  }
+  template <int KS>
+  __device__ static inline void mma(const Frag<KS>& F, int r, const float* A_lds, int a_stride,
+                                    int nrb, f32x16 (&acc)[4][2]) {
+    const int j = (threadIdx.x & 63) & 31;
+    for (int k = 0; k < r; k++) {
+      float w[4][2][4];
+      w2_at(F, k, w);
+#pragma unroll
+      for (int rb = 0; rb < 4; rb++) {
+        if (rb < nrb) {
+          const float a = A_lds[(rb * 32 + j) * a_stride + k];
+#pragma unroll
+          for (int g = 0; g < 4; g++)
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+#pragma unroll
+              for (int p = 0; p < 2; p++) acc[rb][p][4 * g + q] = fmaf(a, w[g][p][q], acc[rb][p][4 * g + q]);
+        }
+      }
+    }
+  }
+  template <int KS>
+  struct Row {
+    const float* w1;
+  };
+  template <int KS>
+  __device__ static __forceinline__ void load_row(Row<KS>& B, const float* __restrict__ W1, int r,
+                                                  int tok) {
+    B.w1 = W1 + (size_t)tok * r;
+  }
+  template <int KS>
+  __device__ static inline void mma_row(const Frag<KS>& F, int r, const Row<KS>& B,
+                                        f32x16 (&acc)[2]) {
+    for (int k = 0; k < r; k++) {
+      float w[4][2][4];
+      w2_at(F, k, w);
+      const float a = B.w1[k];
+#pragma unroll
+      for (int g = 0; g < 4; g++)
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+#pragma unroll
+          for (int p = 0; p < 2; p++) acc[p][4 * g + q] = fmaf(a, w[g][p][q], acc[p][4 * g + q]);
+    }
+  }
+};
+
+// Number of 16-wide k steps rounded up to a power of two (template dispatch).
+__host__ __device__ inline int ks_bucket(int r) {
+  const int n = r / 16;
+  return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : n <= 8 ? 8 : 16;
+}
+#define DSPARK_DISPATCH_KS(r, BODY)                  \
+  switch (ks_bucket(r)) {                            \
+    case 1: { constexpr int KS = 1; BODY; } break;   \
+    case 2: { constexpr int KS = 2; BODY; } break;   \
+    case 4: { constexpr int KS = 4; BODY; } break;   \
+    case 8: { constexpr int KS = 8; BODY; } break;   \
+    default: { constexpr int KS = 16; BODY; } break; \
+  }
+
+// Gather rows A[i] = W1[tok(i)] (i < nrows; the rest zero) into LDS: every
+// thread first issues all of its 16-byte loads (branch-free: a zero row loads
+// row 0 and is masked), then stores them.  tok(i) is supplied by a functor; a
+// negative token gives a zero row.  rows_cap * (r / EPV) must not exceed
+// 256 * PER, PER = the per-thread piece count (blockDim.x == 256).
+template <typename WT, int PER, typename TokF>
+__device__ __forceinline__ void gather_w1_rows(const WT* __restrict__ W1, int V, int r, int nrows,
+                                               int rows_cap, WT* A_lds, int a_stride, TokF tok_of) {
+  constexpr int EPV = 16 / sizeof(WT);  // elements per 16-byte piece
+  const int pieces = r / EPV;
+  const int total = rows_cap * pieces;
+  const rsrc_t rs = make_rsrc(W1, (size_t)V * r * sizeof(WT));
+  u32x4 v[PER];
+  int dst[PER];
+#pragma unroll
+  for (int i = 0; i < PER; i++) {
+    const int idx = threadIdx.x + 256 * i;
+    const int row = idx / pieces, pc = idx - row * pieces;
+    int t = -1;
+    if (idx < total && row < nrows) t = tok_of(row);
+    const u32x4 x = buf_u32x4<0>(rs, (uint32_t)(max(t, 0) * r + pc * EPV) * (uint32_t)sizeof(WT), 0u);
+    v[i] = (t >= 0) ? x : u32x4{0u, 0u, 0u, 0u};
+    dst[i] = (idx < total) ? row * a_stride + pc * EPV : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < PER; i++)
+    if (dst[i] >= 0) *reinterpret_cast<u32x4*>(A_lds + dst[i]) = v[i];
+}
+
+// Logit values of one row at the columns a lane holds in the bias-block
+// layout: out[p][t] for col = cbase + 16 (t/4) + 8 h + 2 (t%4) + p.  The rows
+// are addressed through a buffer resource `rs` anchored at a row-set start and
+// the lane's row byte offset `roff`.  Invalid rows/columns read as -inf.
+__device__ __forceinline__ void load_row_cols(rsrc_t rs, uint32_t roff, bool rowv, int V, int cbase,
+                                              float (&out)[2][16]) {
+  const int h = (threadIdx.x & 63) >> 5;
+  const int c0 = cbase + 8 * h;
+  const uint32_t voff = rowv ? roff + (uint32_t)c0 * 4u : 0u;
+#pragma unroll
+  for (int g = 0; g < 4; g++) {
+    const bool ok = rowv && c0 + 16 * g < V;
+    const f32x4 lo = __builtin_bit_cast(f32x4, buf_u32x4(rs, voff, (uint32_t)g * 64u));
+    const f32x4 hi = __builtin_bit_cast(f32x4, buf_u32x4(rs, voff, (uint32_t)g * 64u + 16u));
+    const float ninf = -INFINITY;
+    out[0][4 * g + 0] = ok ? lo[0] : ninf;
+    out[1][4 * g + 0] = ok ? lo[1] : ninf;
+    out[0][4 * g + 1] = ok ? lo[2] : ninf;
+    out[1][4 * g + 1] = ok ? lo[3] : ninf;
+    out[0][4 * g + 2] = ok ? hi[0] : ninf;
+    out[1][4 * g + 2] = ok ? hi[1] : ninf;
+    out[0][4 * g + 3] = ok ? hi[2] : ninf;
+    out[1][4 * g + 3] = ok ? hi[3] : ninf;
+  }
+}
+
+// Column (relative to cbase) of element (p, t) for a lane with half h.
+__device__ __forceinline__ int elem_col(int p, int t, int h) {
+  return 16 * (t >> 2) + 8 * h + 2 * (t & 3) + p;
+}
+
+// Tree sum of the 32 values a lane holds (fixed order: deterministic).
+__device__ __forceinline__ float tree_sum32(const float (&e)[2][16]) {
+  float s[16];
+#pragma unroll
+  for (int t = 0; t < 16; t++) s[t] = e[0][t] + e[1][t];
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+    for (int t = 0; t < w; t++) s[t] = s[t] + s[t + w];
+  return s[0];
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layout (identical on host and device).  All offsets 256-aligned.
+struct WsLayout {
+  size_t err;      // int32 error word
+  size_t trec;     // float4 [R][nt][2]     draft tile records (see select.h)
+  size_t rowstat;  // double2[R][gamma+1]   target row (max, sum) or (max, argmax)
+  size_t rej;      // int32  [R]            first rejected position (NO_REJECT if none)
+  size_t vpart;    // float2 [R][gamma+1][nvt] target 1024-column tile partials
+  size_t tx;       // float  [R][gamma]     target logit at the drafted token
+  size_t tp;       // float  [R][gamma]     p_k(x_k) of evaluated positions
+  size_t rrec;     // float4 [R][nt][2]     residual tile records
+  size_t total;
+};
+
+__host__ __device__ inline size_t ws_align(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__host__ __device__ inline WsLayout ws_layout(int R, int gamma, int V) {
+  WsLayout L;
+  const size_t nt = (size_t)ceil_div(V, TILE), nvt = (size_t)ceil_div(V, VTILE);
+  size_t o = 0;
+  L.err = o;      o = ws_align(o + 256);
+  L.trec = o;     o = ws_align(o + (size_t)R * nt * 32);
+  L.rowstat = o;  o = ws_align(o + (size_t)R * (gamma + 1) * 16);
+  L.rej = o;      o = ws_align(o + (size_t)R * 4);
+  L.vpart = o;    o = ws_align(o + (size_t)R * (gamma + 1) * nvt * 8);
+  L.tx = o;       o = ws_align(o + (size_t)R * gamma * 4);
+  L.tp = o;       o = ws_align(o + (size_t)R * gamma * 4);
+  L.rrec = o;     o = ws_align(o + (size_t)R * nt * 32);
+  L.total = o;
+  return L;
+}
+
+// Launch-timing hook (host side, thread-local): see dspark_profile_arm.
+void prof_before(int kid, hipStream_t stream);
+void prof_after(int kid, hipStream_t stream);
+
+template <typename T>
+__host__ __device__ inline T* ws_ptr(void* ws, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off);
+}
+
+}  // namespace dspark

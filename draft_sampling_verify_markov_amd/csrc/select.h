@@ -1,0 +1,193 @@
+// Wave-level inverse-CDF selection over tile records (one wave per request).
+//
+// A tile record describes TILE = 256 consecutive columns of one logit (or
+// residual) row as 8 floats: (m, s, s0, s1, s2, s3, 0, 0), where m is a shift
+// (the tile maximum, or 0 for residual mass), s = (s0 + s1) + (s2 + s3) and
+// s0..s3 are the masses of the four 64-column chunks relative to exp(m/T).
+// Selection draws the tile holding u * Z (Z = total mass, fp64) and then the
+// chunk inside it; the caller recomputes that chunk's 64 values and finishes
+// with wave_pick64.
+#pragma once
+
+#include "common.h"
+
+namespace dspark {
+
+// Largest tile count per lane held in registers: nt <= 64 * MAX_TPL, i.e.
+// V <= 64 * 16 * 256 = 262144.
+constexpr int MAX_TPL = 16;
+constexpr int MAX_V = 64 * MAX_TPL * TILE;
+
+struct TilePick {
+  int t;         // chosen tile
+  int w;         // chosen 64-column chunk in the tile
+  double rem;    // remaining mass inside the chunk (INFINITY: take the last positive column)
+  double scale;  // exp((m_t - M) / T): converts chunk values to the row's scale
+  double Z;      // total mass of the row (relative to exp(M / T))
+  float M;       // row shift
+  float mt;      // shift of the chosen tile
+};
+
+__device__ __forceinline__ double wave_excl_scan_d(double v, double* incl_out) {
+  const int lane = threadIdx.x & 63;
+  double incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  *incl_out = incl;
+  const double ex = __shfl_up(incl, 1);
+  return lane == 0 ? 0.0 : ex;
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+
+// recs: the row's records (2 float4 per tile).  use_shift: weights are
+// s * exp((m - M) / T) (softmax partials) or plain s (residual mass, m = 0).
+__device__ inline TilePick wave_select_tile(const float4* __restrict__ recs, int nt, bool use_shift,
+                                            double invTd, double u) {
+  const int lane = threadIdx.x & 63;
+  const int per = ceil_div(nt, 64);
+  const int t0 = min(nt, lane * per), t1 = min(nt, t0 + per);
+  float m[MAX_TPL], s[MAX_TPL];
+  float4 sw[MAX_TPL];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < MAX_TPL; i++) {
+    const int t = t0 + i;
+    const bool ok = (i < per) && (t < t1);
+    const int tc = ok ? t : 0;  // branch-free: clamped address, masked value
+    const float4 r0 = recs[2 * tc], r1 = recs[2 * tc + 1];
+    m[i] = ok ? r0.x : -INFINITY;
+    s[i] = ok ? r0.y : 0.f;
+    sw[i] = ok ? make_float4(r0.z, r0.w, r1.x, r1.y) : make_float4(0.f, 0.f, 0.f, 0.f);
+    mloc = fmaxf(mloc, m[i]);
+  }
+  const float M = use_shift ? wave_max(mloc) : 0.f;
+  double w[MAX_TPL];
+  double loc = 0.0;
+#pragma unroll
+  for (int i = 0; i < MAX_TPL; i++) {
+    w[i] = 0.0;
+    if (t0 + i < t1)
+      w[i] = use_shift ? (double)s[i] * exp(((double)m[i] - (double)M) * invTd) : (double)s[i];
+    loc += w[i];
+  }
+  double incl_unused;
+  const double ex = wave_excl_scan_d(loc, &incl_unused);
+  const int owner_last = (nt - 1) / per;
+  const double Z = __shfl(ex + loc, owner_last);
+  const double target = u * Z;
+
+  int found = 0x7fffffff, lastpos = -1;
+  double before = 0.0, cum = 0.0;
+  float fm = 0.f, lm = 0.f;
+  float4 fsw = make_float4(0.f, 0.f, 0.f, 0.f), lsw = fsw;
+#pragma unroll
+  for (int i = 0; i < MAX_TPL; i++) {
+    const int t = t0 + i;
+    if (t < t1) {
+      const double pp = cum;
+      cum += w[i];
+      if (found == 0x7fffffff && target < ex + cum) {
+        found = t;
+        before = ex + pp;
+        fm = m[i];
+        fsw = sw[i];
+      }
+      if (s[i] > 0.f) {
+        lastpos = t;
+        lm = m[i];
+        lsw = sw[i];
+      }
+    }
+  }
+  TilePick P;
+  P.Z = Z;
+  P.M = M;
+  const int tmin = wave_min_i(found);
+  float4 csw;
+  if (tmin != 0x7fffffff) {
+    const int owner = tmin / per;
+    P.t = tmin;
+    P.rem = __shfl(target - before, owner);
+    P.mt = __shfl(fm, owner);
+    csw = make_float4(__shfl(fsw.x, owner), __shfl(fsw.y, owner), __shfl(fsw.z, owner),
+                      __shfl(fsw.w, owner));
+  } else {
+    // rounding left u*Z past the last boundary: the last tile with mass
+    const int tl = max(wave_max_i(lastpos), 0);
+    const int owner = tl / per;
+    P.t = tl;
+    P.rem = INFINITY;
+    P.mt = __shfl(lm, owner);
+    csw = make_float4(__shfl(lsw.x, owner), __shfl(lsw.y, owner), __shfl(lsw.z, owner),
+                      __shfl(lsw.w, owner));
+  }
+  P.scale = use_shift ? exp(((double)P.mt - (double)M) * invTd) : 1.0;
+  // chunk inside the tile (uniform across the wave)
+  const float cs[4] = {csw.x, csw.y, csw.z, csw.w};
+  double c = 0.0;
+  int wstar = -1;
+  double remw = P.rem;
+  for (int k = 0; k < 4; k++) {
+    const double nc = c + (double)cs[k] * P.scale;
+    if (P.rem < nc) {
+      wstar = k;
+      remw = P.rem - c;
+      break;
+    }
+    c = nc;
+  }
+  if (wstar < 0) {
+    wstar = 0;
+    for (int k = 0; k < 4; k++)
+      if (cs[k] > 0.f) wstar = k;
+    remw = INFINITY;
+  }
+  P.w = wstar;
+  P.rem = remw;
+  return P;
+}
+
+// Gather the 64 chunk values held by lanes 0 and 32 (bias-block layout,
+// element (p, t) of lane 32h is column 16(t/4) + 8h + 2(t%4) + p) so that
+// lane c receives column c.
+__device__ inline float chunk_to_lanes(const float (&v)[2][16]) {
+  const int c = threadIdx.x & 63;
+  const int src = ((c >> 3) & 1) * 32;
+  const int want_t = 4 * (c >> 4) + ((c >> 1) & 3), want_p = c & 1;
+  float out = 0.f;
+#pragma unroll
+  for (int t = 0; t < 16; t++)
+#pragma unroll
+    for (int p = 0; p < 2; p++) {
+      const float x = __shfl(v[p][t], src);
+      if (t == want_t && p == want_p) out = x;
+    }
+  return out;
+}
+
+// Inverse-CDF pick among 64 per-lane values (lane c = column c): smallest c
+// with rem < scale * sum_{i <= c} v_i, else the last c with v_c > 0.
+__device__ inline int wave_pick64(float v, double scale, double rem) {
+  const int lane = threadIdx.x & 63;
+  double incl;
+  wave_excl_scan_d((double)v * scale, &incl);
+  const int hit = (rem < incl) ? lane : 0x7fffffff;
+  const int c = wave_min_i(hit);
+  if (c != 0x7fffffff) return c;
+  return max(wave_max_i(v > 0.f ? lane : -1), 0);
+}
+
+}  // namespace dspark

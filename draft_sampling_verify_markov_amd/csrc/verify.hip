@@ -1,0 +1,544 @@
+// Lossless rejection-sampling verification (dspark_verify).
+//
+// Sources: "DSpark: Aceleração da inferência de LLM com speculative decoding"
+// (pt.news.hada.io), "Definição do problema" (the target verifies a drafted
+// block in one pass and, by rejection sampling, keeps the longest prefix that
+// matches the target distribution, so decoding is lossless) and the decode
+// cycle in "Arquitetura" (E and F accepted, G rejected, a corrected token G*
+// emitted).  "DSpark: la apuesta de DeepSeek ..." (aitalk.it), first section:
+// the output is statistically identical to the target model's.
+//
+// Kernels, in stream order (no kernel waits on another workgroup):
+//   stream    grid = (gamma+1) x R x ceil(V / 4096), position-major.  Streams
+//             target rows j = 0..L_r of request r in 4096-column segments
+//             (non-temporal loads) and writes per-1024-column softmax partials;
+//             the segment holding the drafted token x_{j+1} stores its logit.
+//   decide    one workgroup per request, one wave per position: fp64 row
+//             statistics, p_{j+1}(x_{j+1}), the accept tests u < p/q, and the
+//             first rejected position.
+//   residual  grid = V / 256 column tiles (T > 0 only).  For requests that
+//             rejected at k*, recomputes the draft logits of position k* with
+//             the MFMA bias block and writes tile records of max(0, p - pi).
+//   finalize  one wave per request: residual or bonus inverse-CDF sample (fp64
+//             scan over tiles, recompute of one chunk or tile), emitted tokens
+//             and the p_k(x_k) output.
+#include "select.h"
+
+namespace dspark {
+
+template <typename WT>
+struct VerifyArgs {
+  const float* target;
+  const float* base;
+  const WT* W1;
+  const WT* W2;
+  const int32_t* anchor;
+  const int32_t* dtok;
+  const float* dprob;
+  const float* dstats;
+  const int32_t* vlen;
+  const float* u_acc;
+  const float* u_fin;
+  int R, gamma, V, r;
+  float T, invT;
+  int32_t* out_tokens;
+  int32_t* accept_len;
+  float* target_probs;
+  double2* rowstat;
+  int32_t* rej;
+  float2* vpart;
+  float* tx;
+  float* tp;
+  float4* rrec;
+  int32_t* err;
+
+  __device__ int L_of(int row, bool report = false) const {
+    if (!vlen) return gamma;
+    const int l = vlen[row];
+    if (l < 0 || l > gamma) {
+      if (report) raise_err(err, DSPARK_DERR_LENGTH);
+      return l < 0 ? 0 : gamma;
+    }
+    return l;
+  }
+  // token before position k (1-based) of request row
+  __device__ int prev_of(int row, int k) const {
+    const int t = (k == 1) ? anchor[row] : dtok[(size_t)row * gamma + k - 2];
+    return checked_token(t, V, err);
+  }
+};
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// target-row stream
+
+template <typename WT, bool GREEDY>
+__global__ __launch_bounds__(256) void k_verify_stream(VerifyArgs<WT> P) {
+  const int nseg = ceil_div(P.V, VSEG), nvt = ceil_div(P.V, VTILE);
+  const int b = blockIdx.x;
+  const int jpos = b / (P.R * nseg);
+  const int rem = b - jpos * P.R * nseg;
+  const int row = rem / nseg, seg = rem - row * nseg;
+  const int L = P.L_of(row);
+  if (jpos > L) return;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const size_t rowj = (size_t)row * (P.gamma + 1) + jpos;
+  const float* trow = P.target + rowj * P.V;
+  const bool t_one = (P.T == 1.0f);
+
+  if (tid == 0 && jpos < L) {
+    const int x = P.dtok[(size_t)row * P.gamma + jpos];
+    const int xc = (x < 0 || x >= P.V) ? 0 : x;
+    if (xc / VSEG == seg) P.tx[(size_t)row * P.gamma + jpos] = trow[xc];
+  }
+
+  const int tt = seg * 4 + wave, col0 = tt * VTILE;
+  if (col0 >= P.V) return;
+  float v[16];
+#pragma unroll
+  for (int f = 0; f < 4; f++) {
+    const int c = col0 + f * 256 + lane * 4;
+    f32x4 x = (c < P.V) ? ld_stream4(trow + c) : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int e = 0; e < 4; e++) v[4 * f + e] = x[e];
+  }
+  bool bad = false;
+  if (GREEDY) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int f = 0; f < 4; f++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const float x = v[4 * f + e];
+        bad |= (x != x);
+        if (x > bv) { bv = x; bi = col0 + f * 256 + lane * 4 + e; }
+      }
+    wave_argmax(bv, bi);
+    if (lane == 0) P.vpart[rowj * nvt + tt] = make_float2(bv, __int_as_float(bi));
+  } else {
+    float m = v[0];
+#pragma unroll
+    for (int i = 1; i < 16; i++) m = fmaxf(m, v[i]);
+    m = wave_max(m);
+    float s[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const float d0 = t_one ? (v[i] - m) : (v[i] - m) * P.invT;
+      const float d1 = t_one ? (v[i + 8] - m) : (v[i + 8] - m) * P.invT;
+      s[i] = exp_acc(d0) + exp_acc(d1);
+    }
+#pragma unroll
+    for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+      for (int i = 0; i < w; i++) s[i] += s[i + w];
+    const float sum = wave_sum(s[0]);
+    bad = is_bad(sum) || is_bad(m);
+    if (lane == 0) P.vpart[rowj * nvt + tt] = make_float2(m, sum);
+  }
+  if (bad) raise_err(P.err, DSPARK_DERR_NONFINITE);
+}
+
+// ---------------------------------------------------------------------------
+// accept tests: one workgroup per request, one wave per position
+
+template <typename WT, bool GREEDY>
+__global__ __launch_bounds__(256) void k_verify_decide(VerifyArgs<WT> P) {
+  __shared__ int s_ok[DSPARK_MAX_GAMMA + 1];
+  const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nvt = ceil_div(P.V, VTILE);
+  const int L = P.L_of(row, tid == 0);
+  const bool t_one = (P.T == 1.0f);
+  const double invTd = t_one ? 1.0 : 1.0 / (double)P.T;
+
+  for (int j = wave; j <= L; j += 4) {
+    const size_t rowj = (size_t)row * (P.gamma + 1) + j;
+    const float2* vp = P.vpart + rowj * nvt;
+    const size_t ev = (size_t)row * P.gamma + j;
+    if (GREEDY) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int t = lane; t < nvt; t += 64) argmax_merge(bv, bi, vp[t].x, __float_as_int(vp[t].y));
+      wave_argmax(bv, bi);
+      if (lane == 0) {
+        P.rowstat[rowj] = make_double2((double)bv, (double)bi);
+        if (j < L) {
+          const int x = checked_token(P.dtok[ev], P.V, P.err);
+          const bool ok = (x == bi);
+          P.tp[ev] = ok ? 1.0f : 0.0f;
+          s_ok[j] = ok;
+        }
+      }
+    } else {
+      float ml = -INFINITY;
+      for (int t = lane; t < nvt; t += 64) ml = fmaxf(ml, vp[t].x);
+      const float M = wave_max(ml);
+      double zl = 0.0;
+      for (int t = lane; t < nvt; t += 64)
+        zl += (double)vp[t].y * exp(((double)vp[t].x - (double)M) * invTd);
+      const double Z = wave_sum_d(zl);
+      if (lane == 0) {
+        P.rowstat[rowj] = make_double2((double)M, Z);
+        if (j < L) {
+          checked_token(P.dtok[ev], P.V, P.err);
+          const double p = exp(((double)P.tx[ev] - (double)M) * invTd) / Z;
+          const float q = P.dprob[ev];
+          bool ok;
+          if (!(q > 0.f)) {
+            raise_err(P.err, DSPARK_DERR_PROB);
+            ok = false;
+          } else {
+            const float u = checked_uniform(P.u_acc[ev], P.err);
+            ok = (double)u < p / (double)q;
+          }
+          P.tp[ev] = (float)p;
+          s_ok[j] = ok;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int ks = NO_REJECT;
+    for (int j = 0; j < L; j++)
+      if (!s_ok[j]) { ks = j + 1; break; }
+    P.rej[row] = ks;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// residual max(0, p - pi) tile records for rejected requests
+
+struct ResidualRow {
+  bool valid;
+  float Mt, invZt, mq, invZq;
+  rsrc_t brs, trs;      // base / target rows of the request block, from its first request
+  uint32_t boff, toff;  // byte offsets of this request's rows at k*
+};
+
+// Rows of requests c0.. are addressed from request c0's first base / target row.
+template <typename WT>
+__device__ inline ResidualRow residual_row(const VerifyArgs<WT>& P, int c0, int row, bool valid) {
+  ResidualRow rr;
+  rr.valid = valid;
+  rr.Mt = 0.f; rr.invZt = 0.f; rr.mq = 0.f; rr.invZq = 0.f;
+  const size_t R_left = (size_t)(P.R - c0);
+  rr.brs = make_rsrc(P.base + (size_t)c0 * P.gamma * P.V, R_left * P.gamma * P.V * 4);
+  rr.trs = make_rsrc(P.target + (size_t)c0 * (P.gamma + 1) * P.V, R_left * (P.gamma + 1) * P.V * 4);
+  rr.boff = 0u;
+  rr.toff = 0u;
+  if (valid) {
+    const int ks = P.rej[row];  // k*, 1-based
+    const double2 rs = P.rowstat[(size_t)row * (P.gamma + 1) + ks - 1];
+    const size_t ev = (size_t)row * P.gamma + ks - 1;
+    rr.Mt = (float)rs.x;
+    rr.invZt = (float)(1.0 / rs.y);
+    rr.mq = P.dstats[2 * ev];
+    rr.invZq = (float)(1.0 / (double)P.dstats[2 * ev + 1]);
+    const uint32_t rl = (uint32_t)(row - c0);
+    rr.boff = (rl * (uint32_t)P.gamma + (uint32_t)(ks - 1)) * (uint32_t)P.V * 4u;
+    rr.toff = (rl * (uint32_t)(P.gamma + 1) + (uint32_t)(ks - 1)) * (uint32_t)P.V * 4u;
+  }
+  return rr;
+}
+
+// max(0, p - pi) at the lane's 32 columns: p from the target row, pi from the
+// recomputed draft logits ((base - m_q) + bias) / T normalised by Z_q.
+template <typename WT>
+__device__ inline void residual_values(const VerifyArgs<WT>& P, const ResidualRow& rr, int cbase,
+                                       const f32x16 (&acc)[2], float (&d)[2][16]) {
+  float b[2][16], t[2][16];
+  load_row_cols(rr.brs, rr.boff, rr.valid, P.V, cbase, b);
+  load_row_cols(rr.trs, rr.toff, rr.valid, P.V, cbase, t);
+  const bool t_one = (P.T == 1.0f);
+#pragma unroll
+  for (int p = 0; p < 2; p++)
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      float at = t[p][i] - rr.Mt;
+      float aq = (b[p][i] - rr.mq) + acc[p][i];
+      if (!t_one) { at *= P.invT; aq *= P.invT; }
+      const float pv = exp_acc(at) * rr.invZt;
+      const float qv = exp_acc(aq) * rr.invZq;
+      d[p][i] = fmaxf(0.f, pv - qv);
+    }
+}
+
+template <typename WT, int KS>
+__global__ __launch_bounds__(256) void k_residual_partials(VerifyArgs<WT> P) {
+  constexpr int APAD = BiasBlock<WT>::APAD;
+  __shared__ __align__(16) WT A_lds[RCH * (DSPARK_MAX_RANK + APAD)];
+  __shared__ float red_s[4][RCH];
+  __shared__ int s_rej[RCH];
+
+  const int a_stride = P.r + APAD;
+  const int tile = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = lane & 31;
+  const int cbase = tile * TILE + wave * WCOLS;
+  const int nt = gridDim.x;
+
+  for (int c0 = 0; c0 < P.R; c0 += RCH) {
+    const int nrows = min(RCH, P.R - c0), nrb = ceil_div(nrows, 32);
+    __syncthreads();
+    int mine = 0;
+    if (threadIdx.x < nrows) {
+      const int row = c0 + threadIdx.x;
+      mine = (P.rej[row] <= P.L_of(row)) ? 1 : 0;
+      s_rej[threadIdx.x] = mine;
+    }
+    if (!__syncthreads_or(mine)) continue;
+    typename BiasBlock<WT>::template Frag<KS> F;
+    BiasBlock<WT>::template load<KS>(F, P.W2, P.V, P.r, cbase);
+    gather_w1_rows<WT, KS * sizeof(WT) / 2>(P.W1, P.V, P.r, nrows, nrb * 32, A_lds, a_stride, [&](int i) {
+      const int row = c0 + i;
+      return s_rej[i] ? P.prev_of(row, P.rej[row]) : -1;
+    });
+    __syncthreads();
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int rb = 0; rb < 4; rb++)
+#pragma unroll
+      for (int p = 0; p < 2; p++)
+#pragma unroll
+        for (int t = 0; t < 16; t++) acc[rb][p][t] = 0.f;
+    BiasBlock<WT>::template mma<KS>(F, P.r, A_lds, a_stride, nrb, acc);
+
+#pragma unroll
+    for (int rb = 0; rb < 4; rb++) {
+      if (rb >= nrb) break;
+      const int rl = rb * 32 + j, row = c0 + rl;
+      const bool rowv = rl < nrows && s_rej[rl];
+      const ResidualRow rr = residual_row(P, c0, row, rowv);
+      float d[2][16];
+      residual_values(P, rr, cbase, acc[rb], d);
+      const float sl = tree_sum32(d);
+      const float sw = sl + __shfl_xor(sl, 32);
+      if ((lane >> 5) == 0) red_s[wave][rl] = sw;
+      __syncthreads();
+      if (wave == 0 && (lane >> 5) == 0 && rowv) {
+        const float s0 = red_s[0][rl], s1 = red_s[1][rl], s2 = red_s[2][rl], s3 = red_s[3][rl];
+        float4* rec = P.rrec + ((size_t)row * nt + tile) * 2;
+        rec[0] = make_float4(0.f, (s0 + s1) + (s2 + s3), s0, s1);
+        rec[1] = make_float4(s2, s3, 0.f, 0.f);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// finalize: one wave per request
+
+// Inverse-CDF sample of softmax(target row / T) from its 1024-column tile
+// partials: fp64 scan over tiles, then the recomputed tile (same per-element
+// arithmetic and lane mapping as the stream kernel).
+template <typename WT>
+__device__ int wave_sample_target_row(const VerifyArgs<WT>& P, size_t rowj, double u) {
+  const int lane = threadIdx.x & 63;
+  const int nvt = ceil_div(P.V, VTILE);
+  const float2* vp = P.vpart + rowj * nvt;
+  const bool t_one = (P.T == 1.0f);
+  const double invTd = t_one ? 1.0 : 1.0 / (double)P.T;
+  const int per = ceil_div(nvt, 64);
+  const int t0 = min(nvt, lane * per), t1 = min(nvt, t0 + per);
+  float mloc = -INFINITY;
+  for (int t = t0; t < t1; t++) mloc = fmaxf(mloc, vp[t].x);
+  const float M = wave_max(mloc);
+  double loc = 0.0;
+  for (int t = t0; t < t1; t++) loc += (double)vp[t].y * exp(((double)vp[t].x - (double)M) * invTd);
+  double incl_unused;
+  const double ex = wave_excl_scan_d(loc, &incl_unused);
+  const double Z = __shfl(ex + loc, (nvt - 1) / per);
+  const double target = u * Z;
+  int found = 0x7fffffff, lastpos = -1;
+  double before = 0.0, cum = 0.0;
+  for (int t = t0; t < t1; t++) {
+    const double w = (double)vp[t].y * exp(((double)vp[t].x - (double)M) * invTd);
+    const double pp = cum;
+    cum += w;
+    if (found == 0x7fffffff && target < ex + cum) { found = t; before = ex + pp; }
+    if (vp[t].y > 0.f) lastpos = t;
+  }
+  int tstar = wave_min_i(found);
+  double rem;
+  if (tstar != 0x7fffffff) {
+    rem = __shfl(target - before, tstar / per);
+  } else {
+    tstar = max(wave_max_i(lastpos), 0);
+    rem = INFINITY;
+  }
+  const float mt = vp[tstar].x;
+  const double scale = exp(((double)mt - (double)M) * invTd);
+  const float* trow = P.target + rowj * P.V;
+  // lane l holds columns tstar*1024 + f*256 + 4l + e (the stream kernel's mapping)
+  double carry = 0.0;
+  int pick = -1;
+  int lastc = -1;
+#pragma unroll
+  for (int f = 0; f < 4; f++) {
+    const int c = tstar * VTILE + f * 256 + lane * 4;
+    f32x4 x = (c < P.V) ? ld_stream4(trow + c) : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    double w4[4], s4 = 0.0;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const float d = t_one ? (x[e] - mt) : (x[e] - mt) * P.invT;
+      const float ev = exp_acc(d);
+      w4[e] = (double)ev * scale;
+      s4 += w4[e];
+      if (ev > 0.f) lastc = c + e;
+    }
+    double incl;
+    const double exl = wave_excl_scan_d(s4, &incl);
+    const double tot = __shfl(incl, 63);
+    if (pick < 0 && rem < carry + tot) {
+      double run = carry + exl;
+      int hit = 0x7fffffff;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        run += w4[e];
+        if (hit == 0x7fffffff && rem < run) hit = c + e;
+      }
+      const int hmin = wave_min_i(hit);
+      pick = (hmin != 0x7fffffff) ? hmin : -1;
+    }
+    carry += tot;
+  }
+  if (pick < 0) pick = max(wave_max_i(lastc), 0);
+  return min(pick, P.V - 1);
+}
+
+template <typename WT, bool GREEDY, int KS>
+__global__ __launch_bounds__(256) void k_verify_finalize(VerifyArgs<WT> P) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = lane & 31;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= P.R) return;  // waves are independent
+  const int L = P.L_of(row);
+  const int ks = P.rej[row];
+  const bool rejected = ks <= L;
+  const int A = rejected ? ks - 1 : L;
+  const size_t rowA = (size_t)row * (P.gamma + 1) + A;
+  int y = 0;
+
+  if (GREEDY) {
+    y = (int)P.rowstat[rowA].y;
+    if (y < 0 || y >= P.V) y = 0;
+  } else {
+    const double u = (double)checked_uniform(P.u_fin[row], P.err);
+    bool use_p = !rejected;
+    if (rejected) {
+      const int nt = ceil_div(P.V, TILE);
+      const TilePick S = wave_select_tile(P.rrec + (size_t)row * nt * 2, nt, false, 1.0, u);
+      if (!(S.Z > 0.0)) {
+        use_p = true;  // no residual mass: sample p itself
+      } else {
+        const int cb = S.t * TILE + S.w * WCOLS;
+        const int prev = P.prev_of(row, ks);
+        typename BiasBlock<WT>::template Frag<KS> F;
+        BiasBlock<WT>::template load<KS>(F, P.W2, P.V, P.r, cb);
+        typename BiasBlock<WT>::template Row<KS> w1;
+        BiasBlock<WT>::template load_row<KS>(w1, P.W1, P.r, prev);
+        f32x16 acc[2];
+#pragma unroll
+        for (int p = 0; p < 2; p++)
+#pragma unroll
+          for (int t = 0; t < 16; t++) acc[p][t] = 0.f;
+        BiasBlock<WT>::template mma_row<KS>(F, P.r, w1, acc);
+        const ResidualRow rr = residual_row(P, row, row, j == 0);
+        float d[2][16];
+        residual_values(P, rr, cb, acc, d);
+        const float dc = chunk_to_lanes(d);
+        y = min(cb + wave_pick64(dc, 1.0, S.rem), P.V - 1);
+      }
+    }
+    if (use_p) y = wave_sample_target_row(P, rowA, u);
+  }
+
+  // outputs: lane i writes slot i
+  int32_t* out = P.out_tokens + (size_t)row * (P.gamma + 1);
+  for (int i = lane; i <= P.gamma; i += 64)
+    out[i] = (i < A) ? P.dtok[(size_t)row * P.gamma + i] : ((i == A) ? y : -1);
+  if (lane == 0) P.accept_len[row] = A;
+  if (P.target_probs) {
+    const int lim = min(L, A + 1);
+    for (int k = lane + 1; k <= P.gamma; k += 64)
+      P.target_probs[(size_t)row * P.gamma + k - 1] =
+          (k <= lim) ? P.tp[(size_t)row * P.gamma + k - 1] : -1.0f;
+  }
+}
+
+template <typename WT>
+static int launch_verify(const VerifyArgs<WT>& P, hipStream_t stream) {
+  const int nseg = ceil_div(P.V, VSEG);
+  const long long nblk = (long long)(P.gamma + 1) * P.R * nseg;
+  const bool greedy = (P.T == 0.f);
+  prof_before(DSPARK_KID_VERIFY_STREAM, stream);
+  if (greedy)
+    hipLaunchKernelGGL((k_verify_stream<WT, true>), dim3((unsigned)nblk), dim3(256), 0, stream, P);
+  else
+    hipLaunchKernelGGL((k_verify_stream<WT, false>), dim3((unsigned)nblk), dim3(256), 0, stream, P);
+  prof_after(DSPARK_KID_VERIFY_STREAM, stream);
+  prof_before(DSPARK_KID_VERIFY_DECIDE, stream);
+  if (greedy)
+    hipLaunchKernelGGL((k_verify_decide<WT, true>), dim3(P.R), dim3(256), 0, stream, P);
+  else
+    hipLaunchKernelGGL((k_verify_decide<WT, false>), dim3(P.R), dim3(256), 0, stream, P);
+  prof_after(DSPARK_KID_VERIFY_DECIDE, stream);
+  if (!greedy) {
+    prof_before(DSPARK_KID_RESIDUAL, stream);
+    DSPARK_DISPATCH_KS(P.r, hipLaunchKernelGGL((k_residual_partials<WT, KS>), dim3(ceil_div(P.V, TILE)),
+                                               dim3(256), 0, stream, P));
+    prof_after(DSPARK_KID_RESIDUAL, stream);
+  }
+  prof_before(DSPARK_KID_VERIFY_FINALIZE, stream);
+  if (greedy)
+    hipLaunchKernelGGL((k_verify_finalize<WT, true, 1>), dim3(ceil_div(P.R, 4)), dim3(256), 0, stream, P);
+  else
+    DSPARK_DISPATCH_KS(P.r, hipLaunchKernelGGL((k_verify_finalize<WT, false, KS>), dim3(ceil_div(P.R, 4)),
+                                               dim3(256), 0, stream, P));
+  prof_after(DSPARK_KID_VERIFY_FINALIZE, stream);
+  return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
+}
+
+int verify_impl(const float* target, const float* base, const void* W1, const void* W2,
+                dspark_wtype w_type, const int32_t* anchor, const int32_t* dtok, const float* dprob,
+                const float* dstats, const int32_t* vlen, const float* u_acc, const float* u_fin,
+                int R, int gamma, int V, int r, float T, int32_t* out_tokens, int32_t* accept_len,
+                float* target_probs, void* ws, hipStream_t stream) {
+  const WsLayout Lw = ws_layout(R, gamma, V);
+  auto fill = [&](auto& P) {
+    P.target = target; P.base = base;
+    P.anchor = anchor; P.dtok = dtok; P.dprob = dprob; P.dstats = dstats; P.vlen = vlen;
+    P.u_acc = u_acc; P.u_fin = u_fin;
+    P.R = R; P.gamma = gamma; P.V = V; P.r = r;
+    P.T = T; P.invT = (T > 0.f) ? 1.0f / T : 0.f;
+    P.out_tokens = out_tokens; P.accept_len = accept_len; P.target_probs = target_probs;
+    P.rowstat = ws_ptr<double2>(ws, Lw.rowstat);
+    P.rej = ws_ptr<int32_t>(ws, Lw.rej);
+    P.vpart = ws_ptr<float2>(ws, Lw.vpart);
+    P.tx = ws_ptr<float>(ws, Lw.tx);
+    P.tp = ws_ptr<float>(ws, Lw.tp);
+    P.rrec = ws_ptr<float4>(ws, Lw.rrec);
+    P.err = ws_ptr<int32_t>(ws, Lw.err);
+  };
+  if (w_type == DSPARK_W_BF16) {
+    VerifyArgs<uint16_t> P;
+    fill(P);
+    P.W1 = static_cast<const uint16_t*>(W1);
+    P.W2 = static_cast<const uint16_t*>(W2);
+    return launch_verify(P, stream);
+  }
+  VerifyArgs<float> P;
+  fill(P);
+  P.W1 = static_cast<const float*>(W1);
+  P.W2 = static_cast<const float*>(W2);
+  return launch_verify(P, stream);
+}
+
+}  // namespace dspark

@@ -23,10 +23,15 @@ TID_BASE, TID_TARGET, TID_SIGMA, TID_W1, TID_W2, TID_ANCHOR, TID_CONF = 1, 2, 3,
 def bf16_bits_from_f32(x):
     """Round float32 values to bfloat16 (round to nearest, ties to even).
 
-    Returns the 16-bit patterns as uint16.  Inputs are finite here.
+    Returns the 16-bit patterns as uint16.  Inputs must be finite (no
+    overflow of the 32-bit rounding add).
     """
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    lsb = u >> 16
+    lsb &= 1
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u >>= 16
     return u.astype(np.uint16)
 
 
@@ -71,12 +76,13 @@ def _fill_row(d, seed, r, sigma, base_out, target_out):
     """Draw base rows 0..gamma (gamma + 1 of them) and target rows of request r."""
     g, V = d["gamma"], d["V"]
     rb = np.random.default_rng([seed, TID_BASE, r])
+    ext = rb.standard_normal((g + 1, V), dtype=np.float32)
     if d["base"] == "bimodal":
-        ext = rb.standard_normal((g + 1, V), dtype=np.float32) * np.float32(3.0)
+        ext *= np.float32(3.0)
         for j in range(g + 1):
             ext[j, rb.choice(V, size=min(2, V), replace=False)] += np.float32(6.0)
     elif d["base"] == "peaked":
-        ext = rb.standard_normal((g + 1, V), dtype=np.float32) * np.float32(2.0)
+        ext *= np.float32(2.0)
         for j in range(g + 1):
             cnt = int(rb.integers(1, 4))
             ext[j, rb.choice(V, size=min(cnt, V), replace=False)] += np.float32(8.0)

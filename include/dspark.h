@@ -1,0 +1,211 @@
+/*
+ * dspark.h - C ABI of the DSpark speculative-decoding round on AMD MI355X (gfx950).
+ *
+ * One round is three calls, each stream-ordered on the caller's HIP stream:
+ *
+ *   dspark_draft     Markov-head sequential drafting of gamma tokens per request
+ *   dspark_schedule  hardware-aware prefix scheduler: per-request verify lengths
+ *   dspark_verify    lossless rejection-sampling verification and emission
+ *
+ * Sources (page title, section):
+ *   "DSpark: Aceleração da inferência de LLM com speculative decoding"
+ *   (pt.news.hada.io): "Arquitetura" - the decode cycle (anchor, draft,
+ *   scheduler cut, target verify, corrected token), Semi-Autoregressive
+ *   Generation (parallel stage gives base logits; sequential stage adds a
+ *   prefix-dependent transition bias), the Markov head (first-order bias from
+ *   the previous token, low-rank B = W1 W2, default rank 256), the confidence
+ *   head (c_k in (0,1)) and the Hardware-Aware Prefix Scheduler (survival
+ *   probabilities a_{r,j}, cost table SPS(B), objective tau * SPS(B), global
+ *   sort, greedy admission with early stop, non-anticipation);
+ *   "Definição do problema" - speculative decoding verifies a drafted block in
+ *   one target pass and keeps the longest prefix consistent with the target
+ *   distribution by rejection sampling.
+ *   "DeepSpec ... DSpark" (jdon.com), scheduler sections - one global pool of
+ *   candidates sorted high to low, each admitted token grows the batch by 1.
+ *
+ * Conventions (all calls)
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, except
+ *     where a parameter says "host".  The library allocates nothing, keeps no
+ *     global state and never modifies an input.
+ *   - Arrays are dense, row-major, with the last index contiguous.
+ *   - W1/W2 are bf16 (bit patterns in uint16) or fp32 according to w_type.
+ *   - No random numbers are drawn inside the library: every random choice is
+ *     an inverse-CDF or threshold test on a caller-supplied uniform in [0, 1).
+ *   - Host-side argument checks run before any launch; a failing check returns
+ *     a negative status and launches nothing.  A failed launch returns
+ *     DSPARK_EHIP.  Calls are asynchronous: results are ready when the stream
+ *     reaches them.
+ *   - Bad values in device memory (NaN logits, uniforms outside [0,1), tokens
+ *     outside [0,V), confidences outside (0,1], draft probabilities <= 0) cannot
+ *     be checked from the host (nor verify lengths outside [0, gamma]); kernels
+ *     OR a DSPARK_DERR_* bit into an error
+ *     word inside the workspace, substitute a safe value (token 0, uniform 0,
+ *     confidence clamped) and carry on.  Read it with dspark_device_error.
+ *   - The workspace is caller-allocated device memory of at least
+ *     dspark_workspace_size(R, gamma, V, r) bytes, 256-byte aligned, cleared
+ *     once with dspark_workspace_init.  Calls on one workspace must be ordered
+ *     on one stream; concurrent calls need distinct workspaces.
+ *
+ * Limits (the sizes the kernels are built for): 1 <= gamma <= 16,
+ * 16 <= r <= 256 with r % 16 == 0, 8 <= V <= 262144 with V % 8 == 0
+ * (16-byte aligned rows), R >= 1, R * gamma <= 8192 for dspark_schedule.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSPARK_OK = 0,
+  DSPARK_EINVAL = -1, /* an argument is NULL, out of range, or not aligned   */
+  DSPARK_ENOSPC = -2, /* workspace_bytes < dspark_workspace_size(...)         */
+  DSPARK_EHIP = -3    /* a HIP runtime call or kernel launch failed           */
+} dspark_status;
+
+typedef enum {
+  DSPARK_W_BF16 = 0,  /* W1, W2 hold bfloat16 bit patterns (uint16)           */
+  DSPARK_W_F32 = 1    /* W1, W2 hold float32                                  */
+} dspark_wtype;
+
+/* Device-side data error bits, OR-ed into the workspace error word. */
+#define DSPARK_DERR_NONFINITE 1 /* NaN/inf in a logit row (base + bias or target) */
+#define DSPARK_DERR_UNIFORM 2   /* a uniform outside [0, 1); 0 was used instead    */
+#define DSPARK_DERR_CONF 4      /* a confidence outside (0, 1]; clamped            */
+#define DSPARK_DERR_TOKEN 8     /* a token id outside [0, V); 0 was used instead   */
+#define DSPARK_DERR_PROB 16     /* a draft probability <= 0 or NaN; rejected       */
+#define DSPARK_DERR_LENGTH 32   /* a verify length outside [0, gamma]; clamped     */
+
+#define DSPARK_MAX_GAMMA 16
+#define DSPARK_MAX_RANK 256
+#define DSPARK_MAX_POOL 8192
+
+/* Bytes of workspace the three calls need for these sizes (host-only query).
+ * Returns 0 for sizes outside the limits above. */
+size_t dspark_workspace_size(int R, int gamma, int V, int r);
+
+/* Clear the workspace error word and counters (asynchronous on stream). */
+int dspark_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Copy the workspace error word to *host_bits (host pointer), then clear it.
+ * Synchronizes `stream`. */
+int dspark_device_error(void* workspace, size_t workspace_bytes, int32_t* host_bits,
+                        hipStream_t stream);
+
+/* Human-readable name of a status code (static string). */
+const char* dspark_status_string(int status);
+
+/*
+ * dspark_draft - Markov-head sequential drafting.
+ *
+ * For k = 1..gamma and every request r, with x_0 = anchor[r]:
+ *   z_k[v] = base[r, k-1, v] + sum_i W1[x_{k-1}, i] * W2[i, v]
+ * (row of W1 = previous token, column of W2 = next token; bf16 products are
+ * accumulated in fp32), then x_k is drawn from softmax(z_k / T) by inverse CDF
+ * over ascending token id: x_k = min{v : u_draft[r,k-1] < F(v)}.  T == 0 is
+ * greedy: x_k = argmax z_k, lowest id on ties.
+ *
+ *   base          [R, gamma, V] fp32   base logits of the parallel stage
+ *   W1            [V, r]               previous-token factor
+ *   W2            [r, V]               next-token factor
+ *   anchor        [R] int32            token preceding position 1
+ *   u_draft       [R, gamma] fp32      one uniform per draft event
+ *   temperature   >= 0 (host scalar), 0 = greedy
+ *   draft_tokens  out [R, gamma] int32 x_k
+ *   draft_probs   out [R, gamma] fp32  q_k(x_k) (1 for greedy)
+ *   draft_stats   out [R, gamma, 2] fp32 (m, Z): m = max_v z_k[v],
+ *                 Z = sum_v exp((z_k[v] - m) / T); greedy writes (m, 1)
+ */
+int dspark_draft(const float* base, const void* W1, const void* W2, dspark_wtype w_type,
+                 const int32_t* anchor, const float* u_draft, int R, int gamma, int V, int r,
+                 float temperature, int32_t* draft_tokens, float* draft_probs, float* draft_stats,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dspark_schedule - hardware-aware prefix scheduler.  Reads only confidences
+ * and the cost table, never a drafted token (non-anticipation).
+ *
+ *   a[r,0] = c[r,0],  a[r,j] = fp32(a[r,j-1] * c[r,j])      (survival probability)
+ *   pool of R*gamma candidates sorted by (a descending, r*gamma + j ascending)
+ *   T_n   = R * 2^36 + sum of floor(a * 2^36) over the first n in the pool
+ *           (expected emitted tokens, exact fixed point)
+ *   Theta_n = double(T_n) * double(SPS(R + n)),  SPS(B) = sps[B-1] for
+ *           B <= n_table, else 0
+ *   n* = first n < R*gamma with Theta_{n+1} < Theta_n, else R*gamma
+ *   verify_len[r] = number of row-r candidates among the first n*
+ *
+ *   conf         [R, gamma] fp32  conditional confidences c in (0, 1]
+ *   sps          [n_table] fp32   throughput at verify batch B = i + 1
+ *   verify_len   out [R] int32    L_r in [0, gamma]
+ *   n_admitted   out [1] int32    n*
+ *   cum_conf     out [R, gamma] fp32 a, or NULL
+ */
+int dspark_schedule(const float* conf, const float* sps, int R, int gamma, int n_table,
+                    int32_t* verify_len, int32_t* n_admitted, float* cum_conf, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dspark_verify - lossless rejection-sampling verification.
+ *
+ * Per request r, for k = 1..L_r in order: p = softmax(target[r,k-1] / T);
+ * accept x_k iff u_accept[r,k-1] < p(x_k) / q_k(x_k); stop at the first
+ * rejection k*.  Emitted: x_1..x_{A}, then y, with A = k*-1 on rejection or
+ * L_r otherwise.  On rejection y is drawn by inverse CDF with u_final[r] from
+ * max(0, p - pi_{k*}) normalised (pi_{k*} = the draft distribution at k*,
+ * recomputed from base, W1, W2 and draft_stats; p itself if that mass is 0).
+ * Without rejection y is drawn from softmax(target[r, L_r] / T) (bonus).
+ * T == 0: accept iff x_k == argmax target[r,k-1]; y = argmax of row A.
+ *
+ *   target        [R, gamma+1, V] fp32 target logits; row k-1 scores draft
+ *                 position k, row L_r scores the bonus position
+ *   base, W1, W2, w_type, anchor   as given to dspark_draft
+ *   draft_tokens, draft_probs, draft_stats  outputs of dspark_draft
+ *   verify_len    [R] int32 from dspark_schedule, or NULL for L_r = gamma
+ *   u_accept      [R, gamma] fp32, u_final [R] fp32
+ *   out_tokens    out [R, gamma+1] int32: x_1..x_A, y, then -1
+ *   accept_len    out [R] int32 A (emitted tokens = A + 1)
+ *   target_probs  out [R, gamma] fp32 p_k(x_k) for k <= min(L_r, A + 1),
+ *                 -1 elsewhere (greedy: 1 on a match, 0 on the mismatch); or NULL
+ */
+int dspark_verify(const float* target, const float* base, const void* W1, const void* W2,
+                  dspark_wtype w_type, const int32_t* anchor, const int32_t* draft_tokens,
+                  const float* draft_probs, const float* draft_stats, const int32_t* verify_len,
+                  const float* u_accept, const float* u_final, int R, int gamma, int V, int r,
+                  float temperature, int32_t* out_tokens, int32_t* accept_len, float* target_probs,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Optional launch-timing hook for benchmarks and profilers.
+ *
+ * While armed on the calling thread for kernel id `kid`, every launch of that
+ * kernel made by this thread's dspark_* calls is bracketed by
+ * hipEventRecord(starts[i], stream) before and hipEventRecord(stops[i], stream)
+ * after, for i = 0, 1, ... up to n - 1; later launches are not timed.  The
+ * events are created (with timing enabled) and owned by the caller.  The state
+ * is thread-local; other threads and unarmed calls are unaffected.
+ * dspark_profile_arm returns DSPARK_EINVAL for a bad id, NULL arrays or n < 1.
+ * dspark_profile_disarm returns the number of pairs recorded.
+ */
+typedef enum {
+  DSPARK_KID_DRAFT_PARTIALS = 1,  /* per-step bias GEMM + softmax partials */
+  DSPARK_KID_DRAFT_SELECT = 2,    /* per-step inverse-CDF select            */
+  DSPARK_KID_SCHEDULE = 3,        /* prefix scheduler                       */
+  DSPARK_KID_VERIFY_STREAM = 4,   /* target-row stream (softmax partials)   */
+  DSPARK_KID_VERIFY_DECIDE = 5,   /* row statistics + ordered accept tests  */
+  DSPARK_KID_RESIDUAL = 6,        /* residual max(0, p - q) partials        */
+  DSPARK_KID_VERIFY_FINALIZE = 7  /* residual / bonus sample and outputs    */
+} dspark_kernel_id;
+
+int dspark_profile_arm(int kid, hipEvent_t* starts, hipEvent_t* stops, int n);
+int dspark_profile_disarm(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */

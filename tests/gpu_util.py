@@ -1,0 +1,88 @@
+"""Helpers of the GPU parity tests: device transfer and oracle comparison."""
+
+import sys
+
+import numpy as np
+import torch
+
+import draft_sampling_verify_markov_amd as D
+import oracle as O
+
+ATOL, RTOL = 1e-4, 1e-5   # floating-point parity bar for probabilities and statistics
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def w_to_dev(w, w_dtype, device):
+    if w_dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).to(device)
+
+
+def to_dev(inp, device=None):
+    device = device or dev()
+    t = lambda a, dt=None: None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).to(device)
+    return dict(base=t(inp["base"], np.float32), target=t(inp["target"], np.float32),
+                W1=w_to_dev(inp["W1"], inp["w_dtype"], device),
+                W2=w_to_dev(inp["W2"], inp["w_dtype"], device),
+                anchor=t(inp["anchor"], np.int32), u_draft=t(inp["u_draft"], np.float32),
+                u_accept=t(inp["u_accept"], np.float32), u_final=t(inp["u_final"], np.float32),
+                conf=t(inp["conf"], np.float32), sps=t(inp["sps"], np.float32))
+
+
+def gpu_round(inp, T, use_scheduler=None, device=None):
+    d = to_dev(inp, device)
+    R, g, V = inp["base"].shape
+    r = inp["W1"].shape[1]
+    ws = D.new_workspace(R, g, V, r, d["base"].device)
+    if use_scheduler is None:
+        use_scheduler = inp.get("conf") is not None
+    out = D.run_round(d, T, ws, use_scheduler=use_scheduler)
+    torch.cuda.synchronize()
+    err = D.device_error(ws)
+    res = {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in out.items()}
+    res["device_error"] = err
+    return res
+
+
+def compare_rounds(orc, gpu, rows=None, label=""):
+    """Compare an oracle round with the GPU round on (a subset of) rows.
+
+    orc comes from oracle.run_round on the rows given (or all rows); gpu holds
+    whole-workload arrays, restricted to ``rows``.  Integer outputs must match
+    exactly on rows the oracle does not flag; probabilities within ATOL/RTOL.
+    Returns the number of flagged rows.
+    """
+    sel = slice(None) if rows is None else np.asarray(rows)
+    g_tok = gpu["draft_tokens"][sel]
+    g_prob = gpu["draft_probs"][sel]
+    g_stats = gpu["draft_stats"][sel]
+    g_out = gpu["out_tokens"][sel]
+    g_acc = gpu["accept_len"][sel]
+    g_tp = gpu["target_probs"][sel]
+    flags = orc["flags"]
+    ok = ~flags
+    n_flag = int(flags.sum())
+    say(f"[{label}] rows compared {len(flags)}, flagged {n_flag}")
+    d = orc["draft"]
+    v = orc["verify"]
+    bad_tok = np.flatnonzero(ok & (g_tok != d["tokens"]).any(axis=1))
+    assert len(bad_tok) == 0, f"{label}: draft tokens differ on unflagged rows {bad_tok[:10]}"
+    if orc["schedule"] is not None and gpu.get("verify_len") is not None:
+        gL = gpu["verify_len"][sel]
+        assert (gL == orc["verify_len"]).all(), f"{label}: verify lengths differ"
+    bad_acc = np.flatnonzero(ok & (g_acc != v["accept_len"]))
+    assert len(bad_acc) == 0, f"{label}: accept_len differs on rows {bad_acc[:10]}"
+    bad_out = np.flatnonzero(ok & (g_out != v["out_tokens"]).any(axis=1))
+    assert len(bad_out) == 0, f"{label}: out_tokens differ on rows {bad_out[:10]}"
+    np.testing.assert_allclose(g_prob[ok], d["probs"][ok], atol=ATOL, rtol=RTOL, err_msg=label + " q")
+    np.testing.assert_allclose(g_stats[ok], d["stats"][ok], atol=ATOL, rtol=RTOL, err_msg=label + " stats")
+    np.testing.assert_allclose(g_tp[ok], v["target_probs"][ok], atol=ATOL, rtol=RTOL, err_msg=label + " p")
+    return n_flag

@@ -1,0 +1,111 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, sizes its workspace, and rejects bad arguments on the host
+before launching anything."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import draft_sampling_verify_markov_amd as D
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dspark.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(dspark_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return D.load_library()
+
+
+def test_header_declares_the_round(lib):
+    names = _declared_functions()
+    for n in ("dspark_draft", "dspark_schedule", "dspark_verify", "dspark_workspace_size",
+              "dspark_workspace_init", "dspark_device_error", "dspark_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for n in _declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_workspace_size_limits(lib):
+    assert D.workspace_size(128, 7, 131072, 256) > 0
+    assert lib.dspark_workspace_size(4, 4, 500, 16) == 0      # V % 8 != 0
+    assert lib.dspark_workspace_size(4, 17, 512, 16) == 0     # gamma > 16
+    assert lib.dspark_workspace_size(4, 4, 512, 24) == 0      # r % 16 != 0
+    assert lib.dspark_workspace_size(4, 4, 512, 272) == 0     # r > 256
+    assert lib.dspark_workspace_size(0, 4, 512, 16) == 0      # R < 1
+    # grows with every size
+    a = D.workspace_size(4, 4, 512, 16)
+    assert D.workspace_size(8, 4, 512, 16) > a
+    assert D.workspace_size(4, 8, 512, 16) > a
+    assert D.workspace_size(4, 4, 8192, 16) > a
+
+
+EINVAL, ENOSPC = -1, -2
+
+
+def _draft(lib, **kw):
+    a = dict(base=16, W1=16, W2=16, wt=0, anchor=16, u=16, R=4, g=4, V=512, r=16, T=1.0,
+             tok=16, prob=16, stats=16, ws=256, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.dspark_draft(a["base"], a["W1"], a["W2"], a["wt"], a["anchor"], a["u"], a["R"], a["g"],
+                            a["V"], a["r"], a["T"], a["tok"], a["prob"], a["stats"], a["ws"], a["wsb"],
+                            a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(base=None), EINVAL), (dict(W2=None), EINVAL), (dict(tok=None), EINVAL),
+    (dict(V=500), EINVAL), (dict(g=0), EINVAL), (dict(g=17), EINVAL), (dict(r=8), EINVAL),
+    (dict(R=0), EINVAL), (dict(T=-1.0), EINVAL), (dict(T=float("nan")), EINVAL),
+    (dict(T=float("inf")), EINVAL), (dict(wt=7), EINVAL), (dict(base=18), EINVAL),
+    (dict(ws=None), EINVAL), (dict(ws=128), EINVAL), (dict(wsb=100), ENOSPC),
+])
+def test_draft_rejects_bad_arguments(lib, kw, status):
+    assert _draft(lib, **kw) == status
+
+
+def test_schedule_rejects_bad_arguments(lib):
+    f = lib.dspark_schedule
+    assert f(None, 16, 4, 4, 10, 16, 16, None, 256, 4096, None) == EINVAL
+    assert f(16, 16, 1000, 9, 10, 16, 16, None, 256, 4096, None) == EINVAL   # pool > 8192
+    assert f(16, 16, 4, 4, 0, 16, 16, None, 256, 4096, None) == EINVAL       # empty table
+    assert f(16, 16, 4, 0, 10, 16, 16, None, 256, 4096, None) == EINVAL
+    assert f(16, 16, 4, 4, 10, None, 16, None, 256, 4096, None) == EINVAL
+    assert f(16, 16, 4, 4, 10, 16, 16, None, 256, 100, None) == ENOSPC
+
+
+def test_verify_rejects_bad_arguments(lib):
+    base = [16, 16, 16, 16, 0, 16, 16, 16, 16, None, 16, 16, 4, 4, 512, 16, 1.0, 16, 16, None, 256,
+            1 << 20, None]
+    bad = list(base)
+    bad[0] = None
+    assert lib.dspark_verify(*bad) == EINVAL
+    bad = list(base)
+    bad[14] = 100
+    assert lib.dspark_verify(*bad) == EINVAL
+    bad = list(base)
+    bad[21] = 64
+    assert lib.dspark_verify(*bad) == ENOSPC
+
+
+def test_status_strings(lib):
+    assert b"ENOSPC" in lib.dspark_status_string(-2)
+    assert b"EINVAL" in lib.dspark_status_string(-1)
+    assert b"EHIP" in lib.dspark_status_string(-3)
+
+
+def test_binding_checks_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        D.draft(torch.zeros(2, 2, 8), torch.zeros(8, 16, dtype=torch.float64),
+                torch.zeros(16, 8, dtype=torch.float64), None, None, 1.0, None)

@@ -1,0 +1,269 @@
+"""GPU parity: the HIP round through the C ABI against the float64 oracle.
+
+Token ids, verify lengths and accepted lengths must be equal on every row the
+oracle does not flag (an event within 1e-6 of a decision boundary); the
+flagged rows are counted.  Probabilities and row statistics must agree within
+atol 1e-4 / rtol 1e-5.  All inputs are seeded (gen.make_inputs).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import draft_sampling_verify_markov_amd as D
+import oracle as O
+from gen import make_inputs, config
+from gen.inputs import bf16_bits_from_f32
+
+from gpu_util import compare_rounds, gpu_round, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_and_compare(inp, T, label, rows=None, oracle_inp=None, use_scheduler=None):
+    say(f"[{label}] GPU round R={inp['base'].shape[0]} gamma={inp['base'].shape[1]} "
+        f"V={inp['base'].shape[2]} r={inp['W1'].shape[1]} T={T}")
+    gpu = gpu_round(inp, T, use_scheduler=use_scheduler)
+    assert gpu["device_error"] == 0, f"device error bits {gpu['device_error']}"
+    orc = O.run_round(oracle_inp if oracle_inp is not None else inp, T=T, use_scheduler=use_scheduler)
+    nflag = compare_rounds(orc, gpu, rows=rows, label=label)
+    return gpu, orc, nflag
+
+
+# ---------------------------------------------------------------------------
+# small workloads, whole-round parity
+
+
+def test_tiny_fp32_factors():
+    _run_and_compare(make_inputs(1), 1.0, "tiny f32")
+
+
+def test_tiny_bf16_factors():
+    d = config(1, w_dtype="bf16")
+    _run_and_compare(make_inputs(d, seed=1), 1.0, "tiny bf16")
+
+
+@pytest.mark.parametrize("seed_u", [0, 1, 2, 3])
+def test_tiny_bf16_many_uniforms(seed_u):
+    d = config(1, w_dtype="bf16", R=40, gamma=6, V=1024, r=32)
+    _run_and_compare(make_inputs(d, seed=11, seed_u=seed_u), 1.0, f"tiny bf16 u{seed_u}")
+
+
+def test_32k_full_verify():
+    _run_and_compare(make_inputs(2), 1.0, "32k full verify")
+
+
+@pytest.mark.parametrize("R,g,V,r", [
+    (1, 1, 8, 16),        # smallest sizes
+    (5, 3, 1000, 16),     # ragged vocabulary tail (V % 256 != 0)
+    (33, 2, 520, 48),     # rows spill into a second 32-row block
+    (130, 2, 776, 32),    # two 128-row LDS passes
+    (3, 16, 2048, 256),   # longest block
+])
+@pytest.mark.parametrize("w_dtype", ["bf16", "f32"])
+def test_shapes_and_ragged_tails(R, g, V, r, w_dtype):
+    d = config(1, R=R, gamma=g, V=V, r=r, w_dtype=w_dtype, table="linear")
+    _run_and_compare(make_inputs(d, seed=7), 1.0, f"shape {R},{g},{V},{r},{w_dtype}")
+
+
+@pytest.mark.parametrize("T", [0.0, 0.7])
+def test_greedy_and_temperature(T):
+    d = config(1, R=24, gamma=5, V=2048, r=64, w_dtype="bf16")
+    _run_and_compare(make_inputs(d, seed=3), T, f"T={T}")
+
+
+def test_full_verify_without_scheduler_small():
+    d = config(1, R=16, gamma=5, V=1024, r=32, w_dtype="bf16", conf=None, table=None)
+    _run_and_compare(make_inputs(d, seed=4), 1.0, "no scheduler")
+
+
+# ---------------------------------------------------------------------------
+# worked trace of the decode cycle (numbers in tests/golden/worked_trace.json)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_worked_trace_gpu(T):
+    import json, os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_trace.json")))
+    V, t, peak = g["V"], g["tokens"], g["peak"]
+    base = np.zeros((1, 4, V), np.float32)
+    for k, name in enumerate("EFGH"):
+        base[0, k, t[name]] = peak
+    target = np.zeros((1, 5, V), np.float32)
+    target[0, 0], target[0, 1] = base[0, 0], base[0, 1]
+    target[0, 2, t["K"]] = peak
+    inp = dict(base=base, target=target, W1=np.zeros((V, 16), np.float32),
+               W2=np.zeros((16, V), np.float32), w_dtype="f32", rows=np.array([0]),
+               anchor=np.array([t["D"]], np.int32), u_draft=np.full((1, 4), 0.5, np.float32),
+               u_accept=np.full((1, 4), 0.5, np.float32), u_final=np.full(1, 0.5, np.float32),
+               conf=np.array([g["conf"]], np.float32), sps=np.array(g["sps_B_1_to_5"], np.float32))
+    gpu = gpu_round(inp, T)
+    e = g["expected"]
+    assert gpu["draft_tokens"][0].tolist() == e["draft_tokens"]
+    assert gpu["verify_len"][0] == e["verify_len"]
+    assert gpu["accept_len"][0] == e["accept_len"]
+    assert gpu["out_tokens"][0].tolist() == e["out_tokens"]
+
+
+# ---------------------------------------------------------------------------
+# scheduler: bit-exact lengths
+
+
+def _gpu_schedule(conf, sps):
+    dev = torch.device("cuda:0")
+    c = torch.from_numpy(conf).to(dev)
+    s = torch.from_numpy(sps).to(dev)
+    ws = torch.zeros(4096, dtype=torch.uint8, device=dev)
+    L, n, a = D.schedule(c, s, ws)
+    torch.cuda.synchronize()
+    return L.cpu().numpy(), int(n.cpu()[0]), a.cpu().numpy(), D.device_error(ws)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_schedule_bit_exact(seed):
+    rng = np.random.default_rng(100 + seed)
+    R = int(rng.integers(1, 600))
+    g = int(rng.integers(1, 17))
+    R = min(R, 8192 // g)
+    conf = rng.beta(6, 2, (R, g)).astype(np.float32)
+    if seed % 2:
+        conf[rng.random((R, g)) < 0.2] = 1.0       # ties
+    N = int(rng.integers(1, R * (g + 1) + 50))
+    B = np.arange(1, N + 1)
+    sps = (1.0 / (1.0 + rng.uniform(1e-4, 1e-2) * np.ceil(B / rng.integers(1, 128)))).astype(np.float32)
+    L, n, a, err = _gpu_schedule(conf, sps)
+    o = O.schedule(conf, sps)
+    assert err == 0
+    assert np.array_equal(a, o["cum_conf"])
+    assert n == o["n_admitted"]
+    assert np.array_equal(L, o["verify_len"])
+
+
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_schedule_workload_tables(cfg):
+    inp = make_inputs(cfg, rows=[0])
+    L, n, a, err = _gpu_schedule(inp["conf"], inp["sps"])
+    o = O.schedule(inp["conf"], inp["sps"])
+    say(f"cfg {cfg}: n* = {n} of {inp['conf'].size}")
+    assert err == 0 and n == o["n_admitted"] and np.array_equal(L, o["verify_len"])
+    assert 0 < n < inp["conf"].size
+
+
+def test_schedule_edge_tables():
+    conf = np.full((4, 5), 0.9, np.float32)
+    for sps, expect in [(np.ones(100, np.float32), 20), (np.ones(10, np.float32), 6),
+                        (np.ones(2, np.float32), 20)]:
+        L, n, a, err = _gpu_schedule(conf, sps)
+        assert n == O.schedule(conf, sps)["n_admitted"] == expect
+        assert np.array_equal(L, O.schedule(conf, sps)["verify_len"])
+
+
+# ---------------------------------------------------------------------------
+# stage parity: verify fed with the oracle's draft outputs
+
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_verify_stage_on_oracle_draft(T):
+    d = config(1, R=64, gamma=6, V=4096, r=64, w_dtype="bf16", target=("uniform", 0.2, 1.5))
+    inp = make_inputs(d, seed=21)
+    od = O.draft(inp["base"], inp["W1"], inp["W2"], inp["w_dtype"], inp["anchor"], inp["u_draft"], T)
+    L = O.schedule(inp["conf"], inp["sps"])["verify_len"]
+    ov = O.verify(inp["target"], inp["base"], inp["W1"], inp["W2"], inp["w_dtype"], inp["anchor"],
+                  od["tokens"], od["probs"], L, inp["u_accept"], inp["u_final"], T)
+    dd = to_dev(inp)
+    dev = dd["base"].device
+    ws = D.new_workspace(64, 6, 4096, 64, dev)
+    tok = torch.from_numpy(od["tokens"]).to(dev)
+    prob = torch.from_numpy(od["probs"].astype(np.float32)).to(dev)
+    stats = torch.from_numpy(od["stats"].astype(np.float32)).to(dev)
+    Ld = torch.from_numpy(L).to(dev)
+    ot, al, tp = D.verify(dd["target"], dd["base"], dd["W1"], dd["W2"], dd["anchor"], tok, prob, stats,
+                          Ld, dd["u_accept"], dd["u_final"], T, ws)
+    torch.cuda.synchronize()
+    assert D.device_error(ws) == 0
+    flags = (ov["accept_margin"] < O.FLAG_EPS).any(axis=1) | (ov["final_margin"] < O.FLAG_EPS)
+    ok = ~flags
+    say(f"verify stage T={T}: flagged {int(flags.sum())} of {len(flags)}")
+    assert np.array_equal(al.cpu().numpy()[ok], ov["accept_len"][ok])
+    assert np.array_equal(ot.cpu().numpy()[ok], ov["out_tokens"][ok])
+    np.testing.assert_allclose(tp.cpu().numpy()[ok], ov["target_probs"][ok], atol=1e-4, rtol=1e-5)
+
+
+def test_draft_stage_bias_exact_in_fp32():
+    """bf16 products are exact in fp32: the draft statistics track the fp64 oracle closely."""
+    d = config(1, R=8, gamma=3, V=4096, r=256, w_dtype="bf16")
+    inp = make_inputs(d, seed=5)
+    gpu = gpu_round(inp, 1.0)
+    od = O.draft(inp["base"], inp["W1"], inp["W2"], inp["w_dtype"], inp["anchor"], inp["u_draft"], 1.0)
+    ok = ~(od["margin"] < O.FLAG_EPS).any(axis=1)
+    np.testing.assert_allclose(gpu["draft_stats"][ok][..., 0], od["stats"][ok][..., 0], atol=2e-6)
+    np.testing.assert_allclose(gpu["draft_stats"][ok][..., 1], od["stats"][ok][..., 1], rtol=2e-6)
+
+
+# ---------------------------------------------------------------------------
+# determinism, device-side error reporting
+
+
+def test_deterministic_replay():
+    d = config(1, R=48, gamma=7, V=8192, r=128, w_dtype="bf16")
+    inp = make_inputs(d, seed=8)
+    a = gpu_round(inp, 1.0)
+    b = gpu_round(inp, 1.0)
+    for k in ("draft_tokens", "draft_probs", "draft_stats", "out_tokens", "accept_len", "target_probs"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_device_error_bits():
+    d = config(1, w_dtype="bf16")
+    inp = make_inputs(d, seed=9)
+    inp["anchor"] = inp["anchor"].copy()
+    inp["anchor"][1] = 10 ** 6           # token id out of range
+    inp["u_draft"] = inp["u_draft"].copy()
+    inp["u_draft"][2, 1] = 1.0           # uniform outside [0, 1)
+    gpu = gpu_round(inp, 1.0)
+    assert gpu["device_error"] & 8 and gpu["device_error"] & 2
+    inp2 = make_inputs(d, seed=9)
+    inp2["base"] = inp2["base"].copy()
+    inp2["base"][0, 0, 5] = np.nan
+    gpu2 = gpu_round(inp2, 1.0)
+    assert gpu2["device_error"] & 1
+
+
+# ---------------------------------------------------------------------------
+# lossless property on the GPU: chi-square of the first emitted token
+
+
+def test_chi_square_first_token_gpu():
+    from scipy import stats, special
+    R, g, V, r = 1 << 20, 2, 16, 16
+    rng = np.random.default_rng(40)
+    base1 = (rng.standard_normal((g, V)) * 1.5).astype(np.float32)
+    tgt1 = (base1[0] + rng.standard_normal(V) * 0.8).astype(np.float32)
+    w1 = bf16_bits_from_f32((rng.standard_normal((V, r)) * 0.3).astype(np.float32))
+    w2 = bf16_bits_from_f32((rng.standard_normal((r, V)) * 0.3).astype(np.float32))
+    ur = np.random.default_rng(41)
+    inp = dict(base=np.broadcast_to(base1, (R, g, V)),
+               target=np.broadcast_to(np.stack([tgt1, base1[1], base1[0]]), (R, g + 1, V)),
+               W1=w1, W2=w2, w_dtype="bf16", anchor=np.full(R, 3, np.int32),
+               u_draft=ur.random((R, g), np.float32), u_accept=ur.random((R, g), np.float32),
+               u_final=ur.random(R, np.float32), conf=None, sps=None)
+    dd = to_dev(inp)
+    dev = dd["base"].device
+    ws = D.new_workspace(R, g, V, r, dev)
+    Lr = torch.ones(R, dtype=torch.int32, device=dev)
+    tok, prob, st = D.draft(dd["base"], dd["W1"], dd["W2"], dd["anchor"], dd["u_draft"], 1.0, ws)
+    ot, al, tp = D.verify(dd["target"], dd["base"], dd["W1"], dd["W2"], dd["anchor"], tok, prob, st, Lr,
+                          dd["u_accept"], dd["u_final"], 1.0, ws)
+    torch.cuda.synchronize()
+    y = ot[:, 0].cpu().numpy()
+    p = special.softmax(tgt1.astype(np.float64))
+    obs = np.bincount(y, minlength=V).astype(np.float64)
+    pv = stats.chisquare(obs, p * R).pvalue
+    acc = (al.cpu().numpy() >= 1).mean()
+    W1 = O.widen_weights(w1, "bf16")
+    W2 = O.widen_weights(w2, "bf16")
+    q = special.softmax(base1[0].astype(np.float64) + W1[3] @ W2)
+    se = np.sqrt(acc * (1 - acc) / R)
+    say(f"chi-square p = {pv:.4f}; accept rate {acc:.5f} vs 1 - TV {np.minimum(p, q).sum():.5f}")
+    assert pv >= 1e-3
+    assert abs(acc - np.minimum(p, q).sum()) < 4 * se + 1e-6

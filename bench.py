@@ -158,15 +158,16 @@ def gpu_bench(a):
               sps=None if inp["sps"] is None else t(inp["sps"], np.float32))
     del inp
     ws = D.new_workspace(R, g, V, r, dev)
+    ws_sched = torch.zeros(256, dtype=torch.uint8, device=dev)
     T = a.temperature
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
 
     # one eager round: reference outputs and workload statistics
     with torch.cuda.stream(stream):
-        ref = D.run_round(dd, T, ws)
+        ref = D.run_round(dd, T, ws, ws_sched=ws_sched)
     torch.cuda.synchronize()
-    if D.device_error(ws) != 0:
+    if D.device_error(ws) != 0 or D.device_error(ws_sched) != 0:
         raise RuntimeError("device-side data error in the benchmark inputs")
     ref = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in ref.items()}
 
@@ -176,7 +177,7 @@ def gpu_bench(a):
     if use_graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
-            out = D.run_round(dd, T, ws)
+            out = D.run_round(dd, T, ws, ws_sched=ws_sched)
         torch.cuda.synchronize()
         # replays must reproduce the eager round exactly, replay after replay
         for _ in range(3):
@@ -190,7 +191,7 @@ def gpu_bench(a):
         if use_graph:
             graph.replay()
         else:
-            D.run_round(dd, T, ws)
+            D.run_round(dd, T, ws, ws_sched=ws_sched)
 
     def timed(fn, n):
         t0 = torch.cuda.Event(enable_timing=True)
@@ -223,7 +224,7 @@ def gpu_bench(a):
     stops = ArrT(*[e.cuda_event for e in ev_e])
     lib.dspark_profile_arm(KID_DRAFT_PARTIALS, starts, stops, n_prof)
     with torch.cuda.stream(stream):
-        ms_eager = timed(lambda: D.run_round(dd, T, ws), a.steps)
+        ms_eager = timed(lambda: D.run_round(dd, T, ws, ws_sched=ws_sched), a.steps)
     used = lib.dspark_profile_disarm()
     k1_ms = sum(s.elapsed_time(e) for s, e in zip(ev_s[:used], ev_e[:used])) / max(used, 1)
 

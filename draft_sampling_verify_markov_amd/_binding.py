@@ -192,15 +192,39 @@ def verify(target, base, W1, W2, anchor, draft_tokens, draft_probs, draft_stats,
     return ot, al, tp
 
 
-def run_round(dev_inputs, temperature, ws, use_scheduler=True):
-    """draft -> schedule -> verify on a dict of device tensors (see bench.py)."""
+_side_streams = {}
+
+
+def _side_stream(device):
+    if device not in _side_streams:
+        _side_streams[device] = torch.cuda.Stream(device=device)
+    return _side_streams[device]
+
+
+def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None):
+    """draft -> schedule -> verify on a dict of device tensors.
+
+    The scheduler reads only confidences and the cost table, so it runs on a
+    side stream concurrently with the draft (forked from and joined back to
+    the current stream; capturable into a HIP graph).  It uses its own small
+    workspace ``ws_sched`` (allocated here if not given).
+    """
     d = dev_inputs
+    dev = d["base"].device
+    cur = torch.cuda.current_stream(dev)
+    L = n = None
+    sched = use_scheduler and d.get("conf") is not None
+    if sched:
+        if ws_sched is None:
+            ws_sched = torch.zeros(256, dtype=torch.uint8, device=dev)
+        side = _side_stream(dev)
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            L, n, _ = schedule(d["conf"], d["sps"], ws_sched, with_cum=False)
     tok, prob, stats = draft(d["base"], d["W1"], d["W2"], d["anchor"], d["u_draft"], temperature, ws)
-    L = None
-    n = None
-    if use_scheduler and d.get("conf") is not None:
-        L, n, _ = schedule(d["conf"], d["sps"], ws, with_cum=False)
+    if sched:
+        cur.wait_stream(side)
     ot, al, tp = verify(d["target"], d["base"], d["W1"], d["W2"], d["anchor"], tok, prob, stats, L,
                         d["u_accept"], d["u_final"], temperature, ws)
     return dict(draft_tokens=tok, draft_probs=prob, draft_stats=stats, verify_len=L, n_admitted=n,
-                out_tokens=ot, accept_len=al, target_probs=tp)
+                out_tokens=ot, accept_len=al, target_probs=tp, ws_sched=ws_sched)

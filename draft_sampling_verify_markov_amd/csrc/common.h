@@ -80,7 +80,7 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
 // thread t gets the sum of the values of threads 0..t-1, computed by a fixed
 // tree (deterministic).  `tmp` is __shared__ T[256].
 template <typename T>
-__device__ inline T block_exscan_256(T v, T* tmp) {
+__device__ __forceinline__ T block_exscan_256(T v, T* tmp) {
   const int t = threadIdx.x;
   tmp[t] = v;
   __syncthreads();
@@ -401,6 +401,53 @@ __device__ __forceinline__ void load_row_cols(rsrc_t rs, uint32_t roff, bool row
     const bool ok = rowv && c0 + 16 * g < V;
     const f32x4 lo = __builtin_bit_cast(f32x4, buf_u32x4(rs, voff, (uint32_t)g * 64u));
     const f32x4 hi = __builtin_bit_cast(f32x4, buf_u32x4(rs, voff, (uint32_t)g * 64u + 16u));
+    const float ninf = -INFINITY;
+    out[0][4 * g + 0] = ok ? lo[0] : ninf;
+    out[1][4 * g + 0] = ok ? lo[1] : ninf;
+    out[0][4 * g + 1] = ok ? lo[2] : ninf;
+    out[1][4 * g + 1] = ok ? lo[3] : ninf;
+    out[0][4 * g + 2] = ok ? hi[0] : ninf;
+    out[1][4 * g + 2] = ok ? hi[1] : ninf;
+    out[0][4 * g + 3] = ok ? hi[2] : ninf;
+    out[1][4 * g + 3] = ok ? hi[3] : ninf;
+  }
+}
+
+// Row-contiguous staging of logit rows through LDS.  Reading a 32-row block
+// so that each load instruction covers 1 KiB of a single row (instead of one
+// 32-byte piece of 32 rows, as the MFMA output layout would) doubles the
+// achieved HBM bandwidth on rows that are megabytes apart.
+//
+// Block rb of a 128-row chunk: wave w loads rows 4i + w (i = 0..7) of the
+// block, lane l columns [tile0 + 4l, tile0 + 4l + 4).  Staged row stride:
+constexpr int BSTRIDE = TILE + 4;  // floats
+
+__device__ __forceinline__ void stage_load(u32x4 (&v)[8], rsrc_t rs, uint32_t row_bytes, int rb,
+                                           int nrows, int V, int tile0) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col = tile0 + 4 * lane;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int rl = rb * 32 + 4 * i + wave;
+    const bool ok = rl < nrows && col < V;
+    v[i] = buf_u32x4(rs, ok ? (uint32_t)rl * row_bytes + (uint32_t)col * 4u : 0u, 0u);
+  }
+}
+__device__ __forceinline__ void stage_store(const u32x4 (&v)[8], float* X) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < 8; i++) *reinterpret_cast<u32x4*>(X + (4 * i + wave) * BSTRIDE + 4 * lane) = v[i];
+}
+// The lane's bias-block columns of staged row j (= lane & 31); invalid -> -inf.
+__device__ __forceinline__ void stage_read(const float* X, bool rowv, int V, int cbase, int wcol0,
+                                           float (&out)[2][16]) {
+  const int lane = threadIdx.x & 63, j = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int g = 0; g < 4; g++) {
+    const int c = wcol0 + 16 * g + 8 * h;
+    const bool ok = rowv && cbase + 16 * g + 8 * h < V;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(X + j * BSTRIDE + c);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(X + j * BSTRIDE + c + 4);
     const float ninf = -INFINITY;
     out[0][4 * g + 0] = ok ? lo[0] : ninf;
     out[1][4 * g + 0] = ok ? lo[1] : ninf;

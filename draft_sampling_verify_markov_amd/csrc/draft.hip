@@ -59,41 +59,41 @@ __device__ __forceinline__ float shifted(float b, float m, float bias, float inv
 template <typename WT, bool GREEDY, int KS>
 __global__ __launch_bounds__(256) void k_draft_partials(DraftStep<WT> P) {
   constexpr int APAD = BiasBlock<WT>::APAD;
-  __shared__ __align__(16) WT A_lds[RCH * (DSPARK_MAX_RANK + APAD)];
+  constexpr int A_ELEMS = RCH * (DSPARK_MAX_RANK + APAD);
+  static_assert(A_ELEMS * sizeof(WT) >= 2 * 32 * BSTRIDE * sizeof(float), "staging fits the W1 block");
+  // The gathered W1 block; after the MFMA the same bytes stage base rows.
+  __shared__ __align__(16) WT A_lds[A_ELEMS];
   __shared__ float red_m[4][RCH];
   __shared__ float red_s[4][RCH];
   __shared__ int red_i[4][RCH];
+  float* const X0 = reinterpret_cast<float*>(A_lds);
+  float* const X1 = X0 + 32 * BSTRIDE;
 
   const int a_stride = P.r + APAD;
   const int tile = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 31, h = lane >> 5;
-  const int cbase = tile * TILE + wave * WCOLS;
+  const int tile0 = tile * TILE;
+  const int cbase = tile0 + wave * WCOLS;
   const int nt = gridDim.x;
   const bool t_one = (P.T == 1.0f);
+  const uint32_t row_bytes = (uint32_t)(P.gamma * P.V) * 4u;
 
   for (int c0 = 0; c0 < P.R; c0 += RCH) {
     const int nrows = min(RCH, P.R - c0), nrb = ceil_div(nrows, 32);
-    // W2 slice of this wave for the whole k range: in flight while the W1 rows
-    // are gathered and the base logits are prefetched (re-read per 128-row
-    // chunk so the fragment registers are free after each chunk's MFMA).
+    // W2 slice of this wave for the whole k range (re-read per 128-row chunk so
+    // the fragment registers are free after each chunk's MFMA).
     typename BiasBlock<WT>::template Frag<KS> F;
     BiasBlock<WT>::template load<KS>(F, P.W2, P.V, P.r, cbase);
     __syncthreads();
     gather_w1_rows<WT, KS * sizeof(WT) / 2>(P.W1, P.V, P.r, nrows, nrb * 32, A_lds, a_stride,
                                             [&](int i) { return P.prev_token(c0 + i); });
-    // base logits: row blocks 0-1 now (in flight during the MFMA), 2-3 after it,
-    // when the W2 fragment registers are free.  Rows of this chunk are
-    // addressed from the chunk's first base row.
+    // base rows of this chunk, addressed from its first row: blocks 0-1 in
+    // flight during the MFMA, 2-3 during the first two epilogues
     const size_t first = (size_t)c0 * P.gamma + (P.k - 1);
     const rsrc_t brs = make_rsrc(P.base + first * P.V, ((size_t)P.R * P.gamma - first) * P.V * 4);
-    float b[4][2][16];
-    auto load_base = [&](int rb) {
-      const int rl = rb * 32 + j;
-      const bool rowv = rb < nrb && rl < nrows;
-      load_row_cols(brs, (uint32_t)rl * (uint32_t)(P.gamma * P.V) * 4u, rowv, P.V, cbase, b[rb]);
-    };
-    load_base(0);
-    load_base(1);
+    u32x4 va[8], vb[8];
+    stage_load(va, brs, row_bytes, 0, nrows, P.V, tile0);
+    stage_load(vb, brs, row_bytes, 1, nrows, P.V, tile0);
     __syncthreads();
 
     f32x16 acc[4][2];
@@ -104,14 +104,26 @@ __global__ __launch_bounds__(256) void k_draft_partials(DraftStep<WT> P) {
 #pragma unroll
         for (int t = 0; t < 16; t++) acc[rb][p][t] = 0.f;
     BiasBlock<WT>::template mma<KS>(F, P.r, A_lds, a_stride, nrb, acc);
-    load_base(2);
-    load_base(3);
+    __syncthreads();  // the W1 block is dead: reuse its bytes for staging
+    stage_store(va, X0);
+    stage_store(vb, X1);
+    stage_load(va, brs, row_bytes, 2, nrows, P.V, tile0);
+    stage_load(vb, brs, row_bytes, 3, nrows, P.V, tile0);
+    __syncthreads();
 
 #pragma unroll
     for (int rb = 0; rb < 4; rb++) {
       if (rb >= nrb) break;
+      if (rb == 2) {
+        __syncthreads();
+        stage_store(va, X0);
+        stage_store(vb, X1);
+        __syncthreads();
+      }
       const int rl = rb * 32 + j, row = c0 + rl;
       const bool rowv = rl < nrows;
+      float b[2][16];
+      stage_read((rb & 1) ? X1 : X0, rowv, P.V, cbase, wave * WCOLS, b);
       float4* rec = P.trec + ((size_t)row * nt + tile) * 2;
 
       if (GREEDY) {
@@ -122,7 +134,7 @@ __global__ __launch_bounds__(256) void k_draft_partials(DraftStep<WT> P) {
         for (int t = 0; t < 16; t++)
 #pragma unroll
           for (int p = 0; p < 2; p++) {
-            const float z = b[rb][p][t] + acc[rb][p][t];
+            const float z = b[p][t] + acc[rb][p][t];
             bad |= (z != z);
             if (z > bv) { bv = z; bi = cbase + elem_col(p, t, h); }
           }
@@ -142,7 +154,7 @@ __global__ __launch_bounds__(256) void k_draft_partials(DraftStep<WT> P) {
 #pragma unroll
         for (int p = 0; p < 2; p++)
 #pragma unroll
-          for (int t = 0; t < 16; t++) ml = fmaxf(ml, b[rb][p][t] + acc[rb][p][t]);
+          for (int t = 0; t < 16; t++) ml = fmaxf(ml, b[p][t] + acc[rb][p][t]);
         const float mw = fmaxf(ml, __shfl_xor(ml, 32));
         if (h == 0) red_m[wave][rl] = mw;
         __syncthreads();
@@ -151,7 +163,7 @@ __global__ __launch_bounds__(256) void k_draft_partials(DraftStep<WT> P) {
 #pragma unroll
         for (int p = 0; p < 2; p++)
 #pragma unroll
-          for (int t = 0; t < 16; t++) e[p][t] = exp_acc(shifted(b[rb][p][t], mt, acc[rb][p][t], P.invT, t_one));
+          for (int t = 0; t < 16; t++) e[p][t] = exp_acc(shifted(b[p][t], mt, acc[rb][p][t], P.invT, t_one));
         const float sl = tree_sum32(e);
         const float sw = sl + __shfl_xor(sl, 32);
         if (h == 0) red_s[wave][rl] = sw;

@@ -54,7 +54,7 @@ __device__ __forceinline__ int wave_max_i(int v) {
 
 // recs: the row's records (2 float4 per tile).  use_shift: weights are
 // s * exp((m - M) / T) (softmax partials) or plain s (residual mass, m = 0).
-__device__ inline TilePick wave_select_tile(const float4* __restrict__ recs, int nt, bool use_shift,
+__device__ __forceinline__ TilePick wave_select_tile(const float4* __restrict__ recs, int nt, bool use_shift,
                                             double invTd, double u) {
   const int lane = threadIdx.x & 63;
   const int per = ceil_div(nt, 64);
@@ -80,7 +80,7 @@ __device__ inline TilePick wave_select_tile(const float4* __restrict__ recs, int
   for (int i = 0; i < MAX_TPL; i++) {
     w[i] = 0.0;
     if (t0 + i < t1)
-      w[i] = use_shift ? (double)s[i] * exp(((double)m[i] - (double)M) * invTd) : (double)s[i];
+      w[i] = use_shift ? (double)s[i] * (double)exp_acc((m[i] - M) * (float)invTd) : (double)s[i];
     loc += w[i];
   }
   double incl_unused;
@@ -134,7 +134,7 @@ __device__ inline TilePick wave_select_tile(const float4* __restrict__ recs, int
     csw = make_float4(__shfl(lsw.x, owner), __shfl(lsw.y, owner), __shfl(lsw.z, owner),
                       __shfl(lsw.w, owner));
   }
-  P.scale = use_shift ? exp(((double)P.mt - (double)M) * invTd) : 1.0;
+  P.scale = use_shift ? (double)exp_acc((P.mt - M) * (float)invTd) : 1.0;
   // chunk inside the tile (uniform across the wave)
   const float cs[4] = {csw.x, csw.y, csw.z, csw.w};
   double c = 0.0;
@@ -163,7 +163,7 @@ __device__ inline TilePick wave_select_tile(const float4* __restrict__ recs, int
 // Gather the 64 chunk values held by lanes 0 and 32 (bias-block layout,
 // element (p, t) of lane 32h is column 16(t/4) + 8h + 2(t%4) + p) so that
 // lane c receives column c.
-__device__ inline float chunk_to_lanes(const float (&v)[2][16]) {
+__device__ __forceinline__ float chunk_to_lanes(const float (&v)[2][16]) {
   const int c = threadIdx.x & 63;
   const int src = ((c >> 3) & 1) * 32;
   const int want_t = 4 * (c >> 4) + ((c >> 1) & 3), want_p = c & 1;
@@ -180,7 +180,7 @@ __device__ inline float chunk_to_lanes(const float (&v)[2][16]) {
 
 // Inverse-CDF pick among 64 per-lane values (lane c = column c): smallest c
 // with rem < scale * sum_{i <= c} v_i, else the last c with v_c > 0.
-__device__ inline int wave_pick64(float v, double scale, double rem) {
+__device__ __forceinline__ int wave_pick64(float v, double scale, double rem) {
   const int lane = threadIdx.x & 63;
   double incl;
   wave_excl_scan_d((double)v * scale, &incl);

@@ -181,7 +181,7 @@ __global__ __launch_bounds__(256) void k_verify_decide(VerifyArgs<WT> P) {
       const float M = wave_max(ml);
       double zl = 0.0;
       for (int t = lane; t < nvt; t += 64)
-        zl += (double)vp[t].y * exp(((double)vp[t].x - (double)M) * invTd);
+        zl += (double)vp[t].y * (double)exp_acc((vp[t].x - M) * (float)invTd);
       const double Z = wave_sum_d(zl);
       if (lane == 0) {
         P.rowstat[rowj] = make_double2((double)M, Z);
@@ -224,7 +224,7 @@ struct ResidualRow {
 
 // Rows of requests c0.. are addressed from request c0's first base / target row.
 template <typename WT>
-__device__ inline ResidualRow residual_row(const VerifyArgs<WT>& P, int c0, int row, bool valid) {
+__device__ __forceinline__ ResidualRow residual_row(const VerifyArgs<WT>& P, int c0, int row, bool valid) {
   ResidualRow rr;
   rr.valid = valid;
   rr.Mt = 0.f; rr.invZt = 0.f; rr.mq = 0.f; rr.invZq = 0.f;
@@ -251,7 +251,7 @@ __device__ inline ResidualRow residual_row(const VerifyArgs<WT>& P, int c0, int 
 // max(0, p - pi) at the lane's 32 columns: p from the target row, pi from the
 // recomputed draft logits ((base - m_q) + bias) / T normalised by Z_q.
 template <typename WT>
-__device__ inline void residual_values(const VerifyArgs<WT>& P, const ResidualRow& rr, int cbase,
+__device__ __forceinline__ void residual_values(const VerifyArgs<WT>& P, const ResidualRow& rr, int cbase,
                                        const f32x16 (&acc)[2], float (&d)[2][16]) {
   float b[2][16], t[2][16];
   load_row_cols(rr.brs, rr.boff, rr.valid, P.V, cbase, b);
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256) void k_residual_partials(VerifyArgs<WT> P) {
 // partials: fp64 scan over tiles, then the recomputed tile (same per-element
 // arithmetic and lane mapping as the stream kernel).
 template <typename WT>
-__device__ int wave_sample_target_row(const VerifyArgs<WT>& P, size_t rowj, double u) {
+__device__ __forceinline__ int wave_sample_target_row(const VerifyArgs<WT>& P, size_t rowj, double u) {
   const int lane = threadIdx.x & 63;
   const int nvt = ceil_div(P.V, VTILE);
   const float2* vp = P.vpart + rowj * nvt;
@@ -351,7 +351,7 @@ __device__ int wave_sample_target_row(const VerifyArgs<WT>& P, size_t rowj, doub
   for (int t = t0; t < t1; t++) mloc = fmaxf(mloc, vp[t].x);
   const float M = wave_max(mloc);
   double loc = 0.0;
-  for (int t = t0; t < t1; t++) loc += (double)vp[t].y * exp(((double)vp[t].x - (double)M) * invTd);
+  for (int t = t0; t < t1; t++) loc += (double)vp[t].y * (double)exp_acc((vp[t].x - M) * (float)invTd);
   double incl_unused;
   const double ex = wave_excl_scan_d(loc, &incl_unused);
   const double Z = __shfl(ex + loc, (nvt - 1) / per);
@@ -359,7 +359,7 @@ __device__ int wave_sample_target_row(const VerifyArgs<WT>& P, size_t rowj, doub
   int found = 0x7fffffff, lastpos = -1;
   double before = 0.0, cum = 0.0;
   for (int t = t0; t < t1; t++) {
-    const double w = (double)vp[t].y * exp(((double)vp[t].x - (double)M) * invTd);
+    const double w = (double)vp[t].y * (double)exp_acc((vp[t].x - M) * (float)invTd);
     const double pp = cum;
     cum += w;
     if (found == 0x7fffffff && target < ex + cum) { found = t; before = ex + pp; }
@@ -374,7 +374,7 @@ __device__ int wave_sample_target_row(const VerifyArgs<WT>& P, size_t rowj, doub
     rem = INFINITY;
   }
   const float mt = vp[tstar].x;
-  const double scale = exp(((double)mt - (double)M) * invTd);
+  const double scale = (double)exp_acc((mt - M) * (float)invTd);
   const float* trow = P.target + rowj * P.V;
   // lane l holds columns tstar*1024 + f*256 + 4l + e (the stream kernel's mapping)
   double carry = 0.0;

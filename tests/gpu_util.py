@@ -47,7 +47,10 @@ def gpu_round(inp, T, use_scheduler=None, device=None):
     out = D.run_round(d, T, ws, use_scheduler=use_scheduler)
     torch.cuda.synchronize()
     err = D.device_error(ws)
-    res = {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in out.items()}
+    if out["ws_sched"] is not None:
+        err |= D.device_error(out["ws_sched"])
+    res = {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in out.items()
+           if k != "ws_sched"}
     res["device_error"] = err
     return res
 
@@ -82,6 +85,14 @@ def compare_rounds(orc, gpu, rows=None, label=""):
     assert len(bad_acc) == 0, f"{label}: accept_len differs on rows {bad_acc[:10]}"
     bad_out = np.flatnonzero(ok & (g_out != v["out_tokens"]).any(axis=1))
     assert len(bad_out) == 0, f"{label}: out_tokens differ on rows {bad_out[:10]}"
+    # flagged rows: the draft must still agree up to the first event near a boundary
+    dflag = d["margin"] < O.FLAG_EPS
+    g_len = dflag.shape[1]
+    first = np.where(dflag.any(axis=1), dflag.argmax(axis=1), g_len)
+    for i in np.flatnonzero(flags):
+        assert (g_tok[i, :first[i]] == d["tokens"][i, :first[i]]).all(), f"{label}: row {i} prefix"
+    same = (g_out == v["out_tokens"]).all(axis=1) & (g_tok == d["tokens"]).all(axis=1)
+    say(f"[{label}] flagged rows that still match exactly: {int((same & flags).sum())}/{n_flag}")
     np.testing.assert_allclose(g_prob[ok], d["probs"][ok], atol=ATOL, rtol=RTOL, err_msg=label + " q")
     np.testing.assert_allclose(g_stats[ok], d["stats"][ok], atol=ATOL, rtol=RTOL, err_msg=label + " stats")
     np.testing.assert_allclose(g_tp[ok], v["target_probs"][ok], atol=ATOL, rtol=RTOL, err_msg=label + " p")

@@ -41,7 +41,7 @@ def _whole_round_properties(gpu, d):
     assert ((tp[k <= lim[:, None]] >= 0) & (tp[k <= lim[:, None]] <= 1)).all()
 
 
-@pytest.mark.parametrize("cfg,T,nrows", [(3, 1.0, 12), (4, 1.0, 8), (4, 0.0, 8), (5, 1.0, 8)])
+@pytest.mark.parametrize("cfg,T,nrows", [(3, 1.0, 40), (4, 1.0, 16), (4, 0.0, 16), (5, 1.0, 24)])
 def test_fullsize_sampled_rows(cfg, T, nrows):
     d = config(cfg)
     say(f"[cfg {cfg} T={T}] generating R={d['R']} gamma={d['gamma']} V={d['V']}")

@@ -267,3 +267,36 @@ def test_chi_square_first_token_gpu():
     say(f"chi-square p = {pv:.4f}; accept rate {acc:.5f} vs 1 - TV {np.minimum(p, q).sum():.5f}")
     assert pv >= 1e-3
     assert abs(acc - np.minimum(p, q).sum()) < 4 * se + 1e-6
+
+
+# ---------------------------------------------------------------------------
+# HIP graph capture of the whole round (scheduler on a forked side stream)
+
+
+def test_graph_replay_matches_eager():
+    d = config(1, R=32, gamma=5, V=4096, r=64, w_dtype="bf16")
+    inp = make_inputs(d, seed=31)
+    dd = to_dev(inp)
+    dev = dd["base"].device
+    ws = D.new_workspace(32, 5, 4096, 64, dev)
+    ws_sched = torch.zeros(256, dtype=torch.uint8, device=dev)
+    keys = ("draft_tokens", "draft_probs", "out_tokens", "accept_len", "verify_len", "target_probs")
+    ref = D.run_round(dd, 1.0, ws, ws_sched=ws_sched)
+    torch.cuda.synchronize()
+    ref = {k: ref[k].clone() for k in keys}
+    s = torch.cuda.Stream(device=dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        D.run_round(dd, 1.0, ws, ws_sched=ws_sched)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        out = D.run_round(dd, 1.0, ws, ws_sched=ws_sched)
+    for i in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        for k in keys:
+            assert torch.equal(out[k], ref[k]), (i, k)
+        # eager work between replays, on the same workspace
+        D.run_round(dd, 1.0, ws, ws_sched=ws_sched)
+        torch.cuda.synchronize()
+    assert D.device_error(ws) == 0 and D.device_error(ws_sched) == 0

@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="launch kernels eagerly instead of a graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after timing, run 3 device-to-device copies of this size (counter calibration)")
     ap.add_argument("--cpu-baseline-worker", action="store_true", help=argparse.SUPPRESS)
     return ap.parse_args()
 
@@ -227,6 +229,17 @@ def gpu_bench(a):
         ms_eager = timed(lambda: D.run_round(dd, T, ws, ws_sched=ws_sched), a.steps)
     used = lib.dspark_profile_disarm()
     k1_ms = sum(s.elapsed_time(e) for s, e in zip(ev_s[:used], ev_e[:used])) / max(used, 1)
+
+    if a.copy_calibration_mib > 0:
+        # plain copy of a known size: the HBM counters of its kernel calibrate
+        # FETCH_SIZE / WRITE_SIZE readings of the round's kernels
+        n = a.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     A = ref["accept_len"].cpu().numpy().astype(np.int64)
     L = (ref["verify_len"].cpu().numpy() if ref["verify_len"] is not None else np.full(R, g))

@@ -41,6 +41,14 @@ struct ProfState {
 };
 static thread_local ProfState prof;
 
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return 256;
+  return n;
+}
+
 void prof_before(int kid, hipStream_t stream) {
   if (prof.kid == kid && prof.used < prof.n) (void)hipEventRecord(prof.starts[prof.used], stream);
 }

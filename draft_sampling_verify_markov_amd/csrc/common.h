@@ -33,18 +33,14 @@ constexpr int NO_REJECT = 1 << 30;
 __host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // ---------------------------------------------------------------------------
-// exp(x) for the softmax weights.  2^(x log2 e) with the rounding error of the
-// product x*log2(e) carried separately (split-constant method), so the result
-// keeps v_exp_f32's ~1 ulp accuracy for the arguments used here (x <= ~0).
-// Arguments below -100 return 0 (also -inf); NaN propagates.
+// exp(x) for the softmax weights: 2^(x log2 e) on v_exp_f32.  The relative
+// error is about (|x| + 1) * 6e-8 with a random sign per element; weighted by
+// the probabilities it moves a CDF value by far less than 1e-7 (x <= ~0 here:
+// arguments are shifted by the running maximum).  Arguments below -100
+// return 0 (also -inf); NaN propagates.
 __device__ __forceinline__ float exp_acc(float x) {
   const float L2E = 1.44269502162933349609375f;  // fp32 nearest to log2(e)
-  const float L2E_LO = 1.925963033500011e-8f;    // log2(e) - L2E
-  const float LN2 = 0.693147180559945309f;
-  float t = x * L2E;
-  float err = fmaf(x, L2E, -t) + x * L2E_LO;
-  float e = __builtin_amdgcn_exp2f(t);
-  float r = fmaf(e, err * LN2, e);
+  const float r = __builtin_amdgcn_exp2f(x * L2E);
   return (x < -100.f) ? 0.f : r;
 }
 
@@ -175,24 +171,26 @@ struct BiasBlock<uint16_t> {
   struct Frag {
     uint32_t w[KS][8];
   };
+  // Columns past V load column 0 (a finite weight): every consumer masks
+  // those columns through the logits it adds (-inf there), so no select is
+  // applied here and the loads stay in flight until the first MFMA needs them.
+  // One k step of the fragment (rows kk*16 + 8h + e, e < 8); ks >= r/16
+  // repeats the last step (never multiplied).
+  __device__ static __forceinline__ void load_ks(uint32_t (&w)[8], const uint16_t* __restrict__ W2,
+                                                 int V, int r, int cbase, int ks) {
+    const int lane = threadIdx.x & 63, j = lane & 31, h = lane >> 5;
+    const int col = cbase + 2 * j;
+    const rsrc_t rs = make_rsrc(W2, (size_t)r * V * 2);
+    const uint32_t voff = (uint32_t)(8 * h * V + (col < V ? col : 0)) * 2u;
+    const int kk = min(ks, r / 16 - 1);
+#pragma unroll
+    for (int e = 0; e < 8; e++) w[e] = buf_u32(rs, voff, (uint32_t)((kk * 16 + e) * V) * 2u);
+  }
   template <int KS>
   __device__ static __forceinline__ void load(Frag<KS>& F, const uint16_t* __restrict__ W2, int V,
                                               int r, int cbase) {
-    const int lane = threadIdx.x & 63, j = lane & 31, h = lane >> 5;
-    const int col = cbase + 2 * j;
-    const bool cv = col < V;
-    const rsrc_t rs = make_rsrc(W2, (size_t)r * V * 2);
-    const uint32_t voff = (uint32_t)(8 * h * V + (cv ? col : 0)) * 2u;
-    const int nks = r / 16;
 #pragma unroll
-    for (int ks = 0; ks < KS; ks++) {
-      const int kk = min(ks, nks - 1);
-#pragma unroll
-      for (int e = 0; e < 8; e++) {
-        const uint32_t x = buf_u32(rs, voff, (uint32_t)((kk * 16 + e) * V) * 2u);
-        F.w[ks][e] = cv ? x : 0u;
-      }
-    }
+    for (int ks = 0; ks < KS; ks++) load_ks(F.w[ks], W2, V, r, cbase, ks);
   }
   template <int KS>
   __device__ static __forceinline__ void operands(const Frag<KS>& F, int ks, bf16x8& a0, bf16x8& a1) {
@@ -205,26 +203,62 @@ struct BiasBlock<uint16_t> {
     a0 = __builtin_bit_cast(bf16x8, lo);
     a1 = __builtin_bit_cast(bf16x8, hi);
   }
-  // B operand row block: rows (rb*32 + j) of A_lds.
+  // B operand row block rb: rows (rb*32 + j) of A_lds.  All four row blocks are
+  // computed (rows past the request count are zero in A_lds), so the loop has
+  // no data-dependent branch and the LDS reads of a k step are issued together.
   template <int KS>
   __device__ static __forceinline__ void mma(const Frag<KS>& F, int r, const uint16_t* A_lds,
-                                             int a_stride, int nrb, f32x16 (&acc)[4][2]) {
+                                             int a_stride, int /*nrb*/, f32x16 (&acc)[4][2]) {
     const int lane = threadIdx.x & 63, j = lane & 31, h = lane >> 5;
     const int nks = r / 16;
+    const uint16_t* ap = A_lds + j * a_stride + 8 * h;
 #pragma unroll
     for (int ks = 0; ks < KS; ks++) {
       if (ks < nks) {
+        u32x4 bb[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; rb++)
+          bb[rb] = *reinterpret_cast<const u32x4*>(ap + rb * 32 * a_stride + ks * 16);
         bf16x8 a0, a1;
         operands(F, ks, a0, a1);
 #pragma unroll
         for (int rb = 0; rb < 4; rb++) {
-          if (rb < nrb) {
-            const u32x4 bb =
-                *reinterpret_cast<const u32x4*>(A_lds + (rb * 32 + j) * a_stride + ks * 16 + 8 * h);
-            const bf16x8 b = __builtin_bit_cast(bf16x8, bb);
-            acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc[rb][0], 0, 0, 0);
-            acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[rb][1], 0, 0, 0);
-          }
+          const bf16x8 b = __builtin_bit_cast(bf16x8, bb[rb]);
+          acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc[rb][0], 0, 0, 0);
+          acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[rb][1], 0, 0, 0);
+        }
+      }
+    }
+  }
+  // One row block: rows j of A_rows (32 requests) against the wave's 64
+  // columns; acc[p] as in mma.  The full-rank case has no branch in the k loop.
+  template <int KS>
+  __device__ static __forceinline__ void mma_rb(const Frag<KS>& F, int r, const uint16_t* A_rows,
+                                                int a_stride, f32x16 (&acc)[2]) {
+    const int lane = threadIdx.x & 63, j = lane & 31, h = lane >> 5;
+    const int nks = r / 16;
+    const uint16_t* ap = A_rows + j * a_stride + 8 * h;
+    if (nks == KS) {
+      u32x4 bb[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++) bb[ks] = *reinterpret_cast<const u32x4*>(ap + ks * 16);
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++) {
+        bf16x8 a0, a1;
+        operands(F, ks, a0, a1);
+        const bf16x8 b = __builtin_bit_cast(bf16x8, bb[ks]);
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[1], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++) {
+        if (ks < nks) {
+          bf16x8 a0, a1;
+          operands(F, ks, a0, a1);
+          const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ap + ks * 16));
+          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[1], 0, 0, 0);
         }
       }
     }
@@ -306,7 +340,7 @@ struct BiasBlock<float> {
       w2_at(F, k, w);
 #pragma unroll
       for (int rb = 0; rb < 4; rb++) {
-        if (rb < nrb) {
+        if (rb < nrb) {  // fp32 path: skip empty row blocks
           const float a = A_lds[(rb * 32 + j) * a_stride + k];
 #pragma unroll
           for (int g = 0; g < 4; g++)
@@ -316,6 +350,22 @@ struct BiasBlock<float> {
               for (int p = 0; p < 2; p++) acc[rb][p][4 * g + q] = fmaf(a, w[g][p][q], acc[rb][p][4 * g + q]);
         }
       }
+    }
+  }
+  template <int KS>
+  __device__ static inline void mma_rb(const Frag<KS>& F, int r, const float* A_rows, int a_stride,
+                                       f32x16 (&acc)[2]) {
+    const int j = (threadIdx.x & 63) & 31;
+    for (int k = 0; k < r; k++) {
+      float w[4][2][4];
+      w2_at(F, k, w);
+      const float a = A_rows[j * a_stride + k];
+#pragma unroll
+      for (int g = 0; g < 4; g++)
+#pragma unroll
+        for (int q = 0; q < 4; q++)
+#pragma unroll
+          for (int p = 0; p < 2; p++) acc[p][4 * g + q] = fmaf(a, w[g][p][q], acc[p][4 * g + q]);
     }
   }
   template <int KS>
@@ -363,28 +413,42 @@ __host__ __device__ inline int ks_bucket(int r) {
 // row 0 and is masked), then stores them.  tok(i) is supplied by a functor; a
 // negative token gives a zero row.  rows_cap * (r / EPV) must not exceed
 // 256 * PER, PER = the per-thread piece count (blockDim.x == 256).
+template <typename WT, int PER>
+struct W1Gather {
+  u32x4 v[PER];
+  int dst[PER];
+  // Issue the loads (registers only).
+  template <typename TokF>
+  __device__ __forceinline__ void load(const WT* __restrict__ W1, int V, int r, int nrows, int rows_cap,
+                                       int a_stride, TokF tok_of) {
+    constexpr int EPV = 16 / sizeof(WT);  // elements per 16-byte piece
+    const int pieces = r / EPV;
+    const int total = rows_cap * pieces;
+    const rsrc_t rs = make_rsrc(W1, (size_t)V * r * sizeof(WT));
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+      const int idx = threadIdx.x + 256 * i;
+      const int row = idx / pieces, pc = idx - row * pieces;
+      int t = -1;
+      if (idx < total && row < nrows) t = tok_of(row);
+      const u32x4 x = buf_u32x4<0>(rs, (uint32_t)(max(t, 0) * r + pc * EPV) * (uint32_t)sizeof(WT), 0u);
+      v[i] = (t >= 0) ? x : u32x4{0u, 0u, 0u, 0u};
+      dst[i] = (idx < total) ? row * a_stride + pc * EPV : -1;
+    }
+  }
+  __device__ __forceinline__ void store(WT* A_lds) const {
+#pragma unroll
+    for (int i = 0; i < PER; i++)
+      if (dst[i] >= 0) *reinterpret_cast<u32x4*>(A_lds + dst[i]) = v[i];
+  }
+};
+
 template <typename WT, int PER, typename TokF>
 __device__ __forceinline__ void gather_w1_rows(const WT* __restrict__ W1, int V, int r, int nrows,
                                                int rows_cap, WT* A_lds, int a_stride, TokF tok_of) {
-  constexpr int EPV = 16 / sizeof(WT);  // elements per 16-byte piece
-  const int pieces = r / EPV;
-  const int total = rows_cap * pieces;
-  const rsrc_t rs = make_rsrc(W1, (size_t)V * r * sizeof(WT));
-  u32x4 v[PER];
-  int dst[PER];
-#pragma unroll
-  for (int i = 0; i < PER; i++) {
-    const int idx = threadIdx.x + 256 * i;
-    const int row = idx / pieces, pc = idx - row * pieces;
-    int t = -1;
-    if (idx < total && row < nrows) t = tok_of(row);
-    const u32x4 x = buf_u32x4<0>(rs, (uint32_t)(max(t, 0) * r + pc * EPV) * (uint32_t)sizeof(WT), 0u);
-    v[i] = (t >= 0) ? x : u32x4{0u, 0u, 0u, 0u};
-    dst[i] = (idx < total) ? row * a_stride + pc * EPV : -1;
-  }
-#pragma unroll
-  for (int i = 0; i < PER; i++)
-    if (dst[i] >= 0) *reinterpret_cast<u32x4*>(A_lds + dst[i]) = v[i];
+  W1Gather<WT, PER> g;
+  g.load(W1, V, r, nrows, rows_cap, a_stride, tok_of);
+  g.store(A_lds);
 }
 
 // Logit values of one row at the columns a lane holds in the bias-block
@@ -438,6 +502,36 @@ __device__ __forceinline__ void stage_store(const u32x4 (&v)[8], float* X) {
 #pragma unroll
   for (int i = 0; i < 8; i++) *reinterpret_cast<u32x4*>(X + (4 * i + wave) * BSTRIDE + 4 * lane) = v[i];
 }
+// Direct-to-LDS variant: the 32 rows of block rb go straight from memory to
+// X + i * BSTRIDE (row i of the block) with 16-byte loads, one 1 KiB row
+// piece per instruction and no register staging.  Wave w issues rows w, w+4,
+// ... (always 8 loads per wave, so vmcnt-based waits can count them; rows past
+// nrows re-read row 0 and are masked by the reader).  The whole offset is in
+// the per-lane voffset, which the buffer range check covers: columns past V
+// read the following row or, past the resource, zero; the reader masks them.
+__device__ __forceinline__ void stage_dma(rsrc_t rs, uint32_t row_bytes, int rb, int nrows, int tile0,
+                                          float* X) {
+  // the LDS address (M0) must be provably wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const uint32_t coff = (uint32_t)(tile0 + 4 * lane) * 4u;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int rl = rb * 32 + 4 * i + wave;
+    const uint32_t voff = (rl < nrows ? (uint32_t)rl * row_bytes : 0u) + coff;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (__attribute__((address_space(3))) void*)(X + (4 * i + wave) * BSTRIDE), 16, (int)voff, 0, 0,
+        AUX_NT);
+  }
+}
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 // The lane's bias-block columns of staged row j (= lane & 31); invalid -> -inf.
 __device__ __forceinline__ void stage_read(const float* X, bool rowv, int V, int cbase, int wcol0,
                                            float (&out)[2][16]) {
@@ -508,6 +602,10 @@ __host__ __device__ inline WsLayout ws_layout(int R, int gamma, int V) {
   L.total = o;
   return L;
 }
+
+// Compute units of the current device (host side; one workgroup per CU for the
+// persistent tile loops).
+int device_cu_count();
 
 // Launch-timing hook (host side, thread-local): see dspark_profile_arm.
 void prof_before(int kid, hipStream_t stream);

@@ -9,17 +9,19 @@
 // so the token before position 1 is the anchor.
 //
 // Per step k (sequential in k, data-parallel over requests and vocabulary):
-//   K1 draft_partials  grid = V / 256 column tiles, 4 waves each.
-//        Gathers W1[x_{k-1}] for a block of 128 requests into LDS, runs the
-//        (R x r) . (r x 256) bias product on bf16 MFMA 32x32x16 with fp32
-//        accumulation, adds the base logits in the epilogue and writes per
-//        (request, tile) softmax partials (max, sum exp) plus the four per-wave
-//        sums.  z is never written to memory.
-//   K2 draft_select    one wave per request (4 per workgroup).
-//        Combines the tile records in fp64 (wave shuffles), finds the tile and
-//        then the 64-column chunk holding u * Z, recomputes that chunk's logits
-//        with the same MFMA instruction sequence and does the in-chunk
-//        inverse-CDF search.
+//   K1 draft_partials  persistent, one workgroup (4 waves) per compute unit,
+//        looping over 256-column tiles.  Gathers W1[x_{k-1}] for a chunk of
+//        128 requests into LDS once, runs the (R x r) . (r x 256) bias product
+//        on bf16 MFMA 32x32x16 with fp32 accumulation one 32-request block at
+//        a time, adds the base logits (brought into LDS by direct-to-LDS loads
+//        two blocks ahead) in the epilogue and writes per (request, tile)
+//        softmax partials (max, sum exp) plus the four per-wave sums.  z is
+//        never written to memory.
+//   K2 draft_select    one workgroup per request.
+//        Combines the tile records in fp64, finds the tile and then the
+//        64-column chunk holding u * Z, recomputes that chunk's logits with the
+//        same MFMA instruction sequence and does the in-chunk inverse-CDF
+//        search.
 #include "select.h"
 
 namespace dspark {
@@ -56,76 +58,89 @@ __device__ __forceinline__ float shifted(float b, float m, float bias, float inv
   return t_one ? d : d * invT;
 }
 
+// Requests per chunk (rows of the gathered W1 block held in LDS).
+template <typename WT>
+struct DraftChunk {
+  static constexpr int ROWS = sizeof(WT) == 2 ? 128 : 64;
+};
+
+// Persistent over column tiles: workgroup g handles tiles g, g + G, ... of the
+// vocabulary.  Per request chunk the W1 rows are gathered into LDS once.  The
+// work is cut into units (tile, 32-row block); a unit's base rows arrive in
+// LDS by direct-to-LDS loads issued two units ahead (ring of two buffers), the
+// unit's bias block is one MFMA chain per wave, and the epilogue adds the base
+// logits and reduces per wave.  The next tile's W2 fragment is loaded into
+// registers during the last unit of the current tile.
 template <typename WT, bool GREEDY, int KS>
 __global__ __launch_bounds__(256) void k_draft_partials(DraftStep<WT> P) {
   constexpr int APAD = BiasBlock<WT>::APAD;
-  constexpr int A_ELEMS = RCH * (DSPARK_MAX_RANK + APAD);
-  static_assert(A_ELEMS * sizeof(WT) >= 2 * 32 * BSTRIDE * sizeof(float), "staging fits the W1 block");
-  // The gathered W1 block; after the MFMA the same bytes stage base rows.
-  __shared__ __align__(16) WT A_lds[A_ELEMS];
-  __shared__ float red_m[4][RCH];
-  __shared__ float red_s[4][RCH];
-  __shared__ int red_i[4][RCH];
-  float* const X0 = reinterpret_cast<float*>(A_lds);
-  float* const X1 = X0 + 32 * BSTRIDE;
+  constexpr int CH = DraftChunk<WT>::ROWS;
+  constexpr int EPV = 16 / sizeof(WT);
+  constexpr int GPER = CH * (KS * 16 / EPV) / 256;
+  __shared__ __align__(16) WT A_lds[CH * (DSPARK_MAX_RANK + APAD)];
+  __shared__ __align__(16) float X[2][32 * BSTRIDE];
+  __shared__ float red_m[4][CH];
+  __shared__ float red_s[4][CH];
+  __shared__ int red_i[4][CH];
+  __shared__ int s_tok[CH];
 
   const int a_stride = P.r + APAD;
-  const int tile = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j = lane & 31, h = lane >> 5;
-  const int tile0 = tile * TILE;
-  const int cbase = tile0 + wave * WCOLS;
-  const int nt = gridDim.x;
+  const int nt = ceil_div(P.V, TILE);
+  const int G = gridDim.x;
   const bool t_one = (P.T == 1.0f);
   const uint32_t row_bytes = (uint32_t)(P.gamma * P.V) * 4u;
+  if ((int)blockIdx.x >= nt) return;
+  const int my_tiles = (nt - (int)blockIdx.x + G - 1) / G;
 
-  for (int c0 = 0; c0 < P.R; c0 += RCH) {
-    const int nrows = min(RCH, P.R - c0), nrb = ceil_div(nrows, 32);
-    // W2 slice of this wave for the whole k range (re-read per 128-row chunk so
-    // the fragment registers are free after each chunk's MFMA).
-    typename BiasBlock<WT>::template Frag<KS> F;
-    BiasBlock<WT>::template load<KS>(F, P.W2, P.V, P.r, cbase);
-    __syncthreads();
-    gather_w1_rows<WT, KS * sizeof(WT) / 2>(P.W1, P.V, P.r, nrows, nrb * 32, A_lds, a_stride,
-                                            [&](int i) { return P.prev_token(c0 + i); });
-    // base rows of this chunk, addressed from its first row: blocks 0-1 in
-    // flight during the MFMA, 2-3 during the first two epilogues
+  for (int c0 = 0; c0 < P.R; c0 += CH) {
+    const int nrows = min(CH, P.R - c0), nrb = ceil_div(nrows, 32);
+    const int nunits = my_tiles * nrb;
     const size_t first = (size_t)c0 * P.gamma + (P.k - 1);
     const rsrc_t brs = make_rsrc(P.base + first * P.V, ((size_t)P.R * P.gamma - first) * P.V * 4);
-    u32x4 va[8], vb[8];
-    stage_load(va, brs, row_bytes, 0, nrows, P.V, tile0);
-    stage_load(vb, brs, row_bytes, 1, nrows, P.V, tile0);
-    __syncthreads();
+    auto issue = [&](int u) {
+      if (u < nunits) {
+        const int ti = u / nrb, rb = u - ti * nrb;
+        stage_dma(brs, row_bytes, rb, nrows, ((int)blockIdx.x + ti * G) * TILE, X[u & 1]);
+      }
+    };
 
-    f32x16 acc[4][2];
-#pragma unroll
-    for (int rb = 0; rb < 4; rb++)
+    __syncthreads();  // the previous chunk is done with A_lds, X, red_* and s_tok
+    if ((int)threadIdx.x < CH) s_tok[threadIdx.x] = (int)threadIdx.x < nrows ? P.prev_token(c0 + threadIdx.x) : -1;
+    __syncthreads();
+    // issue order: W1 rows, the first two units' base rows, the W2 fragment;
+    // the waits below count on it
+    W1Gather<WT, GPER> g;
+    g.load(P.W1, P.V, P.r, nrows, CH, a_stride, [&](int i) { return s_tok[i]; });
+    issue(0);
+    issue(1);
+    typename BiasBlock<WT>::template Frag<KS> F;
+    BiasBlock<WT>::template load<KS>(F, P.W2, P.V, P.r, (int)blockIdx.x * TILE + wave * WCOLS);
+    g.store(A_lds);
+
+    for (int u = 0; u < nunits; u++) {
+      const int ti = u / nrb, rb = u - ti * nrb;
+      const int tile = (int)blockIdx.x + ti * G;
+      const int cbase = tile * TILE + wave * WCOLS;
+      if (u + 1 < nunits)
+        wait_vmcnt<8>();  // this unit's rows are in; the next unit's may be in flight
+      else
+        wait_vmcnt<0>();
+      __syncthreads();
+
+      f32x16 acc[2];
 #pragma unroll
       for (int p = 0; p < 2; p++)
 #pragma unroll
-        for (int t = 0; t < 16; t++) acc[rb][p][t] = 0.f;
-    BiasBlock<WT>::template mma<KS>(F, P.r, A_lds, a_stride, nrb, acc);
-    __syncthreads();  // the W1 block is dead: reuse its bytes for staging
-    stage_store(va, X0);
-    stage_store(vb, X1);
-    stage_load(va, brs, row_bytes, 2, nrows, P.V, tile0);
-    stage_load(vb, brs, row_bytes, 3, nrows, P.V, tile0);
-    __syncthreads();
+        for (int t = 0; t < 16; t++) acc[p][t] = 0.f;
+      BiasBlock<WT>::template mma_rb<KS>(F, P.r, A_lds + rb * 32 * a_stride, a_stride, acc);
+      if (rb == nrb - 1 && tile + G < nt)
+        BiasBlock<WT>::template load<KS>(F, P.W2, P.V, P.r, (tile + G) * TILE + wave * WCOLS);
 
-#pragma unroll
-    for (int rb = 0; rb < 4; rb++) {
-      if (rb >= nrb) break;
-      if (rb == 2) {
-        __syncthreads();
-        stage_store(va, X0);
-        stage_store(vb, X1);
-        __syncthreads();
-      }
-      const int rl = rb * 32 + j, row = c0 + rl;
-      const bool rowv = rl < nrows;
+      const int rl = rb * 32 + j;
       float b[2][16];
-      stage_read((rb & 1) ? X1 : X0, rowv, P.V, cbase, wave * WCOLS, b);
-      float4* rec = P.trec + ((size_t)row * nt + tile) * 2;
-
+      stage_read(X[u & 1], rl < nrows, P.V, cbase, wave * WCOLS, b);
       if (GREEDY) {
         float bv = -INFINITY;
         int bi = 0x7fffffff;
@@ -134,60 +149,79 @@ __global__ __launch_bounds__(256) void k_draft_partials(DraftStep<WT> P) {
         for (int t = 0; t < 16; t++)
 #pragma unroll
           for (int p = 0; p < 2; p++) {
-            const float z = b[p][t] + acc[rb][p][t];
+            const float z = b[p][t] + acc[p][t];
             bad |= (z != z);
             if (z > bv) { bv = z; bi = cbase + elem_col(p, t, h); }
           }
         if (bad) raise_err(P.err, DSPARK_DERR_NONFINITE);
         argmax_merge(bv, bi, __shfl_xor(bv, 32), __shfl_xor(bi, 32));
         if (h == 0) { red_m[wave][rl] = bv; red_i[wave][rl] = bi; }
-        __syncthreads();
-        if (wave == 0 && h == 0 && rowv) {
-          float v = red_m[0][rl];
-          int i = red_i[0][rl];
-#pragma unroll
-          for (int w = 1; w < 4; w++) argmax_merge(v, i, red_m[w][rl], red_i[w][rl]);
-          rec[0] = make_float4(v, __int_as_float(i), 0.f, 0.f);
-        }
       } else {
         float ml = -INFINITY;
 #pragma unroll
         for (int p = 0; p < 2; p++)
 #pragma unroll
-          for (int t = 0; t < 16; t++) ml = fmaxf(ml, b[p][t] + acc[rb][p][t]);
+          for (int t = 0; t < 16; t++) ml = fmaxf(ml, b[p][t] + acc[p][t]);
         const float mw = fmaxf(ml, __shfl_xor(ml, 32));
-        if (h == 0) red_m[wave][rl] = mw;
-        __syncthreads();
-        const float mt = fmaxf(fmaxf(red_m[0][rl], red_m[1][rl]), fmaxf(red_m[2][rl], red_m[3][rl]));
+        // a wave whose columns are all past V (or all -inf) has mass 0
+        const float mref = (mw == -INFINITY) ? 0.f : mw;
         float e[2][16];
 #pragma unroll
         for (int p = 0; p < 2; p++)
 #pragma unroll
-          for (int t = 0; t < 16; t++) e[p][t] = exp_acc(shifted(b[p][t], mt, acc[rb][p][t], P.invT, t_one));
+          for (int t = 0; t < 16; t++) e[p][t] = exp_acc(shifted(b[p][t], mref, acc[p][t], P.invT, t_one));
         const float sl = tree_sum32(e);
         const float sw = sl + __shfl_xor(sl, 32);
-        if (h == 0) red_s[wave][rl] = sw;
-        __syncthreads();
-        if (wave == 0 && h == 0 && rowv) {
-          const float s0 = red_s[0][rl], s1 = red_s[1][rl], s2 = red_s[2][rl], s3 = red_s[3][rl];
+        if (h == 0) { red_m[wave][rl] = mw; red_s[wave][rl] = sw; }
+      }
+      __syncthreads();  // X[u & 1] is free again; red_* of this unit complete
+      issue(u + 2);
+
+      // tile records, one thread per request, after the tile's last row block
+      if (rb == nrb - 1 && (int)threadIdx.x < nrows) {
+        const int q = threadIdx.x;
+        float4* rec = P.trec + ((size_t)(c0 + q) * nt + tile) * 2;
+        if (GREEDY) {
+          float v = red_m[0][q];
+          int i = red_i[0][q];
+#pragma unroll
+          for (int w = 1; w < 4; w++) argmax_merge(v, i, red_m[w][q], red_i[w][q]);
+          rec[0] = make_float4(v, __int_as_float(i), 0.f, 0.f);
+        } else {
+          const float m0 = red_m[0][q], m1 = red_m[1][q], m2 = red_m[2][q], m3 = red_m[3][q];
+          const float mt = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+          auto rescale = [&](float sw, float mw) {
+            const float d = t_one ? (mw - mt) : (mw - mt) * P.invT;
+            return (mw == -INFINITY) ? 0.f : sw * exp_acc(d);
+          };
+          const float s0 = rescale(red_s[0][q], m0), s1 = rescale(red_s[1][q], m1);
+          const float s2 = rescale(red_s[2][q], m2), s3 = rescale(red_s[3][q], m3);
           const float st = (s0 + s1) + (s2 + s3);
           rec[0] = make_float4(mt, st, s0, s1);
           rec[1] = make_float4(s2, s3, 0.f, 0.f);
-          if (is_bad(st) || is_bad(mt)) raise_err(P.err, DSPARK_DERR_NONFINITE);
+          // a fully -inf tile (masked vocabulary) is valid: mass 0
+          if (is_bad(st) || !(mt == mt) || mt == INFINITY) raise_err(P.err, DSPARK_DERR_NONFINITE);
         }
       }
     }
   }
 }
 
-// One wave per request: tile selection over the records, recompute of the
-// chosen 64-column chunk, in-chunk inverse CDF.
+// One workgroup per request.  The four waves read the row's tile records
+// together and choose the tile and then the 64-column chunk holding u * Z; each
+// wave fetches a quarter of that chunk's W2 fragment and passes it through
+// LDS, and wave 0 recomputes the chunk's logits with the same MFMA sequence as
+// the partials kernel (so the values are bit-identical to the ones summed
+// there) and does the in-chunk inverse-CDF search.
 template <typename WT, bool GREEDY, int KS>
 __global__ __launch_bounds__(256) void k_draft_select(DraftStep<WT> P) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ BlockSelectSmem sm;
+  __shared__ __align__(16) uint32_t Fl[sizeof(WT) == 2 ? KS * 8 * 64 : 4];
+  __shared__ float gm[4];
+  __shared__ int gi[4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int j = lane & 31, h = lane >> 5;
-  const int row = blockIdx.x * 4 + wave;
-  if (row >= P.R) return;  // waves are independent: no block-level barrier below
+  const int row = blockIdx.x;
   const int nt = ceil_div(P.V, TILE);
   const float4* recs = P.trec + (size_t)row * nt * 2;
   const size_t ev = (size_t)row * P.gamma + (P.k - 1);
@@ -195,12 +229,15 @@ __global__ __launch_bounds__(256) void k_draft_select(DraftStep<WT> P) {
   if (GREEDY) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
-    for (int t = lane; t < nt; t += 64) {
+    for (int t = tid; t < nt; t += 256) {
       const float4 r0 = recs[2 * t];
       argmax_merge(bv, bi, r0.x, __float_as_int(r0.y));
     }
     wave_argmax(bv, bi);
-    if (lane == 0) {
+    if (lane == 0) { gm[wave] = bv; gi[wave] = bi; }
+    __syncthreads();
+    if (tid == 0) {
+      for (int w = 1; w < 4; w++) argmax_merge(bv, bi, gm[w], gi[w]);
       int x = bi;
       if (x < 0 || x >= P.V) x = 0;  // only with non-finite logits (flagged)
       P.tokens[ev] = x;
@@ -214,14 +251,44 @@ __global__ __launch_bounds__(256) void k_draft_select(DraftStep<WT> P) {
   const bool t_one = (P.T == 1.0f);
   const double invTd = t_one ? 1.0 : 1.0 / (double)P.T;
   const int prev = P.prev_token(row);
+  typename BiasBlock<WT>::template Row<KS> w1;
+  BiasBlock<WT>::template load_row<KS>(w1, P.W1, P.r, prev);
   const float u = checked_uniform(P.u_draft[ev], P.err);
-  const TilePick S = wave_select_tile(recs, nt, true, invTd, (double)u);
+  const TilePick S = block_select_tile(recs, nt, true, invTd, (double)u, sm);
   const int cb = S.t * TILE + S.w * WCOLS;
 
   typename BiasBlock<WT>::template Frag<KS> F;
-  BiasBlock<WT>::template load<KS>(F, P.W2, P.V, P.r, cb);
-  typename BiasBlock<WT>::template Row<KS> w1;
-  BiasBlock<WT>::template load_row<KS>(w1, P.W1, P.r, prev);
+  if constexpr (sizeof(WT) == 2) {
+    constexpr int NQ = (KS + 3) / 4;
+    uint32_t v[NQ][8];
+#pragma unroll
+    for (int q = 0; q < NQ; q++) BiasBlock<WT>::load_ks(v[q], P.W2, P.V, P.r, cb, wave + 4 * q);
+#pragma unroll
+    for (int q = 0; q < NQ; q++) {
+      const int ks = wave + 4 * q;
+      if (ks < KS) {
+        u32x4* d = reinterpret_cast<u32x4*>(Fl + (ks * 64 + lane) * 8);
+        d[0] = u32x4{v[q][0], v[q][1], v[q][2], v[q][3]};
+        d[1] = u32x4{v[q][4], v[q][5], v[q][6], v[q][7]};
+      }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+      const u32x4* d = reinterpret_cast<const u32x4*>(Fl + (ks * 64 + lane) * 8);
+      const u32x4 lo = d[0], hi = d[1];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        F.w[ks][e] = lo[e];
+        F.w[ks][4 + e] = hi[e];
+      }
+    }
+  } else {
+    if (wave != 0) return;
+    BiasBlock<WT>::template load<KS>(F, P.W2, P.V, P.r, cb);
+  }
+
   float bvals[2][16];
   load_row_cols(make_rsrc(P.base_row(row), (size_t)P.V * 4), 0u, j == 0, P.V, cb, bvals);
   f32x16 acc[2];
@@ -266,22 +333,23 @@ static int launch_draft(const float* base, const void* W1, const void* W2, const
   P.trec = ws_ptr<float4>(ws, L.trec);
   P.err = ws_ptr<int32_t>(ws, L.err);
   const int nt = ceil_div(V, TILE);
+  const int grid1 = min(nt, device_cu_count());
   for (int k = 1; k <= gamma; k++) {
     P.k = k;
     prof_before(DSPARK_KID_DRAFT_PARTIALS, stream);
     DSPARK_DISPATCH_KS(r, {
       if (T == 0.f)
-        hipLaunchKernelGGL((k_draft_partials<WT, true, KS>), dim3(nt), dim3(256), 0, stream, P);
+        hipLaunchKernelGGL((k_draft_partials<WT, true, KS>), dim3(grid1), dim3(256), 0, stream, P);
       else
-        hipLaunchKernelGGL((k_draft_partials<WT, false, KS>), dim3(nt), dim3(256), 0, stream, P);
+        hipLaunchKernelGGL((k_draft_partials<WT, false, KS>), dim3(grid1), dim3(256), 0, stream, P);
     });
     prof_after(DSPARK_KID_DRAFT_PARTIALS, stream);
     prof_before(DSPARK_KID_DRAFT_SELECT, stream);
     DSPARK_DISPATCH_KS(r, {
       if (T == 0.f)
-        hipLaunchKernelGGL((k_draft_select<WT, true, 1>), dim3(ceil_div(R, 4)), dim3(256), 0, stream, P);
+        hipLaunchKernelGGL((k_draft_select<WT, true, 1>), dim3(R), dim3(256), 0, stream, P);
       else
-        hipLaunchKernelGGL((k_draft_select<WT, false, KS>), dim3(ceil_div(R, 4)), dim3(256), 0, stream, P);
+        hipLaunchKernelGGL((k_draft_select<WT, false, KS>), dim3(R), dim3(256), 0, stream, P);
     });
     prof_after(DSPARK_KID_DRAFT_SELECT, stream);
   }

@@ -160,6 +160,153 @@ __device__ __forceinline__ TilePick wave_select_tile(const float4* __restrict__ 
   return P;
 }
 
+// Workgroup version (256 threads, tiles spread over all of them): the same
+// choice as wave_select_tile with the row's records read by 4 waves, for a
+// shorter latency chain when one workgroup serves one request.  Every thread
+// returns the same pick.  nt <= 256 * BTPL.
+constexpr int BTPL = 4;
+struct BlockSelectSmem {
+  float wmax[4];
+  double wsum[4];
+  double Z;
+  int found[4], last[4];
+  double rem;
+  float mt;
+  float4 csw;
+};
+
+__device__ __forceinline__ TilePick block_select_tile(const float4* __restrict__ recs, int nt,
+                                                      bool use_shift, double invTd, double u,
+                                                      BlockSelectSmem& sm) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int per = ceil_div(nt, 256);
+  const int t0 = min(nt, tid * per), t1 = min(nt, t0 + per);
+  if (tid == 0) {  // defaults when no tile carries mass (Z = 0, reported by the caller)
+    sm.rem = INFINITY;
+    sm.mt = 0.f;
+    sm.csw = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float m[BTPL], s[BTPL];
+  float4 sw[BTPL];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < BTPL; i++) {
+    const int t = t0 + i;
+    const bool ok = (i < per) && (t < t1);
+    const int tc = ok ? t : 0;
+    const float4 r0 = recs[2 * tc], r1 = recs[2 * tc + 1];
+    m[i] = ok ? r0.x : -INFINITY;
+    s[i] = ok ? r0.y : 0.f;
+    sw[i] = ok ? make_float4(r0.z, r0.w, r1.x, r1.y) : make_float4(0.f, 0.f, 0.f, 0.f);
+    mloc = fmaxf(mloc, m[i]);
+  }
+  float M = 0.f;
+  const float wm = wave_max(mloc);
+  if (lane == 0) sm.wmax[wave] = wm;
+  __syncthreads();
+  if (use_shift) M = fmaxf(fmaxf(sm.wmax[0], sm.wmax[1]), fmaxf(sm.wmax[2], sm.wmax[3]));
+  double w[BTPL];
+  double loc = 0.0;
+#pragma unroll
+  for (int i = 0; i < BTPL; i++) {
+    w[i] = 0.0;
+    if (t0 + i < t1)
+      w[i] = use_shift ? (double)s[i] * (double)exp_acc((m[i] - M) * (float)invTd) : (double)s[i];
+    loc += w[i];
+  }
+  double incl;
+  const double ex = wave_excl_scan_d(loc, &incl);
+  if (lane == 63) sm.wsum[wave] = incl;
+  __syncthreads();
+  double base = 0.0;
+  for (int q = 0; q < wave; q++) base += sm.wsum[q];
+  base += ex;
+  // Z is the inclusive prefix at the last tile, so a draw below Z always
+  // lands on a tile
+  const int owner_last = (nt - 1) / per;
+  if (tid == owner_last) sm.Z = base + loc;
+  __syncthreads();
+  const double Z = sm.Z;
+  const double target = u * Z;
+
+  int found = 0x7fffffff, lastpos = -1;
+  double before = 0.0, cum = 0.0;
+  float fm = 0.f, lm = 0.f;
+  float4 fsw = make_float4(0.f, 0.f, 0.f, 0.f), lsw = fsw;
+#pragma unroll
+  for (int i = 0; i < BTPL; i++) {
+    const int t = t0 + i;
+    if (t < t1) {
+      const double pp = cum;
+      cum += w[i];
+      if (found == 0x7fffffff && target < base + cum) {
+        found = t;
+        before = base + pp;
+        fm = m[i];
+        fsw = sw[i];
+      }
+      if (s[i] > 0.f) {
+        lastpos = t;
+        lm = m[i];
+        lsw = sw[i];
+      }
+    }
+  }
+  const int fw = wave_min_i(found), lw = wave_max_i(lastpos);
+  if (lane == 0) {
+    sm.found[wave] = fw;
+    sm.last[wave] = lw;
+  }
+  __syncthreads();
+  const int tmin = min(min(sm.found[0], sm.found[1]), min(sm.found[2], sm.found[3]));
+  const int tl = max(max(max(sm.last[0], sm.last[1]), max(sm.last[2], sm.last[3])), 0);
+  TilePick P;
+  P.Z = Z;
+  P.M = M;
+  if (tmin != 0x7fffffff) {
+    P.t = tmin;
+    if (found == tmin && t0 <= tmin && tmin < t1) {
+      sm.rem = target - before;
+      sm.mt = fm;
+      sm.csw = fsw;
+    }
+  } else {
+    P.t = tl;
+    if (t0 <= tl && tl < t1 && lastpos == tl) {
+      sm.rem = INFINITY;
+      sm.mt = lm;
+      sm.csw = lsw;
+    }
+  }
+  __syncthreads();
+  P.rem = sm.rem;
+  P.mt = sm.mt;
+  const float4 csw = sm.csw;
+  P.scale = use_shift ? (double)exp_acc((P.mt - M) * (float)invTd) : 1.0;
+  const float cs[4] = {csw.x, csw.y, csw.z, csw.w};
+  double c = 0.0;
+  int wstar = -1;
+  double remw = P.rem;
+  for (int k = 0; k < 4; k++) {
+    const double nc = c + (double)cs[k] * P.scale;
+    if (P.rem < nc) {
+      wstar = k;
+      remw = P.rem - c;
+      break;
+    }
+    c = nc;
+  }
+  if (wstar < 0) {
+    wstar = 0;
+    for (int k = 0; k < 4; k++)
+      if (cs[k] > 0.f) wstar = k;
+    remw = INFINITY;
+  }
+  P.w = wstar;
+  P.rem = remw;
+  return P;
+}
+
 // Gather the 64 chunk values held by lanes 0 and 32 (bias-block layout,
 // element (p, t) of lane 32h is column 16(t/4) + 8h + 2(t%4) + p) so that
 // lane c receives column c.

@@ -295,7 +295,7 @@ __global__ __launch_bounds__(256) void k_residual_partials(VerifyArgs<WT> P) {
     if (!__syncthreads_or(mine)) continue;
     typename BiasBlock<WT>::template Frag<KS> F;
     BiasBlock<WT>::template load<KS>(F, P.W2, P.V, P.r, cbase);
-    gather_w1_rows<WT, KS * sizeof(WT) / 2>(P.W1, P.V, P.r, nrows, nrb * 32, A_lds, a_stride, [&](int i) {
+    gather_w1_rows<WT, KS * sizeof(WT) / 2>(P.W1, P.V, P.r, nrows, RCH, A_lds, a_stride, [&](int i) {
       const int row = c0 + i;
       return s_rej[i] ? P.prev_of(row, P.rej[row]) : -1;
     });

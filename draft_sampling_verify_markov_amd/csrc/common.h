@@ -44,6 +44,11 @@ __device__ __forceinline__ float exp_acc(float x) {
   return (x < -100.f) ? 0.f : r;
 }
 
+// exp(x) as a bare 2^(x log2 e) (no clamp; -inf gives 0, NaN propagates).
+// sc = log2(e) / T folds the temperature into the same multiply.
+__device__ __forceinline__ float exp2_scaled(float x, float sc) { return __builtin_amdgcn_exp2f(x * sc); }
+constexpr float LOG2E_F = 1.44269502162933349609375f;
+
 __device__ __forceinline__ bool is_bad(float x) { return !(x == x) || __builtin_isinf(x); }
 
 // ---------------------------------------------------------------------------
@@ -230,6 +235,59 @@ struct BiasBlock<uint16_t> {
       }
     }
   }
+  // In-place conversion of a loaded fragment to MFMA operand form (w[ks][0..3]
+  // = a0, w[ks][4..7] = a1), done once per tile by the partials kernel.
+  template <int KS>
+  __device__ static __forceinline__ void to_operands(Frag<KS>& F) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+      bf16x8 a0, a1;
+      operands(F, ks, a0, a1);
+      const u32x4 lo = __builtin_bit_cast(u32x4, a0), hi = __builtin_bit_cast(u32x4, a1);
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        F.w[ks][e] = lo[e];
+        F.w[ks][4 + e] = hi[e];
+      }
+    }
+  }
+  // mma_rb on a fragment already in operand form.  The B operands of all k
+  // steps are read from LDS before the MFMA chain starts.
+  template <int KS>
+  __device__ static __forceinline__ void mma_rb_op(const Frag<KS>& F, int r, const uint16_t* A_rows,
+                                                   int a_stride, f32x16 (&acc)[2]) {
+    const int lane = threadIdx.x & 63, j = lane & 31, h = lane >> 5;
+    const int nks = r / 16;
+    const uint16_t* ap = A_rows + j * a_stride + 8 * h;
+    auto op = [&](int ks, int half) {
+      return __builtin_bit_cast(bf16x8, u32x4{F.w[ks][4 * half], F.w[ks][4 * half + 1],
+                                              F.w[ks][4 * half + 2], F.w[ks][4 * half + 3]});
+    };
+    if (nks == KS) {
+      u32x4 bb[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++) bb[ks] = *reinterpret_cast<const u32x4*>(ap + ks * 16);
+      // materialise every B operand before the chain (otherwise the
+      // scheduler re-reads LDS into one register set and stalls on each)
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++) asm volatile("" : "+v"(bb[ks]));
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, bb[ks]);
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op(ks, 0), b, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op(ks, 1), b, acc[1], 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++) {
+        if (ks < nks) {
+          const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ap + ks * 16));
+          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op(ks, 0), b, acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(op(ks, 1), b, acc[1], 0, 0, 0);
+        }
+      }
+    }
+  }
   // One row block: rows j of A_rows (32 requests) against the wave's 64
   // columns; acc[p] as in mma.  The full-rank case has no branch in the k loop.
   template <int KS>
@@ -351,6 +409,13 @@ struct BiasBlock<float> {
         }
       }
     }
+  }
+  template <int KS>
+  __device__ static __forceinline__ void to_operands(Frag<KS>&) {}
+  template <int KS>
+  __device__ static inline void mma_rb_op(const Frag<KS>& F, int r, const float* A_rows, int a_stride,
+                                          f32x16 (&acc)[2]) {
+    mma_rb<KS>(F, r, A_rows, a_stride, acc);
   }
   template <int KS>
   __device__ static inline void mma_rb(const Frag<KS>& F, int r, const float* A_rows, int a_stride,
@@ -524,6 +589,14 @@ __device__ __forceinline__ void stage_dma(rsrc_t rs, uint32_t row_bytes, int rb,
         AUX_NT);
   }
 }
+// Workgroup barrier for LDS traffic: completes this wave's LDS operations and
+// meets the other waves.  Unlike __syncthreads it does not wait for the
+// wave's outstanding global loads, so direct-to-LDS loads issued for later
+// units stay in flight; data they write is waited for explicitly (wait_vmcnt)
+// before the barrier that publishes it.  The memory clobber keeps the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
 template <int N>
@@ -532,6 +605,25 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
+// Same without any masking (every column of the tile is below V; rows past
+// the request count are never reported).
+__device__ __forceinline__ void stage_read_full(const float* X, int wcol0, float (&out)[2][16]) {
+  const int lane = threadIdx.x & 63, j = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int g = 0; g < 4; g++) {
+    const int c = wcol0 + 16 * g + 8 * h;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(X + j * BSTRIDE + c);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(X + j * BSTRIDE + c + 4);
+    out[0][4 * g + 0] = lo[0];
+    out[1][4 * g + 0] = lo[1];
+    out[0][4 * g + 1] = lo[2];
+    out[1][4 * g + 1] = lo[3];
+    out[0][4 * g + 2] = hi[0];
+    out[1][4 * g + 2] = hi[1];
+    out[0][4 * g + 3] = hi[2];
+    out[1][4 * g + 3] = hi[3];
+  }
+}
 // The lane's bias-block columns of staged row j (= lane & 31); invalid -> -inf.
 __device__ __forceinline__ void stage_read(const float* X, bool rowv, int V, int cbase, int wcol0,
                                            float (&out)[2][16]) {

@@ -22,6 +22,8 @@
 //        64-column chunk holding u * Z, recomputes that chunk's logits with the
 //        same MFMA instruction sequence and does the in-chunk inverse-CDF
 //        search.
+#include <type_traits>
+
 #include "select.h"
 
 namespace dspark {
@@ -72,7 +74,7 @@ struct DraftChunk {
 // logits and reduces per wave.  The next tile's W2 fragment is loaded into
 // registers during the last unit of the current tile.
 template <typename WT, bool GREEDY, int KS>
-__global__ __launch_bounds__(256) void k_draft_partials(DraftStep<WT> P) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_draft_partials(DraftStep<WT> P) {
   constexpr int APAD = BiasBlock<WT>::APAD;
   constexpr int CH = DraftChunk<WT>::ROWS;
   constexpr int EPV = 16 / sizeof(WT);
@@ -109,38 +111,48 @@ __global__ __launch_bounds__(256) void k_draft_partials(DraftStep<WT> P) {
     __syncthreads();  // the previous chunk is done with A_lds, X, red_* and s_tok
     if ((int)threadIdx.x < CH) s_tok[threadIdx.x] = (int)threadIdx.x < nrows ? P.prev_token(c0 + threadIdx.x) : -1;
     __syncthreads();
-    // issue order: W1 rows, the first two units' base rows, the W2 fragment;
-    // the waits below count on it
+    // issue order: W1 rows, the first unit's base rows, the W2 fragment, the
+    // second unit's rows -- the same order (fragment, then one unit of rows)
+    // as at every later tile start, which the waits below count on
     W1Gather<WT, GPER> g;
     g.load(P.W1, P.V, P.r, nrows, CH, a_stride, [&](int i) { return s_tok[i]; });
     issue(0);
-    issue(1);
     typename BiasBlock<WT>::template Frag<KS> F;
     BiasBlock<WT>::template load<KS>(F, P.W2, P.V, P.r, (int)blockIdx.x * TILE + wave * WCOLS);
+    issue(1);
     g.store(A_lds);
 
-    for (int u = 0; u < nunits; u++) {
-      const int ti = u / nrb, rb = u - ti * nrb;
-      const int tile = (int)blockIdx.x + ti * G;
+    const float sc = t_one ? LOG2E_F : LOG2E_F * P.invT;
+    int u = 0;
+    // One unit: wait for its base rows, MFMA, epilogue, then refill the
+    // freed buffer two units ahead.  CONVERT: first unit of a tile (turns
+    // the loaded fragment into operand form); RELOAD: last unit of a tile
+    // (loads the next tile's fragment once the MFMA chain has used it).
+    auto unit = [&](int tile, int rb, auto convert, auto reload) {
       const int cbase = tile * TILE + wave * WCOLS;
       if (u + 1 < nunits)
         wait_vmcnt<8>();  // this unit's rows are in; the next unit's may be in flight
       else
         wait_vmcnt<0>();
-      __syncthreads();
+      lds_barrier();
+      if constexpr (decltype(convert)::value) BiasBlock<WT>::template to_operands<KS>(F);
 
       f32x16 acc[2];
 #pragma unroll
       for (int p = 0; p < 2; p++)
 #pragma unroll
         for (int t = 0; t < 16; t++) acc[p][t] = 0.f;
-      BiasBlock<WT>::template mma_rb<KS>(F, P.r, A_lds + rb * 32 * a_stride, a_stride, acc);
-      if (rb == nrb - 1 && tile + G < nt)
-        BiasBlock<WT>::template load<KS>(F, P.W2, P.V, P.r, (tile + G) * TILE + wave * WCOLS);
+      BiasBlock<WT>::template mma_rb_op<KS>(F, P.r, A_lds + rb * 32 * a_stride, a_stride, acc);
+      if constexpr (decltype(reload)::value) {
+        if (tile + G < nt) BiasBlock<WT>::template load<KS>(F, P.W2, P.V, P.r, (tile + G) * TILE + wave * WCOLS);
+      }
 
       const int rl = rb * 32 + j;
       float b[2][16];
-      stage_read(X[u & 1], rl < nrows, P.V, cbase, wave * WCOLS, b);
+      if ((tile + 1) * TILE <= P.V)
+        stage_read_full(X[u & 1], wave * WCOLS, b);
+      else
+        stage_read(X[u & 1], true, P.V, cbase, wave * WCOLS, b);
       if (GREEDY) {
         float bv = -INFINITY;
         int bi = 0x7fffffff;
@@ -169,40 +181,56 @@ __global__ __launch_bounds__(256) void k_draft_partials(DraftStep<WT> P) {
 #pragma unroll
         for (int p = 0; p < 2; p++)
 #pragma unroll
-          for (int t = 0; t < 16; t++) e[p][t] = exp_acc(shifted(b[p][t], mref, acc[p][t], P.invT, t_one));
+          for (int t = 0; t < 16; t++) e[p][t] = exp2_scaled((b[p][t] - mref) + acc[p][t], sc);
         const float sl = tree_sum32(e);
         const float sw = sl + __shfl_xor(sl, 32);
         if (h == 0) { red_m[wave][rl] = mw; red_s[wave][rl] = sw; }
       }
-      __syncthreads();  // X[u & 1] is free again; red_* of this unit complete
+      lds_barrier();  // X[u & 1] is free again; red_* of this unit complete
       issue(u + 2);
+      u++;
+    };
 
-      // tile records, one thread per request, after the tile's last row block
-      if (rb == nrb - 1 && (int)threadIdx.x < nrows) {
-        const int q = threadIdx.x;
-        float4* rec = P.trec + ((size_t)(c0 + q) * nt + tile) * 2;
-        if (GREEDY) {
-          float v = red_m[0][q];
-          int i = red_i[0][q];
+    // tile records, one thread per request, after the tile's last row block
+    auto finalize = [&](int tile) {
+      if ((int)threadIdx.x >= nrows) return;
+      const int q = threadIdx.x;
+      float4* rec = P.trec + ((size_t)(c0 + q) * nt + tile) * 2;
+      if (GREEDY) {
+        float v = red_m[0][q];
+        int i = red_i[0][q];
 #pragma unroll
-          for (int w = 1; w < 4; w++) argmax_merge(v, i, red_m[w][q], red_i[w][q]);
-          rec[0] = make_float4(v, __int_as_float(i), 0.f, 0.f);
-        } else {
-          const float m0 = red_m[0][q], m1 = red_m[1][q], m2 = red_m[2][q], m3 = red_m[3][q];
-          const float mt = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
-          auto rescale = [&](float sw, float mw) {
-            const float d = t_one ? (mw - mt) : (mw - mt) * P.invT;
-            return (mw == -INFINITY) ? 0.f : sw * exp_acc(d);
-          };
-          const float s0 = rescale(red_s[0][q], m0), s1 = rescale(red_s[1][q], m1);
-          const float s2 = rescale(red_s[2][q], m2), s3 = rescale(red_s[3][q], m3);
-          const float st = (s0 + s1) + (s2 + s3);
-          rec[0] = make_float4(mt, st, s0, s1);
-          rec[1] = make_float4(s2, s3, 0.f, 0.f);
-          // a fully -inf tile (masked vocabulary) is valid: mass 0
-          if (is_bad(st) || !(mt == mt) || mt == INFINITY) raise_err(P.err, DSPARK_DERR_NONFINITE);
-        }
+        for (int w = 1; w < 4; w++) argmax_merge(v, i, red_m[w][q], red_i[w][q]);
+        rec[0] = make_float4(v, __int_as_float(i), 0.f, 0.f);
+      } else {
+        const float m0 = red_m[0][q], m1 = red_m[1][q], m2 = red_m[2][q], m3 = red_m[3][q];
+        const float mt = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+        auto rescale = [&](float sw, float mw) {
+          const float d = t_one ? (mw - mt) : (mw - mt) * P.invT;
+          return (mw == -INFINITY) ? 0.f : sw * exp_acc(d);
+        };
+        const float s0 = rescale(red_s[0][q], m0), s1 = rescale(red_s[1][q], m1);
+        const float s2 = rescale(red_s[2][q], m2), s3 = rescale(red_s[3][q], m3);
+        const float st = (s0 + s1) + (s2 + s3);
+        rec[0] = make_float4(mt, st, s0, s1);
+        rec[1] = make_float4(s2, s3, 0.f, 0.f);
+        // a fully -inf tile (masked vocabulary) is valid: mass 0
+        if (is_bad(st) || !(mt == mt) || mt == INFINITY) raise_err(P.err, DSPARK_DERR_NONFINITE);
       }
+    };
+
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    for (int ti = 0; ti < my_tiles; ti++) {
+      const int tile = (int)blockIdx.x + ti * G;
+      if (nrb == 1) {
+        unit(tile, 0, T_{}, T_{});
+      } else {
+        unit(tile, 0, T_{}, F_{});
+        for (int rb = 1; rb < nrb - 1; rb++) unit(tile, rb, F_{}, F_{});
+        unit(tile, nrb - 1, F_{}, T_{});
+      }
+      finalize(tile);
     }
   }
 }

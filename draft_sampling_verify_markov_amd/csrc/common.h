@@ -44,6 +44,23 @@ __device__ __forceinline__ float exp_acc(float x) {
   return (x < -100.f) ? 0.f : r;
 }
 
+// Weight element to fp32 (bf16 bits are the high half of an fp32).
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Element c of 8 bytes of weights (4 bf16 or 2 fp32).
+template <typename WT>
+__device__ __forceinline__ float elem_of(uint2 v, int c);
+template <>
+__device__ __forceinline__ float elem_of<uint16_t>(uint2 v, int c) {
+  const uint32_t w = (c < 2) ? v.x : v.y;
+  return __uint_as_float((c & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+template <>
+__device__ __forceinline__ float elem_of<float>(uint2 v, int c) {
+  return __uint_as_float(c == 0 ? v.x : v.y);
+}
+
 // exp(x) as a bare 2^(x log2 e) (no clamp; -inf gives 0, NaN propagates).
 // sc = log2(e) / T folds the temperature into the same multiply.
 __device__ __forceinline__ float exp2_scaled(float x, float sc) { return __builtin_amdgcn_exp2f(x * sc); }

@@ -236,19 +236,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 }
 
 // One workgroup per request.  The four waves read the row's tile records
-// together and choose the tile and then the 64-column chunk holding u * Z; each
-// wave fetches a quarter of that chunk's W2 fragment and passes it through
-// LDS, and wave 0 recomputes the chunk's logits with the same MFMA sequence as
-// the partials kernel (so the values are bit-identical to the ones summed
-// there) and does the in-chunk inverse-CDF search.
+// together and choose the tile and then the 64-column chunk holding u * Z.
+// The chunk's bias W1[x_{k-1}] . W2[:, chunk] is then recomputed on the
+// vector ALUs: thread (c, q) forms the fp32 dot product over k = q, q+4, ...
+// for column c (exact bf16 products, fp32 sums), the four partials are added
+// in a fixed order, and wave 0 does the in-chunk inverse-CDF search with one
+// column per lane.
 template <typename WT, bool GREEDY, int KS>
 __global__ __launch_bounds__(256) void k_draft_select(DraftStep<WT> P) {
+  constexpr int KQ = KS * 4;  // k values per thread (r <= 16 KS)
   __shared__ BlockSelectSmem sm;
-  __shared__ __align__(16) uint32_t Fl[sizeof(WT) == 2 ? KS * 8 * 64 : 4];
+  __shared__ float w1s[DSPARK_MAX_RANK];
+  __shared__ float part[32 / sizeof(WT)][WCOLS];  // [k groups][columns]
   __shared__ float gm[4];
   __shared__ int gi[4];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int j = lane & 31, h = lane >> 5;
   const int row = blockIdx.x;
   const int nt = ceil_div(P.V, TILE);
   const float4* recs = P.trec + (size_t)row * nt * 2;
@@ -278,59 +280,55 @@ __global__ __launch_bounds__(256) void k_draft_select(DraftStep<WT> P) {
 
   const bool t_one = (P.T == 1.0f);
   const double invTd = t_one ? 1.0 : 1.0 / (double)P.T;
+  // W1 row of the previous token into LDS (published by the select's barriers)
   const int prev = P.prev_token(row);
-  typename BiasBlock<WT>::template Row<KS> w1;
-  BiasBlock<WT>::template load_row<KS>(w1, P.W1, P.r, prev);
+  for (int k = tid; k < P.r; k += 256) w1s[k] = to_f32(P.W1[(size_t)prev * P.r + k]);
   const float u = checked_uniform(P.u_draft[ev], P.err);
   const TilePick S = block_select_tile(recs, nt, true, invTd, (double)u, sm);
   const int cb = S.t * TILE + S.w * WCOLS;
 
-  typename BiasBlock<WT>::template Frag<KS> F;
-  if constexpr (sizeof(WT) == 2) {
-    constexpr int NQ = (KS + 3) / 4;
-    uint32_t v[NQ][8];
-#pragma unroll
-    for (int q = 0; q < NQ; q++) BiasBlock<WT>::load_ks(v[q], P.W2, P.V, P.r, cb, wave + 4 * q);
-#pragma unroll
-    for (int q = 0; q < NQ; q++) {
-      const int ks = wave + 4 * q;
-      if (ks < KS) {
-        u32x4* d = reinterpret_cast<u32x4*>(Fl + (ks * 64 + lane) * 8);
-        d[0] = u32x4{v[q][0], v[q][1], v[q][2], v[q][3]};
-        d[1] = u32x4{v[q][4], v[q][5], v[q][6], v[q][7]};
-      }
-    }
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int ks = 0; ks < KS; ks++) {
-      const u32x4* d = reinterpret_cast<const u32x4*>(Fl + (ks * 64 + lane) * 8);
-      const u32x4 lo = d[0], hi = d[1];
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        F.w[ks][e] = lo[e];
-        F.w[ks][4 + e] = hi[e];
-      }
-    }
-  } else {
-    if (wave != 0) return;
-    BiasBlock<WT>::template load<KS>(F, P.W2, P.V, P.r, cb);
-  }
+  // base logit of column cb + lane (wave 0), issued before the W2 loads
+  const int col = cb + lane;
+  float bval = 0.f;
+  if (wave == 0) bval = (col < P.V) ? P.base_row(row)[col] : -INFINITY;
 
-  float bvals[2][16];
-  load_row_cols(make_rsrc(P.base_row(row), (size_t)P.V * 4), 0u, j == 0, P.V, cb, bvals);
-  f32x16 acc[2];
+  // W2[k][c0 .. c0 + CPT) with 8-byte loads: thread (cg, q) covers CPT
+  // consecutive columns of the chunk and k = q, q + NG, ...
+  constexpr int CPT = 8 / sizeof(WT);
+  constexpr int TPG = WCOLS / CPT;
+  constexpr int NG = 256 / TPG;
+  constexpr int KI = (16 * KS + NG - 1) / NG;
+  static_assert(NG == 32 / sizeof(WT), "k groups must match the partial-sum array");
+  const int cg = tid % TPG, q = tid / TPG;
+  const int c0 = cb + CPT * cg;
+  const int c0c = (c0 < P.V) ? c0 : 0;
+  uint2 raw[KI];
 #pragma unroll
-  for (int p = 0; p < 2; p++)
+  for (int i = 0; i < KI; i++) {
+    const int k = min(q + NG * i, P.r - 1);
+    raw[i] = *reinterpret_cast<const uint2*>(P.W2 + (size_t)k * P.V + c0c);
+  }
+  float acc[CPT];
 #pragma unroll
-    for (int t = 0; t < 16; t++) acc[p][t] = 0.f;
-  BiasBlock<WT>::template mma_row<KS>(F, P.r, w1, acc);
-  float e[2][16];
+  for (int c = 0; c < CPT; c++) acc[c] = 0.f;
 #pragma unroll
-  for (int p = 0; p < 2; p++)
+  for (int i = 0; i < KI; i++) {
+    const int k = q + NG * i;
+    if (k < P.r) {
+      const float a = w1s[k];
 #pragma unroll
-    for (int t = 0; t < 16; t++) e[p][t] = exp_acc(shifted(bvals[p][t], S.mt, acc[p][t], P.invT, t_one));
-  const float ec = chunk_to_lanes(e);
+      for (int c = 0; c < CPT; c++) acc[c] = fmaf(a, elem_of<WT>(raw[i], c), acc[c]);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPT; c++) part[q][CPT * cg + c] = acc[c];
+  __syncthreads();
+  if (wave != 0) return;
+  float bias = part[0][lane];
+#pragma unroll
+  for (int g = 1; g < NG; g++) bias += part[g][lane];
+  const float sc = t_one ? LOG2E_F : LOG2E_F * P.invT;
+  const float ec = exp2_scaled((bval - S.mt) + bias, sc);
   const int c = wave_pick64(ec, S.scale, S.rem);
   const float ex = __shfl(ec, c);
   if (lane == 0) {

@@ -16,9 +16,10 @@
 //   decide    one workgroup per request, one wave per position: fp64 row
 //             statistics, p_{j+1}(x_{j+1}), the accept tests u < p/q, and the
 //             first rejected position.
-//   residual  grid = V / 256 column tiles (T > 0 only).  For requests that
-//             rejected at k*, recomputes the draft logits of position k* with
-//             the MFMA bias block and writes tile records of max(0, p - pi).
+//   residual  persistent, one workgroup per compute unit over the 256-column
+//             tiles (T > 0 only).  For requests that rejected at k*,
+//             recomputes the draft logits of position k* with the MFMA bias
+//             block and writes tile records of max(0, p - pi).
 //   finalize  one wave per request: residual or bonus inverse-CDF sample (fp64
 //             scan over tiles, recompute of one chunk or tile), emitted tokens
 //             and the p_k(x_k) output.
@@ -248,85 +249,170 @@ __device__ __forceinline__ ResidualRow residual_row(const VerifyArgs<WT>& P, int
   return rr;
 }
 
-// max(0, p - pi) at the lane's 32 columns: p from the target row, pi from the
-// recomputed draft logits ((base - m_q) + bias) / T normalised by Z_q.
+// max(0, p - pi) of one column: p = 2^((t - Mt) sc) / Zt from the target
+// logit, pi = 2^(((b - m_q) + bias) sc) / Zq from the recomputed draft logit,
+// sc = log2(e) / T.  -inf logits (masked or past V) give 0.
+__device__ __forceinline__ float residual_elem(float t, float b, float bias, float Mt, float invZt, float mq,
+                                               float invZq, float sc) {
+  const float pv = exp2_scaled(t - Mt, sc) * invZt;
+  const float qv = exp2_scaled((b - mq) + bias, sc) * invZq;
+  return fmaxf(0.f, pv - qv);
+}
+
+// residual_elem at the lane's 32 bias-block columns of one request.
 template <typename WT>
 __device__ __forceinline__ void residual_values(const VerifyArgs<WT>& P, const ResidualRow& rr, int cbase,
-                                       const f32x16 (&acc)[2], float (&d)[2][16]) {
+                                                const f32x16 (&acc)[2], float (&d)[2][16]) {
   float b[2][16], t[2][16];
   load_row_cols(rr.brs, rr.boff, rr.valid, P.V, cbase, b);
   load_row_cols(rr.trs, rr.toff, rr.valid, P.V, cbase, t);
-  const bool t_one = (P.T == 1.0f);
+  const float sc = (P.T == 1.0f) ? LOG2E_F : LOG2E_F * P.invT;
 #pragma unroll
   for (int p = 0; p < 2; p++)
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      float at = t[p][i] - rr.Mt;
-      float aq = (b[p][i] - rr.mq) + acc[p][i];
-      if (!t_one) { at *= P.invT; aq *= P.invT; }
-      const float pv = exp_acc(at) * rr.invZt;
-      const float qv = exp_acc(aq) * rr.invZq;
-      d[p][i] = fmaxf(0.f, pv - qv);
-    }
+    for (int i = 0; i < 16; i++)
+      d[p][i] = residual_elem(t[p][i], b[p][i], acc[p][i], rr.Mt, rr.invZt, rr.mq, rr.invZq, sc);
 }
 
+// Persistent over column tiles like the draft partials kernel.  Per chunk of
+// 128 consecutive requests the rejected ones are compacted; their W1 rows at
+// k* are gathered into LDS once, and the work is cut into units (tile, block
+// of 32 rejected requests).  A unit's base and target rows at k* arrive in LDS
+// by direct-to-LDS loads issued one unit ahead (they overlap the unit's MFMA
+// chain), the epilogue forms max(0, p - pi) and per-wave sums, and the tile's
+// last unit writes the residual tile records.
 template <typename WT, int KS>
-__global__ __launch_bounds__(256) void k_residual_partials(VerifyArgs<WT> P) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_residual_partials(
+    VerifyArgs<WT> P) {
   constexpr int APAD = BiasBlock<WT>::APAD;
-  __shared__ __align__(16) WT A_lds[RCH * (DSPARK_MAX_RANK + APAD)];
-  __shared__ float red_s[4][RCH];
-  __shared__ int s_rej[RCH];
+  constexpr int CH = sizeof(WT) == 2 ? 128 : 64;
+  constexpr int EPV = 16 / sizeof(WT);
+  constexpr int GPER = CH * (KS * 16 / EPV) / 256;
+  __shared__ __align__(16) WT A_lds[CH * (DSPARK_MAX_RANK + APAD)];
+  __shared__ __align__(16) float Xb[32 * BSTRIDE];
+  __shared__ __align__(16) float Xt[32 * BSTRIDE];
+  __shared__ float red_s[4][CH];
+  __shared__ int s_list[CH], s_tok[CH], s_cnt[2];
+  __shared__ uint32_t s_boff[CH], s_toff[CH];
+  __shared__ float s_Mt[CH], s_iZt[CH], s_mq[CH], s_iZq[CH];
 
   const int a_stride = P.r + APAD;
-  const int tile = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int j = lane & 31;
-  const int cbase = tile * TILE + wave * WCOLS;
-  const int nt = gridDim.x;
+  const int nt = ceil_div(P.V, TILE);
+  const int G = gridDim.x;
+  if ((int)blockIdx.x >= nt) return;
+  const int my_tiles = (nt - (int)blockIdx.x + G - 1) / G;
+  const float sc = (P.T == 1.0f) ? LOG2E_F : LOG2E_F * P.invT;
 
-  for (int c0 = 0; c0 < P.R; c0 += RCH) {
-    const int nrows = min(RCH, P.R - c0), nrb = ceil_div(nrows, 32);
+  for (int c0 = 0; c0 < P.R; c0 += CH) {
+    const int nrows = min(CH, P.R - c0);
+    __syncthreads();  // the previous chunk is done with every LDS array
+    // compaction of the chunk's rejected requests (order kept)
+    bool mine = false;
+    if (tid < nrows) mine = P.rej[c0 + tid] <= P.L_of(c0 + tid);
+    const uint64_t bal = __ballot(mine);
+    if (tid < CH && lane == 0) s_cnt[wave] = __popcll(bal);
     __syncthreads();
-    int mine = 0;
-    if (threadIdx.x < nrows) {
-      const int row = c0 + threadIdx.x;
-      mine = (P.rej[row] <= P.L_of(row)) ? 1 : 0;
-      s_rej[threadIdx.x] = mine;
+    const int nrej = (CH > 64 ? s_cnt[0] + s_cnt[1] : s_cnt[0]);
+    if (nrej == 0) continue;  // uniform
+    if (mine) {
+      const int pos = (wave == 1 ? s_cnt[0] : 0) + __popcll(bal & ((1ull << lane) - 1ull));
+      s_list[pos] = tid;
     }
-    if (!__syncthreads_or(mine)) continue;
-    typename BiasBlock<WT>::template Frag<KS> F;
-    BiasBlock<WT>::template load<KS>(F, P.W2, P.V, P.r, cbase);
-    gather_w1_rows<WT, KS * sizeof(WT) / 2>(P.W1, P.V, P.r, nrows, RCH, A_lds, a_stride, [&](int i) {
-      const int row = c0 + i;
-      return s_rej[i] ? P.prev_of(row, P.rej[row]) : -1;
-    });
+    __syncthreads();
+    if (tid < nrej) {
+      const int i = s_list[tid], row = c0 + i;
+      const int ks = P.rej[row];  // k*, 1-based
+      const double2 rs = P.rowstat[(size_t)row * (P.gamma + 1) + ks - 1];
+      const size_t ev = (size_t)row * P.gamma + ks - 1;
+      s_Mt[tid] = (float)rs.x;
+      s_iZt[tid] = (float)(1.0 / rs.y);
+      s_mq[tid] = P.dstats[2 * ev];
+      s_iZq[tid] = (float)(1.0 / (double)P.dstats[2 * ev + 1]);
+      s_boff[tid] = ((uint32_t)i * (uint32_t)P.gamma + (uint32_t)(ks - 1)) * (uint32_t)P.V * 4u;
+      s_toff[tid] = ((uint32_t)i * (uint32_t)(P.gamma + 1) + (uint32_t)(ks - 1)) * (uint32_t)P.V * 4u;
+      s_tok[tid] = P.prev_of(row, ks);
+    }
     __syncthreads();
 
-    f32x16 acc[4][2];
+    const int nrb = ceil_div(nrej, 32);
+    const int nunits = my_tiles * nrb;
+    const size_t R_left = (size_t)(P.R - c0);
+    const rsrc_t brs = make_rsrc(P.base + (size_t)c0 * P.gamma * P.V, R_left * P.gamma * P.V * 4);
+    const rsrc_t trs = make_rsrc(P.target + (size_t)c0 * (P.gamma + 1) * P.V, R_left * (P.gamma + 1) * P.V * 4);
+    // unit u's rows: wave w loads compacted rows 4i + w of the block (8 base,
+    // 8 target loads per wave; rows past nrej re-read row 0)
+    auto issue = [&](int u) {
+      if (u >= nunits) return;
+      const int ti = u / nrb, rb = u - ti * nrb;
+      const int tile0 = ((int)blockIdx.x + ti * G) * TILE;
+      const int w = __builtin_amdgcn_readfirstlane(wave);
+      const uint32_t coff = (uint32_t)(tile0 + 4 * lane) * 4u;
 #pragma unroll
-    for (int rb = 0; rb < 4; rb++)
-#pragma unroll
-      for (int p = 0; p < 2; p++)
-#pragma unroll
-        for (int t = 0; t < 16; t++) acc[rb][p][t] = 0.f;
-    BiasBlock<WT>::template mma<KS>(F, P.r, A_lds, a_stride, nrb, acc);
+      for (int i = 0; i < 8; i++) {
+        const int q = rb * 32 + 4 * i + w;
+        const int qc = q < nrej ? q : 0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            brs, (__attribute__((address_space(3))) void*)(Xb + (4 * i + w) * BSTRIDE), 16,
+            (int)(s_boff[qc] + coff), 0, 0, AUX_NT);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            trs, (__attribute__((address_space(3))) void*)(Xt + (4 * i + w) * BSTRIDE), 16,
+            (int)(s_toff[qc] + coff), 0, 0, AUX_NT);
+      }
+    };
 
+    W1Gather<WT, GPER> g;
+    g.load(P.W1, P.V, P.r, nrej, CH, a_stride, [&](int i) { return s_tok[i]; });
+    issue(0);
+    typename BiasBlock<WT>::template Frag<KS> F;
+    BiasBlock<WT>::template load<KS>(F, P.W2, P.V, P.r, (int)blockIdx.x * TILE + wave * WCOLS);
+    g.store(A_lds);
+    lds_barrier();  // A_lds complete; the base/target rows and W2 stay in flight
+
+    int u = 0;
+    for (int ti = 0; ti < my_tiles; ti++) {
+      const int tile = (int)blockIdx.x + ti * G;
+      const int cbase = tile * TILE + wave * WCOLS;
+      BiasBlock<WT>::template to_operands<KS>(F);
+      for (int rb = 0; rb < nrb; rb++, u++) {
+        f32x16 acc[2];
 #pragma unroll
-    for (int rb = 0; rb < 4; rb++) {
-      if (rb >= nrb) break;
-      const int rl = rb * 32 + j, row = c0 + rl;
-      const bool rowv = rl < nrows && s_rej[rl];
-      const ResidualRow rr = residual_row(P, c0, row, rowv);
-      float d[2][16];
-      residual_values(P, rr, cbase, acc[rb], d);
-      const float sl = tree_sum32(d);
-      const float sw = sl + __shfl_xor(sl, 32);
-      if ((lane >> 5) == 0) red_s[wave][rl] = sw;
-      __syncthreads();
-      if (wave == 0 && (lane >> 5) == 0 && rowv) {
-        const float s0 = red_s[0][rl], s1 = red_s[1][rl], s2 = red_s[2][rl], s3 = red_s[3][rl];
-        float4* rec = P.rrec + ((size_t)row * nt + tile) * 2;
-        rec[0] = make_float4(0.f, (s0 + s1) + (s2 + s3), s0, s1);
-        rec[1] = make_float4(s2, s3, 0.f, 0.f);
+        for (int p = 0; p < 2; p++)
+#pragma unroll
+          for (int t = 0; t < 16; t++) acc[p][t] = 0.f;
+        BiasBlock<WT>::template mma_rb_op<KS>(F, P.r, A_lds + rb * 32 * a_stride, a_stride, acc);
+        wait_vmcnt<0>();  // this unit's rows (the only loads in flight)
+        lds_barrier();
+        if (rb == nrb - 1 && tile + G < nt)
+          BiasBlock<WT>::template load<KS>(F, P.W2, P.V, P.r, (tile + G) * TILE + wave * WCOLS);
+        const int q = rb * 32 + j;
+        float b[2][16], t[2][16];
+        if ((tile + 1) * TILE <= P.V) {
+          stage_read_full(Xb, wave * WCOLS, b);
+          stage_read_full(Xt, wave * WCOLS, t);
+        } else {
+          stage_read(Xb, true, P.V, cbase, wave * WCOLS, b);
+          stage_read(Xt, true, P.V, cbase, wave * WCOLS, t);
+        }
+        const int qc = q < nrej ? q : 0;
+        const float Mt = s_Mt[qc], iZt = s_iZt[qc], mq = s_mq[qc], iZq = s_iZq[qc];
+        float d[2][16];
+#pragma unroll
+        for (int p = 0; p < 2; p++)
+#pragma unroll
+          for (int i = 0; i < 16; i++) d[p][i] = residual_elem(t[p][i], b[p][i], acc[p][i], Mt, iZt, mq, iZq, sc);
+        const float sl = tree_sum32(d);
+        const float sw = sl + __shfl_xor(sl, 32);
+        if ((lane >> 5) == 0) red_s[wave][q] = sw;
+        lds_barrier();  // Xb / Xt free; red_s of this unit complete
+        issue(u + 1);
+        if (rb == nrb - 1 && tid < nrej) {
+          const float s0 = red_s[0][tid], s1 = red_s[1][tid], s2 = red_s[2][tid], s3 = red_s[3][tid];
+          float4* rec = P.rrec + ((size_t)(c0 + s_list[tid]) * nt + tile) * 2;
+          rec[0] = make_float4(0.f, (s0 + s1) + (s2 + s3), s0, s1);
+          rec[1] = make_float4(s2, s3, 0.f, 0.f);
+        }
       }
     }
   }
@@ -492,8 +578,9 @@ static int launch_verify(const VerifyArgs<WT>& P, hipStream_t stream) {
   prof_after(DSPARK_KID_VERIFY_DECIDE, stream);
   if (!greedy) {
     prof_before(DSPARK_KID_RESIDUAL, stream);
-    DSPARK_DISPATCH_KS(P.r, hipLaunchKernelGGL((k_residual_partials<WT, KS>), dim3(ceil_div(P.V, TILE)),
-                                               dim3(256), 0, stream, P));
+    const int grid_r = min(ceil_div(P.V, TILE), device_cu_count());
+    DSPARK_DISPATCH_KS(P.r, hipLaunchKernelGGL((k_residual_partials<WT, KS>), dim3(grid_r), dim3(256), 0,
+                                               stream, P));
     prof_after(DSPARK_KID_RESIDUAL, stream);
   }
   prof_before(DSPARK_KID_VERIFY_FINALIZE, stream);

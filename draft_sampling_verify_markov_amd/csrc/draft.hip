@@ -292,41 +292,8 @@ __global__ __launch_bounds__(256) void k_draft_select(DraftStep<WT> P) {
   float bval = 0.f;
   if (wave == 0) bval = (col < P.V) ? P.base_row(row)[col] : -INFINITY;
 
-  // W2[k][c0 .. c0 + CPT) with 8-byte loads: thread (cg, q) covers CPT
-  // consecutive columns of the chunk and k = q, q + NG, ...
-  constexpr int CPT = 8 / sizeof(WT);
-  constexpr int TPG = WCOLS / CPT;
-  constexpr int NG = 256 / TPG;
-  constexpr int KI = (16 * KS + NG - 1) / NG;
-  static_assert(NG == 32 / sizeof(WT), "k groups must match the partial-sum array");
-  const int cg = tid % TPG, q = tid / TPG;
-  const int c0 = cb + CPT * cg;
-  const int c0c = (c0 < P.V) ? c0 : 0;
-  uint2 raw[KI];
-#pragma unroll
-  for (int i = 0; i < KI; i++) {
-    const int k = min(q + NG * i, P.r - 1);
-    raw[i] = *reinterpret_cast<const uint2*>(P.W2 + (size_t)k * P.V + c0c);
-  }
-  float acc[CPT];
-#pragma unroll
-  for (int c = 0; c < CPT; c++) acc[c] = 0.f;
-#pragma unroll
-  for (int i = 0; i < KI; i++) {
-    const int k = q + NG * i;
-    if (k < P.r) {
-      const float a = w1s[k];
-#pragma unroll
-      for (int c = 0; c < CPT; c++) acc[c] = fmaf(a, elem_of<WT>(raw[i], c), acc[c]);
-    }
-  }
-#pragma unroll
-  for (int c = 0; c < CPT; c++) part[q][CPT * cg + c] = acc[c];
-  __syncthreads();
+  const float bias = chunk_bias<WT, KS>(P.W2, P.V, P.r, cb, w1s, part);
   if (wave != 0) return;
-  float bias = part[0][lane];
-#pragma unroll
-  for (int g = 1; g < NG; g++) bias += part[g][lane];
   const float sc = t_one ? LOG2E_F : LOG2E_F * P.invT;
   const float ec = exp2_scaled((bval - S.mt) + bias, sc);
   const int c = wave_pick64(ec, S.scale, S.rem);

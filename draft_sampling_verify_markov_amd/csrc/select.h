@@ -307,6 +307,54 @@ __device__ __forceinline__ TilePick block_select_tile(const float4* __restrict__
   return P;
 }
 
+// Bias of one 64-column chunk for one request: bias[c] = sum_k w1[k] *
+// W2[k][cb + c] (w1 in LDS as fp32; exact bf16 products, fp32 sums).  Thread
+// (cg, q) of the 256 covers CPT = 8 / sizeof(WT) consecutive columns and
+// k = q, q + NG, ... with 8-byte loads (64 consecutive columns per k row); the
+// NG partial sums of a column are added in a fixed order.  Call from all 256
+// threads (it has a barrier); lane c of wave 0 gets column cb + c, the other
+// waves 0.  part must hold NG = 32 / sizeof(WT) rows of 64 floats.
+template <typename WT, int KS>
+__device__ __forceinline__ float chunk_bias(const WT* __restrict__ W2, int V, int r, int cb,
+                                            const float* w1s, float (*part)[WCOLS]) {
+  constexpr int CPT = 8 / sizeof(WT);
+  constexpr int TPG = WCOLS / CPT;
+  constexpr int NG = 256 / TPG;
+  constexpr int KI = (16 * KS + NG - 1) / NG;
+  static_assert(NG == 32 / sizeof(WT), "k groups must match the partial-sum array");
+  const int tid = threadIdx.x;
+  const int cg = tid % TPG, q = tid / TPG;
+  const int c0 = cb + CPT * cg;
+  const int c0c = (c0 < V) ? c0 : 0;  // columns past V: any valid column (masked by the caller)
+  uint2 raw[KI];
+#pragma unroll
+  for (int i = 0; i < KI; i++) {
+    const int k = min(q + NG * i, r - 1);
+    raw[i] = *reinterpret_cast<const uint2*>(W2 + (size_t)k * V + c0c);
+  }
+  float acc[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; c++) acc[c] = 0.f;
+#pragma unroll
+  for (int i = 0; i < KI; i++) {
+    const int k = q + NG * i;
+    if (k < r) {
+      const float a = w1s[k];
+#pragma unroll
+      for (int c = 0; c < CPT; c++) acc[c] = fmaf(a, elem_of<WT>(raw[i], c), acc[c]);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPT; c++) part[q][CPT * cg + c] = acc[c];
+  __syncthreads();
+  if ((tid >> 6) != 0) return 0.f;
+  const int lane = tid & 63;
+  float bias = part[0][lane];
+#pragma unroll
+  for (int g = 1; g < NG; g++) bias += part[g][lane];
+  return bias;
+}
+
 // Gather the 64 chunk values held by lanes 0 and 32 (bias-block layout,
 // element (p, t) of lane 32h is column 16(t/4) + 8h + 2(t%4) + p) so that
 // lane c receives column c.

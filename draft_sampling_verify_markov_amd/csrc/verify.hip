@@ -20,9 +20,9 @@
 //             tiles (T > 0 only).  For requests that rejected at k*,
 //             recomputes the draft logits of position k* with the MFMA bias
 //             block and writes tile records of max(0, p - pi).
-//   finalize  one wave per request: residual or bonus inverse-CDF sample (fp64
-//             scan over tiles, recompute of one chunk or tile), emitted tokens
-//             and the p_k(x_k) output.
+//   finalize  one workgroup per request: residual or bonus inverse-CDF sample
+//             (fp64 scan over tiles, recompute of one chunk or tile), emitted
+//             tokens and the p_k(x_k) output.
 #include "select.h"
 
 namespace dspark {
@@ -216,39 +216,6 @@ __global__ __launch_bounds__(256) void k_verify_decide(VerifyArgs<WT> P) {
 // ---------------------------------------------------------------------------
 // residual max(0, p - pi) tile records for rejected requests
 
-struct ResidualRow {
-  bool valid;
-  float Mt, invZt, mq, invZq;
-  rsrc_t brs, trs;      // base / target rows of the request block, from its first request
-  uint32_t boff, toff;  // byte offsets of this request's rows at k*
-};
-
-// Rows of requests c0.. are addressed from request c0's first base / target row.
-template <typename WT>
-__device__ __forceinline__ ResidualRow residual_row(const VerifyArgs<WT>& P, int c0, int row, bool valid) {
-  ResidualRow rr;
-  rr.valid = valid;
-  rr.Mt = 0.f; rr.invZt = 0.f; rr.mq = 0.f; rr.invZq = 0.f;
-  const size_t R_left = (size_t)(P.R - c0);
-  rr.brs = make_rsrc(P.base + (size_t)c0 * P.gamma * P.V, R_left * P.gamma * P.V * 4);
-  rr.trs = make_rsrc(P.target + (size_t)c0 * (P.gamma + 1) * P.V, R_left * (P.gamma + 1) * P.V * 4);
-  rr.boff = 0u;
-  rr.toff = 0u;
-  if (valid) {
-    const int ks = P.rej[row];  // k*, 1-based
-    const double2 rs = P.rowstat[(size_t)row * (P.gamma + 1) + ks - 1];
-    const size_t ev = (size_t)row * P.gamma + ks - 1;
-    rr.Mt = (float)rs.x;
-    rr.invZt = (float)(1.0 / rs.y);
-    rr.mq = P.dstats[2 * ev];
-    rr.invZq = (float)(1.0 / (double)P.dstats[2 * ev + 1]);
-    const uint32_t rl = (uint32_t)(row - c0);
-    rr.boff = (rl * (uint32_t)P.gamma + (uint32_t)(ks - 1)) * (uint32_t)P.V * 4u;
-    rr.toff = (rl * (uint32_t)(P.gamma + 1) + (uint32_t)(ks - 1)) * (uint32_t)P.V * 4u;
-  }
-  return rr;
-}
-
 // max(0, p - pi) of one column: p = 2^((t - Mt) sc) / Zt from the target
 // logit, pi = 2^(((b - m_q) + bias) sc) / Zq from the recomputed draft logit,
 // sc = log2(e) / T.  -inf logits (masked or past V) give 0.
@@ -257,21 +224,6 @@ __device__ __forceinline__ float residual_elem(float t, float b, float bias, flo
   const float pv = exp2_scaled(t - Mt, sc) * invZt;
   const float qv = exp2_scaled((b - mq) + bias, sc) * invZq;
   return fmaxf(0.f, pv - qv);
-}
-
-// residual_elem at the lane's 32 bias-block columns of one request.
-template <typename WT>
-__device__ __forceinline__ void residual_values(const VerifyArgs<WT>& P, const ResidualRow& rr, int cbase,
-                                                const f32x16 (&acc)[2], float (&d)[2][16]) {
-  float b[2][16], t[2][16];
-  load_row_cols(rr.brs, rr.boff, rr.valid, P.V, cbase, b);
-  load_row_cols(rr.trs, rr.toff, rr.valid, P.V, cbase, t);
-  const float sc = (P.T == 1.0f) ? LOG2E_F : LOG2E_F * P.invT;
-#pragma unroll
-  for (int p = 0; p < 2; p++)
-#pragma unroll
-    for (int i = 0; i < 16; i++)
-      d[p][i] = residual_elem(t[p][i], b[p][i], acc[p][i], rr.Mt, rr.invZt, rr.mq, rr.invZq, sc);
 }
 
 // Persistent over column tiles like the draft partials kernel.  Per chunk of
@@ -499,12 +451,17 @@ __device__ __forceinline__ int wave_sample_target_row(const VerifyArgs<WT>& P, s
   return min(pick, P.V - 1);
 }
 
+// One workgroup per request.  Residual sample: the four waves choose the tile
+// and chunk from the residual records, recompute that chunk's draft bias with
+// vector FMAs (chunk_bias), and wave 0 does the in-chunk search.  Bonus sample
+// (or a residual with no mass): wave 0 samples the target row.
 template <typename WT, bool GREEDY, int KS>
 __global__ __launch_bounds__(256) void k_verify_finalize(VerifyArgs<WT> P) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int j = lane & 31;
-  const int row = blockIdx.x * 4 + wave;
-  if (row >= P.R) return;  // waves are independent
+  __shared__ BlockSelectSmem sm;
+  __shared__ float w1s[DSPARK_MAX_RANK];
+  __shared__ float part[32 / sizeof(WT)][WCOLS];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int row = blockIdx.x;
   const int L = P.L_of(row);
   const int ks = P.rej[row];
   const bool rejected = ks <= L;
@@ -513,40 +470,42 @@ __global__ __launch_bounds__(256) void k_verify_finalize(VerifyArgs<WT> P) {
   int y = 0;
 
   if (GREEDY) {
+    if (wave != 0) return;
     y = (int)P.rowstat[rowA].y;
     if (y < 0 || y >= P.V) y = 0;
   } else {
     const double u = (double)checked_uniform(P.u_fin[row], P.err);
     bool use_p = !rejected;
-    if (rejected) {
+    if (rejected) {  // uniform over the workgroup
+      const int prev = P.prev_of(row, ks);
+      for (int k = tid; k < P.r; k += 256) w1s[k] = to_f32(P.W1[(size_t)prev * P.r + k]);
       const int nt = ceil_div(P.V, TILE);
-      const TilePick S = wave_select_tile(P.rrec + (size_t)row * nt * 2, nt, false, 1.0, u);
+      const TilePick S = block_select_tile(P.rrec + (size_t)row * nt * 2, nt, false, 1.0, u, sm);
       if (!(S.Z > 0.0)) {
         use_p = true;  // no residual mass: sample p itself
       } else {
         const int cb = S.t * TILE + S.w * WCOLS;
-        const int prev = P.prev_of(row, ks);
-        typename BiasBlock<WT>::template Frag<KS> F;
-        BiasBlock<WT>::template load<KS>(F, P.W2, P.V, P.r, cb);
-        typename BiasBlock<WT>::template Row<KS> w1;
-        BiasBlock<WT>::template load_row<KS>(w1, P.W1, P.r, prev);
-        f32x16 acc[2];
-#pragma unroll
-        for (int p = 0; p < 2; p++)
-#pragma unroll
-          for (int t = 0; t < 16; t++) acc[p][t] = 0.f;
-        BiasBlock<WT>::template mma_row<KS>(F, P.r, w1, acc);
-        const ResidualRow rr = residual_row(P, row, row, j == 0);
-        float d[2][16];
-        residual_values(P, rr, cb, acc, d);
-        const float dc = chunk_to_lanes(d);
-        y = min(cb + wave_pick64(dc, 1.0, S.rem), P.V - 1);
+        const int col = cb + lane;
+        const size_t ev = (size_t)row * P.gamma + ks - 1;
+        float b = -INFINITY, t = -INFINITY;
+        if (wave == 0 && col < P.V) {
+          b = P.base[ev * P.V + col];
+          t = P.target[((size_t)row * (P.gamma + 1) + ks - 1) * P.V + col];
+        }
+        const float bias = chunk_bias<WT, KS>(P.W2, P.V, P.r, cb, w1s, part);
+        if (wave != 0) return;
+        const double2 rs = P.rowstat[(size_t)row * (P.gamma + 1) + ks - 1];
+        const float sc = (P.T == 1.0f) ? LOG2E_F : LOG2E_F * P.invT;
+        const float d = residual_elem(t, b, bias, (float)rs.x, (float)(1.0 / rs.y), P.dstats[2 * ev],
+                                      (float)(1.0 / (double)P.dstats[2 * ev + 1]), sc);
+        y = min(cb + wave_pick64(d, 1.0, S.rem), P.V - 1);
       }
     }
+    if (wave != 0) return;
     if (use_p) y = wave_sample_target_row(P, rowA, u);
   }
 
-  // outputs: lane i writes slot i
+  // outputs (wave 0): lane i writes slot i
   int32_t* out = P.out_tokens + (size_t)row * (P.gamma + 1);
   for (int i = lane; i <= P.gamma; i += 64)
     out[i] = (i < A) ? P.dtok[(size_t)row * P.gamma + i] : ((i == A) ? y : -1);
@@ -585,10 +544,10 @@ static int launch_verify(const VerifyArgs<WT>& P, hipStream_t stream) {
   }
   prof_before(DSPARK_KID_VERIFY_FINALIZE, stream);
   if (greedy)
-    hipLaunchKernelGGL((k_verify_finalize<WT, true, 1>), dim3(ceil_div(P.R, 4)), dim3(256), 0, stream, P);
+    hipLaunchKernelGGL((k_verify_finalize<WT, true, 1>), dim3(P.R), dim3(256), 0, stream, P);
   else
-    DSPARK_DISPATCH_KS(P.r, hipLaunchKernelGGL((k_verify_finalize<WT, false, KS>), dim3(ceil_div(P.R, 4)),
-                                               dim3(256), 0, stream, P));
+    DSPARK_DISPATCH_KS(P.r, hipLaunchKernelGGL((k_verify_finalize<WT, false, KS>), dim3(P.R), dim3(256), 0,
+                                               stream, P));
   prof_after(DSPARK_KID_VERIFY_FINALIZE, stream);
   return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
 }

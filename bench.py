@@ -33,6 +33,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
 PROFILE_KERNEL = "k_draft_partials"
 KID_DRAFT_PARTIALS = 1   # dspark_kernel_id of the dominant kernel
+K1_REPEAT = 8            # back-to-back launches per timed event pair
 
 
 def parse():
@@ -212,9 +213,16 @@ def gpu_bench(a):
             one_round()
     ms = timed(one_round, a.steps)
 
-    # Second timed pass, eager launches: HIP events recorded by the library's
-    # launch hook around every launch of the dominant kernel, on its stream.
-    n_prof = g * a.steps
+    # Eager round time (no graph), for reference.
+    with torch.cuda.stream(stream):
+        ms_eager = timed(lambda: D.run_round(dd, T, ws, ws_sched=ws_sched), a.steps)
+
+    # Dominant-kernel duration: HIP events recorded by the library's launch
+    # hook on the kernel's stream, each pair around K1_REPEAT back-to-back
+    # launches of the same draft step (the kernel is idempotent), so the
+    # per-launch figure excludes most of the event and dispatch latency.
+    n_rounds = min(a.steps, 10)
+    n_prof = g * n_rounds
     ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(n_prof)]
     ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(n_prof)]
     with torch.cuda.stream(stream):
@@ -224,11 +232,14 @@ def gpu_bench(a):
     ArrT = ctypes.c_void_p * n_prof
     starts = ArrT(*[e.cuda_event for e in ev_s])
     stops = ArrT(*[e.cuda_event for e in ev_e])
-    lib.dspark_profile_arm(KID_DRAFT_PARTIALS, starts, stops, n_prof)
+    status = lib.dspark_profile_arm(KID_DRAFT_PARTIALS, starts, stops, n_prof, K1_REPEAT)
+    assert status == 0, f"dspark_profile_arm failed ({status})"
     with torch.cuda.stream(stream):
-        ms_eager = timed(lambda: D.run_round(dd, T, ws, ws_sched=ws_sched), a.steps)
+        for _ in range(n_rounds):
+            D.run_round(dd, T, ws, ws_sched=ws_sched)
+    torch.cuda.synchronize()
     used = lib.dspark_profile_disarm()
-    k1_ms = sum(s.elapsed_time(e) for s, e in zip(ev_s[:used], ev_e[:used])) / max(used, 1)
+    k1_ms = sum(s.elapsed_time(e) for s, e in zip(ev_s[:used], ev_e[:used])) / max(used, 1) / K1_REPEAT
 
     if a.copy_calibration_mib > 0:
         # plain copy of a known size: the HBM counters of its kernel calibrate
@@ -253,7 +264,7 @@ def gpu_bench(a):
         ms=ms, tokens=tokens, A=A, L=L, n_admitted=(int(ref["n_admitted"].cpu()[0])
                                                     if ref["n_admitted"] is not None else None),
         b_min=b_min, b_sched=b_sched, k1_ms=k1_ms, k1_bytes=k1_bytes, k1_flops=k1_flops,
-        traffic=traffic, graph=use_graph, cfg=d, ms_eager=ms_eager, n_k1=used)
+        traffic=traffic, graph=use_graph, cfg=d, ms_eager=ms_eager, n_k1=used * K1_REPEAT)
 
 
 def main():

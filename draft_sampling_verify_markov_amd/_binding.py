@@ -48,7 +48,7 @@ def load_library():
     lib.dspark_schedule.restype = I
     lib.dspark_verify.argtypes = [P, P, P, P, I, P, P, P, P, P, P, P, I, I, I, I, F, P, P, P, P, Z, P]
     lib.dspark_verify.restype = I
-    lib.dspark_profile_arm.argtypes = [I, P, P, I]
+    lib.dspark_profile_arm.argtypes = [I, P, P, I, I]
     lib.dspark_profile_arm.restype = I
     lib.dspark_profile_disarm.argtypes = []
     lib.dspark_profile_disarm.restype = I

@@ -37,7 +37,7 @@ struct ProfState {
   int kid = 0;
   hipEvent_t* starts = nullptr;
   hipEvent_t* stops = nullptr;
-  int n = 0, used = 0;
+  int n = 0, used = 0, repeat = 1;
 };
 static thread_local ProfState prof;
 
@@ -55,6 +55,7 @@ void prof_before(int kid, hipStream_t stream) {
 void prof_after(int kid, hipStream_t stream) {
   if (prof.kid == kid && prof.used < prof.n) (void)hipEventRecord(prof.stops[prof.used++], stream);
 }
+int prof_repeat(int kid) { return (prof.kid == kid && prof.used < prof.n) ? prof.repeat : 1; }
 
 static int check_ws(void* ws, size_t bytes, int R, int gamma, int V) {
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return DSPARK_EINVAL;
@@ -94,15 +95,16 @@ int dspark_device_error(void* workspace, size_t workspace_bytes, int32_t* host_b
   return hipStreamSynchronize(stream) == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
 }
 
-int dspark_profile_arm(int kid, hipEvent_t* starts, hipEvent_t* stops, int n) {
+int dspark_profile_arm(int kid, hipEvent_t* starts, hipEvent_t* stops, int n, int repeat) {
   if (kid < DSPARK_KID_DRAFT_PARTIALS || kid > DSPARK_KID_VERIFY_FINALIZE || !starts || !stops ||
-      n < 1)
+      n < 1 || repeat < 1 || repeat > 1000)
     return DSPARK_EINVAL;
   prof.kid = kid;
   prof.starts = starts;
   prof.stops = stops;
   prof.n = n;
   prof.used = 0;
+  prof.repeat = repeat;
   return DSPARK_OK;
 }
 

@@ -719,6 +719,9 @@ int device_cu_count();
 // Launch-timing hook (host side, thread-local): see dspark_profile_arm.
 void prof_before(int kid, hipStream_t stream);
 void prof_after(int kid, hipStream_t stream);
+// Launches to issue for one call site of kernel kid (more than 1 only while
+// the timing hook is armed with a repeat count for it).
+int prof_repeat(int kid);
 
 template <typename T>
 __host__ __device__ inline T* ws_ptr(void* ws, size_t off) {

@@ -330,20 +330,24 @@ static int launch_draft(const float* base, const void* W1, const void* W2, const
   for (int k = 1; k <= gamma; k++) {
     P.k = k;
     prof_before(DSPARK_KID_DRAFT_PARTIALS, stream);
-    DSPARK_DISPATCH_KS(r, {
-      if (T == 0.f)
-        hipLaunchKernelGGL((k_draft_partials<WT, true, KS>), dim3(grid1), dim3(256), 0, stream, P);
-      else
-        hipLaunchKernelGGL((k_draft_partials<WT, false, KS>), dim3(grid1), dim3(256), 0, stream, P);
-    });
+    for (int rep = prof_repeat(DSPARK_KID_DRAFT_PARTIALS); rep > 0; rep--) {
+      DSPARK_DISPATCH_KS(r, {
+        if (T == 0.f)
+          hipLaunchKernelGGL((k_draft_partials<WT, true, KS>), dim3(grid1), dim3(256), 0, stream, P);
+        else
+          hipLaunchKernelGGL((k_draft_partials<WT, false, KS>), dim3(grid1), dim3(256), 0, stream, P);
+      });
+    }
     prof_after(DSPARK_KID_DRAFT_PARTIALS, stream);
     prof_before(DSPARK_KID_DRAFT_SELECT, stream);
-    DSPARK_DISPATCH_KS(r, {
-      if (T == 0.f)
-        hipLaunchKernelGGL((k_draft_select<WT, true, 1>), dim3(R), dim3(256), 0, stream, P);
-      else
-        hipLaunchKernelGGL((k_draft_select<WT, false, KS>), dim3(R), dim3(256), 0, stream, P);
-    });
+    for (int rep = prof_repeat(DSPARK_KID_DRAFT_SELECT); rep > 0; rep--) {
+      DSPARK_DISPATCH_KS(r, {
+        if (T == 0.f)
+          hipLaunchKernelGGL((k_draft_select<WT, true, 1>), dim3(R), dim3(256), 0, stream, P);
+        else
+          hipLaunchKernelGGL((k_draft_select<WT, false, KS>), dim3(R), dim3(256), 0, stream, P);
+      });
+    }
     prof_after(DSPARK_KID_DRAFT_SELECT, stream);
   }
   return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;

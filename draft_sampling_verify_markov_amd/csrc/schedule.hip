@@ -191,18 +191,20 @@ int schedule_impl(const float* conf, const float* sps, int R, int gamma, int n_t
   const int n = R * gamma;
   int32_t* err = ws_ptr<int32_t>(ws, L.err);
   prof_before(DSPARK_KID_SCHEDULE, stream);
-  if (n <= SCHED_THREADS)
-    hipLaunchKernelGGL(k_schedule<1>, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, sps, R, gamma, n_table,
-                       verify_len, n_admitted, cum_conf, err);
-  else if (n <= 2 * SCHED_THREADS)
-    hipLaunchKernelGGL(k_schedule<2>, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, sps, R, gamma, n_table,
-                       verify_len, n_admitted, cum_conf, err);
-  else if (n <= 4 * SCHED_THREADS)
-    hipLaunchKernelGGL(k_schedule<4>, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, sps, R, gamma, n_table,
-                       verify_len, n_admitted, cum_conf, err);
-  else
-    hipLaunchKernelGGL(k_schedule<8>, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, sps, R, gamma, n_table,
-                       verify_len, n_admitted, cum_conf, err);
+  for (int rep = prof_repeat(DSPARK_KID_SCHEDULE); rep > 0; rep--) {
+    if (n <= SCHED_THREADS)
+      hipLaunchKernelGGL(k_schedule<1>, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, sps, R, gamma, n_table,
+                         verify_len, n_admitted, cum_conf, err);
+    else if (n <= 2 * SCHED_THREADS)
+      hipLaunchKernelGGL(k_schedule<2>, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, sps, R, gamma, n_table,
+                         verify_len, n_admitted, cum_conf, err);
+    else if (n <= 4 * SCHED_THREADS)
+      hipLaunchKernelGGL(k_schedule<4>, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, sps, R, gamma, n_table,
+                         verify_len, n_admitted, cum_conf, err);
+    else
+      hipLaunchKernelGGL(k_schedule<8>, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, sps, R, gamma, n_table,
+                         verify_len, n_admitted, cum_conf, err);
+  }
   prof_after(DSPARK_KID_SCHEDULE, stream);
   return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
 }

@@ -524,30 +524,38 @@ static int launch_verify(const VerifyArgs<WT>& P, hipStream_t stream) {
   const long long nblk = (long long)(P.gamma + 1) * P.R * nseg;
   const bool greedy = (P.T == 0.f);
   prof_before(DSPARK_KID_VERIFY_STREAM, stream);
-  if (greedy)
-    hipLaunchKernelGGL((k_verify_stream<WT, true>), dim3((unsigned)nblk), dim3(256), 0, stream, P);
-  else
-    hipLaunchKernelGGL((k_verify_stream<WT, false>), dim3((unsigned)nblk), dim3(256), 0, stream, P);
+  for (int rep = prof_repeat(DSPARK_KID_VERIFY_STREAM); rep > 0; rep--) {
+    if (greedy)
+      hipLaunchKernelGGL((k_verify_stream<WT, true>), dim3((unsigned)nblk), dim3(256), 0, stream, P);
+    else
+      hipLaunchKernelGGL((k_verify_stream<WT, false>), dim3((unsigned)nblk), dim3(256), 0, stream, P);
+  }
   prof_after(DSPARK_KID_VERIFY_STREAM, stream);
   prof_before(DSPARK_KID_VERIFY_DECIDE, stream);
-  if (greedy)
-    hipLaunchKernelGGL((k_verify_decide<WT, true>), dim3(P.R), dim3(256), 0, stream, P);
-  else
-    hipLaunchKernelGGL((k_verify_decide<WT, false>), dim3(P.R), dim3(256), 0, stream, P);
+  for (int rep = prof_repeat(DSPARK_KID_VERIFY_DECIDE); rep > 0; rep--) {
+    if (greedy)
+      hipLaunchKernelGGL((k_verify_decide<WT, true>), dim3(P.R), dim3(256), 0, stream, P);
+    else
+      hipLaunchKernelGGL((k_verify_decide<WT, false>), dim3(P.R), dim3(256), 0, stream, P);
+  }
   prof_after(DSPARK_KID_VERIFY_DECIDE, stream);
   if (!greedy) {
     prof_before(DSPARK_KID_RESIDUAL, stream);
-    const int grid_r = min(ceil_div(P.V, TILE), device_cu_count());
-    DSPARK_DISPATCH_KS(P.r, hipLaunchKernelGGL((k_residual_partials<WT, KS>), dim3(grid_r), dim3(256), 0,
-                                               stream, P));
+    for (int rep = prof_repeat(DSPARK_KID_RESIDUAL); rep > 0; rep--) {
+      const int grid_r = min(ceil_div(P.V, TILE), device_cu_count());
+      DSPARK_DISPATCH_KS(P.r, hipLaunchKernelGGL((k_residual_partials<WT, KS>), dim3(grid_r), dim3(256), 0,
+                                                 stream, P));
+    }
     prof_after(DSPARK_KID_RESIDUAL, stream);
   }
   prof_before(DSPARK_KID_VERIFY_FINALIZE, stream);
-  if (greedy)
-    hipLaunchKernelGGL((k_verify_finalize<WT, true, 1>), dim3(P.R), dim3(256), 0, stream, P);
-  else
-    DSPARK_DISPATCH_KS(P.r, hipLaunchKernelGGL((k_verify_finalize<WT, false, KS>), dim3(P.R), dim3(256), 0,
-                                               stream, P));
+  for (int rep = prof_repeat(DSPARK_KID_VERIFY_FINALIZE); rep > 0; rep--) {
+    if (greedy)
+      hipLaunchKernelGGL((k_verify_finalize<WT, true, 1>), dim3(P.R), dim3(256), 0, stream, P);
+    else
+      DSPARK_DISPATCH_KS(P.r, hipLaunchKernelGGL((k_verify_finalize<WT, false, KS>), dim3(P.R), dim3(256), 0,
+                                                 stream, P));
+  }
   prof_after(DSPARK_KID_VERIFY_FINALIZE, stream);
   return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
 }

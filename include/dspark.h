@@ -185,11 +185,16 @@ int dspark_verify(const float* target, const float* base, const void* W1, const 
  * While armed on the calling thread for kernel id `kid`, every launch of that
  * kernel made by this thread's dspark_* calls is bracketed by
  * hipEventRecord(starts[i], stream) before and hipEventRecord(stops[i], stream)
- * after, for i = 0, 1, ... up to n - 1; later launches are not timed.  The
+ * after, for i = 0, 1, ... up to n - 1; later launches are not timed.  With
+ * repeat > 1 each timed launch is issued `repeat` times back to back inside its
+ * event pair (every kernel of the library is idempotent for fixed inputs, so
+ * results are unchanged); (stop - start) / repeat then approximates the kernel
+ * duration without the event and dispatch latency of a single launch.  The
  * events are created (with timing enabled) and owned by the caller.  The state
  * is thread-local; other threads and unarmed calls are unaffected.
- * dspark_profile_arm returns DSPARK_EINVAL for a bad id, NULL arrays or n < 1.
- * dspark_profile_disarm returns the number of pairs recorded.
+ * dspark_profile_arm returns DSPARK_EINVAL for a bad id, NULL arrays, n < 1 or
+ * repeat outside [1, 1000].  dspark_profile_disarm returns the number of pairs
+ * recorded.
  */
 typedef enum {
   DSPARK_KID_DRAFT_PARTIALS = 1,  /* per-step bias GEMM + softmax partials */
@@ -201,7 +206,7 @@ typedef enum {
   DSPARK_KID_VERIFY_FINALIZE = 7  /* residual / bonus sample and outputs    */
 } dspark_kernel_id;
 
-int dspark_profile_arm(int kid, hipEvent_t* starts, hipEvent_t* stops, int n);
+int dspark_profile_arm(int kid, hipEvent_t* starts, hipEvent_t* stops, int n, int repeat);
 int dspark_profile_disarm(void);
 
 #ifdef __cplusplus

@@ -98,6 +98,21 @@ def test_verify_rejects_bad_arguments(lib):
     assert lib.dspark_verify(*bad) == ENOSPC
 
 
+def test_profile_hook_arguments(lib):
+    # arming only stores the caller's event arrays; nothing is recorded until a launch
+    arr = (ctypes.c_void_p * 4)(1, 2, 3, 4)
+    EINVAL = -1
+    assert lib.dspark_profile_arm(0, arr, arr, 4, 1) == EINVAL          # unknown kernel id
+    assert lib.dspark_profile_arm(8, arr, arr, 4, 1) == EINVAL
+    assert lib.dspark_profile_arm(1, None, arr, 4, 1) == EINVAL         # NULL arrays
+    assert lib.dspark_profile_arm(1, arr, None, 4, 1) == EINVAL
+    assert lib.dspark_profile_arm(1, arr, arr, 0, 1) == EINVAL          # no pairs
+    assert lib.dspark_profile_arm(1, arr, arr, 4, 0) == EINVAL          # repeat out of range
+    assert lib.dspark_profile_arm(1, arr, arr, 4, 1001) == EINVAL
+    assert lib.dspark_profile_arm(1, arr, arr, 4, 8) == 0
+    assert lib.dspark_profile_disarm() == 0
+
+
 def test_status_strings(lib):
     assert b"ENOSPC" in lib.dspark_status_string(-2)
     assert b"EINVAL" in lib.dspark_status_string(-1)

@@ -147,13 +147,17 @@ __device__ __forceinline__ uint32_t ld_stream_u32(const uint16_t* p) {
 // VGPR of address instead of a 64-bit address pair each.  Offsets at or past
 // num_records read 0.  AUX_NT marks the load non-temporal.
 constexpr int AUX_NT = 2;
+// W2 is re-read every draft step: plain (temporal) loads let it stay in the
+// memory-side cache while the streamed logit rows go non-temporal.
+constexpr int AUX_W2 = 0;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, size_t bytes) {
   const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
 }
+template <int AUX = AUX_NT>
 __device__ __forceinline__ uint32_t buf_u32(rsrc_t rs, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(rs, (int)voff, (int)soff, AUX_NT);
+  return __builtin_amdgcn_raw_buffer_load_b32(rs, (int)voff, (int)soff, AUX);
 }
 template <int AUX = AUX_NT>
 __device__ __forceinline__ u32x4 buf_u32x4(rsrc_t rs, uint32_t voff, uint32_t soff) {
@@ -206,7 +210,7 @@ struct BiasBlock<uint16_t> {
     const uint32_t voff = (uint32_t)(8 * h * V + (col < V ? col : 0)) * 2u;
     const int kk = min(ks, r / 16 - 1);
 #pragma unroll
-    for (int e = 0; e < 8; e++) w[e] = buf_u32(rs, voff, (uint32_t)((kk * 16 + e) * V) * 2u);
+    for (int e = 0; e < 8; e++) w[e] = buf_u32<AUX_W2>(rs, voff, (uint32_t)((kk * 16 + e) * V) * 2u);
   }
   template <int KS>
   __device__ static __forceinline__ void load(Frag<KS>& F, const uint16_t* __restrict__ W2, int V,

@@ -13,6 +13,7 @@ from .dspark_oracle import (  # noqa: F401
     inverse_cdf,
     draft,
     schedule,
+    schedule_async,
     verify,
     run_round,
     row_flags,

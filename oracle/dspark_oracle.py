@@ -160,27 +160,26 @@ def draft(base, W1, W2, w_dtype, anchor, u_draft, T):
 # 2. Hardware-aware prefix scheduler  ([HADA] Hardware-Aware Prefix Scheduler)
 
 
-def schedule(conf, sps):
-    """Confidence scheduler: per-request verify lengths from confidences only.
+def _pool(conf, sps):
+    """Survival probabilities, sorted candidate pool and the throughput curve.
 
-    conf [R, gamma] fp32 conditional confidences c_{r,j} in (0, 1];
-    sps [N] fp32 cost table, sps[i] = throughput at verify batch B = i + 1.
-    Never reads a drafted token (the non-anticipation requirement).
-    Returns dict(verify_len int32 [R], n_admitted, cum_conf fp32 [R, gamma],
-    theta float64 [R*gamma + 1], order int64 [R*gamma]).
+    a_{r,j} is the fp32 running product of the conditional confidences; the
+    R*gamma candidates are sorted by a descending, flat index ascending on
+    ties; T_n = R + (sum of the n best a) in exact 2^-36 fixed point (the
+    expected emitted tokens of a verify batch of R anchors plus n drafts) and
+    Theta_n = T_n * SPS(R + n) in float64, n = 0 .. R*gamma, with SPS = 0 past
+    the end of the table ([HADA] Hardware-Aware Prefix Scheduler; [JDON]
+    global pool).
     """
     c = np.asarray(conf, dtype=np.float32)
     R, g = c.shape
-    # survival probability a_{r,j}: fp32 running product of the conditionals
     a = np.empty_like(c)
     a[:, 0] = c[:, 0]
     for j in range(1, g):
         a[:, j] = a[:, j - 1] * c[:, j]          # float32 * float32 -> float32
     flat = np.arange(R * g, dtype=np.int64)
     af = a.reshape(-1)
-    # global pool sorted by a descending, ties by flat index ascending
     order = np.lexsort((flat, -af.astype(np.float64)))
-    # expected emitted tokens tau_n = R + sum of the n best a, in 2^-36 units
     a_fx = np.floor(af[order].astype(np.float64) * float(1 << FIX_SHIFT)).astype(np.int64)
     T_n = np.concatenate([[0], np.cumsum(a_fx)]) + np.int64(R) * (np.int64(1) << FIX_SHIFT)
     n = np.arange(R * g + 1)
@@ -189,10 +188,47 @@ def schedule(conf, sps):
     ok = B <= len(sps)
     S[ok] = np.asarray(sps, dtype=np.float32)[B[ok] - 1].astype(np.float64)
     theta = T_n.astype(np.float64) * S
+    return a, order, theta
+
+
+def schedule(conf, sps):
+    """Confidence scheduler: per-request verify lengths from confidences only.
+
+    conf [R, gamma] fp32 conditional confidences c_{r,j} in (0, 1];
+    sps [N] fp32 cost table, sps[i] = throughput at verify batch B = i + 1.
+    Never reads a drafted token (the non-anticipation requirement).  The walk
+    over the sorted pool admits candidates while Theta rises and stops at the
+    first strict drop.
+    Returns dict(verify_len int32 [R], n_admitted, cum_conf fp32 [R, gamma],
+    theta float64 [R*gamma + 1], order int64 [R*gamma]).
+    """
+    R, g = np.shape(conf)
+    a, order, theta = _pool(conf, sps)
     drops = np.flatnonzero(theta[1:] < theta[:-1])
     n_star = int(drops[0]) if len(drops) else R * g
     L = np.bincount(order[:n_star] // g, minlength=R).astype(np.int32)
     return dict(verify_len=L, n_admitted=n_star, cum_conf=a, theta=theta, order=order)
+
+
+def schedule_async(conf, conf_lag, sps):
+    """Asynchronous production variant of the scheduler.
+
+    The cut length K is the global maximiser of Theta over the pool built from
+    the confidences of two steps earlier (conf_lag), with no early stop; the
+    current step's candidates, sorted by their own cumulative confidence, are
+    admitted top-K ([HADA] Implantação em produção, practical application of
+    the scheduler: lagged confidences only set K, the current ones order the
+    candidates, early stopping is removed).  Ties of Theta take the smallest n.
+    conf_lag has the shape of conf.
+    Returns dict(verify_len int32 [R], n_admitted = K, cum_conf fp32 [R, gamma],
+    theta_lag float64 [R*gamma + 1], order int64 [R*gamma]).
+    """
+    R, g = np.shape(conf)
+    _, _, theta_lag = _pool(conf_lag, sps)
+    K = int(np.argmax(theta_lag))                 # first maximum
+    a, order, _ = _pool(conf, sps)
+    L = np.bincount(order[:K] // g, minlength=R).astype(np.int32)
+    return dict(verify_len=L, n_admitted=K, cum_conf=a, theta_lag=theta_lag, order=order)
 
 
 # ---------------------------------------------------------------------------

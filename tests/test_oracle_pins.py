@@ -501,3 +501,101 @@ def test_verify_length_ignores_drafted_tokens():
     perm = np.random.default_rng(5).permutation(a["base"].shape[2])
     c = dict(a, base=a["base"][:, :, perm], target=a["target"][:, :, perm], W2=a["W2"][:, perm])
     assert (O.run_round(c)["verify_len"] == ra["verify_len"]).all()
+
+
+# ---------------------------------------------------------------------------
+# asynchronous production scheduler ([HADA] Implantação em produção)
+
+
+def test_async_schedule_worked_example():
+    g = json.load(open(os.path.join(GOLD, "async_schedule.json")))
+    c = np.array([g["conf"]], np.float32)
+    cl = np.array([g["conf_lag"]], np.float32)
+    sps = np.array(g["sps_B_1_to_5"], np.float32)
+    s = O.schedule_async(c, cl, sps)
+    e = g["expected"]
+    np.testing.assert_allclose(s["theta_lag"] / float(1 << 36), e["theta_lag_scaled"], rtol=1e-6)
+    assert s["n_admitted"] == e["K"]
+    assert int(s["verify_len"][0]) == e["verify_len"]
+    assert int(O.schedule(c, sps)["verify_len"][0]) == e["early_stop_verify_len"]
+
+
+def test_async_with_current_confidences_matches_early_stop_on_unimodal_objective():
+    """Theta along the sorted pool is unimodal for SPS(B) = 1/(1 + beta B) (the
+    increments a_{n+1}(1 + beta(R+n)) - beta T_n never increase), so the global
+    maximiser equals the first drop when the lag is the current pool."""
+    checked = 0
+    for seed in range(70, 90):
+        rng = np.random.default_rng(seed)
+        R, g = int(rng.integers(2, 9)), int(rng.integers(1, 8))
+        c = rng.uniform(0.2, 1.0, (R, g)).astype(np.float32)
+        beta = rng.uniform(0.002, 0.3)
+        sps = (1.0 / (1.0 + beta * np.arange(1, R * (g + 1) + 5))).astype(np.float32)
+        s0, s1 = O.schedule(c, sps), O.schedule_async(c, c, sps)
+        th = s0["theta"]
+        if (np.diff(th) == 0).any():
+            continue                                   # plateau: the two tie rules differ
+        checked += 1
+        assert s1["n_admitted"] == s0["n_admitted"]
+        assert (s1["verify_len"] == s0["verify_len"]).all()
+    assert checked >= 15
+
+
+def test_async_cut_is_exact_argmax():
+    """K against the maximiser of Theta recomputed in exact rationals."""
+    from fractions import Fraction
+    checked = differs = 0
+    for seed in range(90, 130):
+        rng = np.random.default_rng(seed)
+        R, g = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+        cl = rng.uniform(0.05, 1.0, (R, g)).astype(np.float32)
+        c = rng.uniform(0.05, 1.0, (R, g)).astype(np.float32)
+        sps = np.sort(rng.uniform(0.1, 1.0, R * g + 3))[::-1].astype(np.float32)
+        sps[rng.integers(0, len(sps))] *= np.float32(1.5)   # a bump: objective not unimodal
+        a = np.empty_like(cl)
+        a[:, 0] = cl[:, 0]
+        for j in range(1, g):
+            a[:, j] = a[:, j - 1] * cl[:, j]
+        vals = sorted((Fraction(float(v)) for v in a.reshape(-1)), reverse=True)
+        thetas = []
+        for n in range(R * g + 1):
+            B = R + n
+            S = Fraction(float(sps[B - 1])) if B <= len(sps) else Fraction(0)
+            thetas.append((R + sum(vals[:n])) * S)
+        best = max(thetas)
+        K_exact = thetas.index(best)
+        second = max((t for i, t in enumerate(thetas) if i != K_exact), default=Fraction(0))
+        if best - second < best * Fraction(1, 10 ** 8):
+            continue                                    # fixed-point rounding could decide
+        assert O.schedule_async(c, cl, sps)["n_admitted"] == K_exact
+        checked += 1
+        differs += O.schedule(cl, sps)["n_admitted"] != K_exact   # early stop would cut elsewhere
+    assert checked >= 30 and differs >= 3
+
+
+def test_async_schedule_invariants():
+    rng = np.random.default_rng(33)
+    R, g = 16, 6
+    c = _sched_case(34, R=R, g=g, ties=True)
+    cl = rng.uniform(0.3, 1.0, (R, g)).astype(np.float32)
+    sps = (1.0 / (1.0 + 0.02 * np.arange(1, 200))).astype(np.float32)
+    s = O.schedule_async(c, cl, sps)
+    L, K = s["verify_len"], s["n_admitted"]
+    assert L.sum() == K and 0 <= K <= R * g
+    admitted = set(int(f) for f in s["order"][:K])
+    for r in range(R):                                  # admitted sets are prefixes
+        assert admitted & set(range(r * g, r * g + g)) == set(range(r * g, r * g + L[r]))
+    # K comes from the lagged pool only: independent of the current confidences
+    # and of which request each lagged row belongs to
+    c2 = rng.uniform(0.3, 1.0, (R, g)).astype(np.float32)
+    assert O.schedule_async(c2, cl, sps)["n_admitted"] == K
+    assert O.schedule_async(c, cl[rng.permutation(R)], sps)["n_admitted"] == K
+
+
+def test_lossless_with_async_scheduler_lengths():
+    t = _Tiny(15)
+    sched = O.schedule_async(np.array([[0.9, 0.6]], np.float32), np.array([[0.7, 0.9]], np.float32),
+                             np.array([1.0, 0.8, 0.5], np.float32))
+    L = int(sched["verify_len"][0])
+    P = t.first_token_law(lambda a: L)
+    np.testing.assert_allclose(P, _softmax(t.T1), atol=1e-12)

@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="3", help="workload key (default 3: R=128, gamma=7, V=131072)")
     ap.add_argument("--temperature", type=float, default=1.0)
+    ap.add_argument("--scheduler", choices=("early", "async"), default="early",
+                    help="early-stop prefix scheduler (default) or the asynchronous production variant")
     ap.add_argument("--eager", action="store_true", help="launch kernels eagerly instead of a graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -100,7 +102,7 @@ def cpu_worker(a):
     t0 = time.perf_counter()
     n, toks = 0, 0
     while True:
-        res = O.run_round(inp, T=a.temperature)
+        res = O.run_round(inp, T=a.temperature, scheduler=a.scheduler)
         n += 1
         toks += int((res["verify"]["accept_len"] + 1).sum())
         if time.perf_counter() - t0 >= a.cpu_seconds:
@@ -116,7 +118,8 @@ def cpu_baseline(a):
     for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
         env.setdefault(k, str(ncpu))
     cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-worker", "--config", a.config,
-           "--cpu-seconds", str(a.cpu_seconds), "--temperature", str(a.temperature)]
+           "--cpu-seconds", str(a.cpu_seconds), "--temperature", str(a.temperature),
+           "--scheduler", a.scheduler]
     out = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=600)
     if out.returncode != 0:
         return dict(error=out.stderr[-400:])
@@ -158,6 +161,7 @@ def gpu_bench(a):
               u_draft=t(inp["u_draft"], np.float32), u_accept=t(inp["u_accept"], np.float32),
               u_final=t(inp["u_final"], np.float32),
               conf=None if inp["conf"] is None else t(inp["conf"], np.float32),
+              conf_lag=None if inp["conf_lag"] is None else t(inp["conf_lag"], np.float32),
               sps=None if inp["sps"] is None else t(inp["sps"], np.float32))
     del inp
     ws = D.new_workspace(R, g, V, r, dev)
@@ -168,7 +172,7 @@ def gpu_bench(a):
 
     # one eager round: reference outputs and workload statistics
     with torch.cuda.stream(stream):
-        ref = D.run_round(dd, T, ws, ws_sched=ws_sched)
+        ref = D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler)
     torch.cuda.synchronize()
     if D.device_error(ws) != 0 or D.device_error(ws_sched) != 0:
         raise RuntimeError("device-side data error in the benchmark inputs")
@@ -180,7 +184,7 @@ def gpu_bench(a):
     if use_graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
-            out = D.run_round(dd, T, ws, ws_sched=ws_sched)
+            out = D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler)
         torch.cuda.synchronize()
         # replays must reproduce the eager round exactly, replay after replay
         for _ in range(3):
@@ -194,7 +198,7 @@ def gpu_bench(a):
         if use_graph:
             graph.replay()
         else:
-            D.run_round(dd, T, ws, ws_sched=ws_sched)
+            D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler)
 
     def timed(fn, n):
         t0 = torch.cuda.Event(enable_timing=True)
@@ -215,7 +219,7 @@ def gpu_bench(a):
 
     # Eager round time (no graph), for reference.
     with torch.cuda.stream(stream):
-        ms_eager = timed(lambda: D.run_round(dd, T, ws, ws_sched=ws_sched), a.steps)
+        ms_eager = timed(lambda: D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler), a.steps)
 
     # Dominant-kernel duration: HIP events recorded by the library's launch
     # hook on the kernel's stream, each pair around K1_REPEAT back-to-back
@@ -236,7 +240,7 @@ def gpu_bench(a):
     assert status == 0, f"dspark_profile_arm failed ({status})"
     with torch.cuda.stream(stream):
         for _ in range(n_rounds):
-            D.run_round(dd, T, ws, ws_sched=ws_sched)
+            D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler)
     torch.cuda.synchronize()
     used = lib.dspark_profile_disarm()
     k1_ms = sum(s.elapsed_time(e) for s, e in zip(ev_s[:used], ev_e[:used])) / max(used, 1) / K1_REPEAT
@@ -298,7 +302,8 @@ def main():
                                f"{d['w_dtype']} factors, base {d['base']}, target {d['target']}, "
                                f"conf {d['conf']}, table {d['table']}",
                    "R": d["R"], "gamma": d["gamma"], "V": d["V"], "r": d["r"],
-                   "temperature": a.temperature, "launch": "hip graph" if gb["graph"] else "eager"},
+                   "temperature": a.temperature, "scheduler": a.scheduler,
+                   "launch": "hip graph" if gb["graph"] else "eager"},
         "ms_per_step_eager": gb["ms_eager"],
         "rounds_per_s": 1e3 / ms,
         "tokens_per_round": gb["tokens"],

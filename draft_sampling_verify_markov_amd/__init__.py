@@ -20,12 +20,13 @@ from ._binding import (  # noqa: F401
     device_error,
     draft,
     schedule,
+    schedule_async,
     verify,
     run_round,
 )
 
 __all__ = [
     "DSPARK_W_BF16", "DSPARK_W_F32", "DERR_BITS", "DSparkError", "lib_path", "load_library",
-    "workspace_size", "new_workspace", "workspace_init", "device_error", "draft", "schedule",
+    "workspace_size", "new_workspace", "workspace_init", "device_error", "draft", "schedule", "schedule_async",
     "verify", "run_round",
 ]

@@ -46,6 +46,8 @@ def load_library():
     lib.dspark_draft.restype = I
     lib.dspark_schedule.argtypes = [P, P, I, I, I, P, P, P, P, Z, P]
     lib.dspark_schedule.restype = I
+    lib.dspark_schedule_async.argtypes = [P, P, P, I, I, I, P, P, P, P, Z, P]
+    lib.dspark_schedule_async.restype = I
     lib.dspark_verify.argtypes = [P, P, P, P, I, P, P, P, P, P, P, P, I, I, I, I, F, P, P, P, P, Z, P]
     lib.dspark_verify.restype = I
     lib.dspark_profile_arm.argtypes = [I, P, P, I, I]
@@ -159,6 +161,25 @@ def schedule(conf, sps, ws, out=None, with_cum=True):
     return L, n, a
 
 
+def schedule_async(conf, conf_lag, sps, ws, out=None, with_cum=True):
+    """dspark_schedule_async.  Returns (verify_len, K[1], cum_conf or None)."""
+    R, g = conf.shape
+    dev = conf.device
+    if out is None:
+        out = (torch.empty(R, dtype=torch.int32, device=dev),
+               torch.empty(1, dtype=torch.int32, device=dev),
+               torch.empty((R, g), dtype=torch.float32, device=dev) if with_cum else None)
+    L, n, a = out
+    args = (_ptr(conf, torch.float32, (R, g), "conf", dev),
+            _ptr(conf_lag, torch.float32, (R, g), "conf_lag", dev),
+            _ptr(sps, torch.float32, (sps.numel(),), "sps", dev), R, g, sps.numel(),
+            _ptr(L, torch.int32, (R,), "verify_len", dev), _ptr(n, torch.int32, (1,), "n_admitted", dev),
+            _ptr(a, torch.float32, (R, g), "cum_conf", dev),
+            ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("dspark_schedule_async", load_library().dspark_schedule_async(*args))
+    return L, n, a
+
+
 def verify(target, base, W1, W2, anchor, draft_tokens, draft_probs, draft_stats, verify_len,
            u_accept, u_final, temperature, ws, out=None, with_probs=True):
     """dspark_verify.  Returns (out_tokens, accept_len, target_probs or None)."""
@@ -201,14 +222,18 @@ def _side_stream(device):
     return _side_streams[device]
 
 
-def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None):
+def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, scheduler="early"):
     """draft -> schedule -> verify on a dict of device tensors.
 
     The scheduler reads only confidences and the cost table, so it runs on a
     side stream concurrently with the draft (forked from and joined back to
     the current stream; capturable into a HIP graph).  It uses its own small
-    workspace ``ws_sched`` (allocated here if not given).
+    workspace ``ws_sched`` (allocated here if not given).  ``scheduler`` is
+    "early" (dspark_schedule) or "async" (dspark_schedule_async with the
+    lagged confidences ``conf_lag`` of the input dict).
     """
+    if scheduler not in ("early", "async"):
+        raise ValueError(f"scheduler must be 'early' or 'async', got {scheduler!r}")
     d = dev_inputs
     dev = d["base"].device
     cur = torch.cuda.current_stream(dev)
@@ -220,7 +245,10 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None):
         side = _side_stream(dev)
         side.wait_stream(cur)
         with torch.cuda.stream(side):
-            L, n, _ = schedule(d["conf"], d["sps"], ws_sched, with_cum=False)
+            if scheduler == "async":
+                L, n, _ = schedule_async(d["conf"], d["conf_lag"], d["sps"], ws_sched, with_cum=False)
+            else:
+                L, n, _ = schedule(d["conf"], d["sps"], ws_sched, with_cum=False)
     tok, prob, stats = draft(d["base"], d["W1"], d["W2"], d["anchor"], d["u_draft"], temperature, ws)
     if sched:
         cur.wait_stream(side)

@@ -9,6 +9,9 @@ int draft_impl(const float* base, const void* W1, const void* W2, dspark_wtype w
 int schedule_impl(const float* conf, const float* sps, int R, int gamma, int n_table,
                   int32_t* verify_len, int32_t* n_admitted, float* cum_conf, void* ws,
                   hipStream_t stream);
+int schedule_async_impl(const float* conf, const float* conf_lag, const float* sps, int R, int gamma,
+                        int n_table, int32_t* verify_len, int32_t* n_admitted, float* cum_conf, void* ws,
+                        hipStream_t stream);
 int verify_impl(const float* target, const float* base, const void* W1, const void* W2,
                 dspark_wtype w_type, const int32_t* anchor, const int32_t* dtok, const float* dprob,
                 const float* dstats, const int32_t* vlen, const float* u_acc, const float* u_fin,
@@ -151,6 +154,19 @@ int dspark_schedule(const float* conf, const float* sps, int R, int gamma, int n
   if (workspace_bytes < 256) return DSPARK_ENOSPC;
   return schedule_impl(conf, sps, R, gamma, n_table, verify_len, n_admitted, cum_conf, workspace,
                        stream);
+}
+
+int dspark_schedule_async(const float* conf, const float* conf_lag, const float* sps, int R, int gamma,
+                          int n_table, int32_t* verify_len, int32_t* n_admitted, float* cum_conf,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (R < 1 || gamma < 1 || gamma > DSPARK_MAX_GAMMA || (long long)R * gamma > DSPARK_MAX_POOL)
+    return DSPARK_EINVAL;
+  if (n_table < 1) return DSPARK_EINVAL;
+  if (!conf || !conf_lag || !sps || !verify_len || !n_admitted) return DSPARK_EINVAL;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DSPARK_EINVAL;
+  if (workspace_bytes < 256) return DSPARK_ENOSPC;
+  return schedule_async_impl(conf, conf_lag, sps, R, gamma, n_table, verify_len, n_admitted, cum_conf,
+                             workspace, stream);
 }
 
 int dspark_verify(const float* target, const float* base, const void* W1, const void* W2,

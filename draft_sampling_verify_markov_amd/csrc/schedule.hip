@@ -22,6 +22,12 @@
 //      emitted tokens)
 //   4. Theta_n = double(T_n) * double(SPS(R + n)); n* = first strict drop
 //   5. verify_len[r] = admitted candidates of row r (LDS counters)
+//
+// dspark_schedule_async (HADA, "Implantação em produção", practical
+// application of the scheduler): the cut length K is the first maximiser of
+// Theta over the pool of the confidences of two steps earlier (steps 1-4
+// without the early stop), and step 5 admits the first K candidates of the
+// current pool.
 #include "common.h"
 
 namespace dspark {
@@ -39,25 +45,30 @@ __device__ __forceinline__ long long shfl_up_i64(long long v, int d) {
   return (long long)(((uint64_t)hi << 32) | lo);
 }
 
+// LDS of the scheduler kernels: two exchange buffers of NS keys (also the
+// confidence staging and the per-request counters), per-wave partials.
 template <int KPT>
-__global__ __launch_bounds__(SCHED_THREADS) void k_schedule(const float* __restrict__ conf,
-                                                           const float* __restrict__ sps, int R,
-                                                           int gamma, int n_table,
-                                                           int32_t* __restrict__ verify_len,
-                                                           int32_t* __restrict__ n_admitted,
-                                                           float* __restrict__ cum_conf,
-                                                           int32_t* err) {
+struct SchedSmem {
+  uint64_t bufs[2][SCHED_THREADS * KPT];
+  long long wsum[SCHED_THREADS / 64];
+  double wmax[SCHED_THREADS / 64];
+  int wmin[SCHED_THREADS / 64];
+  int s_n;
+};
+
+// Steps 1-2 for one confidence array: running products (written to cum_conf
+// when non-NULL), 64-bit keys, bitonic sort.  On return slot t + 1024 m of
+// the sorted pool is k[m] of thread t.  Every thread must call it.
+template <int KPT>
+__device__ __forceinline__ void pool_sort(const float* __restrict__ conf, int R, int gamma,
+                                          float* __restrict__ cum_conf, int32_t* err, SchedSmem<KPT>& sm,
+                                          uint64_t (&k)[KPT]) {
   constexpr int NT = SCHED_THREADS, NS = NT * KPT;
-  __shared__ uint64_t bufs[2][NS];
-  __shared__ long long wsum[NT / 64];
-  __shared__ int s_nstar;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int n = R * gamma;
-
-  // 1. survival probabilities and sort keys (slot = flat index).  The
-  // confidences are first read in parallel (coalesced) into LDS.
-  float* cl = reinterpret_cast<float*>(&bufs[1][0]);
+  __syncthreads();  // a previous user of the LDS buffers is done
+  // confidences read in parallel (coalesced) into LDS
+  float* cl = reinterpret_cast<float*>(&sm.bufs[1][0]);
   for (int f = tid; f < n; f += NT) {
     float c = conf[f];
     if (!(c > 0.f && c <= 1.f)) {
@@ -73,17 +84,14 @@ __global__ __launch_bounds__(SCHED_THREADS) void k_schedule(const float* __restr
       const int f = r * gamma + j;
       a = (j == 0) ? cl[f] : __fmul_rn(a, cl[f]);
       if (cum_conf) cum_conf[f] = a;
-      bufs[0][f] = ((uint64_t)(~__float_as_uint(a)) << 32) | (uint32_t)f;
+      sm.bufs[0][f] = ((uint64_t)(~__float_as_uint(a)) << 32) | (uint32_t)f;
     }
   }
-  for (int i = n + tid; i < NS; i += NT) bufs[0][i] = ~0ull;
-  if (tid == 0) s_nstar = n;
+  for (int i = n + tid; i < NS; i += NT) sm.bufs[0][i] = ~0ull;
   __syncthreads();
-  uint64_t k[KPT];
 #pragma unroll
-  for (int m = 0; m < KPT; m++) k[m] = bufs[0][tid + NT * m];
+  for (int m = 0; m < KPT; m++) k[m] = sm.bufs[0][tid + NT * m];
 
-  // 2. bitonic sort over slots
   int nb = 1;  // next exchange buffer (bufs[0] is still being read above)
   for (int kk = 2; kk <= NS; kk <<= 1) {
     for (int jj = kk >> 1; jj > 0; jj >>= 1) {
@@ -102,7 +110,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void k_schedule(const float* __restr
           }
         }
       } else if (jj >= 64) {
-        uint64_t* B = bufs[nb];
+        uint64_t* B = sm.bufs[nb];
         nb ^= 1;
 #pragma unroll
         for (int m = 0; m < KPT; m++) B[tid + NT * m] = k[m];
@@ -125,55 +133,56 @@ __global__ __launch_bounds__(SCHED_THREADS) void k_schedule(const float* __restr
       }
     }
   }
+}
 
-  // 3./4. exclusive fixed-point prefix in slot order and the drop test of
-  // each slot (T_n before slot n, T_n + v after it)
-  auto fixv = [&](int m) -> long long {
-    const int i = tid + NT * m;
-    const float a = __uint_as_float(~(uint32_t)(k[m] >> 32));
-    return (i < n) ? (long long)floor((double)a * (double)(1LL << FIX_SHIFT)) : 0;
-  };
+// Step 3: exact fixed-point prefix in slot order.  Calls f(i, Tn, v) for every
+// slot i < n of the thread, with Tn = R * 2^36 + (sum of the first i values)
+// and v = floor(a_i * 2^36).  Every thread must call it.
+template <int KPT, typename Fn>
+__device__ __forceinline__ void pool_scan(const uint64_t (&k)[KPT], int n, int R, SchedSmem<KPT>& sm, Fn f) {
+  constexpr int NT = SCHED_THREADS;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   long long carry = 0;
-  int drop = n;
 #pragma unroll
   for (int m = 0; m < KPT; m++) {
-    const long long vm = fixv(m);
+    const int i = tid + NT * m;
+    const float a = __uint_as_float(~(uint32_t)(k[m] >> 32));
+    const long long vm = (i < n) ? (long long)floor((double)a * (double)(1LL << FIX_SHIFT)) : 0;
     long long incl = vm;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const long long y = shfl_up_i64(incl, d);
       if (lane >= d) incl += y;
     }
-    if (lane == 63) wsum[wave] = incl;
+    if (lane == 63) sm.wsum[wave] = incl;
     __syncthreads();
     long long before = 0, total = 0;
 #pragma unroll
     for (int w = 0; w < NT / 64; w++) {
-      const long long x = wsum[w];
+      const long long x = sm.wsum[w];
       if (w < wave) before += x;
       total += x;
     }
-    const int i = tid + NT * m;
-    if (i < n) {
-      const long long Tn = ((long long)R << FIX_SHIFT) + carry + before + (incl - vm);
-      const long long Tn1 = Tn + vm;
-      const int B0 = R + i, B1 = R + i + 1;
-      const double S0 = (B0 <= n_table) ? (double)sps[B0 - 1] : 0.0;
-      const double S1 = (B1 <= n_table) ? (double)sps[B1 - 1] : 0.0;
-      if ((double)Tn1 * S1 < (double)Tn * S0) drop = min(drop, i);
-    }
+    if (i < n) f(i, ((long long)R << FIX_SHIFT) + carry + before + (incl - vm), vm);
     carry += total;
     __syncthreads();  // wsum is rewritten for the next m
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) drop = min(drop, __shfl_xor(drop, o));
-  if (lane == 0 && drop < n) atomicMin(&s_nstar, drop);
-  int* cnt = reinterpret_cast<int*>(&bufs[0][0]);  // keys live in registers now
+}
+
+__device__ __forceinline__ double sps_at(const float* __restrict__ sps, int n_table, int B) {
+  return (B <= n_table) ? (double)sps[B - 1] : 0.0;
+}
+
+// Step 5: verify_len[r] = admitted candidates (the first nstar slots) of row r.
+template <int KPT>
+__device__ __forceinline__ void pool_admit(const uint64_t (&k)[KPT], int nstar, int R, int gamma,
+                                           SchedSmem<KPT>& sm, int32_t* __restrict__ verify_len) {
+  constexpr int NT = SCHED_THREADS;
+  const int tid = threadIdx.x;
+  int* cnt = reinterpret_cast<int*>(&sm.bufs[0][0]);  // keys live in registers now
+  __syncthreads();
   for (int r = tid; r < R; r += NT) cnt[r] = 0;
   __syncthreads();
-  const int nstar = s_nstar;
-
-  // 5. per-request verify lengths
 #pragma unroll
   for (int m = 0; m < KPT; m++) {
     const int i = tid + NT * m;
@@ -181,7 +190,110 @@ __global__ __launch_bounds__(SCHED_THREADS) void k_schedule(const float* __restr
   }
   __syncthreads();
   for (int r = tid; r < R; r += NT) verify_len[r] = cnt[r];
+}
+
+// Early-stop walk: n* = first slot whose admission lowers Theta.
+template <int KPT>
+__global__ __launch_bounds__(SCHED_THREADS) void k_schedule(const float* __restrict__ conf,
+                                                           const float* __restrict__ sps, int R,
+                                                           int gamma, int n_table,
+                                                           int32_t* __restrict__ verify_len,
+                                                           int32_t* __restrict__ n_admitted,
+                                                           float* __restrict__ cum_conf,
+                                                           int32_t* err) {
+  __shared__ SchedSmem<KPT> sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int n = R * gamma;
+  if (tid == 0) sm.s_n = n;
+  uint64_t k[KPT];
+  pool_sort<KPT>(conf, R, gamma, cum_conf, err, sm, k);
+  int drop = n;
+  pool_scan<KPT>(k, n, R, sm, [&](int i, long long Tn, long long v) {
+    const double th0 = (double)Tn * sps_at(sps, n_table, R + i);
+    const double th1 = (double)(Tn + v) * sps_at(sps, n_table, R + i + 1);
+    if (th1 < th0) drop = min(drop, i);
+  });
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) drop = min(drop, __shfl_xor(drop, o));
+  if (lane == 0 && drop < n) atomicMin(&sm.s_n, drop);
+  __syncthreads();
+  const int nstar = sm.s_n;
+  pool_admit<KPT>(k, nstar, R, gamma, sm, verify_len);
   if (tid == 0) *n_admitted = nstar;
+}
+
+// Asynchronous production variant: K = the first maximiser of Theta over the
+// lagged pool (no early stop), then the current pool's top K are admitted.
+template <int KPT>
+__global__ __launch_bounds__(SCHED_THREADS) void k_schedule_async(const float* __restrict__ conf,
+                                                                 const float* __restrict__ conf_lag,
+                                                                 const float* __restrict__ sps, int R,
+                                                                 int gamma, int n_table,
+                                                                 int32_t* __restrict__ verify_len,
+                                                                 int32_t* __restrict__ n_admitted,
+                                                                 float* __restrict__ cum_conf,
+                                                                 int32_t* err) {
+  __shared__ SchedSmem<KPT> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = R * gamma;
+  uint64_t k[KPT];
+  pool_sort<KPT>(conf_lag, R, gamma, nullptr, err, sm, k);
+  // Theta_0 (no draft admitted) belongs to thread 0; slot i gives Theta_{i+1}
+  const double theta0 = (double)((long long)R << FIX_SHIFT) * sps_at(sps, n_table, R);
+  double best = (tid == 0) ? theta0 : -1.0;
+  pool_scan<KPT>(k, n, R, sm, [&](int i, long long Tn, long long v) {
+    best = fmax(best, (double)(Tn + v) * sps_at(sps, n_table, R + i + 1));
+  });
+  // block arg-max: largest Theta, then the smallest n holding it
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) best = fmax(best, __shfl_xor(best, o));
+  if (lane == 0) sm.wmax[wave] = best;
+  __syncthreads();
+  double bmax = sm.wmax[0];
+#pragma unroll
+  for (int w = 1; w < SCHED_THREADS / 64; w++) bmax = fmax(bmax, sm.wmax[w]);
+  int cand = 0x7fffffff;
+  pool_scan<KPT>(k, n, R, sm, [&](int i, long long Tn, long long v) {
+    const double th = (double)(Tn + v) * sps_at(sps, n_table, R + i + 1);
+    if (th == bmax) cand = min(cand, i + 1);
+  });
+  if (tid == 0 && theta0 == bmax) cand = 0;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) cand = min(cand, __shfl_xor(cand, o));
+  if (lane == 0) sm.wmin[wave] = cand;
+  __syncthreads();
+  int K = sm.wmin[0];
+#pragma unroll
+  for (int w = 1; w < SCHED_THREADS / 64; w++) K = min(K, sm.wmin[w]);
+
+  pool_sort<KPT>(conf, R, gamma, cum_conf, err, sm, k);
+  pool_admit<KPT>(k, K, R, gamma, sm, verify_len);
+  if (tid == 0) *n_admitted = K;
+}
+
+int schedule_async_impl(const float* conf, const float* conf_lag, const float* sps, int R, int gamma,
+                        int n_table, int32_t* verify_len, int32_t* n_admitted, float* cum_conf, void* ws,
+                        hipStream_t stream) {
+  const WsLayout L = ws_layout(R, gamma, 8);
+  const int n = R * gamma;
+  int32_t* err = ws_ptr<int32_t>(ws, L.err);
+  prof_before(DSPARK_KID_SCHEDULE, stream);
+  for (int rep = prof_repeat(DSPARK_KID_SCHEDULE); rep > 0; rep--) {
+    if (n <= SCHED_THREADS)
+      hipLaunchKernelGGL(k_schedule_async<1>, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, conf_lag, sps, R,
+                         gamma, n_table, verify_len, n_admitted, cum_conf, err);
+    else if (n <= 2 * SCHED_THREADS)
+      hipLaunchKernelGGL(k_schedule_async<2>, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, conf_lag, sps, R,
+                         gamma, n_table, verify_len, n_admitted, cum_conf, err);
+    else if (n <= 4 * SCHED_THREADS)
+      hipLaunchKernelGGL(k_schedule_async<4>, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, conf_lag, sps, R,
+                         gamma, n_table, verify_len, n_admitted, cum_conf, err);
+    else
+      hipLaunchKernelGGL(k_schedule_async<8>, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, conf_lag, sps, R,
+                         gamma, n_table, verify_len, n_admitted, cum_conf, err);
+  }
+  prof_after(DSPARK_KID_SCHEDULE, stream);
+  return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
 }
 
 int schedule_impl(const float* conf, const float* sps, int R, int gamma, int n_table,

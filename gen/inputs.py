@@ -18,6 +18,7 @@ import numpy as np
 from .configs import config as _config
 
 TID_BASE, TID_TARGET, TID_SIGMA, TID_W1, TID_W2, TID_ANCHOR, TID_CONF = 1, 2, 3, 4, 5, 6, 7
+TID_CONF_LAG = 8   # confidences of two steps earlier (asynchronous scheduler input)
 
 
 def bf16_bits_from_f32(x):
@@ -141,16 +142,22 @@ def make_inputs(cfg, seed=None, seed_u=0, rows=None, with_target=True, threads=N
         w1, w2 = bf16_bits_from_f32(w1), bf16_bits_from_f32(w2)
     anchor = np.random.default_rng([seed, TID_ANCHOR]).integers(0, V, R).astype(np.int32)
 
-    conf = None
-    if d["conf"] is not None:
-        rc = np.random.default_rng([seed, TID_CONF])
+    def draw_conf(tid):
+        rc = np.random.default_rng([seed, tid])
         if d["conf"][0] == "uniform":
-            conf = rc.uniform(d["conf"][1], d["conf"][2], (R, g))
+            c = rc.uniform(d["conf"][1], d["conf"][2], (R, g))
         elif d["conf"][0] == "beta":
-            conf = rc.beta(d["conf"][1], d["conf"][2], (R, g))
+            c = rc.beta(d["conf"][1], d["conf"][2], (R, g))
         else:
             raise ValueError(f"unknown confidence recipe {d['conf']!r}")
-        conf = conf.astype(np.float32)
+        return c.astype(np.float32)
+
+    conf = conf_lag = None
+    if d["conf"] is not None:
+        conf = draw_conf(TID_CONF)
+        # stand-in for the confidences of two steps earlier: same recipe,
+        # independent draws
+        conf_lag = draw_conf(TID_CONF_LAG)
 
     ru = np.random.default_rng(seed_u)
     u_draft = ru.random((R, g), dtype=np.float32)
@@ -160,7 +167,7 @@ def make_inputs(cfg, seed=None, seed_u=0, rows=None, with_target=True, threads=N
     out = dict(cfg=d, rows=row_ids, base=base, target=target, W1=w1, W2=w2,
                w_dtype=d["w_dtype"], anchor=anchor[row_ids], anchor_all=anchor,
                u_draft=u_draft[row_ids], u_accept=u_accept[row_ids], u_final=u_final[row_ids],
-               conf=conf, sps=cost_table(d["table"], R, g))
+               conf=conf, conf_lag=conf_lag, sps=cost_table(d["table"], R, g))
     return out
 
 

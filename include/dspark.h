@@ -5,6 +5,8 @@
  *
  *   dspark_draft     Markov-head sequential drafting of gamma tokens per request
  *   dspark_schedule  hardware-aware prefix scheduler: per-request verify lengths
+ *                    (dspark_schedule_async: the production variant with a
+ *                    lagged cut length)
  *   dspark_verify    lossless rejection-sampling verification and emission
  *
  * Sources (page title, section):
@@ -148,6 +150,34 @@ int dspark_draft(const float* base, const void* W1, const void* W2, dspark_wtype
 int dspark_schedule(const float* conf, const float* sps, int R, int gamma, int n_table,
                     int32_t* verify_len, int32_t* n_admitted, float* cum_conf, void* workspace,
                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dspark_schedule_async - asynchronous production variant of the scheduler
+ * ("DSpark: Aceleração da inferência de LLM com speculative decoding",
+ * pt.news.hada.io, section "Implantação em produção", practical application
+ * of the scheduler).  The serving engine needs the next verify batch size
+ * before the current step finishes, so the cut length comes from the
+ * confidences of two steps earlier and the early stop is removed:
+ *
+ *   K = the smallest n in [0, R*gamma] maximising Theta_n of the pool built
+ *       from conf_lag (same a, T_n, Theta_n as dspark_schedule)
+ *   verify_len[r] = number of row-r candidates among the first K of the pool
+ *       built from conf (current cumulative confidences)
+ *
+ * K never depends on the current step's confidences or tokens.  The caller
+ * keeps the two-step history (the library holds no state).
+ *
+ *   conf         [R, gamma] fp32  current conditional confidences in (0, 1]
+ *   conf_lag     [R, gamma] fp32  confidences of two steps earlier, same shape
+ *   sps, n_table                  as for dspark_schedule
+ *   verify_len   out [R] int32    L_r
+ *   n_admitted   out [1] int32    K
+ *   cum_conf     out [R, gamma] fp32 a of conf, or NULL
+ * Same checks and status codes as dspark_schedule (conf_lag must be non-NULL).
+ */
+int dspark_schedule_async(const float* conf, const float* conf_lag, const float* sps, int R, int gamma,
+                          int n_table, int32_t* verify_len, int32_t* n_admitted, float* cum_conf,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * dspark_verify - lossless rejection-sampling verification.

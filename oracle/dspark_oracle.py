@@ -46,7 +46,12 @@ Readings where the pages are silent (each also listed in the design doc):
   * the scheduler's a is an fp32 sequential product; the sort key is
     (a descending, flat index r*gamma + j ascending); sums of a are exact
     2^-36 fixed point; Theta_n = T_n * SPS(R + n) in fp64, SPS beyond the
-    table is 0; the walk stops at the first strict drop.
+    table is 0; the walk stops at the first strict drop;
+  * the asynchronous production scheduler ([HADA] Implantação em produção)
+    takes the cut length K as the first maximiser of Theta over the pool of
+    the lagged confidences (same shape as the current ones, supplied by the
+    caller) and admits the current pool's first K candidates; a table that
+    ends before B = R gives Theta = 0 everywhere and K = 0.
 
 All floating point is float64 on the exact input values (bf16 and fp32
 inputs widen exactly), except the scheduler's fp32 cumulative product.
@@ -305,15 +310,22 @@ def verify(target, base, W1, W2, w_dtype, anchor, draft_tokens, draft_probs,
 # whole round and boundary flags
 
 
-def run_round(inp, T=1.0, use_scheduler=None):
-    """Draft -> schedule -> verify on one input dict from ``gen.make_inputs``."""
+def run_round(inp, T=1.0, use_scheduler=None, scheduler="early"):
+    """Draft -> schedule -> verify on one input dict from ``gen.make_inputs``.
+
+    scheduler: "early" (the early-stop walk) or "async" (the production
+    variant, with the lagged confidences ``conf_lag``).
+    """
     sched = None
     if use_scheduler is None:
         use_scheduler = inp.get("conf") is not None
     d = draft(inp["base"], inp["W1"], inp["W2"], inp["w_dtype"], inp["anchor"], inp["u_draft"], T)
     L = None
     if use_scheduler:
-        sched = schedule(inp["conf"], inp["sps"])
+        if scheduler == "async":
+            sched = schedule_async(inp["conf"], inp["conf_lag"], inp["sps"])
+        else:
+            sched = schedule(inp["conf"], inp["sps"])
         L = sched["verify_len"][inp["rows"]] if "rows" in inp else sched["verify_len"]
     v = verify(inp["target"], inp["base"], inp["W1"], inp["W2"], inp["w_dtype"], inp["anchor"],
                d["tokens"], d["probs"], L, inp["u_accept"], inp["u_final"], T)

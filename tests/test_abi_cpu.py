@@ -84,6 +84,17 @@ def test_schedule_rejects_bad_arguments(lib):
     assert f(16, 16, 4, 4, 10, 16, 16, None, 256, 100, None) == ENOSPC
 
 
+def test_schedule_async_rejects_bad_arguments(lib):
+    f = lib.dspark_schedule_async
+    assert f(None, 16, 16, 4, 4, 10, 16, 16, None, 256, 4096, None) == EINVAL
+    assert f(16, None, 16, 4, 4, 10, 16, 16, None, 256, 4096, None) == EINVAL    # no lagged pool
+    assert f(16, 16, 16, 1000, 9, 10, 16, 16, None, 256, 4096, None) == EINVAL   # pool > 8192
+    assert f(16, 16, 16, 4, 4, 0, 16, 16, None, 256, 4096, None) == EINVAL       # empty table
+    assert f(16, 16, 16, 4, 4, 10, None, 16, None, 256, 4096, None) == EINVAL
+    assert f(16, 16, 16, 4, 4, 10, 16, 16, None, 250, 4096, None) == EINVAL      # misaligned workspace
+    assert f(16, 16, 16, 4, 4, 10, 16, 16, None, 256, 100, None) == ENOSPC
+
+
 def test_verify_rejects_bad_arguments(lib):
     base = [16, 16, 16, 16, 0, 16, 16, 16, 16, None, 16, 16, 4, 4, 512, 16, 1.0, 16, 16, None, 256,
             1 << 20, None]

@@ -15,7 +15,7 @@ import oracle as O
 from gen import make_inputs, config
 from gen.inputs import bf16_bits_from_f32
 
-from gpu_util import compare_rounds, gpu_round, say, to_dev
+from gpu_util import compare_rounds, dev, gpu_round, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -156,6 +156,71 @@ def test_schedule_edge_tables():
         L, n, a, err = _gpu_schedule(conf, sps)
         assert n == O.schedule(conf, sps)["n_admitted"] == expect
         assert np.array_equal(L, O.schedule(conf, sps)["verify_len"])
+
+
+def _gpu_schedule_async(conf, conf_lag, sps):
+    dv = dev()
+    c = torch.from_numpy(np.ascontiguousarray(conf)).to(dv)
+    cl = torch.from_numpy(np.ascontiguousarray(conf_lag)).to(dv)
+    s = torch.from_numpy(np.ascontiguousarray(sps)).to(dv)
+    ws = torch.zeros(256, dtype=torch.uint8, device=dv)
+    L, n, a = D.schedule_async(c, cl, s, ws)
+    torch.cuda.synchronize()
+    return L.cpu().numpy(), int(n.cpu()[0]), a.cpu().numpy(), D.device_error(ws)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_schedule_async_bit_exact(seed):
+    rng = np.random.default_rng(300 + seed)
+    g = int(rng.integers(1, 17))
+    # pool sizes over every register layout: <= 1024, 2048, 4096, 8192 slots
+    R = [int(rng.integers(1, 1024 // g + 1)), 2000 // g, 4000 // g, 8192 // g][seed % 4]
+    conf = rng.beta(6, 2, (R, g)).astype(np.float32)
+    conf_lag = rng.beta(6, 2, (R, g)).astype(np.float32)
+    if seed % 3 == 0:
+        conf_lag = conf.copy()
+    if seed % 2:
+        conf[rng.random((R, g)) < 0.2] = 1.0       # ties
+    N = int(rng.integers(1, R * (g + 1) + 50))
+    B = np.arange(1, N + 1)
+    sps = (1.0 / (1.0 + rng.uniform(1e-4, 5e-2) * np.ceil(B / rng.integers(1, 128)))).astype(np.float32)
+    if seed % 4 == 1:
+        sps[N // 2:] *= np.float32(0.5)            # a cliff
+    L, n, a, err = _gpu_schedule_async(conf, conf_lag, sps)
+    o = O.schedule_async(conf, conf_lag, sps)
+    say(f"async seed {seed}: R={R} g={g} N={N} K={n} (oracle {o['n_admitted']})")
+    assert err == 0
+    assert np.array_equal(a, o["cum_conf"])
+    assert n == o["n_admitted"]
+    assert np.array_equal(L, o["verify_len"])
+
+
+def test_schedule_async_worked_example_gpu():
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "async_schedule.json")))
+    L, n, a, err = _gpu_schedule_async(np.array([g["conf"]], np.float32), np.array([g["conf_lag"]], np.float32),
+                                       np.array(g["sps_B_1_to_5"], np.float32))
+    assert err == 0 and n == g["expected"]["K"] and int(L[0]) == g["expected"]["verify_len"]
+
+
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_schedule_async_workload_tables(cfg):
+    inp = make_inputs(cfg, rows=[0])
+    L, n, a, err = _gpu_schedule_async(inp["conf"], inp["conf_lag"], inp["sps"])
+    o = O.schedule_async(inp["conf"], inp["conf_lag"], inp["sps"])
+    say(f"cfg {cfg}: K = {n} of {inp['conf'].size} (early stop: {O.schedule(inp['conf'], inp['sps'])['n_admitted']})")
+    assert err == 0 and n == o["n_admitted"] and np.array_equal(L, o["verify_len"])
+
+
+def test_schedule_async_edge_tables():
+    conf = np.full((4, 5), 0.9, np.float32)
+    lag = np.full((4, 5), 0.5, np.float32)
+    for sps in [np.ones(100, np.float32), np.ones(10, np.float32), np.ones(2, np.float32),
+                np.linspace(1.0, 0.1, 30).astype(np.float32)]:
+        L, n, a, err = _gpu_schedule_async(conf, lag, sps)
+        o = O.schedule_async(conf, lag, sps)
+        assert err == 0 and n == o["n_admitted"] and np.array_equal(L, o["verify_len"])
 
 
 # ---------------------------------------------------------------------------

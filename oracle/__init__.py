@@ -14,6 +14,8 @@ from .dspark_oracle import (  # noqa: F401
     draft,
     schedule,
     schedule_async,
+    schedule_threshold,
+    accept_rates,
     verify,
     run_round,
     row_flags,

@@ -236,6 +236,24 @@ def schedule_async(conf, conf_lag, sps):
     return dict(verify_len=L, n_admitted=K, cum_conf=a, theta_lag=theta_lag, order=order)
 
 
+def schedule_threshold(conf, theta):
+    """Static-threshold baseline: verify while the survival probability holds.
+
+    L_r = number of positions j with a_{r,j} >= theta (a is non-increasing in
+    j, so these form a prefix).  The fixed rule ignores the system load that
+    the prefix scheduler weighs ([HADA] Análise dos experimentos: the static
+    threshold sweep and why static thresholds are suboptimal).
+    Returns dict(verify_len int32 [R], n_admitted, cum_conf fp32 [R, gamma]).
+    """
+    c = np.asarray(conf, dtype=np.float32)
+    a = np.empty_like(c)
+    a[:, 0] = c[:, 0]
+    for j in range(1, c.shape[1]):
+        a[:, j] = a[:, j - 1] * c[:, j]
+    L = (a >= np.float32(theta)).sum(axis=1).astype(np.int32)
+    return dict(verify_len=L, n_admitted=int(L.sum()), cum_conf=a)
+
+
 # ---------------------------------------------------------------------------
 # 3. Lossless verification  ([HADA] Definição do problema; decode cycle)
 
@@ -343,3 +361,32 @@ def row_flags(d, v, eps=FLAG_EPS):
     """
     return ((d["margin"] < eps).any(axis=1) | (v["accept_margin"] < eps).any(axis=1)
             | (v["final_margin"] < eps))
+
+
+# ---------------------------------------------------------------------------
+# Per-position acceptance labels ([HADA] Arquitetura, confidence head)
+
+
+def accept_rates(target, base, W1, W2, w_dtype, anchor, draft_tokens, T):
+    """c*_k = 1 - (1/2) || q_k - p_k ||_1 for every request and draft position.
+
+    q_k is the draft distribution at position k given the drafted prefix
+    (base row k-1 plus the Markov bias of x_{k-1}, x_0 = anchor), p_k the
+    target distribution softmax(target[r, k-1] / T); c*_k is the probability
+    that the rejection test accepts position k given the prefix, the analytic
+    signal the confidence head is trained on ([HADA] Arquitetura,
+    Confidence-Scheduled Verification, confidence head; Treinamento, L_tv).
+    T > 0.
+    Returns float64 [R, gamma].
+    """
+    R, g, V = base.shape
+    W1_64, W2_64 = widen_weights(W1, w_dtype), widen_weights(W2, w_dtype)
+    x = np.asarray(draft_tokens, dtype=np.int64)
+    out = np.zeros((R, g))
+    for k in range(g):
+        prev = np.asarray(anchor, np.int64) if k == 0 else x[:, k - 1]
+        z = base[:, k, :].astype(np.float64) + markov_bias(W1_64, W2_64, prev)
+        q, _, _ = draft_distribution(z, T)
+        p, _, _ = draft_distribution(target[:, k, :].astype(np.float64), T)
+        out[:, k] = 1.0 - 0.5 * np.abs(q - p).sum(axis=1)
+    return out

@@ -599,3 +599,115 @@ def test_lossless_with_async_scheduler_lengths():
     L = int(sched["verify_len"][0])
     P = t.first_token_law(lambda a: L)
     np.testing.assert_allclose(P, _softmax(t.T1), atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# per-position acceptance labels c*_k and the static-threshold baseline
+
+
+def test_accept_rate_equals_enumerated_acceptance_probability():
+    """c*_1 and c*_2 against the exact acceptance probabilities of the oracle's
+    own rejection test, found by bisection over the uniforms."""
+    t = _Tiny(17)
+    _, m1 = t.mid_u1(0)
+    P1 = 0.0
+    for a in range(4):
+        if m1[a] == 0:
+            continue
+        u1, _ = t.mid_u1(a)
+        x, qq = t.draft(u1, 0.5)
+        P1 += m1[a] * _bisect_first(lambda ua: t.verify(x, qq, 1, ua, 0.0, 0.5)["accept_len"][0] == 0)
+        # position 2 given x1 = a accepted: average the test over x2 ~ q2(. | a)
+        m2, _ = _interval_masses(lambda u: t.draft(u1, u)[0][1], 4)
+        e2 = np.concatenate([[0.0], np.cumsum(m2)])
+        P2 = 0.0
+        for b in range(4):
+            if m2[b] == 0:
+                continue
+            x2, q2 = t.draft(u1, 0.5 * (e2[b] + e2[b + 1]))
+            P2 += m2[b] * _bisect_first(lambda ua: t.verify(x2, q2, 2, 0.0, ua, 0.5)["accept_len"][0] == 1)
+        tgt = np.stack([t.T1, t.T2[a], t.T3])[None]
+        c = O.accept_rates(tgt, t.base, t.W1, t.W2, "f32", t.anchor, x2[None], 1.0)
+        np.testing.assert_allclose(c[0, 1], P2, atol=1e-12)
+        c1 = c[0, 0]
+    np.testing.assert_allclose(c1, P1, atol=1e-12)
+
+
+def test_accept_rate_is_one_when_target_equals_draft():
+    rng = np.random.default_rng(18)
+    R, g, V, r = 3, 4, 32, 16
+    base = rng.standard_normal((R, g, V)).astype(np.float32)
+    W1 = (rng.standard_normal((V, r)) * 0.3).astype(np.float32)
+    W2 = (rng.standard_normal((r, V)) * 0.3).astype(np.float32)
+    anchor = rng.integers(0, V, R).astype(np.int32)
+    d = O.draft(base, W1, W2, "f32", anchor, rng.random((R, g)), 1.0)
+    # target rows = the draft logits themselves
+    prev = np.concatenate([anchor[:, None], d["tokens"][:, :-1]], axis=1)
+    z = np.stack([base[:, k].astype(np.float64) + O.markov_bias(W1.astype(np.float64), W2.astype(np.float64),
+                                                                   prev[:, k]) for k in range(g)], axis=1)
+    tgt = np.concatenate([z, z[:, -1:]], axis=1)
+    c = O.accept_rates(tgt, base, W1, W2, "f32", anchor, d["tokens"], 1.0)
+    np.testing.assert_allclose(c, 1.0, atol=1e-12)
+
+
+def test_accept_rate_is_one_minus_residual_mass_at_the_rejection():
+    rng = np.random.default_rng(19)
+    R, g, V, r = 64, 3, 40, 16
+    base = (rng.standard_normal((R, g, V)) * 2).astype(np.float32)
+    W1 = (rng.standard_normal((V, r)) * 0.4).astype(np.float32)
+    W2 = (rng.standard_normal((r, V)) * 0.4).astype(np.float32)
+    anchor = rng.integers(0, V, R).astype(np.int32)
+    tgt = np.concatenate([base, base[:, -1:]], axis=1) + rng.standard_normal((R, g + 1, V)).astype(np.float32)
+    d = O.draft(base, W1, W2, "f32", anchor, rng.random((R, g)), 1.0)
+    v = O.verify(tgt, base, W1, W2, "f32", anchor, d["tokens"], d["probs"], None,
+                 rng.random((R, g)), rng.random(R), 1.0)
+    c = O.accept_rates(tgt, base, W1, W2, "f32", anchor, d["tokens"], 1.0)
+    rej = np.flatnonzero(v["accept_len"] < g)
+    assert len(rej) > 10
+    k = v["accept_len"][rej]                       # 0-based rejected position
+    np.testing.assert_allclose(c[rej, k], 1.0 - v["residual_mass"][rej], atol=1e-12)
+
+
+def test_accept_rate_of_disjoint_distributions_is_zero():
+    V = 8
+    base = np.full((1, 1, V), -40.0, np.float32)
+    base[0, 0, 2] = 40.0
+    tgt = np.full((1, 2, V), -40.0, np.float32)
+    tgt[0, 0, 5] = 40.0
+    z = np.zeros((V, 16), np.float32)
+    c = O.accept_rates(tgt, base, z, z.T.copy(), "f32", np.array([0], np.int32), np.array([[2]]), 1.0)
+    assert 0.0 <= c[0, 0] < 1e-30
+
+
+def test_threshold_schedule_limits_and_prefixes():
+    c = _sched_case(35, R=20, g=7, ties=True)
+    s0 = O.schedule_threshold(c, 0.0)
+    assert (s0["verify_len"] == 7).all()
+    assert O.schedule_threshold(c, 1.5)["n_admitted"] == 0
+    last = None
+    for th in np.linspace(0.0, 1.0, 41):
+        s = O.schedule_threshold(c, th)
+        a, L = s["cum_conf"], s["verify_len"]
+        for r in range(20):                          # admitted positions form a prefix
+            assert (a[r, :L[r]] >= np.float32(th)).all() and (L[r] == 7 or a[r, L[r]] < np.float32(th))
+        if last is not None:
+            assert (L <= last).all()                 # raising the threshold never adds
+        last = L
+
+
+def test_threshold_at_the_cut_reproduces_the_prefix_scheduler():
+    """The prefix scheduler's admitted set is {a >= a_(n*)} (distinct values),
+    so a static threshold placed exactly at the cut selects the same set."""
+    for seed in range(36, 46):
+        rng = np.random.default_rng(seed)
+        c = rng.uniform(0.3, 1.0, (24, 6)).astype(np.float32)
+        sps = (1.0 / (1.0 + rng.uniform(0.005, 0.05) * np.arange(1, 200))).astype(np.float32)
+        s = O.schedule(c, sps)
+        n = s["n_admitted"]
+        if n == 0 or n == c.size:
+            continue
+        a_sorted = s["cum_conf"].reshape(-1)[s["order"]]
+        if a_sorted[n - 1] == a_sorted[n]:
+            continue                                  # tie at the cut
+        t = O.schedule_threshold(c, a_sorted[n - 1])
+        assert t["n_admitted"] == n and (t["verify_len"] == s["verify_len"]).all()

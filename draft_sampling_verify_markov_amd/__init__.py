@@ -21,12 +21,14 @@ from ._binding import (  # noqa: F401
     draft,
     schedule,
     schedule_async,
+    schedule_threshold,
+    accept_rates,
     verify,
     run_round,
 )
 
 __all__ = [
     "DSPARK_W_BF16", "DSPARK_W_F32", "DERR_BITS", "DSparkError", "lib_path", "load_library",
-    "workspace_size", "new_workspace", "workspace_init", "device_error", "draft", "schedule", "schedule_async",
+    "workspace_size", "new_workspace", "workspace_init", "device_error", "draft", "schedule", "schedule_async", "schedule_threshold", "accept_rates",
     "verify", "run_round",
 ]

@@ -48,6 +48,10 @@ def load_library():
     lib.dspark_schedule.restype = I
     lib.dspark_schedule_async.argtypes = [P, P, P, I, I, I, P, P, P, P, Z, P]
     lib.dspark_schedule_async.restype = I
+    lib.dspark_schedule_threshold.argtypes = [P, F, I, I, P, P, P, P, Z, P]
+    lib.dspark_schedule_threshold.restype = I
+    lib.dspark_accept_rates.argtypes = [P, P, P, P, I, P, P, P, I, I, I, I, F, P, P, Z, P]
+    lib.dspark_accept_rates.restype = I
     lib.dspark_verify.argtypes = [P, P, P, P, I, P, P, P, P, P, P, P, I, I, I, I, F, P, P, P, P, Z, P]
     lib.dspark_verify.restype = I
     lib.dspark_profile_arm.argtypes = [I, P, P, I, I]
@@ -178,6 +182,45 @@ def schedule_async(conf, conf_lag, sps, ws, out=None, with_cum=True):
             ws.data_ptr(), ws.numel(), _stream(dev))
     _check("dspark_schedule_async", load_library().dspark_schedule_async(*args))
     return L, n, a
+
+
+def schedule_threshold(conf, theta, ws, out=None, with_cum=True):
+    """dspark_schedule_threshold.  Returns (verify_len, n_admitted[1], cum_conf or None)."""
+    R, g = conf.shape
+    dev = conf.device
+    if out is None:
+        out = (torch.empty(R, dtype=torch.int32, device=dev),
+               torch.empty(1, dtype=torch.int32, device=dev),
+               torch.empty((R, g), dtype=torch.float32, device=dev) if with_cum else None)
+    L, n, a = out
+    args = (_ptr(conf, torch.float32, (R, g), "conf", dev), float(theta), R, g,
+            _ptr(L, torch.int32, (R,), "verify_len", dev), _ptr(n, torch.int32, (1,), "n_admitted", dev),
+            _ptr(a, torch.float32, (R, g), "cum_conf", dev),
+            ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("dspark_schedule_threshold", load_library().dspark_schedule_threshold(*args))
+    return L, n, a
+
+
+def accept_rates(target, base, W1, W2, anchor, draft_tokens, draft_stats, temperature, ws, out=None):
+    """dspark_accept_rates.  Returns accept_rate [R, gamma] fp32."""
+    R, g1, V = target.shape
+    g = g1 - 1
+    r = W1.shape[1]
+    dev = target.device
+    wt = _wtype(W1)
+    wdt = W1.dtype
+    if out is None:
+        out = torch.empty((R, g), dtype=torch.float32, device=dev)
+    args = (_ptr(target, torch.float32, (R, g + 1, V), "target", dev),
+            _ptr(base, torch.float32, (R, g, V), "base", dev),
+            _ptr(W1, wdt, (V, r), "W1", dev), _ptr(W2, wdt, (r, V), "W2", dev), wt,
+            _ptr(anchor, torch.int32, (R,), "anchor", dev),
+            _ptr(draft_tokens, torch.int32, (R, g), "draft_tokens", dev),
+            _ptr(draft_stats, torch.float32, (R, g, 2), "draft_stats", dev),
+            R, g, V, r, float(temperature), _ptr(out, torch.float32, (R, g), "accept_rate", dev),
+            ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("dspark_accept_rates", load_library().dspark_accept_rates(*args))
+    return out
 
 
 def verify(target, base, W1, W2, anchor, draft_tokens, draft_probs, draft_stats, verify_len,

@@ -12,6 +12,11 @@ int schedule_impl(const float* conf, const float* sps, int R, int gamma, int n_t
 int schedule_async_impl(const float* conf, const float* conf_lag, const float* sps, int R, int gamma,
                         int n_table, int32_t* verify_len, int32_t* n_admitted, float* cum_conf, void* ws,
                         hipStream_t stream);
+int schedule_threshold_impl(const float* conf, float theta, int R, int gamma, int32_t* verify_len,
+                            int32_t* n_admitted, float* cum_conf, void* ws, hipStream_t stream);
+int accept_rates_impl(const float* target, const float* base, const void* W1, const void* W2,
+                      dspark_wtype w_type, const int32_t* anchor, const int32_t* dtok, const float* dstats,
+                      int R, int gamma, int V, int r, float T, float* out, void* ws, hipStream_t stream);
 int verify_impl(const float* target, const float* base, const void* W1, const void* W2,
                 dspark_wtype w_type, const int32_t* anchor, const int32_t* dtok, const float* dprob,
                 const float* dstats, const int32_t* vlen, const float* u_acc, const float* u_fin,
@@ -167,6 +172,33 @@ int dspark_schedule_async(const float* conf, const float* conf_lag, const float*
   if (workspace_bytes < 256) return DSPARK_ENOSPC;
   return schedule_async_impl(conf, conf_lag, sps, R, gamma, n_table, verify_len, n_admitted, cum_conf,
                              workspace, stream);
+}
+
+int dspark_schedule_threshold(const float* conf, float theta, int R, int gamma, int32_t* verify_len,
+                              int32_t* n_admitted, float* cum_conf, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  if (R < 1 || gamma < 1 || gamma > DSPARK_MAX_GAMMA || (long long)R * gamma > DSPARK_MAX_POOL)
+    return DSPARK_EINVAL;
+  if (!(theta == theta)) return DSPARK_EINVAL;
+  if (!conf || !verify_len || !n_admitted) return DSPARK_EINVAL;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DSPARK_EINVAL;
+  if (workspace_bytes < 256) return DSPARK_ENOSPC;
+  return schedule_threshold_impl(conf, theta, R, gamma, verify_len, n_admitted, cum_conf, workspace, stream);
+}
+
+int dspark_accept_rates(const float* target, const float* base, const void* W1, const void* W2,
+                        dspark_wtype w_type, const int32_t* anchor, const int32_t* draft_tokens,
+                        const float* draft_stats, int R, int gamma, int V, int r, float temperature,
+                        float* accept_rate, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!sizes_ok(R, gamma, V, r)) return DSPARK_EINVAL;
+  if (w_type != DSPARK_W_BF16 && w_type != DSPARK_W_F32) return DSPARK_EINVAL;
+  if (!(temperature > 0.f) || !(temperature < INFINITY)) return DSPARK_EINVAL;
+  if (!target || !base || !W1 || !W2 || !anchor || !draft_tokens || !draft_stats || !accept_rate)
+    return DSPARK_EINVAL;
+  const int st = check_ws(workspace, workspace_bytes, R, gamma, V);
+  if (st != DSPARK_OK) return st;
+  return accept_rates_impl(target, base, W1, W2, w_type, anchor, draft_tokens, draft_stats, R, gamma, V, r,
+                           temperature, accept_rate, workspace, stream);
 }
 
 int dspark_verify(const float* target, const float* base, const void* W1, const void* W2,

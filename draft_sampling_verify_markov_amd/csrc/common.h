@@ -695,6 +695,7 @@ struct WsLayout {
   size_t tx;       // float  [R][gamma]     target logit at the drafted token
   size_t tp;       // float  [R][gamma]     p_k(x_k) of evaluated positions
   size_t rrec;     // float4 [R][nt][2]     residual tile records
+  size_t tvpart;   // float  [R*gamma][nt]  acceptance-label tile sums
   size_t total;
 };
 
@@ -712,6 +713,7 @@ __host__ __device__ inline WsLayout ws_layout(int R, int gamma, int V) {
   L.tx = o;       o = ws_align(o + (size_t)R * gamma * 4);
   L.tp = o;       o = ws_align(o + (size_t)R * gamma * 4);
   L.rrec = o;     o = ws_align(o + (size_t)R * nt * 32);
+  L.tvpart = o;   o = ws_align(o + (size_t)R * gamma * nt * 4);
   L.total = o;
   return L;
 }

@@ -23,6 +23,9 @@
 //   4. Theta_n = double(T_n) * double(SPS(R + n)); n* = first strict drop
 //   5. verify_len[r] = admitted candidates of row r (LDS counters)
 //
+// dspark_schedule_threshold: the static-threshold baseline L_r = #{j : a_{r,j}
+// >= theta} (HADA, "Análise dos experimentos": the static threshold sweep).
+//
 // dspark_schedule_async (HADA, "Implantação em produção", practical
 // application of the scheduler): the cut length K is the first maximiser of
 // Theta over the pool of the confidences of two steps earlier (steps 1-4
@@ -269,6 +272,56 @@ __global__ __launch_bounds__(SCHED_THREADS) void k_schedule_async(const float* _
   pool_sort<KPT>(conf, R, gamma, cum_conf, err, sm, k);
   pool_admit<KPT>(k, K, R, gamma, sm, verify_len);
   if (tid == 0) *n_admitted = K;
+}
+
+// Static-threshold baseline: L_r = #{j : a_{r,j} >= theta}.  One workgroup;
+// thread t handles requests t, t + 1024, ...; the admitted total is summed in
+// a fixed order through LDS.
+__global__ __launch_bounds__(SCHED_THREADS) void k_schedule_threshold(const float* __restrict__ conf,
+                                                                     float theta, int R, int gamma,
+                                                                     int32_t* __restrict__ verify_len,
+                                                                     int32_t* __restrict__ n_admitted,
+                                                                     float* __restrict__ cum_conf, int32_t* err) {
+  __shared__ int wsum[SCHED_THREADS / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tot = 0;
+  for (int r = tid; r < R; r += SCHED_THREADS) {
+    float a = 1.0f;
+    int L = 0;
+    for (int j = 0; j < gamma; j++) {
+      const size_t f = (size_t)r * gamma + j;
+      float c = conf[f];
+      if (!(c > 0.f && c <= 1.f)) {
+        raise_err(err, DSPARK_DERR_CONF);
+        c = (c > 1.f) ? 1.f : 0.f;
+      }
+      a = (j == 0) ? c : __fmul_rn(a, c);
+      if (cum_conf) cum_conf[f] = a;
+      L += (a >= theta) ? 1 : 0;
+    }
+    verify_len[r] = L;
+    tot += L;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
+  if (lane == 0) wsum[wave] = tot;
+  __syncthreads();
+  if (tid == 0) {
+    int n = 0;
+    for (int w = 0; w < SCHED_THREADS / 64; w++) n += wsum[w];
+    *n_admitted = n;
+  }
+}
+
+int schedule_threshold_impl(const float* conf, float theta, int R, int gamma, int32_t* verify_len,
+                            int32_t* n_admitted, float* cum_conf, void* ws, hipStream_t stream) {
+  const WsLayout L = ws_layout(R, gamma, 8);
+  prof_before(DSPARK_KID_SCHEDULE, stream);
+  for (int rep = prof_repeat(DSPARK_KID_SCHEDULE); rep > 0; rep--)
+    hipLaunchKernelGGL(k_schedule_threshold, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, theta, R, gamma,
+                       verify_len, n_admitted, cum_conf, ws_ptr<int32_t>(ws, L.err));
+  prof_after(DSPARK_KID_SCHEDULE, stream);
+  return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
 }
 
 int schedule_async_impl(const float* conf, const float* conf_lag, const float* sps, int R, int gamma,

@@ -20,6 +20,8 @@
 //             tiles (T > 0 only).  For requests that rejected at k*,
 //             recomputes the draft logits of position k* with the MFMA bias
 //             block and writes tile records of max(0, p - pi).
+//   (dspark_accept_rates reuses the stream and the residual pipeline over
+//   every request and position to form c*_k = 1 - |q_k - p_k|_1 / 2.)
 //   finalize  one workgroup per request: residual or bonus inverse-CDF sample
 //             (fp64 scan over tiles, recompute of one chunk or tile), emitted
 //             tokens and the p_k(x_k) output.
@@ -51,6 +53,7 @@ struct VerifyArgs {
   float* tx;
   float* tp;
   float4* rrec;
+  float* tvpart;  // [R*gamma][V/256] per-tile sums of max(0, p - q) (acceptance labels)
   int32_t* err;
 
   __device__ int L_of(int row, bool report = false) const {
@@ -233,7 +236,10 @@ __device__ __forceinline__ float residual_elem(float t, float b, float bias, flo
 // by direct-to-LDS loads issued one unit ahead (they overlap the unit's MFMA
 // chain), the epilogue forms max(0, p - pi) and per-wave sums, and the tile's
 // last unit writes the residual tile records.
-template <typename WT, int KS>
+// TVM (acceptance labels): the items are every (request, position k) pair,
+// k = 1..gamma, in chunks of CH consecutive flat indices r*gamma + k-1, and
+// each (item, tile) writes the tile's sum of max(0, p - q) to tvpart.
+template <typename WT, int KS, bool TVM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_residual_partials(
     VerifyArgs<WT> P) {
   constexpr int APAD = BiasBlock<WT>::APAD;
@@ -257,42 +263,59 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int my_tiles = (nt - (int)blockIdx.x + G - 1) / G;
   const float sc = (P.T == 1.0f) ? LOG2E_F : LOG2E_F * P.invT;
 
-  for (int c0 = 0; c0 < P.R; c0 += CH) {
-    const int nrows = min(CH, P.R - c0);
+  const int nitems = TVM ? P.R * P.gamma : P.R;
+  for (int c0 = 0; c0 < nitems; c0 += CH) {
+    // request whose rows anchor the buffer resources of this chunk
+    const int r0 = TVM ? c0 / P.gamma : c0;
+    int nrej;
     __syncthreads();  // the previous chunk is done with every LDS array
-    // compaction of the chunk's rejected requests (order kept)
-    bool mine = false;
-    if (tid < nrows) mine = P.rej[c0 + tid] <= P.L_of(c0 + tid);
-    const uint64_t bal = __ballot(mine);
-    if (tid < CH && lane == 0) s_cnt[wave] = __popcll(bal);
-    __syncthreads();
-    const int nrej = (CH > 64 ? s_cnt[0] + s_cnt[1] : s_cnt[0]);
-    if (nrej == 0) continue;  // uniform
-    if (mine) {
-      const int pos = (wave == 1 ? s_cnt[0] : 0) + __popcll(bal & ((1ull << lane) - 1ull));
-      s_list[pos] = tid;
+    if (TVM) {
+      nrej = min(CH, nitems - c0);
+    } else {
+      // compaction of the chunk's rejected requests (order kept)
+      const int nrows = min(CH, P.R - c0);
+      bool mine = false;
+      if (tid < nrows) mine = P.rej[c0 + tid] <= P.L_of(c0 + tid);
+      const uint64_t bal = __ballot(mine);
+      if (tid < CH && lane == 0) s_cnt[wave] = __popcll(bal);
+      __syncthreads();
+      nrej = (CH > 64 ? s_cnt[0] + s_cnt[1] : s_cnt[0]);
+      if (nrej == 0) continue;  // uniform
+      if (mine) {
+        const int pos = (wave == 1 ? s_cnt[0] : 0) + __popcll(bal & ((1ull << lane) - 1ull));
+        s_list[pos] = tid;
+      }
+      __syncthreads();
     }
-    __syncthreads();
     if (tid < nrej) {
-      const int i = s_list[tid], row = c0 + i;
-      const int ks = P.rej[row];  // k*, 1-based
+      int row, ks;  // request and 1-based position of the item
+      if (TVM) {
+        const int item = c0 + tid;
+        row = item / P.gamma;
+        ks = item - row * P.gamma + 1;
+        s_list[tid] = tid;
+      } else {
+        row = c0 + s_list[tid];
+        ks = P.rej[row];  // k*
+      }
       const double2 rs = P.rowstat[(size_t)row * (P.gamma + 1) + ks - 1];
       const size_t ev = (size_t)row * P.gamma + ks - 1;
       s_Mt[tid] = (float)rs.x;
       s_iZt[tid] = (float)(1.0 / rs.y);
       s_mq[tid] = P.dstats[2 * ev];
       s_iZq[tid] = (float)(1.0 / (double)P.dstats[2 * ev + 1]);
-      s_boff[tid] = ((uint32_t)i * (uint32_t)P.gamma + (uint32_t)(ks - 1)) * (uint32_t)P.V * 4u;
-      s_toff[tid] = ((uint32_t)i * (uint32_t)(P.gamma + 1) + (uint32_t)(ks - 1)) * (uint32_t)P.V * 4u;
+      const uint32_t rl = (uint32_t)(row - r0);
+      s_boff[tid] = (rl * (uint32_t)P.gamma + (uint32_t)(ks - 1)) * (uint32_t)P.V * 4u;
+      s_toff[tid] = (rl * (uint32_t)(P.gamma + 1) + (uint32_t)(ks - 1)) * (uint32_t)P.V * 4u;
       s_tok[tid] = P.prev_of(row, ks);
     }
     __syncthreads();
 
     const int nrb = ceil_div(nrej, 32);
     const int nunits = my_tiles * nrb;
-    const size_t R_left = (size_t)(P.R - c0);
-    const rsrc_t brs = make_rsrc(P.base + (size_t)c0 * P.gamma * P.V, R_left * P.gamma * P.V * 4);
-    const rsrc_t trs = make_rsrc(P.target + (size_t)c0 * (P.gamma + 1) * P.V, R_left * (P.gamma + 1) * P.V * 4);
+    const size_t R_left = (size_t)(P.R - r0);
+    const rsrc_t brs = make_rsrc(P.base + (size_t)r0 * P.gamma * P.V, R_left * P.gamma * P.V * 4);
+    const rsrc_t trs = make_rsrc(P.target + (size_t)r0 * (P.gamma + 1) * P.V, R_left * (P.gamma + 1) * P.V * 4);
     // unit u's rows: wave w loads compacted rows 4i + w of the block (8 base,
     // 8 target loads per wave; rows past nrej re-read row 0)
     auto issue = [&](int u) {
@@ -361,9 +384,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         issue(u + 1);
         if (rb == nrb - 1 && tid < nrej) {
           const float s0 = red_s[0][tid], s1 = red_s[1][tid], s2 = red_s[2][tid], s3 = red_s[3][tid];
-          float4* rec = P.rrec + ((size_t)(c0 + s_list[tid]) * nt + tile) * 2;
-          rec[0] = make_float4(0.f, (s0 + s1) + (s2 + s3), s0, s1);
-          rec[1] = make_float4(s2, s3, 0.f, 0.f);
+          if (TVM) {
+            P.tvpart[(size_t)(c0 + tid) * nt + tile] = (s0 + s1) + (s2 + s3);
+          } else {
+            float4* rec = P.rrec + ((size_t)(c0 + s_list[tid]) * nt + tile) * 2;
+            rec[0] = make_float4(0.f, (s0 + s1) + (s2 + s3), s0, s1);
+            rec[1] = make_float4(s2, s3, 0.f, 0.f);
+          }
         }
       }
     }
@@ -518,6 +545,59 @@ __global__ __launch_bounds__(256) void k_verify_finalize(VerifyArgs<WT> P) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// acceptance labels c*_k = 1 - |q_k - p_k|_1 / 2 (dspark_accept_rates)
+
+// Target row statistics (M, Z) of rows j < gamma: one workgroup per request,
+// one wave per row, from the stream kernel's 1024-column partials.
+template <typename WT>
+__global__ __launch_bounds__(256) void k_target_rowstats(VerifyArgs<WT> P) {
+  const int row = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int nvt = ceil_div(P.V, VTILE);
+  const double invTd = (P.T == 1.0f) ? 1.0 : 1.0 / (double)P.T;
+  for (int j = wave; j < P.gamma; j += 4) {
+    const size_t rowj = (size_t)row * (P.gamma + 1) + j;
+    const float2* vp = P.vpart + rowj * nvt;
+    float ml = -INFINITY;
+    for (int t = lane; t < nvt; t += 64) ml = fmaxf(ml, vp[t].x);
+    const float M = wave_max(ml);
+    double zl = 0.0;
+    for (int t = lane; t < nvt; t += 64) zl += (double)vp[t].y * (double)exp_acc((vp[t].x - M) * (float)invTd);
+    const double Z = wave_sum_d(zl);
+    if (lane == 0) P.rowstat[rowj] = make_double2((double)M, Z);
+  }
+}
+
+// c* of one item (one wave): 1 - sum over tiles of the residual sums, the
+// per-lane strided sums added in a fixed order (fp64).
+template <typename WT>
+__global__ __launch_bounds__(256) void k_accept_finalize(VerifyArgs<WT> P, float* __restrict__ out) {
+  const int item = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (item >= P.R * P.gamma) return;
+  const int nt = ceil_div(P.V, TILE);
+  const float* tp = P.tvpart + (size_t)item * nt;
+  double s = 0.0;
+  for (int t = lane; t < nt; t += 64) s += (double)tp[t];
+  const double D = wave_sum_d(s);
+  if (lane == 0) {
+    out[item] = (float)(1.0 - D);
+    if (!(D == D)) raise_err(P.err, DSPARK_DERR_NONFINITE);
+  }
+}
+
+template <typename WT>
+static int launch_accept_rates(const VerifyArgs<WT>& P, float* out, hipStream_t stream) {
+  const int nseg = ceil_div(P.V, VSEG);
+  const long long nblk = (long long)(P.gamma + 1) * P.R * nseg;
+  hipLaunchKernelGGL((k_verify_stream<WT, false>), dim3((unsigned)nblk), dim3(256), 0, stream, P);
+  hipLaunchKernelGGL((k_target_rowstats<WT>), dim3(P.R), dim3(256), 0, stream, P);
+  const int grid_r = min(ceil_div(P.V, TILE), device_cu_count());
+  DSPARK_DISPATCH_KS(P.r, hipLaunchKernelGGL((k_residual_partials<WT, KS, true>), dim3(grid_r), dim3(256), 0,
+                                             stream, P));
+  hipLaunchKernelGGL((k_accept_finalize<WT>), dim3(ceil_div(P.R * P.gamma, 4)), dim3(256), 0, stream, P, out);
+  return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
+}
+
 template <typename WT>
 static int launch_verify(const VerifyArgs<WT>& P, hipStream_t stream) {
   const int nseg = ceil_div(P.V, VSEG);
@@ -543,8 +623,8 @@ static int launch_verify(const VerifyArgs<WT>& P, hipStream_t stream) {
     prof_before(DSPARK_KID_RESIDUAL, stream);
     for (int rep = prof_repeat(DSPARK_KID_RESIDUAL); rep > 0; rep--) {
       const int grid_r = min(ceil_div(P.V, TILE), device_cu_count());
-      DSPARK_DISPATCH_KS(P.r, hipLaunchKernelGGL((k_residual_partials<WT, KS>), dim3(grid_r), dim3(256), 0,
-                                                 stream, P));
+      DSPARK_DISPATCH_KS(P.r, hipLaunchKernelGGL((k_residual_partials<WT, KS, false>), dim3(grid_r), dim3(256),
+                                                 0, stream, P));
     }
     prof_after(DSPARK_KID_RESIDUAL, stream);
   }
@@ -579,6 +659,7 @@ int verify_impl(const float* target, const float* base, const void* W1, const vo
     P.tx = ws_ptr<float>(ws, Lw.tx);
     P.tp = ws_ptr<float>(ws, Lw.tp);
     P.rrec = ws_ptr<float4>(ws, Lw.rrec);
+    P.tvpart = ws_ptr<float>(ws, Lw.tvpart);
     P.err = ws_ptr<int32_t>(ws, Lw.err);
   };
   if (w_type == DSPARK_W_BF16) {
@@ -593,6 +674,36 @@ int verify_impl(const float* target, const float* base, const void* W1, const vo
   P.W1 = static_cast<const float*>(W1);
   P.W2 = static_cast<const float*>(W2);
   return launch_verify(P, stream);
+}
+
+int accept_rates_impl(const float* target, const float* base, const void* W1, const void* W2,
+                      dspark_wtype w_type, const int32_t* anchor, const int32_t* dtok, const float* dstats,
+                      int R, int gamma, int V, int r, float T, float* out, void* ws, hipStream_t stream) {
+  const WsLayout Lw = ws_layout(R, gamma, V);
+  auto fill = [&](auto& P) {
+    P = {};
+    P.target = target; P.base = base;
+    P.anchor = anchor; P.dtok = dtok; P.dstats = dstats; P.vlen = nullptr;
+    P.R = R; P.gamma = gamma; P.V = V; P.r = r;
+    P.T = T; P.invT = 1.0f / T;
+    P.rowstat = ws_ptr<double2>(ws, Lw.rowstat);
+    P.vpart = ws_ptr<float2>(ws, Lw.vpart);
+    P.tx = ws_ptr<float>(ws, Lw.tx);
+    P.tvpart = ws_ptr<float>(ws, Lw.tvpart);
+    P.err = ws_ptr<int32_t>(ws, Lw.err);
+  };
+  if (w_type == DSPARK_W_BF16) {
+    VerifyArgs<uint16_t> P;
+    fill(P);
+    P.W1 = static_cast<const uint16_t*>(W1);
+    P.W2 = static_cast<const uint16_t*>(W2);
+    return launch_accept_rates(P, out, stream);
+  }
+  VerifyArgs<float> P;
+  fill(P);
+  P.W1 = static_cast<const float*>(W1);
+  P.W2 = static_cast<const float*>(W2);
+  return launch_accept_rates(P, out, stream);
 }
 
 }  // namespace dspark

@@ -180,6 +180,21 @@ int dspark_schedule_async(const float* conf, const float* conf_lag, const float*
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * dspark_schedule_threshold - static-threshold baseline ("DSpark: Aceleração da
+ * inferência de LLM com speculative decoding", pt.news.hada.io, section
+ * "Análise dos experimentos": the static threshold sweep, and why a fixed
+ * threshold that ignores the system load is suboptimal in serving).
+ *
+ *   verify_len[r] = number of positions j with a[r,j] >= theta (a prefix,
+ *                   since a is non-increasing); n_admitted = sum of them
+ *
+ *   conf, cum_conf  as for dspark_schedule; theta: host scalar (not NaN)
+ */
+int dspark_schedule_threshold(const float* conf, float theta, int R, int gamma, int32_t* verify_len,
+                              int32_t* n_admitted, float* cum_conf, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/*
  * dspark_verify - lossless rejection-sampling verification.
  *
  * Per request r, for k = 1..L_r in order: p = softmax(target[r,k-1] / T);
@@ -208,6 +223,33 @@ int dspark_verify(const float* target, const float* base, const void* W1, const 
                   const float* u_accept, const float* u_final, int R, int gamma, int V, int r,
                   float temperature, int32_t* out_tokens, int32_t* accept_len, float* target_probs,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dspark_accept_rates - per-position acceptance labels ("DSpark: Aceleração da
+ * inferência de LLM com speculative decoding", pt.news.hada.io, section
+ * "Arquitetura", Confidence-Scheduled Verification: the confidence head is
+ * trained on the analytic per-step acceptance rate; section "Treinamento":
+ * that rate is 1 - |p_d - p_t|_1 / 2).
+ *
+ * For every request r and draft position k = 1..gamma:
+ *   accept_rate[r, k-1] = 1 - (1/2) sum_v | q_k(v) - p_k(v) |
+ * with q_k the draft distribution at k given the drafted prefix (base row
+ * k-1 plus the Markov bias of x_{k-1}, x_0 = anchor, normalised with
+ * draft_stats) and p_k = softmax(target[r, k-1] / T): the probability that
+ * the rejection test accepts position k when the prefix is accepted.
+ * Computed as 1 - sum_v max(0, p_k(v) - q_k(v)) (fp32 per 256-column tile,
+ * fp64 across tiles).  Not part of the round; an offline label pass.
+ *
+ *   target, base, W1, W2, w_type, anchor  as for dspark_verify
+ *   draft_tokens, draft_stats             outputs of dspark_draft
+ *   temperature    > 0 (host scalar; T == 0 returns DSPARK_EINVAL)
+ *   accept_rate    out [R, gamma] fp32
+ * Uses the same workspace as dspark_verify (its verify scratch is overwritten).
+ */
+int dspark_accept_rates(const float* target, const float* base, const void* W1, const void* W2,
+                        dspark_wtype w_type, const int32_t* anchor, const int32_t* draft_tokens,
+                        const float* draft_stats, int R, int gamma, int V, int r, float temperature,
+                        float* accept_rate, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Optional launch-timing hook for benchmarks and profilers.

@@ -95,6 +95,31 @@ def test_schedule_async_rejects_bad_arguments(lib):
     assert f(16, 16, 16, 4, 4, 10, 16, 16, None, 256, 100, None) == ENOSPC
 
 
+def test_schedule_threshold_rejects_bad_arguments(lib):
+    f = lib.dspark_schedule_threshold
+    assert f(None, 0.5, 4, 4, 16, 16, None, 256, 4096, None) == EINVAL
+    assert f(16, float("nan"), 4, 4, 16, 16, None, 256, 4096, None) == EINVAL
+    assert f(16, 0.5, 1000, 9, 16, 16, None, 256, 4096, None) == EINVAL      # pool > 8192
+    assert f(16, 0.5, 4, 4, None, 16, None, 256, 4096, None) == EINVAL
+    assert f(16, 0.5, 4, 4, 16, 16, None, 256, 100, None) == ENOSPC
+
+
+def test_accept_rates_rejects_bad_arguments(lib):
+    good = [16, 16, 16, 16, 0, 16, 16, 16, 4, 4, 512, 16, 1.0, 16, 256, 1 << 24, None]
+    bad = list(good); bad[12] = 0.0
+    assert lib.dspark_accept_rates(*bad) == EINVAL                      # greedy has no label
+    bad = list(good); bad[12] = float("inf")
+    assert lib.dspark_accept_rates(*bad) == EINVAL
+    bad = list(good); bad[4] = 7
+    assert lib.dspark_accept_rates(*bad) == EINVAL                      # unknown weight type
+    bad = list(good); bad[7] = None
+    assert lib.dspark_accept_rates(*bad) == EINVAL                      # no draft statistics
+    bad = list(good); bad[11] = 24
+    assert lib.dspark_accept_rates(*bad) == EINVAL                      # r % 16 != 0
+    bad = list(good); bad[15] = 1024
+    assert lib.dspark_accept_rates(*bad) == ENOSPC
+
+
 def test_verify_rejects_bad_arguments(lib):
     base = [16, 16, 16, 16, 0, 16, 16, 16, 16, None, 16, 16, 4, 4, 512, 16, 1.0, 16, 16, None, 256,
             1 << 20, None]

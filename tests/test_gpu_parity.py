@@ -266,6 +266,53 @@ def test_draft_stage_bias_exact_in_fp32():
 
 
 # ---------------------------------------------------------------------------
+# static-threshold scheduler and per-position acceptance labels
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_schedule_threshold_bit_exact(seed):
+    rng = np.random.default_rng(400 + seed)
+    g = int(rng.integers(1, 17))
+    R = int(rng.integers(1, 8192 // g + 1))
+    conf = rng.beta(6, 2, (R, g)).astype(np.float32)
+    conf[rng.random((R, g)) < 0.1] = 1.0
+    a = O.schedule_threshold(conf, 0.0)["cum_conf"]
+    thetas = [0.0, 0.5, 1.0, 1.5, float(a.reshape(-1)[rng.integers(0, a.size)])]   # the last sits on a value
+    dv = dev()
+    c = torch.from_numpy(conf).to(dv)
+    ws = torch.zeros(256, dtype=torch.uint8, device=dv)
+    for th in thetas:
+        L, n, ca = D.schedule_threshold(c, th, ws)
+        torch.cuda.synchronize()
+        o = O.schedule_threshold(conf, th)
+        assert D.device_error(ws) == 0
+        assert np.array_equal(ca.cpu().numpy(), o["cum_conf"])
+        assert int(n.cpu()[0]) == o["n_admitted"] and np.array_equal(L.cpu().numpy(), o["verify_len"])
+
+
+@pytest.mark.parametrize("shape", [(4, 4, 512, 16, "f32"), (24, 7, 4096, 64, "bf16"), (33, 5, 520, 48, "bf16"),
+                                   (40, 7, 2056, 256, "bf16"), (20, 9, 1000, 32, "f32")])
+@pytest.mark.parametrize("T", [1.0, 0.7])
+def test_accept_rates_on_oracle_draft(shape, T):
+    R, g, V, r, wd = shape
+    d = config(1, R=R, gamma=g, V=V, r=r, w_dtype=wd, target=("uniform", 0.2, 1.5))
+    inp = make_inputs(d, seed=23)
+    od = O.draft(inp["base"], inp["W1"], inp["W2"], inp["w_dtype"], inp["anchor"], inp["u_draft"], T)
+    oc = O.accept_rates(inp["target"], inp["base"], inp["W1"], inp["W2"], inp["w_dtype"], inp["anchor"],
+                        od["tokens"], T)
+    dd = to_dev(inp)
+    dv = dd["base"].device
+    ws = D.new_workspace(R, g, V, r, dv)
+    tok = torch.from_numpy(od["tokens"]).to(dv)
+    stats = torch.from_numpy(od["stats"].astype(np.float32)).to(dv)
+    c = D.accept_rates(dd["target"], dd["base"], dd["W1"], dd["W2"], dd["anchor"], tok, stats, T, ws)
+    torch.cuda.synchronize()
+    assert D.device_error(ws) == 0
+    say(f"accept rates {shape} T={T}: mean {oc.mean():.4f}, max |diff| {np.abs(c.cpu().numpy() - oc).max():.2e}")
+    np.testing.assert_allclose(c.cpu().numpy(), oc, atol=1e-4, rtol=1e-5)
+
+
+# ---------------------------------------------------------------------------
 # determinism, device-side error reporting
 
 

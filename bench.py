@@ -43,8 +43,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="3", help="workload key (default 3: R=128, gamma=7, V=131072)")
     ap.add_argument("--temperature", type=float, default=1.0)
-    ap.add_argument("--scheduler", choices=("early", "async"), default="early",
-                    help="early-stop prefix scheduler (default) or the asynchronous production variant")
+    ap.add_argument("--scheduler", choices=("early", "async", "threshold"), default="early",
+                    help="early-stop prefix scheduler (default), the asynchronous production variant, "
+                         "or the static-threshold baseline")
+    ap.add_argument("--theta", default="cut",
+                    help="threshold for --scheduler threshold: a number, or 'cut' = the survival "
+                         "probability at the early-stop scheduler's cut (equal verify bytes)")
+    ap.add_argument("--labels", action="store_true",
+                    help="also time the acceptance-label pass (dspark_accept_rates) on the workload")
     ap.add_argument("--eager", action="store_true", help="launch kernels eagerly instead of a graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -99,10 +105,13 @@ def cpu_worker(a):
     from gen import make_inputs
     import oracle as O
     inp = make_inputs(cfg_key(a.config))
+    theta = None
+    if a.scheduler == "threshold":
+        theta = oracle_theta(O, inp, a.theta)
     t0 = time.perf_counter()
     n, toks = 0, 0
     while True:
-        res = O.run_round(inp, T=a.temperature, scheduler=a.scheduler)
+        res = O.run_round(inp, T=a.temperature, scheduler=a.scheduler, theta=theta)
         n += 1
         toks += int((res["verify"]["accept_len"] + 1).sum())
         if time.perf_counter() - t0 >= a.cpu_seconds:
@@ -112,6 +121,15 @@ def cpu_worker(a):
     print(json.dumps(dict(rounds=n, seconds=dt, tokens=toks, threads=threads)))
 
 
+def oracle_theta(O, inp, theta_arg):
+    """Threshold for the static baseline on the CPU side (same rule as the GPU side)."""
+    if theta_arg != "cut":
+        return float(theta_arg)
+    s = O.schedule(inp["conf"], inp["sps"])
+    a, L = s["cum_conf"], s["verify_len"]
+    return float(min(a[r, L[r] - 1] for r in range(len(L)) if L[r] > 0))
+
+
 def cpu_baseline(a):
     ncpu = len(os.sched_getaffinity(0))
     env = dict(os.environ)
@@ -119,7 +137,7 @@ def cpu_baseline(a):
         env.setdefault(k, str(ncpu))
     cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-worker", "--config", a.config,
            "--cpu-seconds", str(a.cpu_seconds), "--temperature", str(a.temperature),
-           "--scheduler", a.scheduler]
+           "--scheduler", a.scheduler, "--theta", a.theta]
     out = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=600)
     if out.returncode != 0:
         return dict(error=out.stderr[-400:])
@@ -167,12 +185,23 @@ def gpu_bench(a):
     ws = D.new_workspace(R, g, V, r, dev)
     ws_sched = torch.zeros(256, dtype=torch.uint8, device=dev)
     T = a.temperature
+    theta = None
+    if a.scheduler == "threshold":
+        if a.theta == "cut":
+            # survival probability at the early-stop scheduler's cut: the same
+            # number of verified candidates, so equal verify bytes
+            Lc, _, ac = D.schedule(dd["conf"], dd["sps"], ws_sched)
+            torch.cuda.synchronize()
+            Lc, ac = Lc.cpu().numpy(), ac.cpu().numpy()
+            theta = float(min(ac[i, Lc[i] - 1] for i in range(R) if Lc[i] > 0))
+        else:
+            theta = float(a.theta)
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
 
     # one eager round: reference outputs and workload statistics
     with torch.cuda.stream(stream):
-        ref = D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler)
+        ref = D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta)
     torch.cuda.synchronize()
     if D.device_error(ws) != 0 or D.device_error(ws_sched) != 0:
         raise RuntimeError("device-side data error in the benchmark inputs")
@@ -184,7 +213,7 @@ def gpu_bench(a):
     if use_graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
-            out = D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler)
+            out = D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta)
         torch.cuda.synchronize()
         # replays must reproduce the eager round exactly, replay after replay
         for _ in range(3):
@@ -198,7 +227,7 @@ def gpu_bench(a):
         if use_graph:
             graph.replay()
         else:
-            D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler)
+            D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta)
 
     def timed(fn, n):
         t0 = torch.cuda.Event(enable_timing=True)
@@ -219,7 +248,7 @@ def gpu_bench(a):
 
     # Eager round time (no graph), for reference.
     with torch.cuda.stream(stream):
-        ms_eager = timed(lambda: D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler), a.steps)
+        ms_eager = timed(lambda: D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta), a.steps)
 
     # Dominant-kernel duration: HIP events recorded by the library's launch
     # hook on the kernel's stream, each pair around K1_REPEAT back-to-back
@@ -240,10 +269,25 @@ def gpu_bench(a):
     assert status == 0, f"dspark_profile_arm failed ({status})"
     with torch.cuda.stream(stream):
         for _ in range(n_rounds):
-            D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler)
+            D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta)
     torch.cuda.synchronize()
     used = lib.dspark_profile_disarm()
     k1_ms = sum(s.elapsed_time(e) for s, e in zip(ev_s[:used], ev_e[:used])) / max(used, 1) / K1_REPEAT
+
+    labels = None
+    if a.labels and T > 0:
+        # acceptance-label pass on the reference round's draft outputs
+        lab_out = torch.empty((R, g), dtype=torch.float32, device=dev)
+        with torch.cuda.stream(stream):
+            D.accept_rates(dd["target"], dd["base"], dd["W1"], dd["W2"], dd["anchor"], ref["draft_tokens"],
+                           ref["draft_stats"], T, ws, out=lab_out)
+            lab_ms = timed(lambda: D.accept_rates(dd["target"], dd["base"], dd["W1"], dd["W2"], dd["anchor"],
+                                                  ref["draft_tokens"], ref["draft_stats"], T, ws, out=lab_out),
+                           max(a.steps // 2, 3))
+        wb_ = 2 if d["w_dtype"] == "bf16" else 4
+        lab_bytes = 8 * R * g * V + wb_ * r * V   # target and base rows of every position, W2 once
+        labels = dict(ms=lab_ms, items=R * g, mean_accept_rate=float(lab_out.mean().cpu()),
+                      algorithmic_bytes=lab_bytes, achieved_GBs=lab_bytes / (lab_ms * 1e-3) / 1e9)
 
     if a.copy_calibration_mib > 0:
         # plain copy of a known size: the HBM counters of its kernel calibrate
@@ -268,7 +312,8 @@ def gpu_bench(a):
         ms=ms, tokens=tokens, A=A, L=L, n_admitted=(int(ref["n_admitted"].cpu()[0])
                                                     if ref["n_admitted"] is not None else None),
         b_min=b_min, b_sched=b_sched, k1_ms=k1_ms, k1_bytes=k1_bytes, k1_flops=k1_flops,
-        traffic=traffic, graph=use_graph, cfg=d, ms_eager=ms_eager, n_k1=used * K1_REPEAT)
+        traffic=traffic, graph=use_graph, cfg=d, ms_eager=ms_eager, n_k1=used * K1_REPEAT, theta=theta,
+        labels=labels)
 
 
 def main():
@@ -303,6 +348,7 @@ def main():
                                f"conf {d['conf']}, table {d['table']}",
                    "R": d["R"], "gamma": d["gamma"], "V": d["V"], "r": d["r"],
                    "temperature": a.temperature, "scheduler": a.scheduler,
+                   **({"theta": gb["theta"]} if gb["theta"] is not None else {}),
                    "launch": "hip graph" if gb["graph"] else "eager"},
         "ms_per_step_eager": gb["ms_eager"],
         "rounds_per_s": 1e3 / ms,
@@ -329,6 +375,8 @@ def main():
             "frac": gb["k1_flops"] / (gb["k1_ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         },
     }
+    if gb["labels"] is not None:
+        res["accept_rates"] = gb["labels"]
     if not a.no_cpu_baseline and rank == 0:
         res["cpu_baseline"] = cpu_baseline(a)
     print(json.dumps(res), flush=True)

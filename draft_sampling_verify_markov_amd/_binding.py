@@ -265,18 +265,21 @@ def _side_stream(device):
     return _side_streams[device]
 
 
-def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, scheduler="early"):
+def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, scheduler="early", theta=None):
     """draft -> schedule -> verify on a dict of device tensors.
 
     The scheduler reads only confidences and the cost table, so it runs on a
     side stream concurrently with the draft (forked from and joined back to
     the current stream; capturable into a HIP graph).  It uses its own small
     workspace ``ws_sched`` (allocated here if not given).  ``scheduler`` is
-    "early" (dspark_schedule) or "async" (dspark_schedule_async with the
-    lagged confidences ``conf_lag`` of the input dict).
+    "early" (dspark_schedule), "async" (dspark_schedule_async with the
+    lagged confidences ``conf_lag`` of the input dict) or "threshold"
+    (dspark_schedule_threshold with ``theta``).
     """
-    if scheduler not in ("early", "async"):
-        raise ValueError(f"scheduler must be 'early' or 'async', got {scheduler!r}")
+    if scheduler not in ("early", "async", "threshold"):
+        raise ValueError(f"scheduler must be 'early', 'async' or 'threshold', got {scheduler!r}")
+    if scheduler == "threshold" and theta is None:
+        raise ValueError("scheduler='threshold' needs theta")
     d = dev_inputs
     dev = d["base"].device
     cur = torch.cuda.current_stream(dev)
@@ -290,6 +293,8 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
         with torch.cuda.stream(side):
             if scheduler == "async":
                 L, n, _ = schedule_async(d["conf"], d["conf_lag"], d["sps"], ws_sched, with_cum=False)
+            elif scheduler == "threshold":
+                L, n, _ = schedule_threshold(d["conf"], theta, ws_sched, with_cum=False)
             else:
                 L, n, _ = schedule(d["conf"], d["sps"], ws_sched, with_cum=False)
     tok, prob, stats = draft(d["base"], d["W1"], d["W2"], d["anchor"], d["u_draft"], temperature, ws)

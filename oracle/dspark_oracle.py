@@ -328,11 +328,12 @@ def verify(target, base, W1, W2, w_dtype, anchor, draft_tokens, draft_probs,
 # whole round and boundary flags
 
 
-def run_round(inp, T=1.0, use_scheduler=None, scheduler="early"):
+def run_round(inp, T=1.0, use_scheduler=None, scheduler="early", theta=None):
     """Draft -> schedule -> verify on one input dict from ``gen.make_inputs``.
 
-    scheduler: "early" (the early-stop walk) or "async" (the production
-    variant, with the lagged confidences ``conf_lag``).
+    scheduler: "early" (the early-stop walk), "async" (the production
+    variant, with the lagged confidences ``conf_lag``) or "threshold" (the
+    static baseline with ``theta``).
     """
     sched = None
     if use_scheduler is None:
@@ -342,6 +343,8 @@ def run_round(inp, T=1.0, use_scheduler=None, scheduler="early"):
     if use_scheduler:
         if scheduler == "async":
             sched = schedule_async(inp["conf"], inp["conf_lag"], inp["sps"])
+        elif scheduler == "threshold":
+            sched = schedule_threshold(inp["conf"], theta)
         else:
             sched = schedule(inp["conf"], inp["sps"])
         L = sched["verify_len"][inp["rows"]] if "rows" in inp else sched["verify_len"]

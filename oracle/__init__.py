@@ -19,4 +19,7 @@ from .dspark_oracle import (  # noqa: F401
     verify,
     run_round,
     row_flags,
+    sts_calibrate,
+    ece,
+    sts_fit,
 )

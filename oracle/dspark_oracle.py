@@ -51,7 +51,12 @@ Readings where the pages are silent (each also listed in the design doc):
     takes the cut length K as the first maximiser of Theta over the pool of
     the lagged confidences (same shape as the current ones, supplied by the
     caller) and admits the current pool's first K candidates; a table that
-    ends before B = R gives Theta = 0 everywhere and K = 0.
+    ends before B = R gives Theta = 0 everywhere and K = 0;
+  * sequential temperature scaling divides the head's logit by one
+    temperature per position; ECE uses equal-width bins and the cumulative
+    product of the conditional labels as the target of the cumulative
+    product of calibrated confidences; ties in the grid search go to the
+    first grid entry.
 
 All floating point is float64 on the exact input values (bf16 and fp32
 inputs widen exactly), except the scheduler's fp32 cumulative product.
@@ -393,3 +398,77 @@ def accept_rates(target, base, W1, W2, w_dtype, anchor, draft_tokens, T):
         p, _, _ = draft_distribution(target[:, k, :].astype(np.float64), T)
         out[:, k] = 1.0 - 0.5 * np.abs(q - p).sum(axis=1)
     return out
+
+
+# ---------------------------------------------------------------------------
+# 4. Sequential temperature scaling  ([HADA] Arquitetura, Confidence-Scheduled
+#    Verification, post-hoc calibration; Análise dos experimentos, ECE before
+#    and after calibration)
+
+
+def sts_calibrate(conf, tau):
+    """Temperature-scaled confidences c'_{i,k} = sigmoid(logit(c_{i,k}) / tau_k).
+
+    The confidence head ends in a sigmoid, so dividing its logit
+    log(c) - log(1 - c) by a per-position temperature is the calibration map
+    ([HADA] confidence head: linear projection + sigmoid; STS).  c = 0 and
+    c = 1 are fixed points.  conf [N, gamma] in [0, 1], tau [gamma] > 0.
+    Returns float64 [N, gamma].
+    """
+    c = np.asarray(conf, dtype=np.float64)
+    with np.errstate(divide="ignore"):
+        ell = np.log(c) - np.log1p(-c)
+    x = ell / np.asarray(tau, dtype=np.float64)[None, :]
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-x))
+
+
+def ece(pred, target, bins):
+    """Expected calibration error over `bins` equal-width bins of [0, 1].
+
+    ECE = sum_b |sum_{i in bin b} (pred_i - target_i)| / N, i.e. the bin
+    weight n_b / N times |mean prediction - mean target| in the bin; the bin
+    of p is min(floor(p * bins), bins - 1).  Targets may be soft (in [0, 1]).
+    """
+    p = np.asarray(pred, dtype=np.float64)
+    t = np.asarray(target, dtype=np.float64)
+    b = np.minimum(np.floor(p * bins).astype(np.int64), bins - 1)
+    s = np.bincount(b, weights=p - t, minlength=bins)
+    return float(np.abs(s).sum() / len(p))
+
+
+def sts_fit(conf, labels, grid, bins, follow=None):
+    """Left-to-right 1-D grid search of one temperature per draft position.
+
+    Each c_k is a conditional probability, so the survival estimate of a
+    prefix is the cumulative product of the calibrated c'_j.  For k = 1..gamma
+    in order, with tau_1..tau_{k-1} already fixed, every candidate grid[g] is
+    scored by ECE(prod_{j<=k} c'_j, prod_{j<=k} l_j) on the held-out set and
+    tau_k is the first minimiser ([HADA] STS: held-out grid search left to
+    right minimising ECE, token order preserved).  labels are the conditional
+    per-position targets: acceptance rates c*_k from accept_rates, or 0/1
+    outcomes (1 while the prefix is accepted).
+
+    conf, labels [N, gamma]; grid [G] candidate temperatures; bins >= 1.
+    follow: optional [gamma] grid indices; position k then continues with
+    grid[follow[k]] instead of its own minimiser (scores later positions
+    after a near-tie).
+    Returns dict(tau [gamma], index [gamma], ece [gamma] = score of the index
+    used, table [gamma, G] = every candidate's score).
+    """
+    c = np.asarray(conf, dtype=np.float64)
+    lab = np.asarray(labels, dtype=np.float64)
+    grid = np.asarray(grid, dtype=np.float64)
+    N, g = c.shape
+    A = np.ones(N)
+    Y = np.ones(N)
+    table = np.zeros((g, len(grid)))
+    idx = np.zeros(g, dtype=np.int64)
+    for k in range(g):
+        Y = Y * lab[:, k]
+        ck = c[:, k:k + 1]
+        for j in range(len(grid)):
+            table[k, j] = ece(A * sts_calibrate(ck, grid[j:j + 1])[:, 0], Y, bins)
+        idx[k] = int(np.argmin(table[k])) if follow is None else int(follow[k])
+        A = A * sts_calibrate(ck, grid[idx[k]:idx[k] + 1])[:, 0]
+    return dict(tau=grid[idx], index=idx, ece=table[np.arange(g), idx], table=table)

@@ -711,3 +711,113 @@ def test_threshold_at_the_cut_reproduces_the_prefix_scheduler():
             continue                                  # tie at the cut
         t = O.schedule_threshold(c, a_sorted[n - 1])
         assert t["n_admitted"] == n and (t["verify_len"] == s["verify_len"]).all()
+
+
+# ---------------------------------------------------------------------------
+# sequential temperature scaling (calibration map, ECE, left-to-right search)
+
+
+def _sts_gold():
+    return json.load(open(os.path.join(GOLD, "sts_worked_example.json")))
+
+
+def _frac(s):
+    """'a/b' or 'a/b - d' from the fixture, as a float."""
+    if " - " in s:
+        a, b = s.split(" - ")
+        return abs(float(Fraction(a)) - float(b))
+    return float(Fraction(s))
+
+
+def test_sts_calibration_closed_forms():
+    """c' = 1 / (1 + ((1 - c)/c)^(1/tau)): exact rationals when the odds ratio
+    is a perfect power (worked example fixture)."""
+    g = _sts_gold()
+    for pos, key in ((0, "calibrated_pos1"), (1, "calibrated_pos2")):
+        c = np.array([[g["conf"][0][pos]]])
+        for tau, want in zip(g["grid"], g[key]):
+            got = O.sts_calibrate(c, [tau])[0, 0]
+            assert got == pytest.approx(float(Fraction(want)), rel=1e-14)
+    # temperature 1 is the identity; 0 and 1 are fixed points; the map is
+    # increasing in c for every temperature (token order preserved)
+    rng = np.random.default_rng(3)
+    c = np.sort(rng.uniform(0.001, 0.999, 200))[:, None]
+    assert np.allclose(O.sts_calibrate(c, [1.0]), c, rtol=1e-13, atol=0)
+    for tau in (0.3, 1.0, 2.5):
+        ends = O.sts_calibrate(np.array([[0.0], [1.0]]), [tau])[:, 0]
+        assert ends[0] == 0.0 and ends[1] == 1.0
+        assert (np.diff(O.sts_calibrate(c, [tau])[:, 0]) > 0).all()
+    # tau -> large flattens towards 1/2, tau -> small sharpens towards 0/1
+    assert abs(O.sts_calibrate(np.array([[0.9]]), [1e6])[0, 0] - 0.5) < 1e-6
+    assert O.sts_calibrate(np.array([[0.6]]), [0.01])[0, 0] > 1 - 1e-12
+
+
+def test_ece_hand_example():
+    e = _sts_gold()["ece_example"]
+    assert O.ece(e["pred"], e["target"], 10) == pytest.approx(e["ece_bins10"], abs=1e-15)
+    assert O.ece(e["pred"], e["target"], 2) == pytest.approx(e["ece_bins2"], abs=1e-15)
+    # bin edges: p = k/bins opens bin k, p = 1 falls in the last bin
+    assert O.ece([0.5, 1.0], [0.0, 0.0], 2) == pytest.approx(0.75)          # bins {0.5,1.0} -> |1.5|/2
+    assert O.ece([0.5, 0.4999], [1.0, 0.0], 2) == pytest.approx((0.5 + 0.4999) / 2)
+    # one bin: |mean prediction - mean target|; perfect predictions score 0
+    rng = np.random.default_rng(4)
+    p, t = rng.uniform(size=500), rng.uniform(size=500)
+    assert O.ece(p, t, 1) == pytest.approx(abs(p.mean() - t.mean()), rel=1e-12)
+    assert O.ece(p, p, 15) == 0.0
+
+
+def test_sts_worked_example_is_cumulative():
+    g = _sts_gold()
+    r = O.sts_fit(np.array(g["conf"]), np.array(g["labels"]), g["grid"], g["bins"])
+    want = np.array([[_frac(s) for s in row] for row in g["table"]])
+    assert np.allclose(r["table"], want, rtol=1e-12, atol=1e-15)
+    assert list(r["index"]) == g["index"] and list(r["tau"]) == g["tau"]
+    assert list(r["index"]) != g["index_if_not_cumulative"]
+
+
+def _planted_sts(seed, N, gamma, grid):
+    """Labels l_k = sigmoid(t_k), confidences c_k = sigmoid(s_k t_k) with s_k a
+    grid entry: temperature s_k undoes the distortion exactly."""
+    rng = np.random.default_rng(seed)
+    s = rng.choice(grid, size=gamma)
+    t = rng.normal(1.0, 1.5, (N, gamma))
+    lab = special.expit(t)
+    conf = special.expit(s[None, :] * t)
+    return conf, lab, s
+
+
+def test_sts_recovers_planted_temperatures():
+    grid = np.array([0.5, 0.75, 1.0, 1.5, 2.0, 3.0])
+    for seed in range(3):
+        conf, lab, s = _planted_sts(seed, 2000, 5, grid)
+        r = O.sts_fit(conf, lab, grid, 15)
+        assert np.array_equal(r["tau"], s)
+        assert (r["ece"] < 1e-12).all()
+        # every other candidate scores strictly worse
+        for k in range(5):
+            others = np.delete(r["table"][k], r["index"][k])
+            assert (others > 1e-6).all()
+
+
+def test_sts_left_to_right():
+    """tau_k depends on positions 1..k only; follow= replays given choices."""
+    grid = np.geomspace(0.25, 4.0, 17)
+    rng = np.random.default_rng(9)
+    conf = rng.uniform(0.05, 0.995, (800, 4))
+    lab = np.clip(conf ** 1.7 + rng.normal(0, 0.05, conf.shape), 0, 1)
+    r = O.sts_fit(conf, lab, grid, 10)
+    conf2, lab2 = conf.copy(), lab.copy()
+    conf2[:, 2:] = rng.uniform(0.05, 0.995, (800, 2))
+    lab2[:, 2:] = rng.uniform(0, 1, (800, 2))
+    r2 = O.sts_fit(conf2, lab2, grid, 10)
+    assert np.array_equal(r["index"][:2], r2["index"][:2])
+    assert np.array_equal(r["table"][:2], r2["table"][:2])
+    # following a different choice at position 1 changes later tables only
+    f = r["index"].copy()
+    f[0] = (f[0] + 3) % len(grid)
+    r3 = O.sts_fit(conf, lab, grid, 10, follow=f)
+    assert np.array_equal(r3["table"][0], r["table"][0])
+    assert not np.array_equal(r3["table"][1], r["table"][1])
+    # a labels-all-one block with c = 1 everywhere scores 0 for every tau
+    r4 = O.sts_fit(np.ones((10, 3)), np.ones((10, 3)), grid, 10)
+    assert (r4["table"] == 0).all() and (r4["index"] == 0).all()

@@ -25,10 +25,14 @@ from ._binding import (  # noqa: F401
     accept_rates,
     verify,
     run_round,
+    sts_workspace_size,
+    new_sts_workspace,
+    sts_fit,
+    sts_apply,
 )
 
 __all__ = [
     "DSPARK_W_BF16", "DSPARK_W_F32", "DERR_BITS", "DSparkError", "lib_path", "load_library",
     "workspace_size", "new_workspace", "workspace_init", "device_error", "draft", "schedule", "schedule_async", "schedule_threshold", "accept_rates",
-    "verify", "run_round",
+    "verify", "run_round", "sts_workspace_size", "new_sts_workspace", "sts_fit", "sts_apply",
 ]

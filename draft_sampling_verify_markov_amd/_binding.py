@@ -8,7 +8,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 DSPARK_W_BF16, DSPARK_W_F32 = 0, 1
 STATUS = {0: "DSPARK_OK", -1: "DSPARK_EINVAL", -2: "DSPARK_ENOSPC", -3: "DSPARK_EHIP"}
-DERR_BITS = {1: "NONFINITE", 2: "UNIFORM", 4: "CONF", 8: "TOKEN", 16: "PROB", 32: "LENGTH"}
+DERR_BITS = {1: "NONFINITE", 2: "UNIFORM", 4: "CONF", 8: "TOKEN", 16: "PROB", 32: "LENGTH", 64: "CALIB"}
 
 _lib = None
 
@@ -54,6 +54,12 @@ def load_library():
     lib.dspark_accept_rates.restype = I
     lib.dspark_verify.argtypes = [P, P, P, P, I, P, P, P, P, P, P, P, I, I, I, I, F, P, P, P, P, Z, P]
     lib.dspark_verify.restype = I
+    lib.dspark_sts_workspace_size.argtypes = [I, I, I, I]
+    lib.dspark_sts_workspace_size.restype = Z
+    lib.dspark_sts_fit.argtypes = [P, P, P, I, I, I, I, P, P, P, P, P, Z, P]
+    lib.dspark_sts_fit.restype = I
+    lib.dspark_sts_apply.argtypes = [P, P, I, I, P, P, Z, P]
+    lib.dspark_sts_apply.restype = I
     lib.dspark_profile_arm.argtypes = [I, P, P, I, I]
     lib.dspark_profile_arm.restype = I
     lib.dspark_profile_disarm.argtypes = []
@@ -254,6 +260,52 @@ def verify(target, base, W1, W2, anchor, draft_tokens, draft_probs, draft_stats,
             ws.data_ptr(), ws.numel(), _stream(dev))
     _check("dspark_verify", load_library().dspark_verify(*args))
     return ot, al, tp
+
+
+def sts_workspace_size(N, gamma, G, bins):
+    n = load_library().dspark_sts_workspace_size(N, gamma, G, bins)
+    if n == 0:
+        raise ValueError(f"sizes outside the calibration limits: N={N} gamma={gamma} G={G} bins={bins}")
+    return n
+
+
+def new_sts_workspace(N, gamma, G, bins, device):
+    """Allocate (torch) and clear a calibration workspace for these sizes."""
+    ws = torch.empty(sts_workspace_size(N, gamma, G, bins), dtype=torch.uint8, device=device)
+    workspace_init(ws)
+    return ws
+
+
+def sts_fit(conf, labels, grid, bins, ws, out=None, with_table=False):
+    """dspark_sts_fit.  Returns (tau [gamma] fp32, tau_index [gamma] int32,
+    ece [gamma] fp64, ece_table [gamma, G] fp64 or None)."""
+    N, g = conf.shape
+    G = grid.shape[0]
+    dev = conf.device
+    if out is None:
+        out = (torch.empty(g, dtype=torch.float32, device=dev), torch.empty(g, dtype=torch.int32, device=dev),
+               torch.empty(g, dtype=torch.float64, device=dev),
+               torch.empty((g, G), dtype=torch.float64, device=dev) if with_table else None)
+    tau, idx, ece, table = out
+    args = (_ptr(conf, torch.float32, (N, g), "conf", dev), _ptr(labels, torch.float32, (N, g), "labels", dev),
+            _ptr(grid, torch.float32, (G,), "grid", dev), N, g, G, int(bins),
+            _ptr(tau, torch.float32, (g,), "tau", dev), _ptr(idx, torch.int32, (g,), "tau_index", dev),
+            _ptr(ece, torch.float64, (g,), "ece", dev), _ptr(table, torch.float64, (g, G), "ece_table", dev),
+            ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("dspark_sts_fit", load_library().dspark_sts_fit(*args))
+    return tau, idx, ece, table
+
+
+def sts_apply(conf, tau, ws, out=None):
+    """dspark_sts_apply.  Returns the calibrated confidences [R, gamma] fp32."""
+    R, g = conf.shape
+    dev = conf.device
+    if out is None:
+        out = torch.empty((R, g), dtype=torch.float32, device=dev)
+    args = (_ptr(conf, torch.float32, (R, g), "conf", dev), _ptr(tau, torch.float32, (g,), "tau", dev), R, g,
+            _ptr(out, torch.float32, (R, g), "conf_out", dev), ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("dspark_sts_apply", load_library().dspark_sts_apply(*args))
+    return out
 
 
 _side_streams = {}

@@ -23,6 +23,12 @@ int verify_impl(const float* target, const float* base, const void* W1, const vo
                 int R, int gamma, int V, int r, float T, int32_t* out_tokens, int32_t* accept_len,
                 float* target_probs, void* ws, hipStream_t stream);
 
+size_t sts_workspace_size_impl(int N, int gamma, int G, int bins);
+int sts_fit_impl(const float* conf, const float* labels, const float* grid, int N, int gamma, int G, int bins,
+                 float* tau, int32_t* tau_index, double* ece, double* ece_table, void* ws, hipStream_t stream);
+int sts_apply_impl(const float* conf, const float* tau, int R, int gamma, float* out, void* ws,
+                   hipStream_t stream);
+
 __global__ void k_fill_i32(int32_t* p, int n, int32_t v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -220,6 +226,36 @@ int dspark_verify(const float* target, const float* base, const void* W1, const 
   return verify_impl(target, base, W1, W2, w_type, anchor, draft_tokens, draft_probs, draft_stats,
                      verify_len, u_accept, u_final, R, gamma, V, r, temperature, out_tokens,
                      accept_len, target_probs, workspace, stream);
+}
+
+static bool sts_sizes_ok(int N, int gamma, int G, int bins) {
+  return N >= 1 && N <= DSPARK_STS_MAX_N && gamma >= 1 && gamma <= DSPARK_MAX_GAMMA && G >= 1 &&
+         G <= DSPARK_STS_MAX_GRID && bins >= 1 && bins <= DSPARK_STS_MAX_BINS;
+}
+
+size_t dspark_sts_workspace_size(int N, int gamma, int G, int bins) {
+  if (!sts_sizes_ok(N, gamma, G, bins)) return 0;
+  return sts_workspace_size_impl(N, gamma, G, bins);
+}
+
+int dspark_sts_fit(const float* conf, const float* labels, const float* grid, int N, int gamma, int G,
+                   int bins, float* tau, int32_t* tau_index, double* ece, double* ece_table,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!sts_sizes_ok(N, gamma, G, bins)) return DSPARK_EINVAL;
+  if (!conf || !labels || !grid || !tau || !ece) return DSPARK_EINVAL;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DSPARK_EINVAL;
+  if (workspace_bytes < sts_workspace_size_impl(N, gamma, G, bins)) return DSPARK_ENOSPC;
+  return sts_fit_impl(conf, labels, grid, N, gamma, G, bins, tau, tau_index, ece, ece_table, workspace,
+                      stream);
+}
+
+int dspark_sts_apply(const float* conf, const float* tau, int R, int gamma, float* conf_out,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (R < 1 || gamma < 1 || gamma > DSPARK_MAX_GAMMA || (long long)R * gamma > MAX_ELEMS) return DSPARK_EINVAL;
+  if (!conf || !tau || !conf_out) return DSPARK_EINVAL;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DSPARK_EINVAL;
+  if (workspace_bytes < 256) return DSPARK_ENOSPC;
+  return sts_apply_impl(conf, tau, R, gamma, conf_out, workspace, stream);
 }
 
 }  // extern "C"

@@ -82,10 +82,17 @@ typedef enum {
 #define DSPARK_DERR_TOKEN 8     /* a token id outside [0, V); 0 was used instead   */
 #define DSPARK_DERR_PROB 16     /* a draft probability <= 0 or NaN; rejected       */
 #define DSPARK_DERR_LENGTH 32   /* a verify length outside [0, gamma]; clamped     */
+#define DSPARK_DERR_CALIB 64    /* calibration input out of range: a confidence or
+                                   label outside [0, 1] (clamped, NaN -> 0) or a
+                                   temperature that is not finite and > 0 (never
+                                   chosen; dspark_sts_apply leaves c unchanged)  */
 
 #define DSPARK_MAX_GAMMA 16
 #define DSPARK_MAX_RANK 256
 #define DSPARK_MAX_POOL 8192
+#define DSPARK_STS_MAX_N (1 << 21)   /* held-out blocks per calibration fit */
+#define DSPARK_STS_MAX_GRID 1024     /* candidate temperatures               */
+#define DSPARK_STS_MAX_BINS 64       /* ECE bins                             */
 
 /* Bytes of workspace the three calls need for these sizes (host-only query).
  * Returns 0 for sizes outside the limits above. */
@@ -280,6 +287,55 @@ typedef enum {
 
 int dspark_profile_arm(int kid, hipEvent_t* starts, hipEvent_t* stops, int n, int repeat);
 int dspark_profile_disarm(void);
+
+/*
+ * dspark_sts_fit - sequential temperature scaling of the confidence head
+ * ("DSpark: Aceleração da inferência de LLM com speculative decoding",
+ * pt.news.hada.io, section "Arquitetura", Confidence-Scheduled Verification,
+ * post-hoc calibration: each c_k is a conditional probability, the survival
+ * estimate is the cumulative product over the prefix, and a 1-D grid search
+ * runs left to right over the positions on a held-out set minimising ECE;
+ * section "Análise dos experimentos": an over-confident head, ECE down to
+ * about 1 % after calibration).
+ *
+ * Calibration map c' = sigmoid(logit(c) / tau_k), logit(c) = log(c / (1 - c)).
+ * For k = 1..gamma in order, with tau_1..tau_{k-1} fixed, each candidate
+ * grid[g] is scored by
+ *   ECE = sum_b | sum_{i in bin b} (prod_{j<=k} c'_{i,j} - prod_{j<=k} labels[i,j]) | / N
+ * with bins equal-width bins of [0, 1] (a prediction p falls in bin
+ * min(floor(p * bins), bins - 1)); tau_k is the FIRST grid entry with the
+ * smallest score.  Bin sums are exact 2^-40 fixed-point sums, so results are
+ * bit-reproducible.
+ *
+ *   conf        [N, gamma] fp32  raw head outputs in [0, 1] (held-out blocks)
+ *   labels      [N, gamma] fp32  conditional targets in [0, 1]: acceptance
+ *                                rates from dspark_accept_rates, or 0/1 outcomes
+ *   grid        [G] fp32         candidate temperatures (finite, > 0)
+ *   bins        1..DSPARK_STS_MAX_BINS
+ *   tau         out [gamma] fp32 chosen temperatures (copies of grid entries)
+ *   tau_index   out [gamma] int32 chosen grid indices, or NULL
+ *   ece         out [gamma] fp64 score of the chosen entry
+ *   ece_table   out [gamma, G] fp64 every candidate's score, or NULL
+ *   workspace   >= dspark_sts_workspace_size(N, gamma, G, bins) bytes,
+ *               256-byte aligned; its first word is the device error word
+ *               (read it with dspark_device_error)
+ * Limits: 1 <= N <= DSPARK_STS_MAX_N, 1 <= gamma <= DSPARK_MAX_GAMMA,
+ * 1 <= G <= DSPARK_STS_MAX_GRID.  Returns DSPARK_EINVAL / DSPARK_ENOSPC before
+ * any launch on bad sizes, NULL required pointers or a short workspace.
+ */
+size_t dspark_sts_workspace_size(int N, int gamma, int G, int bins);
+int dspark_sts_fit(const float* conf, const float* labels, const float* grid, int N, int gamma, int G,
+                   int bins, float* tau, int32_t* tau_index, double* ece, double* ece_table,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dspark_sts_apply - calibrated confidences for the scheduler (same source):
+ *   conf_out[r, k] = fp32( sigmoid(logit(conf[r, k]) / tau[k]) )
+ * evaluated in fp64 with the same expression as dspark_sts_fit.  conf_out may
+ * alias conf.  workspace: any workspace of >= 256 bytes (error word only).
+ */
+int dspark_sts_apply(const float* conf, const float* tau, int R, int gamma, float* conf_out,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -120,6 +120,33 @@ def test_accept_rates_rejects_bad_arguments(lib):
     assert lib.dspark_accept_rates(*bad) == ENOSPC
 
 
+def test_sts_workspace_and_argument_checks(lib):
+    sz = lib.dspark_sts_workspace_size
+    assert sz(65536, 7, 256, 15) >= 256 + 2 * 8 * 65536 + 7 * 256 * 8 + 32 * 256 * 15 * 8
+    assert sz(1, 1, 1, 1) > 0 and sz(1 << 21, 16, 1024, 64) > 0
+    for bad in ((0, 7, 8, 15), ((1 << 21) + 1, 7, 8, 15), (10, 0, 8, 15), (10, 17, 8, 15), (10, 7, 0, 15),
+                (10, 7, 1025, 15), (10, 7, 8, 0), (10, 7, 8, 65)):
+        assert sz(*bad) == 0, bad
+    f = lib.dspark_sts_fit
+    need = sz(100, 4, 8, 10)
+    good = [16, 16, 16, 100, 4, 8, 10, 16, None, 16, None, 256, need, None]
+    for i in (0, 1, 2, 7, 9):                                           # required pointers
+        bad = list(good); bad[i] = None
+        assert f(*bad) == EINVAL, i
+    for i, v in ((3, 0), (4, 17), (5, 0), (6, 65)):
+        bad = list(good); bad[i] = v
+        assert f(*bad) == EINVAL, i
+    bad = list(good); bad[11] = 128                                     # unaligned workspace
+    assert f(*bad) == EINVAL
+    bad = list(good); bad[12] = need - 1
+    assert f(*bad) == ENOSPC
+    a = lib.dspark_sts_apply
+    assert a(None, 16, 4, 4, 16, 256, 256, None) == EINVAL
+    assert a(16, 16, 4, 0, 16, 256, 256, None) == EINVAL
+    assert a(16, 16, 4, 4, None, 256, 256, None) == EINVAL
+    assert a(16, 16, 4, 4, 16, 256, 255, None) == ENOSPC
+
+
 def test_verify_rejects_bad_arguments(lib):
     base = [16, 16, 16, 16, 0, 16, 16, 16, 16, None, 16, 16, 4, 4, 512, 16, 1.0, 16, 16, None, 256,
             1 << 20, None]

@@ -51,6 +51,9 @@ def parse():
                          "probability at the early-stop scheduler's cut (equal verify bytes)")
     ap.add_argument("--labels", action="store_true",
                     help="also time the acceptance-label pass (dspark_accept_rates) on the workload")
+    ap.add_argument("--sts", action="store_true",
+                    help="also time the calibration fit (dspark_sts_fit) on a synthetic held-out set of "
+                         "65536 blocks, 256 candidate temperatures, 15 ECE bins")
     ap.add_argument("--eager", action="store_true", help="launch kernels eagerly instead of a graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -102,8 +105,18 @@ def stored_traffic(kernel, workload):
 
 def cpu_worker(a):
     from threadpoolctl import threadpool_info
-    from gen import make_inputs
+    from gen import make_inputs, config
     import oracle as O
+    if a.sts:
+        # the calibration fit of the same held-out set, once
+        from gen.sts import make_sts_inputs
+        sd = make_sts_inputs(65536, config(cfg_key(a.config))["gamma"], 256, 15, seed=0)
+        t0 = time.perf_counter()
+        O.sts_fit(sd["conf"], sd["labels"], sd["grid"], 15)
+        dt = time.perf_counter() - t0
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        print(json.dumps(dict(seconds=dt, threads=threads)))
+        return
     inp = make_inputs(cfg_key(a.config))
     theta = None
     if a.scheduler == "threshold":
@@ -128,6 +141,17 @@ def oracle_theta(O, inp, theta_arg):
     s = O.schedule(inp["conf"], inp["sps"])
     a, L = s["cum_conf"], s["verify_len"]
     return float(min(a[r, L[r] - 1] for r in range(len(L)) if L[r] > 0))
+
+
+def cpu_sts_baseline(a):
+    """The oracle's calibration fit of the bench's held-out set, timed once."""
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-worker", "--sts", "--config", a.config]
+    out = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    if out.returncode != 0:
+        return dict(error=out.stderr[-400:])
+    r = json.loads(out.stdout.strip().splitlines()[-1])
+    return dict(ms=r["seconds"] * 1e3, cores=r["threads"], kind="oracle",
+                sample="one whole fit of the same held-out set (65536 blocks, 256 candidates, 15 bins)")
 
 
 def cpu_baseline(a):
@@ -289,6 +313,10 @@ def gpu_bench(a):
         labels = dict(ms=lab_ms, items=R * g, mean_accept_rate=float(lab_out.mean().cpu()),
                       algorithmic_bytes=lab_bytes, achieved_GBs=lab_bytes / (lab_ms * 1e-3) / 1e9)
 
+    sts = None
+    if a.sts:
+        sts = sts_bench(D, torch, dev, stream, timed, g, max(a.steps // 4, 3))
+
     if a.copy_calibration_mib > 0:
         # plain copy of a known size: the HBM counters of its kernel calibrate
         # FETCH_SIZE / WRITE_SIZE readings of the round's kernels
@@ -313,7 +341,44 @@ def gpu_bench(a):
                                                     if ref["n_admitted"] is not None else None),
         b_min=b_min, b_sched=b_sched, k1_ms=k1_ms, k1_bytes=k1_bytes, k1_flops=k1_flops,
         traffic=traffic, graph=use_graph, cfg=d, ms_eager=ms_eager, n_k1=used * K1_REPEAT, theta=theta,
-        labels=labels)
+        labels=labels, sts=sts)
+
+
+# VALU instructions per (sample, candidate) evaluation in the inner loop of
+# k_sts_bins (fp64 exp and divide, binning, fixed-point conversion), counted in
+# the gfx950 assembly of this build.  With 256 CUs x 4 SIMDs x 16 lanes at
+# 2.4 GHz (39.3e12 fp64 lane operations/s, the chip's 78.6 TFLOP/s of fp64 FMA)
+# that bounds the fit at 39.3e12 / 55 evaluations per second.
+STS_VALU_PER_EVAL = 55
+STS_PEAK_EVALS = 256 * 4 * 16 * 2.4e9 / STS_VALU_PER_EVAL
+
+
+def sts_bench(D, torch, dev, stream, timed, gamma, reps):
+    import numpy as np
+    from gen.sts import make_sts_inputs
+    N, G, bins = 65536, 256, 15
+    sd = make_sts_inputs(N, gamma, G, bins, seed=0)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+    c_t, l_t, g_t = t(sd["conf"]), t(sd["labels"]), t(sd["grid"])
+    ws = D.new_sts_workspace(N, gamma, G, bins, dev)
+    with torch.cuda.stream(stream):
+        out = D.sts_fit(c_t, l_t, g_t, bins, ws)
+        ms = timed(lambda: D.sts_fit(c_t, l_t, g_t, bins, ws, out=out), reps)
+    torch.cuda.synchronize()
+    if D.device_error(ws) != 0:
+        raise RuntimeError("device-side data error in the calibration inputs")
+    tau, _, ece, _ = out
+    # ECE of the uncalibrated product: the same fit with the single candidate
+    # tau = 1 (the identity map)
+    ws1 = D.new_sts_workspace(N, gamma, 1, bins, dev)
+    _, _, ece1, _ = D.sts_fit(c_t, l_t, t(np.ones(1)), bins, ws1)
+    before = [float(x) for x in ece1.cpu()]
+    evals = N * G * gamma
+    rate = evals / (ms * 1e-3)
+    return dict(ms=ms, held_out_blocks=N, gamma=gamma, grid=G, bins=bins, evaluations=evals,
+                tau=[float(x) for x in tau.cpu()], ece_before=before, ece_after=[float(x) for x in ece.cpu()],
+                roofline=dict(bound="alu", achieved=rate, peak=STS_PEAK_EVALS, unit="evaluations/s",
+                              frac=rate / STS_PEAK_EVALS))
 
 
 def main():
@@ -375,10 +440,14 @@ def main():
             "frac": gb["k1_flops"] / (gb["k1_ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         },
     }
+    if gb["sts"] is not None:
+        res["sts_fit"] = gb["sts"]
     if gb["labels"] is not None:
         res["accept_rates"] = gb["labels"]
     if not a.no_cpu_baseline and rank == 0:
         res["cpu_baseline"] = cpu_baseline(a)
+        if gb["sts"] is not None:
+            res["sts_fit"]["cpu_oracle"] = cpu_sts_baseline(a)
     print(json.dumps(res), flush=True)
     return 0
 

@@ -19,10 +19,10 @@
 // tau_k = grid[first minimiser], then A and Y advance by position k.
 //
 // Per position three launches:
-//   k_sts_bins     grid (N / 2048, G / 16), 256 threads: thread (g, lane) owns
+//   k_sts_bins     grid (N / 1024, G / 16), 256 threads: thread (g, lane) owns
 //                  one grid value and one sample lane; samples are staged 256 at
 //                  a time in LDS (logit, A, y as fp64) and every thread folds
-//                  16 of them into its own LDS bin column with ds_add_u64 of a
+//                  16 of them (four at a time) into its own LDS bin column with ds_add_u64 of a
 //                  2^-40 fixed-point difference (exact, order-independent
 //                  sums, so the score and the arg-min are deterministic);
 //                  per-(chunk, g, bin) sums go to the workspace.
@@ -35,10 +35,11 @@
 
 namespace dspark {
 
-constexpr int STS_CHUNK = 2048;  // samples per workgroup of k_sts_bins
+constexpr int STS_CHUNK = 1024;  // samples per workgroup of k_sts_bins
 constexpr int STS_GPW = 16;      // grid values per workgroup
 constexpr int STS_SUB = 256;     // samples staged in LDS at a time
 constexpr int STS_LANES = 256 / STS_GPW;
+constexpr int STS_ILP = 4;       // samples per thread per step of k_sts_bins
 
 struct StsLayout {
   size_t err, A, Y, table, part, total;
@@ -123,12 +124,25 @@ __global__ __launch_bounds__(256) void k_sts_bins(StsArgs P, int k) {
     }
     __syncthreads();
     if (gok) {
-      for (int j = lane; j < n; j += STS_LANES) {
-        const double ah = s_a[j] * calibrated(s_l[j], inv);
-        int b = (int)(ah * fb);
-        b = min(max(b, 0), nb - 1);
-        const long long q = (long long)rint((ah - s_y[j]) * 0x1p40);
-        atomicAdd(&s_bins[b * 256 + t], (unsigned long long)q);
+      // four independent samples per step (j0 + 16u): four exp/divide chains
+      // in flight per thread; past the sub-chunk's end a slot recomputes the
+      // last sample and adds nothing
+      for (int j0 = lane; j0 < n; j0 += STS_ILP * STS_LANES) {
+        double ah[STS_ILP], ys[STS_ILP];
+#pragma unroll
+        for (int u = 0; u < STS_ILP; u++) {
+          const int j = min(j0 + u * STS_LANES, n - 1);
+          ah[u] = s_a[j] * calibrated(s_l[j], inv);
+          ys[u] = s_y[j];
+        }
+#pragma unroll
+        for (int u = 0; u < STS_ILP; u++) {
+          int b = (int)(ah[u] * fb);
+          b = min(max(b, 0), nb - 1);
+          const long long q = (long long)rint((ah[u] - ys[u]) * 0x1p40);
+          // branch-free: a slot past the end adds 0
+          atomicAdd(&s_bins[b * 256 + t], (unsigned long long)(j0 + u * STS_LANES < n ? q : 0ll));
+        }
       }
     }
   }
@@ -151,8 +165,18 @@ __device__ __forceinline__ unsigned long long shfl_xor_u64s(unsigned long long v
 __global__ __launch_bounds__(64) void k_sts_score(StsArgs P, int k) {
   const int g = blockIdx.x, lane = threadIdx.x;
   long long s = 0;
-  if (lane < P.bins)
-    for (int c = 0; c < P.nchunk; c++) s += P.part[((size_t)c * P.G + g) * P.bins + lane];
+  if (lane < P.bins) {
+    // eight independent partial sums keep eight loads in flight
+    long long p[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    const long long* src = P.part + (size_t)g * P.bins + lane;
+    const size_t stride = (size_t)P.G * P.bins;
+    int c = 0;
+    for (; c + 8 <= P.nchunk; c += 8)
+#pragma unroll
+      for (int u = 0; u < 8; u++) p[u] += src[(size_t)(c + u) * stride];
+    for (; c < P.nchunk; c++) p[0] += src[(size_t)c * stride];
+    s = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+  }
   unsigned long long a = (unsigned long long)(s < 0 ? -s : s);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) a += shfl_xor_u64s(a, m);

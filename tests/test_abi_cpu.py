@@ -122,7 +122,7 @@ def test_accept_rates_rejects_bad_arguments(lib):
 
 def test_sts_workspace_and_argument_checks(lib):
     sz = lib.dspark_sts_workspace_size
-    assert sz(65536, 7, 256, 15) >= 256 + 2 * 8 * 65536 + 7 * 256 * 8 + 32 * 256 * 15 * 8
+    assert sz(65536, 7, 256, 15) >= 256 + 2 * 8 * 65536 + 7 * 256 * 8 + 64 * 256 * 15 * 8
     assert sz(1, 1, 1, 1) > 0 and sz(1 << 21, 16, 1024, 64) > 0
     for bad in ((0, 7, 8, 15), ((1 << 21) + 1, 7, 8, 15), (10, 0, 8, 15), (10, 17, 8, 15), (10, 7, 0, 15),
                 (10, 7, 1025, 15), (10, 7, 8, 0), (10, 7, 8, 65)):

@@ -67,14 +67,21 @@ def cfg_key(s):
     return int(s) if s.isdigit() else s
 
 
+# Sources the draft partials kernel is compiled from (its translation unit and
+# the headers it includes).
+DRAFT_KERNEL_SOURCES = ("draft_sampling_verify_markov_amd/csrc/draft.hip",
+                        "draft_sampling_verify_markov_amd/csrc/common.h",
+                        "draft_sampling_verify_markov_amd/csrc/select.h",
+                        "include/dspark.h")
+
+
 def source_digest():
-    """sha256 of the HIP sources: ties stored counter readings to this build."""
+    """sha256 of the draft kernel's sources: ties stored counter readings to
+    the kernel they were taken on."""
     h = hashlib.sha256()
-    d = os.path.join(ROOT, "draft_sampling_verify_markov_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".h")):
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in DRAFT_KERNEL_SOURCES:
+        h.update(f.encode())
+        h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()[:16]
 
 

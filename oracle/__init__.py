@@ -22,4 +22,7 @@ from .dspark_oracle import (  # noqa: F401
     sts_calibrate,
     ece,
     sts_fit,
+    to_storage,
+    rnn_state_update,
+    draft_rnn,
 )

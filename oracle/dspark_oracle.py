@@ -141,15 +141,21 @@ def draft(base, W1, W2, w_dtype, anchor, u_draft, T):
     For T = 0 (greedy) probs are 1, stats are (max z, 1) and margin is the
     top-1 minus top-2 logit gap.
     """
-    R, g, V = base.shape
     W1_64, W2_64 = widen_weights(W1, w_dtype), widen_weights(W2, w_dtype)
+    return _draft_loop(base, u_draft, T, anchor, lambda k, prev: markov_bias(W1_64, W2_64, prev))
+
+
+def _draft_loop(base, u_draft, T, anchor, bias_of):
+    """Left-to-right drafting: at step k the logits are base row k plus
+    bias_of(k, previous tokens), and x_k is drawn from their softmax."""
+    R, g, V = base.shape
     tokens = np.zeros((R, g), dtype=np.int32)
     probs = np.zeros((R, g))
     stats = np.zeros((R, g, 2))
     margin = np.zeros((R, g))
     prev = np.asarray(anchor, dtype=np.int64)
     for k in range(g):
-        z = base[:, k, :].astype(np.float64) + markov_bias(W1_64, W2_64, prev)
+        z = base[:, k, :].astype(np.float64) + bias_of(k, prev)
         if T == 0:
             idx, top1, gap = _greedy(z)
             tokens[:, k] = idx
@@ -264,7 +270,7 @@ def schedule_threshold(conf, theta):
 
 
 def verify(target, base, W1, W2, w_dtype, anchor, draft_tokens, draft_probs,
-           verify_len, u_accept, u_final, T):
+           verify_len, u_accept, u_final, T, states=None):
     """Rejection-sampling verification of the drafted blocks.
 
     target [R, gamma+1, V]: row k-1 scores draft position k, row L_r scores the
@@ -274,11 +280,15 @@ def verify(target, base, W1, W2, w_dtype, anchor, draft_tokens, draft_probs,
     target_probs [R, gamma] (p_k(x_k) for every evaluated position, -1 for the
     rest), accept_margin [R, gamma] (inf where not evaluated), final_margin [R],
     residual_mass [R] (NaN for bonus rows)).
+    states: the RNN head's per-position rows [R, gamma, r] (see draft_rnn);
+    when given, the draft row at the rejection is base + states[k*] @ W2 and
+    W1 / anchor are not used.
     """
     R, g1, V = target.shape
     g = g1 - 1
     L = np.full(R, g, dtype=np.int64) if verify_len is None else np.asarray(verify_len, np.int64)
-    W1_64, W2_64 = widen_weights(W1, w_dtype), widen_weights(W2, w_dtype)
+    W2_64 = widen_weights(W2, w_dtype)
+    W1_64 = None if states is not None else widen_weights(W1, w_dtype)
     x = np.asarray(draft_tokens, dtype=np.int64)
     q = np.asarray(draft_probs, dtype=np.float64)
     out = np.full((R, g + 1), -1, dtype=np.int32)
@@ -316,8 +326,12 @@ def verify(target, base, W1, W2, w_dtype, anchor, draft_tokens, draft_probs,
             p, _, _ = draft_distribution(row, T)
             w = p
             if kstar is not None:
-                prev = anchor[i] if kstar == 1 else x[i, kstar - 2]
-                z = base[i, kstar - 1].astype(np.float64) + markov_bias(W1_64, W2_64, [prev])[0]
+                if states is not None:
+                    bias = np.asarray(states[i, kstar - 1], dtype=np.float64) @ W2_64
+                else:
+                    prev = anchor[i] if kstar == 1 else x[i, kstar - 2]
+                    bias = markov_bias(W1_64, W2_64, [prev])[0]
+                z = base[i, kstar - 1].astype(np.float64) + bias
                 pi, _, _ = draft_distribution(z, T)
                 d = np.maximum(0.0, p - pi)
                 res_mass[i] = d.sum()
@@ -472,3 +486,76 @@ def sts_fit(conf, labels, grid, bins, follow=None):
         idx[k] = int(np.argmin(table[k])) if follow is None else int(follow[k])
         A = A * sts_calibrate(ck, grid[idx[k]:idx[k] + 1])[:, 0]
     return dict(tau=grid[idx], index=idx, ece=table[np.arange(g), idx], table=table)
+
+
+# ---------------------------------------------------------------------------
+# 5. RNN head  ([HADA] Arquitetura, Semi-Autoregressive Generation, RNN head;
+#    Experimentos, proposal length: small extra gain at long blocks)
+
+
+def to_storage(x, w_dtype):
+    """Round float64 values to fp32 (nearest, ties to even) and, for bf16
+    weights, on to bf16 (nearest, ties to even); returned as float64."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    if w_dtype != "bf16":
+        return f.astype(np.float64)
+    u = np.ascontiguousarray(f).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def rnn_state_update(e, s, Wx_64, Ws_64, b_64, w_dtype):
+    """One gated update of the recurrent state (GRU form, Cho et al. 2014):
+
+      u = sigmoid(e Wx[0] + s Ws[0] + b[0])        update gate
+      g = sigmoid(e Wx[1] + s Ws[1] + b[1])        reset gate
+      h = tanh(e Wx[2] + (g * s) Ws[2] + b[2])     candidate
+      s' = storage((1 - u) * s + u * h)
+
+    e [R, r] the previous token's input row, s [R, r] the state; the new state
+    is carried in the weights' storage type.  The pages describe the head as a
+    recurrent state over the whole in-block prefix with a gated update and give
+    no equations; this is the plainest gated recurrence.
+    """
+    u = _sigmoid(e @ Wx_64[0] + s @ Ws_64[0] + b_64[0])
+    g = _sigmoid(e @ Wx_64[1] + s @ Ws_64[1] + b_64[1])
+    h = np.tanh(e @ Wx_64[2] + (g * s) @ Ws_64[2] + b_64[2])
+    return to_storage((1.0 - u) * s + u * h, w_dtype)
+
+
+def _rnn_params(W1, Wx, Ws, bias, w_dtype):
+    r = np.asarray(Wx).shape[-1]
+    return (widen_weights(W1, w_dtype), widen_weights(Wx, w_dtype).reshape(3, r, r),
+            widen_weights(Ws, w_dtype).reshape(3, r, r),
+            np.asarray(bias, dtype=np.float32).astype(np.float64).reshape(3, r))
+
+
+def draft_rnn(base, W1, W2, Wx, Ws, bias, w_dtype, anchor, u_draft, T):
+    """Sequential drafting with the RNN head.
+
+    The state s_k accumulates the in-block prefix x_0..x_{k-1} (x_0 = anchor,
+    s_0 = 0, input row e = W1[x_{k-1}], rnn_state_update), and the transition
+    bias at position k is s_k @ W2, added to base row k; sampling as in draft.
+    Wx, Ws [3, r, r] (input and recurrent weights of the update, reset and
+    candidate gates, same storage as W1/W2), bias [3, r] fp32.
+    Returns draft's dict plus states [R, gamma, r] (float64 values of s_1..s_gamma,
+    exact in the storage type).
+    """
+    R, g, V = base.shape
+    W1_64, Wx_64, Ws_64, b_64 = _rnn_params(W1, Wx, Ws, bias, w_dtype)
+    W2_64 = widen_weights(W2, w_dtype)
+    states = np.zeros((R, g, W1_64.shape[1]))
+    cur = {"s": np.zeros((R, W1_64.shape[1]))}
+
+    def bias_of(k, prev):
+        cur["s"] = rnn_state_update(W1_64[prev], cur["s"], Wx_64, Ws_64, b_64, w_dtype)
+        states[:, k] = cur["s"]
+        return cur["s"] @ W2_64
+
+    out = _draft_loop(base, u_draft, T, anchor, bias_of)
+    out["states"] = states
+    return out

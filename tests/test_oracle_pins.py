@@ -821,3 +821,148 @@ def test_sts_left_to_right():
     # a labels-all-one block with c = 1 everywhere scores 0 for every tau
     r4 = O.sts_fit(np.ones((10, 3)), np.ones((10, 3)), grid, 10)
     assert (r4["table"] == 0).all() and (r4["index"] == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# RNN head (gated recurrent state over the in-block prefix)
+
+
+def test_storage_rounding_ties_to_even():
+    # bf16 keeps 8 significant bits: 1 + 2^-8 is halfway between 1 and
+    # 1 + 2^-7 (goes to the even 1), 1 + 3 * 2^-8 halfway between 1 + 2^-7 and
+    # 1 + 2^-6 (goes to the even 1 + 2^-6); just above a tie rounds up
+    v = O.to_storage([1 + 2**-8, 1 + 3 * 2**-8, 1 + 2**-8 + 2**-20, -(1 + 2**-8), 0.0], "bf16")
+    assert list(v) == [1.0, 1 + 2**-6, 1 + 2**-7, -1.0, 0.0]
+    assert O.to_storage([1 + 2**-30, 1 + 2**-23], "f32").tolist() == [1.0, 1 + 2**-23]
+
+
+def _rnn_case(r=16, V=64, R=3, g=5, seed=0):
+    rng = np.random.default_rng(seed)
+    base = (rng.standard_normal((R, g, V)) * 2).astype(np.float32)
+    W1 = (rng.standard_normal((V, r)) * 0.7).astype(np.float32)
+    W2 = (rng.standard_normal((r, V)) * 0.7).astype(np.float32)
+    anchor = rng.integers(0, V, R).astype(np.int32)
+    u = rng.uniform(size=(R, g)).astype(np.float32)
+    return base, W1, W2, anchor, u
+
+
+def test_rnn_constant_candidate_closed_form():
+    """Wx = Ws = 0, update bias 0 (u = 1/2), candidate bias c: h = tanh(c) and
+    s_k = (1 - 2^-k) tanh(c), up to the fp32 rounding of each stored state."""
+    r, g = 16, 5
+    base, W1, W2, anchor, u = _rnn_case(r=r, g=g)
+    Wx = np.zeros((3, r, r), np.float32)
+    Ws = np.zeros((3, r, r), np.float32)
+    b = np.zeros((3, r), np.float32)
+    b[1] = 0.7
+    b[2] = np.linspace(-2, 2, r)
+    out = O.draft_rnn(base, W1, W2, Wx, Ws, b, "f32", anchor, u, 1.0)
+    want = (1 - 2.0 ** -np.arange(1, g + 1))[:, None] * np.tanh(b[2].astype(np.float64))[None, :]
+    np.testing.assert_allclose(out["states"], np.broadcast_to(want, out["states"].shape), rtol=0, atol=5e-7)
+
+
+@pytest.mark.parametrize("w_dtype", ["f32", "bf16"])
+def test_rnn_with_open_update_gate_is_a_markov_head(w_dtype):
+    """u = 1, candidate tanh(e) and no recurrence: s_k = tanh(W1[x_{k-1}]) in
+    storage, so the RNN draft is the Markov draft with table tanh(W1)."""
+    from gen.inputs import bf16_bits_from_f32
+    r = 16
+    base, W1, W2, anchor, u = _rnn_case(r=r, seed=1)
+    Wx = np.zeros((3, r, r), np.float32)
+    Wx[2] = np.eye(r, dtype=np.float32)
+    Ws = np.zeros((3, r, r), np.float32)
+    b = np.zeros((3, r), np.float32)
+    b[0] = 60.0                                      # sigmoid(60) == 1.0 in float64
+    conv = (lambda x: bf16_bits_from_f32(x)) if w_dtype == "bf16" else (lambda x: x)
+    W1s, W2s, Wxs, Wss = conv(W1), conv(W2), conv(Wx), conv(Ws)
+    W1t = O.to_storage(np.tanh(O.widen_weights(W1s, w_dtype)), w_dtype).astype(np.float32)
+    for T in (1.0, 0.0):
+        a = O.draft_rnn(base, W1s, W2s, Wxs, Wss, b, w_dtype, anchor, u, T)
+        m = O.draft(base, conv(W1t), W2s, w_dtype, anchor, u, T)
+        assert np.array_equal(a["tokens"], m["tokens"])
+        np.testing.assert_allclose(a["probs"], m["probs"], rtol=1e-13, atol=0)
+        np.testing.assert_allclose(a["stats"], m["stats"], rtol=1e-13, atol=0)
+
+
+def test_rnn_state_remembers_beyond_the_previous_token():
+    """With u = 1/2 and candidate tanh(e): s_2 = 1/4 tanh(W1[x_0]) + 1/2 tanh(W1[x_1]),
+    so the anchor still moves the position-2 bias (the Markov bias does not)."""
+    r, V = 16, 64
+    _, W1, W2, _, _ = _rnn_case(r=r, V=V, seed=2)
+    W1_64 = W1.astype(np.float64)
+    Wx = np.zeros((3, r, r))
+    Wx[2] = np.eye(r)
+    Ws = np.zeros((3, r, r))
+    b = np.zeros((3, r))
+    s0 = np.zeros((1, r))
+    x1 = 5
+    s2 = {}
+    for a in (3, 9):
+        s1 = O.rnn_state_update(W1_64[[a]], s0, Wx, Ws, b, "f32")
+        s2[a] = O.rnn_state_update(W1_64[[x1]], s1, Wx, Ws, b, "f32")[0]
+        want = 0.25 * np.tanh(W1_64[a]) + 0.5 * np.tanh(W1_64[x1])
+        np.testing.assert_allclose(s2[a], want, rtol=0, atol=3e-7)
+    assert np.abs(s2[3] - s2[9]).max() > 1e-2
+
+
+def test_rnn_reset_gate_closes_the_recurrence():
+    """u = 1, candidate tanh(e + (g * s) M): a closed reset gate (g = 0) gives
+    s_2 = tanh(e_1); an open one (g = 1) gives s_2 = tanh(e_1 + s_1 M)."""
+    r, V = 8, 32
+    rng = np.random.default_rng(3)
+    W1_64 = rng.standard_normal((V, r)) * 0.8
+    M = rng.standard_normal((r, r)) * 0.8
+    Wx = np.zeros((3, r, r))
+    Wx[2] = np.eye(r)
+    Ws = np.zeros((3, r, r))
+    Ws[2] = M
+    for bg, open_gate in ((-60.0, False), (60.0, True)):
+        b = np.zeros((3, r))
+        b[0], b[1] = 60.0, bg
+        s1 = O.rnn_state_update(W1_64[[2]], np.zeros((1, r)), Wx, Ws, b, "f32")
+        s2 = O.rnn_state_update(W1_64[[7]], s1, Wx, Ws, b, "f32")
+        want = np.tanh(W1_64[7] + (s1[0] @ M if open_gate else 0.0))
+        np.testing.assert_allclose(s2[0], want, rtol=0, atol=3e-7)
+
+
+class _TinyRNN(_Tiny):
+    """The same single-request V = 4, gamma = 2 round drafted by an RNN head."""
+
+    def __init__(self, seed, T=1.0):
+        super().__init__(seed, T)
+        rng = np.random.default_rng(seed + 1000)
+        self.Wx = (rng.standard_normal((3, 2, 2)) * 1.2).astype(np.float32)
+        self.Ws = (rng.standard_normal((3, 2, 2)) * 1.2).astype(np.float32)
+        self.b = (rng.standard_normal((3, 2)) * 0.5).astype(np.float32)
+        self.W2 = (self.W2 * 2.5).astype(np.float32)     # a stronger state bias
+
+    def draft(self, u1, u2):
+        r = O.draft_rnn(self.base, self.W1, self.W2, self.Wx, self.Ws, self.b, "f32", self.anchor,
+                        np.array([[u1, u2]]), self.T)
+        return r["tokens"][0], r["probs"][0]
+
+    def verify(self, x, q, L, ua1, ua2, uf):
+        # the states of this drafted prefix (they depend on the anchor and x_1 only)
+        u = np.zeros((1, 2))
+        st = O.draft_rnn(self.base, self.W1, self.W2, self.Wx, self.Ws, self.b, "f32", self.anchor,
+                         u, 0.0)["states"]
+        W1_64 = self.W1.astype(np.float64)
+        Wx, Ws, b = (self.Wx.astype(np.float64), self.Ws.astype(np.float64), self.b.astype(np.float64))
+        s1 = O.rnn_state_update(W1_64[self.anchor], np.zeros((1, 2)), Wx, Ws, b, "f32")
+        s2 = O.rnn_state_update(W1_64[[x[0]]], s1, Wx, Ws, b, "f32")
+        assert np.array_equal(st[0, 0], s1[0])          # s_1 does not depend on any drafted token
+        states = np.stack([s1[0], s2[0]])[None]
+        tgt = np.stack([self.T1, self.T2[x[0]], self.T3])[None]
+        return O.verify(tgt, self.base, None, self.W2, "f32", None, x[None], q[None], np.array([L]),
+                        np.array([[ua1, ua2]]), np.array([uf]), self.T, states=states)
+
+
+@pytest.mark.parametrize("seed", [21, 22])
+@pytest.mark.parametrize("L", [1, 2])
+def test_rnn_lossless_exact(seed, L):
+    """Exact laws of the first and second emitted tokens equal the target's
+    when the RNN head drafts and verify recomputes its rows from the states."""
+    t = _TinyRNN(seed)
+    np.testing.assert_allclose(t.first_token_law(lambda a: L), _softmax(t.T1), atol=1e-12)
+    for a in range(4):
+        np.testing.assert_allclose(t.second_token_law(a, L), _softmax(t.T2[a]), atol=1e-12)

@@ -54,6 +54,10 @@ def load_library():
     lib.dspark_accept_rates.restype = I
     lib.dspark_verify.argtypes = [P, P, P, P, I, P, P, P, P, P, P, P, I, I, I, I, F, P, P, P, P, Z, P]
     lib.dspark_verify.restype = I
+    lib.dspark_draft_rnn.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, F, P, P, P, P, P, Z, P]
+    lib.dspark_draft_rnn.restype = I
+    lib.dspark_verify_rnn.argtypes = [P, P, P, P, I, P, P, P, P, P, P, I, I, I, I, F, P, P, P, P, Z, P]
+    lib.dspark_verify_rnn.restype = I
     lib.dspark_sts_workspace_size.argtypes = [I, I, I, I]
     lib.dspark_sts_workspace_size.restype = Z
     lib.dspark_sts_fit.argtypes = [P, P, P, I, I, I, I, P, P, P, P, P, Z, P]
@@ -262,6 +266,61 @@ def verify(target, base, W1, W2, anchor, draft_tokens, draft_probs, draft_stats,
     return ot, al, tp
 
 
+def draft_rnn(base, W1, W2, Wx, Ws, rnn_bias, anchor, u_draft, temperature, ws, out=None):
+    """dspark_draft_rnn.  Returns (draft_tokens, draft_probs, draft_stats, states)."""
+    R, g, V = base.shape
+    r = W1.shape[1]
+    dev = base.device
+    wt, wdt = _wtype(W1), W1.dtype
+    if out is None:
+        out = (torch.empty((R, g), dtype=torch.int32, device=dev),
+               torch.empty((R, g), dtype=torch.float32, device=dev),
+               torch.empty((R, g, 2), dtype=torch.float32, device=dev),
+               torch.empty((R, g, r), dtype=wdt, device=dev))
+    tok, prob, stats, states = out
+    args = (_ptr(base, torch.float32, (R, g, V), "base", dev), _ptr(W1, wdt, (V, r), "W1", dev),
+            _ptr(W2, wdt, (r, V), "W2", dev), _ptr(Wx, wdt, (3, r, r), "Wx", dev), _ptr(Ws, wdt, (3, r, r), "Ws", dev),
+            _ptr(rnn_bias, torch.float32, (3, r), "rnn_bias", dev), wt,
+            _ptr(anchor, torch.int32, (R,), "anchor", dev), _ptr(u_draft, torch.float32, (R, g), "u_draft", dev),
+            R, g, V, r, float(temperature),
+            _ptr(tok, torch.int32, (R, g), "draft_tokens", dev), _ptr(prob, torch.float32, (R, g), "draft_probs", dev),
+            _ptr(stats, torch.float32, (R, g, 2), "draft_stats", dev), _ptr(states, wdt, (R, g, r), "states", dev),
+            ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("dspark_draft_rnn", load_library().dspark_draft_rnn(*args))
+    return tok, prob, stats, states
+
+
+def verify_rnn(target, base, states, W2, draft_tokens, draft_probs, draft_stats, verify_len, u_accept, u_final,
+               temperature, ws, out=None, with_probs=True):
+    """dspark_verify_rnn.  Returns (out_tokens, accept_len, target_probs or None)."""
+    R, g1, V = target.shape
+    g = g1 - 1
+    r = states.shape[2]
+    dev = target.device
+    wt, wdt = _wtype(W2), W2.dtype
+    if out is None:
+        out = (torch.empty((R, g + 1), dtype=torch.int32, device=dev),
+               torch.empty(R, dtype=torch.int32, device=dev),
+               torch.empty((R, g), dtype=torch.float32, device=dev) if with_probs else None)
+    ot, al, tp = out
+    args = (_ptr(target, torch.float32, (R, g + 1, V), "target", dev),
+            _ptr(base, torch.float32, (R, g, V), "base", dev),
+            _ptr(states, wdt, (R, g, r), "states", dev), _ptr(W2, wdt, (r, V), "W2", dev), wt,
+            _ptr(draft_tokens, torch.int32, (R, g), "draft_tokens", dev),
+            _ptr(draft_probs, torch.float32, (R, g), "draft_probs", dev),
+            _ptr(draft_stats, torch.float32, (R, g, 2), "draft_stats", dev),
+            _ptr(verify_len, torch.int32, (R,), "verify_len", dev),
+            _ptr(u_accept, torch.float32, (R, g), "u_accept", dev),
+            _ptr(u_final, torch.float32, (R,), "u_final", dev),
+            R, g, V, r, float(temperature),
+            _ptr(ot, torch.int32, (R, g + 1), "out_tokens", dev),
+            _ptr(al, torch.int32, (R,), "accept_len", dev),
+            _ptr(tp, torch.float32, (R, g), "target_probs", dev),
+            ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("dspark_verify_rnn", load_library().dspark_verify_rnn(*args))
+    return ot, al, tp
+
+
 def sts_workspace_size(N, gamma, G, bins):
     n = load_library().dspark_sts_workspace_size(N, gamma, G, bins)
     if n == 0:
@@ -317,7 +376,8 @@ def _side_stream(device):
     return _side_streams[device]
 
 
-def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, scheduler="early", theta=None):
+def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, scheduler="early", theta=None,
+              head="markov"):
     """draft -> schedule -> verify on a dict of device tensors.
 
     The scheduler reads only confidences and the cost table, so it runs on a
@@ -326,8 +386,12 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
     workspace ``ws_sched`` (allocated here if not given).  ``scheduler`` is
     "early" (dspark_schedule), "async" (dspark_schedule_async with the
     lagged confidences ``conf_lag`` of the input dict) or "threshold"
-    (dspark_schedule_threshold with ``theta``).
+    (dspark_schedule_threshold with ``theta``).  ``head`` "rnn" drafts with
+    dspark_draft_rnn (gate weights ``Wx``, ``Ws``, ``rnn_bias`` of the input
+    dict) and verifies with dspark_verify_rnn.
     """
+    if head not in ("markov", "rnn"):
+        raise ValueError(f"head must be 'markov' or 'rnn', got {head!r}")
     if scheduler not in ("early", "async", "threshold"):
         raise ValueError(f"scheduler must be 'early', 'async' or 'threshold', got {scheduler!r}")
     if scheduler == "threshold" and theta is None:
@@ -349,10 +413,19 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
                 L, n, _ = schedule_threshold(d["conf"], theta, ws_sched, with_cum=False)
             else:
                 L, n, _ = schedule(d["conf"], d["sps"], ws_sched, with_cum=False)
-    tok, prob, stats = draft(d["base"], d["W1"], d["W2"], d["anchor"], d["u_draft"], temperature, ws)
+    states = None
+    if head == "rnn":
+        tok, prob, stats, states = draft_rnn(d["base"], d["W1"], d["W2"], d["Wx"], d["Ws"], d["rnn_bias"],
+                                             d["anchor"], d["u_draft"], temperature, ws)
+    else:
+        tok, prob, stats = draft(d["base"], d["W1"], d["W2"], d["anchor"], d["u_draft"], temperature, ws)
     if sched:
         cur.wait_stream(side)
-    ot, al, tp = verify(d["target"], d["base"], d["W1"], d["W2"], d["anchor"], tok, prob, stats, L,
-                        d["u_accept"], d["u_final"], temperature, ws)
+    if head == "rnn":
+        ot, al, tp = verify_rnn(d["target"], d["base"], states, d["W2"], tok, prob, stats, L, d["u_accept"],
+                                d["u_final"], temperature, ws)
+    else:
+        ot, al, tp = verify(d["target"], d["base"], d["W1"], d["W2"], d["anchor"], tok, prob, stats, L,
+                            d["u_accept"], d["u_final"], temperature, ws)
     return dict(draft_tokens=tok, draft_probs=prob, draft_stats=stats, verify_len=L, n_admitted=n,
-                out_tokens=ot, accept_len=al, target_probs=tp, ws_sched=ws_sched)
+                out_tokens=ot, accept_len=al, target_probs=tp, ws_sched=ws_sched, states=states)

@@ -5,7 +5,8 @@
 namespace dspark {
 int draft_impl(const float* base, const void* W1, const void* W2, dspark_wtype w_type,
                const int32_t* anchor, const float* u_draft, int R, int gamma, int V, int r, float T,
-               int32_t* tokens, float* probs, float* stats, void* ws, hipStream_t stream);
+               int32_t* tokens, float* probs, float* stats, void* ws, hipStream_t stream,
+               const RnnHead* rnn = nullptr);
 int schedule_impl(const float* conf, const float* sps, int R, int gamma, int n_table,
                   int32_t* verify_len, int32_t* n_admitted, float* cum_conf, void* ws,
                   hipStream_t stream);
@@ -21,7 +22,7 @@ int verify_impl(const float* target, const float* base, const void* W1, const vo
                 dspark_wtype w_type, const int32_t* anchor, const int32_t* dtok, const float* dprob,
                 const float* dstats, const int32_t* vlen, const float* u_acc, const float* u_fin,
                 int R, int gamma, int V, int r, float T, int32_t* out_tokens, int32_t* accept_len,
-                float* target_probs, void* ws, hipStream_t stream);
+                float* target_probs, void* ws, hipStream_t stream, bool dense_rows = false);
 
 size_t sts_workspace_size_impl(int N, int gamma, int G, int bins);
 int sts_fit_impl(const float* conf, const float* labels, const float* grid, int N, int gamma, int G, int bins,
@@ -226,6 +227,47 @@ int dspark_verify(const float* target, const float* base, const void* W1, const 
   return verify_impl(target, base, W1, W2, w_type, anchor, draft_tokens, draft_probs, draft_stats,
                      verify_len, u_accept, u_final, R, gamma, V, r, temperature, out_tokens,
                      accept_len, target_probs, workspace, stream);
+}
+
+int dspark_draft_rnn(const float* base, const void* W1, const void* W2, const void* Wx, const void* Ws,
+                     const float* rnn_bias, dspark_wtype w_type, const int32_t* anchor, const float* u_draft,
+                     int R, int gamma, int V, int r, float temperature, int32_t* draft_tokens,
+                     float* draft_probs, float* draft_stats, void* states, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  if (!sizes_ok(R, gamma, V, r)) return DSPARK_EINVAL;
+  if (w_type != DSPARK_W_BF16 && w_type != DSPARK_W_F32) return DSPARK_EINVAL;
+  if (!base || !W1 || !W2 || !Wx || !Ws || !rnn_bias || !anchor || !u_draft || !draft_tokens || !draft_probs ||
+      !draft_stats || !states)
+    return DSPARK_EINVAL;
+  if (!aligned16(base) || !aligned16(W1) || !aligned16(W2) || !aligned16(states)) return DSPARK_EINVAL;
+  if ((unsigned long long)R * gamma * r * (w_type == DSPARK_W_BF16 ? 2 : 4) >= (1ull << 32)) return DSPARK_EINVAL;
+  if (!(temperature >= 0.f) || __builtin_isinf(temperature)) return DSPARK_EINVAL;
+  const int wsr = check_ws(workspace, workspace_bytes, R, gamma, V);
+  if (wsr != DSPARK_OK) return wsr;
+  const RnnHead head{Wx, Ws, rnn_bias, states};
+  return draft_impl(base, W1, W2, w_type, anchor, u_draft, R, gamma, V, r, temperature, draft_tokens,
+                    draft_probs, draft_stats, workspace, stream, &head);
+}
+
+int dspark_verify_rnn(const float* target, const float* base, const void* states, const void* W2,
+                      dspark_wtype w_type, const int32_t* draft_tokens, const float* draft_probs,
+                      const float* draft_stats, const int32_t* verify_len, const float* u_accept,
+                      const float* u_final, int R, int gamma, int V, int r, float temperature,
+                      int32_t* out_tokens, int32_t* accept_len, float* target_probs, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  if (!sizes_ok(R, gamma, V, r)) return DSPARK_EINVAL;
+  if (w_type != DSPARK_W_BF16 && w_type != DSPARK_W_F32) return DSPARK_EINVAL;
+  if (!target || !base || !states || !W2 || !draft_tokens || !draft_probs || !draft_stats || !u_accept ||
+      !u_final || !out_tokens || !accept_len)
+    return DSPARK_EINVAL;
+  if (!aligned16(target) || !aligned16(base) || !aligned16(states) || !aligned16(W2)) return DSPARK_EINVAL;
+  if ((unsigned long long)R * gamma * r * (w_type == DSPARK_W_BF16 ? 2 : 4) >= (1ull << 32)) return DSPARK_EINVAL;
+  if (!(temperature >= 0.f) || __builtin_isinf(temperature)) return DSPARK_EINVAL;
+  const int wsr = check_ws(workspace, workspace_bytes, R, gamma, V);
+  if (wsr != DSPARK_OK) return wsr;
+  return verify_impl(target, base, states, W2, w_type, nullptr, draft_tokens, draft_probs, draft_stats,
+                     verify_len, u_accept, u_final, R, gamma, V, r, temperature, out_tokens, accept_len,
+                     target_probs, workspace, stream, true);
 }
 
 static bool sts_sizes_ok(int N, int gamma, int G, int bins) {

@@ -686,6 +686,14 @@ __device__ __forceinline__ float tree_sum32(const float (&e)[2][16]) {
 
 // ---------------------------------------------------------------------------
 // Workspace layout (identical on host and device).  All offsets 256-aligned.
+// RNN head parameters and its state table (see k_rnn_state).
+struct RnnHead {
+  const void* Wx;      // [3][r][r] input weights of the update, reset and candidate gates
+  const void* Ws;      // [3][r][r] recurrent weights, same gate order
+  const float* bias;   // [3][r]
+  void* states;        // [R][gamma][r] out: s_1..s_gamma in the weights' storage type
+};
+
 struct WsLayout {
   size_t err;      // int32 error word
   size_t trec;     // float4 [R][nt][2]     draft tile records (see select.h)

@@ -24,6 +24,7 @@
 //        search.
 #include <type_traits>
 
+#include "rnn.h"
 #include "select.h"
 
 namespace dspark {
@@ -42,8 +43,14 @@ struct DraftStep {
   float* stats;
   float4* trec;  // [R][nt][2] tile records
   int32_t* err;
+  // Bias rows: W1 indexed by the previous token (Markov head), or, with dense
+  // set, a table of a_rows = R * gamma rows where row r * gamma + k - 1 holds
+  // the RNN head's state s_k of request r.
+  bool dense;
+  int a_rows;
 
   __device__ int prev_token(int row) const {
+    if (dense) return row * gamma + k - 1;
     const int t = (k == 1) ? anchor[row] : tokens[(size_t)row * gamma + k - 2];
     return checked_token(t, V, err);
   }
@@ -115,7 +122,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // second unit's rows -- the same order (fragment, then one unit of rows)
     // as at every later tile start, which the waits below count on
     W1Gather<WT, GPER> g;
-    g.load(P.W1, P.V, P.r, nrows, CH, a_stride, [&](int i) { return s_tok[i]; });
+    g.load(P.W1, P.a_rows, P.r, nrows, CH, a_stride, [&](int i) { return s_tok[i]; });
     issue(0);
     typename BiasBlock<WT>::template Frag<KS> F;
     BiasBlock<WT>::template load<KS>(F, P.W2, P.V, P.r, (int)blockIdx.x * TILE + wave * WCOLS);
@@ -311,11 +318,14 @@ __global__ __launch_bounds__(256) void k_draft_select(DraftStep<WT> P) {
 template <typename WT>
 static int launch_draft(const float* base, const void* W1, const void* W2, const int32_t* anchor,
                         const float* u_draft, int R, int gamma, int V, int r, float T,
-                        int32_t* tokens, float* probs, float* stats, void* ws, hipStream_t stream) {
+                        int32_t* tokens, float* probs, float* stats, void* ws, hipStream_t stream,
+                        const RnnHead* rnn = nullptr) {
   const WsLayout L = ws_layout(R, gamma, V);
   DraftStep<WT> P;
   P.base = base;
-  P.W1 = static_cast<const WT*>(W1);
+  P.W1 = static_cast<const WT*>(rnn ? rnn->states : W1);
+  P.dense = rnn != nullptr;
+  P.a_rows = rnn ? R * gamma : V;
   P.W2 = static_cast<const WT*>(W2);
   P.anchor = anchor;
   P.u_draft = u_draft;
@@ -329,6 +339,7 @@ static int launch_draft(const float* base, const void* W1, const void* W2, const
   const int grid1 = min(nt, device_cu_count());
   for (int k = 1; k <= gamma; k++) {
     P.k = k;
+    if (rnn) launch_rnn_state<WT>(*rnn, static_cast<const WT*>(W1), anchor, tokens, R, gamma, V, r, k, P.err, stream);
     prof_before(DSPARK_KID_DRAFT_PARTIALS, stream);
     for (int rep = prof_repeat(DSPARK_KID_DRAFT_PARTIALS); rep > 0; rep--) {
       DSPARK_DISPATCH_KS(r, {
@@ -355,12 +366,13 @@ static int launch_draft(const float* base, const void* W1, const void* W2, const
 
 int draft_impl(const float* base, const void* W1, const void* W2, dspark_wtype w_type,
                const int32_t* anchor, const float* u_draft, int R, int gamma, int V, int r, float T,
-               int32_t* tokens, float* probs, float* stats, void* ws, hipStream_t stream) {
+               int32_t* tokens, float* probs, float* stats, void* ws, hipStream_t stream,
+               const RnnHead* rnn = nullptr) {
   if (w_type == DSPARK_W_BF16)
     return launch_draft<uint16_t>(base, W1, W2, anchor, u_draft, R, gamma, V, r, T, tokens, probs,
-                                  stats, ws, stream);
+                                  stats, ws, stream, rnn);
   return launch_draft<float>(base, W1, W2, anchor, u_draft, R, gamma, V, r, T, tokens, probs, stats,
-                             ws, stream);
+                             ws, stream, rnn);
 }
 
 }  // namespace dspark

@@ -55,6 +55,10 @@ struct VerifyArgs {
   float4* rrec;
   float* tvpart;  // [R*gamma][V/256] per-tile sums of max(0, p - q) (acceptance labels)
   int32_t* err;
+  // Draft bias rows: W1 by previous token, or (dense) the RNN head's state
+  // table of a_rows = R * gamma rows, row r * gamma + k - 1 = s_k of request r.
+  bool dense;
+  int a_rows;
 
   __device__ int L_of(int row, bool report = false) const {
     if (!vlen) return gamma;
@@ -67,6 +71,7 @@ struct VerifyArgs {
   }
   // token before position k (1-based) of request row
   __device__ int prev_of(int row, int k) const {
+    if (dense) return row * gamma + k - 1;
     const int t = (k == 1) ? anchor[row] : dtok[(size_t)row * gamma + k - 2];
     return checked_token(t, V, err);
   }
@@ -338,7 +343,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
 
     W1Gather<WT, GPER> g;
-    g.load(P.W1, P.V, P.r, nrej, CH, a_stride, [&](int i) { return s_tok[i]; });
+    g.load(P.W1, P.a_rows, P.r, nrej, CH, a_stride, [&](int i) { return s_tok[i]; });
     issue(0);
     typename BiasBlock<WT>::template Frag<KS> F;
     BiasBlock<WT>::template load<KS>(F, P.W2, P.V, P.r, (int)blockIdx.x * TILE + wave * WCOLS);
@@ -644,9 +649,11 @@ int verify_impl(const float* target, const float* base, const void* W1, const vo
                 dspark_wtype w_type, const int32_t* anchor, const int32_t* dtok, const float* dprob,
                 const float* dstats, const int32_t* vlen, const float* u_acc, const float* u_fin,
                 int R, int gamma, int V, int r, float T, int32_t* out_tokens, int32_t* accept_len,
-                float* target_probs, void* ws, hipStream_t stream) {
+                float* target_probs, void* ws, hipStream_t stream, bool dense_rows = false) {
   const WsLayout Lw = ws_layout(R, gamma, V);
   auto fill = [&](auto& P) {
+    P.dense = dense_rows;
+    P.a_rows = dense_rows ? R * gamma : V;
     P.target = target; P.base = base;
     P.anchor = anchor; P.dtok = dtok; P.dprob = dprob; P.dstats = dstats; P.vlen = vlen;
     P.u_acc = u_acc; P.u_fin = u_fin;
@@ -682,6 +689,8 @@ int accept_rates_impl(const float* target, const float* base, const void* W1, co
   const WsLayout Lw = ws_layout(R, gamma, V);
   auto fill = [&](auto& P) {
     P = {};
+    P.dense = false;
+    P.a_rows = V;
     P.target = target; P.base = base;
     P.anchor = anchor; P.dtok = dtok; P.dstats = dstats; P.vlen = nullptr;
     P.R = R; P.gamma = gamma; P.V = V; P.r = r;

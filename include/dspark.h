@@ -289,6 +289,48 @@ int dspark_profile_arm(int kid, hipEvent_t* starts, hipEvent_t* stops, int n, in
 int dspark_profile_disarm(void);
 
 /*
+ * dspark_draft_rnn - drafting with the RNN head instead of the Markov head
+ * ("DSpark: Aceleração da inferência de LLM com speculative decoding",
+ * pt.news.hada.io, section "Arquitetura", Semi-Autoregressive Generation, RNN
+ * head: a recurrent state accumulates the whole in-block prefix with a gated
+ * update; section "Experimentos": a small extra gain at long blocks).  The
+ * pages give no equations; the update is the GRU form, with s_0 = 0 and
+ * e = W1[x_{k-1}] (x_0 = anchor):
+ *   u = sigmoid(e Wx[0] + s Ws[0] + b[0])       g = sigmoid(e Wx[1] + s Ws[1] + b[1])
+ *   h = tanh(e Wx[2] + (g * s) Ws[2] + b[2])   s_k = (1 - u) * s + u * h
+ * evaluated in fp64 and stored in the weights' type (fp32, then bf16
+ * round-to-nearest-even for bf16 weights).  The transition bias at position k
+ * is s_k . W2; everything else is dspark_draft.
+ *
+ *   base, W1, W2, w_type, anchor, u_draft, temperature, outputs: as dspark_draft
+ *   Wx, Ws     [3, r, r] gate weights (update, reset, candidate), storage w_type;
+ *              row = input unit, column = state unit
+ *   rnn_bias   [3, r] fp32
+ *   states     out [R, gamma, r] (w_type, 16-byte aligned): s_1..s_gamma, the
+ *              rows dspark_verify_rnn recomputes the draft from
+ * Same checks and status codes as dspark_draft; additionally R*gamma*r
+ * elements of states must stay below 4 GiB.
+ */
+int dspark_draft_rnn(const float* base, const void* W1, const void* W2, const void* Wx, const void* Ws,
+                     const float* rnn_bias, dspark_wtype w_type, const int32_t* anchor, const float* u_draft,
+                     int R, int gamma, int V, int r, float temperature, int32_t* draft_tokens,
+                     float* draft_probs, float* draft_stats, void* states, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * dspark_verify_rnn - dspark_verify for blocks drafted by dspark_draft_rnn:
+ * identical tests and emission, except that the draft distribution at the
+ * rejected position k* is recomputed as softmax((base[r, k*-1] + s_{k*} . W2) / T)
+ * from the states dspark_draft_rnn wrote (W1 and the anchor are not needed).
+ */
+int dspark_verify_rnn(const float* target, const float* base, const void* states, const void* W2,
+                      dspark_wtype w_type, const int32_t* draft_tokens, const float* draft_probs,
+                      const float* draft_stats, const int32_t* verify_len, const float* u_accept,
+                      const float* u_final, int R, int gamma, int V, int r, float temperature,
+                      int32_t* out_tokens, int32_t* accept_len, float* target_probs, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/*
  * dspark_sts_fit - sequential temperature scaling of the confidence head
  * ("DSpark: Aceleração da inferência de LLM com speculative decoding",
  * pt.news.hada.io, section "Arquitetura", Confidence-Scheduled Verification,

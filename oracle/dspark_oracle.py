@@ -347,17 +347,23 @@ def verify(target, base, W1, W2, w_dtype, anchor, draft_tokens, draft_probs,
 # whole round and boundary flags
 
 
-def run_round(inp, T=1.0, use_scheduler=None, scheduler="early", theta=None):
+def run_round(inp, T=1.0, use_scheduler=None, scheduler="early", theta=None, head="markov"):
     """Draft -> schedule -> verify on one input dict from ``gen.make_inputs``.
 
     scheduler: "early" (the early-stop walk), "async" (the production
     variant, with the lagged confidences ``conf_lag``) or "threshold" (the
-    static baseline with ``theta``).
+    static baseline with ``theta``).  head: "markov", or "rnn" (draft_rnn with
+    the gate weights ``Wx``, ``Ws``, ``rnn_bias`` of the input dict; verify
+    recomputes from the states).
     """
     sched = None
     if use_scheduler is None:
         use_scheduler = inp.get("conf") is not None
-    d = draft(inp["base"], inp["W1"], inp["W2"], inp["w_dtype"], inp["anchor"], inp["u_draft"], T)
+    if head == "rnn":
+        d = draft_rnn(inp["base"], inp["W1"], inp["W2"], inp["Wx"], inp["Ws"], inp["rnn_bias"], inp["w_dtype"],
+                      inp["anchor"], inp["u_draft"], T)
+    else:
+        d = draft(inp["base"], inp["W1"], inp["W2"], inp["w_dtype"], inp["anchor"], inp["u_draft"], T)
     L = None
     if use_scheduler:
         if scheduler == "async":
@@ -368,7 +374,7 @@ def run_round(inp, T=1.0, use_scheduler=None, scheduler="early", theta=None):
             sched = schedule(inp["conf"], inp["sps"])
         L = sched["verify_len"][inp["rows"]] if "rows" in inp else sched["verify_len"]
     v = verify(inp["target"], inp["base"], inp["W1"], inp["W2"], inp["w_dtype"], inp["anchor"],
-               d["tokens"], d["probs"], L, inp["u_accept"], inp["u_final"], T)
+               d["tokens"], d["probs"], L, inp["u_accept"], inp["u_final"], T, states=d.get("states"))
     flags = row_flags(d, v)
     return dict(draft=d, schedule=sched, verify=v, flags=flags,
                 verify_len=(np.full(len(inp["anchor"]), inp["base"].shape[1], np.int32)

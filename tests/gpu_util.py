@@ -34,23 +34,26 @@ def to_dev(inp, device=None):
                 W2=w_to_dev(inp["W2"], inp["w_dtype"], device),
                 anchor=t(inp["anchor"], np.int32), u_draft=t(inp["u_draft"], np.float32),
                 u_accept=t(inp["u_accept"], np.float32), u_final=t(inp["u_final"], np.float32),
-                conf=t(inp["conf"], np.float32), sps=t(inp["sps"], np.float32))
+                conf=t(inp["conf"], np.float32), sps=t(inp["sps"], np.float32),
+                **({} if "Wx" not in inp else dict(Wx=w_to_dev(inp["Wx"], inp["w_dtype"], device),
+                                                   Ws=w_to_dev(inp["Ws"], inp["w_dtype"], device),
+                                                   rnn_bias=t(inp["rnn_bias"], np.float32))))
 
 
-def gpu_round(inp, T, use_scheduler=None, device=None):
+def gpu_round(inp, T, use_scheduler=None, device=None, head="markov"):
     d = to_dev(inp, device)
     R, g, V = inp["base"].shape
     r = inp["W1"].shape[1]
     ws = D.new_workspace(R, g, V, r, d["base"].device)
     if use_scheduler is None:
         use_scheduler = inp.get("conf") is not None
-    out = D.run_round(d, T, ws, use_scheduler=use_scheduler)
+    out = D.run_round(d, T, ws, use_scheduler=use_scheduler, head=head)
     torch.cuda.synchronize()
     err = D.device_error(ws)
     if out["ws_sched"] is not None:
         err |= D.device_error(out["ws_sched"])
-    res = {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in out.items()
-           if k != "ws_sched"}
+    res = {k: ((v.float() if v.dtype == torch.bfloat16 else v).cpu().numpy() if isinstance(v, torch.Tensor) else v)
+           for k, v in out.items() if k != "ws_sched"}
     res["device_error"] = err
     return res
 

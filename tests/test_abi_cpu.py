@@ -120,6 +120,32 @@ def test_accept_rates_rejects_bad_arguments(lib):
     assert lib.dspark_accept_rates(*bad) == ENOSPC
 
 
+def test_rnn_entry_points_reject_bad_arguments(lib):
+    need = lib.dspark_workspace_size(4, 4, 512, 16)
+    # base W1 W2 Wx Ws bias wt anchor u R g V r T tok prob stats states ws wsb stream
+    good = [16, 16, 16, 16, 16, 16, 0, 16, 16, 4, 4, 512, 16, 1.0, 16, 16, 16, 16, 256, need, None]
+    f = lib.dspark_draft_rnn
+    for i in (0, 1, 2, 3, 4, 5, 7, 8, 14, 15, 16, 17):
+        bad = list(good); bad[i] = None
+        assert f(*bad) == EINVAL, i
+    for i, v in ((6, 7), (9, 0), (10, 17), (11, 500), (12, 24), (13, -1.0), (17, 18)):
+        bad = list(good); bad[i] = v
+        assert f(*bad) == EINVAL, i
+    bad = list(good); bad[19] = need - 1
+    assert f(*bad) == ENOSPC
+    # target base states W2 wt tok prob stats L ua uf R g V r T out acc tp ws wsb stream
+    vg = [16, 16, 16, 16, 0, 16, 16, 16, None, 16, 16, 4, 4, 512, 16, 1.0, 16, 16, None, 256, need, None]
+    v = lib.dspark_verify_rnn
+    for i in (0, 1, 2, 3, 5, 6, 7, 9, 10, 16, 17):
+        bad = list(vg); bad[i] = None
+        assert v(*bad) == EINVAL, i
+    for i, val in ((4, 9), (12, 0), (13, 12), (15, float("nan")), (2, 20)):
+        bad = list(vg); bad[i] = val
+        assert v(*bad) == EINVAL, i
+    bad = list(vg); bad[20] = 1000
+    assert v(*bad) == ENOSPC
+
+
 def test_sts_workspace_and_argument_checks(lib):
     sz = lib.dspark_sts_workspace_size
     assert sz(65536, 7, 256, 15) >= 256 + 2 * 8 * 65536 + 7 * 256 * 8 + 64 * 256 * 15 * 8

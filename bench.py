@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--theta", default="cut",
                     help="threshold for --scheduler threshold: a number, or 'cut' = the survival "
                          "probability at the early-stop scheduler's cut (equal verify bytes)")
+    ap.add_argument("--head", choices=("markov", "rnn"), default="markov",
+                    help="sequential head: the Markov head (default) or the gated recurrent (RNN) head "
+                         "with synthetic gate weights")
     ap.add_argument("--labels", action="store_true",
                     help="also time the acceptance-label pass (dspark_accept_rates) on the workload")
     ap.add_argument("--sts", action="store_true",
@@ -125,13 +128,15 @@ def cpu_worker(a):
         print(json.dumps(dict(seconds=dt, threads=threads)))
         return
     inp = make_inputs(cfg_key(a.config))
+    if a.head == "rnn":
+        inp.update(rnn_weights(inp))
     theta = None
     if a.scheduler == "threshold":
         theta = oracle_theta(O, inp, a.theta)
     t0 = time.perf_counter()
     n, toks = 0, 0
     while True:
-        res = O.run_round(inp, T=a.temperature, scheduler=a.scheduler, theta=theta)
+        res = O.run_round(inp, T=a.temperature, scheduler=a.scheduler, theta=theta, head=a.head)
         n += 1
         toks += int((res["verify"]["accept_len"] + 1).sum())
         if time.perf_counter() - t0 >= a.cpu_seconds:
@@ -139,6 +144,13 @@ def cpu_worker(a):
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     print(json.dumps(dict(rounds=n, seconds=dt, tokens=toks, threads=threads)))
+
+
+def rnn_weights(inp):
+    """Synthetic gate weights of the RNN head for this workload (seeded)."""
+    from gen.rnn import make_rnn_weights
+    w = make_rnn_weights(inp["W1"].shape[1], inp["w_dtype"], seed=0)
+    return dict(Wx=w["Wx"], Ws=w["Ws"], rnn_bias=w["bias"])
 
 
 def oracle_theta(O, inp, theta_arg):
@@ -168,7 +180,7 @@ def cpu_baseline(a):
         env.setdefault(k, str(ncpu))
     cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-worker", "--config", a.config,
            "--cpu-seconds", str(a.cpu_seconds), "--temperature", str(a.temperature),
-           "--scheduler", a.scheduler, "--theta", a.theta]
+           "--scheduler", a.scheduler, "--theta", a.theta, "--head", a.head]
     out = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=600)
     if out.returncode != 0:
         return dict(error=out.stderr[-400:])
@@ -212,6 +224,9 @@ def gpu_bench(a):
               conf=None if inp["conf"] is None else t(inp["conf"], np.float32),
               conf_lag=None if inp["conf_lag"] is None else t(inp["conf_lag"], np.float32),
               sps=None if inp["sps"] is None else t(inp["sps"], np.float32))
+    if a.head == "rnn":
+        rw = rnn_weights(inp)
+        dd.update(Wx=w(rw["Wx"]), Ws=w(rw["Ws"]), rnn_bias=t(rw["rnn_bias"], np.float32))
     del inp
     ws = D.new_workspace(R, g, V, r, dev)
     ws_sched = torch.zeros(256, dtype=torch.uint8, device=dev)
@@ -232,7 +247,7 @@ def gpu_bench(a):
 
     # one eager round: reference outputs and workload statistics
     with torch.cuda.stream(stream):
-        ref = D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta)
+        ref = D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta, head=a.head)
     torch.cuda.synchronize()
     if D.device_error(ws) != 0 or D.device_error(ws_sched) != 0:
         raise RuntimeError("device-side data error in the benchmark inputs")
@@ -244,7 +259,7 @@ def gpu_bench(a):
     if use_graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
-            out = D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta)
+            out = D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta, head=a.head)
         torch.cuda.synchronize()
         # replays must reproduce the eager round exactly, replay after replay
         for _ in range(3):
@@ -258,7 +273,7 @@ def gpu_bench(a):
         if use_graph:
             graph.replay()
         else:
-            D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta)
+            D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta, head=a.head)
 
     def timed(fn, n):
         t0 = torch.cuda.Event(enable_timing=True)
@@ -279,7 +294,7 @@ def gpu_bench(a):
 
     # Eager round time (no graph), for reference.
     with torch.cuda.stream(stream):
-        ms_eager = timed(lambda: D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta), a.steps)
+        ms_eager = timed(lambda: D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta, head=a.head), a.steps)
 
     # Dominant-kernel duration: HIP events recorded by the library's launch
     # hook on the kernel's stream, each pair around K1_REPEAT back-to-back
@@ -300,7 +315,7 @@ def gpu_bench(a):
     assert status == 0, f"dspark_profile_arm failed ({status})"
     with torch.cuda.stream(stream):
         for _ in range(n_rounds):
-            D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta)
+            D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta, head=a.head)
     torch.cuda.synchronize()
     used = lib.dspark_profile_disarm()
     k1_ms = sum(s.elapsed_time(e) for s, e in zip(ev_s[:used], ev_e[:used])) / max(used, 1) / K1_REPEAT
@@ -419,7 +434,7 @@ def main():
                                f"{d['w_dtype']} factors, base {d['base']}, target {d['target']}, "
                                f"conf {d['conf']}, table {d['table']}",
                    "R": d["R"], "gamma": d["gamma"], "V": d["V"], "r": d["r"],
-                   "temperature": a.temperature, "scheduler": a.scheduler,
+                   "temperature": a.temperature, "scheduler": a.scheduler, "head": a.head,
                    **({"theta": gb["theta"]} if gb["theta"] is not None else {}),
                    "launch": "hip graph" if gb["graph"] else "eager"},
         "ms_per_step_eager": gb["ms_eager"],

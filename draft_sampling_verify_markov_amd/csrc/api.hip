@@ -239,12 +239,13 @@ int dspark_draft_rnn(const float* base, const void* W1, const void* W2, const vo
   if (!base || !W1 || !W2 || !Wx || !Ws || !rnn_bias || !anchor || !u_draft || !draft_tokens || !draft_probs ||
       !draft_stats || !states)
     return DSPARK_EINVAL;
-  if (!aligned16(base) || !aligned16(W1) || !aligned16(W2) || !aligned16(states)) return DSPARK_EINVAL;
+  if (!aligned16(base) || !aligned16(W1) || !aligned16(W2) || !aligned16(Wx) || !aligned16(Ws) || !aligned16(states))
+    return DSPARK_EINVAL;
   if ((unsigned long long)R * gamma * r * (w_type == DSPARK_W_BF16 ? 2 : 4) >= (1ull << 32)) return DSPARK_EINVAL;
   if (!(temperature >= 0.f) || __builtin_isinf(temperature)) return DSPARK_EINVAL;
   const int wsr = check_ws(workspace, workspace_bytes, R, gamma, V);
   if (wsr != DSPARK_OK) return wsr;
-  const RnnHead head{Wx, Ws, rnn_bias, states};
+  const RnnHead head{Wx, Ws, rnn_bias, states, ws_ptr<double>(workspace, ws_layout(R, gamma, V).rnn)};
   return draft_impl(base, W1, W2, w_type, anchor, u_draft, R, gamma, V, r, temperature, draft_tokens,
                     draft_probs, draft_stats, workspace, stream, &head);
 }

@@ -692,6 +692,7 @@ struct RnnHead {
   const void* Ws;      // [3][r][r] recurrent weights, same gate order
   const float* bias;   // [3][r]
   void* states;        // [R][gamma][r] out: s_1..s_gamma in the weights' storage type
+  double* gates;       // workspace [3][R][r]: u, candidate input part, g * s
 };
 
 struct WsLayout {
@@ -704,6 +705,7 @@ struct WsLayout {
   size_t tp;       // float  [R][gamma]     p_k(x_k) of evaluated positions
   size_t rrec;     // float4 [R][nt][2]     residual tile records
   size_t tvpart;   // float  [R*gamma][nt]  acceptance-label tile sums
+  size_t rnn;      // double [3][R][256]   RNN head gate outputs (update, candidate input part, reset * state)
   size_t total;
 };
 
@@ -722,6 +724,7 @@ __host__ __device__ inline WsLayout ws_layout(int R, int gamma, int V) {
   L.tp = o;       o = ws_align(o + (size_t)R * gamma * 4);
   L.rrec = o;     o = ws_align(o + (size_t)R * nt * 32);
   L.tvpart = o;   o = ws_align(o + (size_t)R * gamma * nt * 4);
+  L.rnn = o;      o = ws_align(o + (size_t)3 * R * DSPARK_MAX_RANK * 8);
   L.total = o;
   return L;
 }

@@ -303,7 +303,8 @@ int dspark_profile_disarm(void);
  * is s_k . W2; everything else is dspark_draft.
  *
  *   base, W1, W2, w_type, anchor, u_draft, temperature, outputs: as dspark_draft
- *   Wx, Ws     [3, r, r] gate weights (update, reset, candidate), storage w_type;
+ *   Wx, Ws     [3, r, r] gate weights (update, reset, candidate), storage w_type,
+ *              16-byte aligned;
  *              row = input unit, column = state unit
  *   rnn_bias   [3, r] fp32
  *   states     out [R, gamma, r] (w_type, 16-byte aligned): s_1..s_gamma, the

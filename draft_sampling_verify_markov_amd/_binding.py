@@ -54,6 +54,12 @@ def load_library():
     lib.dspark_accept_rates.restype = I
     lib.dspark_verify.argtypes = [P, P, P, P, I, P, P, P, P, P, P, P, I, I, I, I, F, P, P, P, P, Z, P]
     lib.dspark_verify.restype = I
+    lib.dspark_verify_stream.argtypes = [P, P, I, I, I, F, P, Z, P]
+    lib.dspark_verify_stream.restype = I
+    lib.dspark_verify_finish.argtypes = lib.dspark_verify.argtypes
+    lib.dspark_verify_finish.restype = I
+    lib.dspark_verify_rnn_finish.argtypes = [P, P, P, P, I, P, P, P, P, P, P, I, I, I, I, F, P, P, P, P, Z, P]
+    lib.dspark_verify_rnn_finish.restype = I
     lib.dspark_draft_rnn.argtypes = [P, P, P, P, P, P, I, P, P, I, I, I, I, F, P, P, P, P, P, Z, P]
     lib.dspark_draft_rnn.restype = I
     lib.dspark_verify_rnn.argtypes = [P, P, P, P, I, P, P, P, P, P, P, I, I, I, I, F, P, P, P, P, Z, P]
@@ -234,8 +240,9 @@ def accept_rates(target, base, W1, W2, anchor, draft_tokens, draft_stats, temper
 
 
 def verify(target, base, W1, W2, anchor, draft_tokens, draft_probs, draft_stats, verify_len,
-           u_accept, u_final, temperature, ws, out=None, with_probs=True):
-    """dspark_verify.  Returns (out_tokens, accept_len, target_probs or None)."""
+           u_accept, u_final, temperature, ws, out=None, with_probs=True, finish_only=False):
+    """dspark_verify (dspark_verify_finish with finish_only, after verify_stream).
+    Returns (out_tokens, accept_len, target_probs or None)."""
     R, g1, V = target.shape
     g = g1 - 1
     r = W1.shape[1]
@@ -262,8 +269,19 @@ def verify(target, base, W1, W2, anchor, draft_tokens, draft_probs, draft_stats,
             _ptr(al, torch.int32, (R,), "accept_len", dev),
             _ptr(tp, torch.float32, (R, g), "target_probs", dev),
             ws.data_ptr(), ws.numel(), _stream(dev))
-    _check("dspark_verify", load_library().dspark_verify(*args))
+    fn = "dspark_verify_finish" if finish_only else "dspark_verify"
+    _check(fn, getattr(load_library(), fn)(*args))
     return ot, al, tp
+
+
+def verify_stream(target, verify_len, temperature, ws):
+    """dspark_verify_stream: the target-row partials (draft-independent part of verify)."""
+    R, g1, V = target.shape
+    dev = target.device
+    args = (_ptr(target, torch.float32, (R, g1, V), "target", dev),
+            _ptr(verify_len, torch.int32, (R,), "verify_len", dev), R, g1 - 1, V, float(temperature),
+            ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("dspark_verify_stream", load_library().dspark_verify_stream(*args))
 
 
 def draft_rnn(base, W1, W2, Wx, Ws, rnn_bias, anchor, u_draft, temperature, ws, out=None):
@@ -291,8 +309,9 @@ def draft_rnn(base, W1, W2, Wx, Ws, rnn_bias, anchor, u_draft, temperature, ws, 
 
 
 def verify_rnn(target, base, states, W2, draft_tokens, draft_probs, draft_stats, verify_len, u_accept, u_final,
-               temperature, ws, out=None, with_probs=True):
-    """dspark_verify_rnn.  Returns (out_tokens, accept_len, target_probs or None)."""
+               temperature, ws, out=None, with_probs=True, finish_only=False):
+    """dspark_verify_rnn (dspark_verify_rnn_finish with finish_only, after verify_stream).
+    Returns (out_tokens, accept_len, target_probs or None)."""
     R, g1, V = target.shape
     g = g1 - 1
     r = states.shape[2]
@@ -317,7 +336,8 @@ def verify_rnn(target, base, states, W2, draft_tokens, draft_probs, draft_stats,
             _ptr(al, torch.int32, (R,), "accept_len", dev),
             _ptr(tp, torch.float32, (R, g), "target_probs", dev),
             ws.data_ptr(), ws.numel(), _stream(dev))
-    _check("dspark_verify_rnn", load_library().dspark_verify_rnn(*args))
+    fn = "dspark_verify_rnn_finish" if finish_only else "dspark_verify_rnn"
+    _check(fn, getattr(load_library(), fn)(*args))
     return ot, al, tp
 
 
@@ -380,10 +400,12 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
               head="markov"):
     """draft -> schedule -> verify on a dict of device tensors.
 
-    The scheduler reads only confidences and the cost table, so it runs on a
-    side stream concurrently with the draft (forked from and joined back to
-    the current stream; capturable into a HIP graph).  It uses its own small
-    workspace ``ws_sched`` (allocated here if not given).  ``scheduler`` is
+    The scheduler reads only confidences and the cost table, and verify's
+    target-row stream only the target and the verify lengths, so both run on
+    a side stream concurrently with the draft (forked from and joined back to
+    the current stream; capturable into a HIP graph); verify then finishes
+    on the current stream.  The scheduler uses its own small workspace
+    ``ws_sched`` (allocated here if not given).  ``scheduler`` is
     "early" (dspark_schedule), "async" (dspark_schedule_async with the
     lagged confidences ``conf_lag`` of the input dict) or "threshold"
     (dspark_schedule_threshold with ``theta``).  ``head`` "rnn" drafts with
@@ -401,31 +423,33 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
     cur = torch.cuda.current_stream(dev)
     L = n = None
     sched = use_scheduler and d.get("conf") is not None
-    if sched:
-        if ws_sched is None:
-            ws_sched = torch.zeros(256, dtype=torch.uint8, device=dev)
-        side = _side_stream(dev)
-        side.wait_stream(cur)
-        with torch.cuda.stream(side):
+    if sched and ws_sched is None:
+        ws_sched = torch.zeros(256, dtype=torch.uint8, device=dev)
+    # side stream: the scheduler, then the target-row stream of verify (it
+    # needs only the verify lengths), both overlapping the draft
+    side = _side_stream(dev)
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        if sched:
             if scheduler == "async":
                 L, n, _ = schedule_async(d["conf"], d["conf_lag"], d["sps"], ws_sched, with_cum=False)
             elif scheduler == "threshold":
                 L, n, _ = schedule_threshold(d["conf"], theta, ws_sched, with_cum=False)
             else:
                 L, n, _ = schedule(d["conf"], d["sps"], ws_sched, with_cum=False)
+        verify_stream(d["target"], L, temperature, ws)
     states = None
     if head == "rnn":
         tok, prob, stats, states = draft_rnn(d["base"], d["W1"], d["W2"], d["Wx"], d["Ws"], d["rnn_bias"],
                                              d["anchor"], d["u_draft"], temperature, ws)
     else:
         tok, prob, stats = draft(d["base"], d["W1"], d["W2"], d["anchor"], d["u_draft"], temperature, ws)
-    if sched:
-        cur.wait_stream(side)
+    cur.wait_stream(side)
     if head == "rnn":
         ot, al, tp = verify_rnn(d["target"], d["base"], states, d["W2"], tok, prob, stats, L, d["u_accept"],
-                                d["u_final"], temperature, ws)
+                                d["u_final"], temperature, ws, finish_only=True)
     else:
         ot, al, tp = verify(d["target"], d["base"], d["W1"], d["W2"], d["anchor"], tok, prob, stats, L,
-                            d["u_accept"], d["u_final"], temperature, ws)
+                            d["u_accept"], d["u_final"], temperature, ws, finish_only=True)
     return dict(draft_tokens=tok, draft_probs=prob, draft_stats=stats, verify_len=L, n_admitted=n,
                 out_tokens=ot, accept_len=al, target_probs=tp, ws_sched=ws_sched, states=states)

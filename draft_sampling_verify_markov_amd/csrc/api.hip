@@ -22,7 +22,8 @@ int verify_impl(const float* target, const float* base, const void* W1, const vo
                 dspark_wtype w_type, const int32_t* anchor, const int32_t* dtok, const float* dprob,
                 const float* dstats, const int32_t* vlen, const float* u_acc, const float* u_fin,
                 int R, int gamma, int V, int r, float T, int32_t* out_tokens, int32_t* accept_len,
-                float* target_probs, void* ws, hipStream_t stream, bool dense_rows = false);
+                float* target_probs, void* ws, hipStream_t stream, bool dense_rows = false,
+                int part = VERIFY_ALL);
 
 size_t sts_workspace_size_impl(int N, int gamma, int G, int bins);
 int sts_fit_impl(const float* conf, const float* labels, const float* grid, int N, int gamma, int G, int bins,
@@ -208,12 +209,12 @@ int dspark_accept_rates(const float* target, const float* base, const void* W1, 
                            temperature, accept_rate, workspace, stream);
 }
 
-int dspark_verify(const float* target, const float* base, const void* W1, const void* W2,
-                  dspark_wtype w_type, const int32_t* anchor, const int32_t* draft_tokens,
-                  const float* draft_probs, const float* draft_stats, const int32_t* verify_len,
-                  const float* u_accept, const float* u_final, int R, int gamma, int V, int r,
-                  float temperature, int32_t* out_tokens, int32_t* accept_len, float* target_probs,
-                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+static int verify_checked(const float* target, const float* base, const void* W1, const void* W2,
+                          dspark_wtype w_type, const int32_t* anchor, const int32_t* draft_tokens,
+                          const float* draft_probs, const float* draft_stats, const int32_t* verify_len,
+                          const float* u_accept, const float* u_final, int R, int gamma, int V, int r,
+                          float temperature, int32_t* out_tokens, int32_t* accept_len, float* target_probs,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream, int part) {
   if (!sizes_ok(R, gamma, V, r)) return DSPARK_EINVAL;
   if (w_type != DSPARK_W_BF16 && w_type != DSPARK_W_F32) return DSPARK_EINVAL;
   if (!target || !base || !W1 || !W2 || !anchor || !draft_tokens || !draft_probs || !draft_stats ||
@@ -226,7 +227,41 @@ int dspark_verify(const float* target, const float* base, const void* W1, const 
   if (wsr != DSPARK_OK) return wsr;
   return verify_impl(target, base, W1, W2, w_type, anchor, draft_tokens, draft_probs, draft_stats,
                      verify_len, u_accept, u_final, R, gamma, V, r, temperature, out_tokens,
-                     accept_len, target_probs, workspace, stream);
+                     accept_len, target_probs, workspace, stream, false, part);
+}
+
+int dspark_verify(const float* target, const float* base, const void* W1, const void* W2,
+                  dspark_wtype w_type, const int32_t* anchor, const int32_t* draft_tokens,
+                  const float* draft_probs, const float* draft_stats, const int32_t* verify_len,
+                  const float* u_accept, const float* u_final, int R, int gamma, int V, int r,
+                  float temperature, int32_t* out_tokens, int32_t* accept_len, float* target_probs,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return verify_checked(target, base, W1, W2, w_type, anchor, draft_tokens, draft_probs, draft_stats, verify_len,
+                        u_accept, u_final, R, gamma, V, r, temperature, out_tokens, accept_len, target_probs,
+                        workspace, workspace_bytes, stream, VERIFY_ALL);
+}
+
+int dspark_verify_finish(const float* target, const float* base, const void* W1, const void* W2,
+                         dspark_wtype w_type, const int32_t* anchor, const int32_t* draft_tokens,
+                         const float* draft_probs, const float* draft_stats, const int32_t* verify_len,
+                         const float* u_accept, const float* u_final, int R, int gamma, int V, int r,
+                         float temperature, int32_t* out_tokens, int32_t* accept_len, float* target_probs,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return verify_checked(target, base, W1, W2, w_type, anchor, draft_tokens, draft_probs, draft_stats, verify_len,
+                        u_accept, u_final, R, gamma, V, r, temperature, out_tokens, accept_len, target_probs,
+                        workspace, workspace_bytes, stream, VERIFY_FINISH);
+}
+
+int dspark_verify_stream(const float* target, const int32_t* verify_len, int R, int gamma, int V,
+                         float temperature, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!sizes_ok(R, gamma, V, 16)) return DSPARK_EINVAL;
+  if (!target || !aligned16(target)) return DSPARK_EINVAL;
+  if (!(temperature >= 0.f) || __builtin_isinf(temperature)) return DSPARK_EINVAL;
+  const int wsr = check_ws(workspace, workspace_bytes, R, gamma, V);
+  if (wsr != DSPARK_OK) return wsr;
+  return verify_impl(target, nullptr, nullptr, nullptr, DSPARK_W_BF16, nullptr, nullptr, nullptr, nullptr,
+                     verify_len, nullptr, nullptr, R, gamma, V, 16, temperature, nullptr, nullptr, nullptr,
+                     workspace, stream, false, VERIFY_STREAM);
 }
 
 int dspark_draft_rnn(const float* base, const void* W1, const void* W2, const void* Wx, const void* Ws,
@@ -250,12 +285,12 @@ int dspark_draft_rnn(const float* base, const void* W1, const void* W2, const vo
                     draft_probs, draft_stats, workspace, stream, &head);
 }
 
-int dspark_verify_rnn(const float* target, const float* base, const void* states, const void* W2,
-                      dspark_wtype w_type, const int32_t* draft_tokens, const float* draft_probs,
-                      const float* draft_stats, const int32_t* verify_len, const float* u_accept,
-                      const float* u_final, int R, int gamma, int V, int r, float temperature,
-                      int32_t* out_tokens, int32_t* accept_len, float* target_probs, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream) {
+static int verify_rnn_checked(const float* target, const float* base, const void* states, const void* W2,
+                              dspark_wtype w_type, const int32_t* draft_tokens, const float* draft_probs,
+                              const float* draft_stats, const int32_t* verify_len, const float* u_accept,
+                              const float* u_final, int R, int gamma, int V, int r, float temperature,
+                              int32_t* out_tokens, int32_t* accept_len, float* target_probs, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream, int part) {
   if (!sizes_ok(R, gamma, V, r)) return DSPARK_EINVAL;
   if (w_type != DSPARK_W_BF16 && w_type != DSPARK_W_F32) return DSPARK_EINVAL;
   if (!target || !base || !states || !W2 || !draft_tokens || !draft_probs || !draft_stats || !u_accept ||
@@ -268,7 +303,29 @@ int dspark_verify_rnn(const float* target, const float* base, const void* states
   if (wsr != DSPARK_OK) return wsr;
   return verify_impl(target, base, states, W2, w_type, nullptr, draft_tokens, draft_probs, draft_stats,
                      verify_len, u_accept, u_final, R, gamma, V, r, temperature, out_tokens, accept_len,
-                     target_probs, workspace, stream, true);
+                     target_probs, workspace, stream, true, part);
+}
+
+int dspark_verify_rnn(const float* target, const float* base, const void* states, const void* W2,
+                      dspark_wtype w_type, const int32_t* draft_tokens, const float* draft_probs,
+                      const float* draft_stats, const int32_t* verify_len, const float* u_accept,
+                      const float* u_final, int R, int gamma, int V, int r, float temperature,
+                      int32_t* out_tokens, int32_t* accept_len, float* target_probs, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  return verify_rnn_checked(target, base, states, W2, w_type, draft_tokens, draft_probs, draft_stats, verify_len,
+                            u_accept, u_final, R, gamma, V, r, temperature, out_tokens, accept_len, target_probs,
+                            workspace, workspace_bytes, stream, VERIFY_ALL);
+}
+
+int dspark_verify_rnn_finish(const float* target, const float* base, const void* states, const void* W2,
+                             dspark_wtype w_type, const int32_t* draft_tokens, const float* draft_probs,
+                             const float* draft_stats, const int32_t* verify_len, const float* u_accept,
+                             const float* u_final, int R, int gamma, int V, int r, float temperature,
+                             int32_t* out_tokens, int32_t* accept_len, float* target_probs, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  return verify_rnn_checked(target, base, states, W2, w_type, draft_tokens, draft_probs, draft_stats, verify_len,
+                            u_accept, u_final, R, gamma, V, r, temperature, out_tokens, accept_len, target_probs,
+                            workspace, workspace_bytes, stream, VERIFY_FINISH);
 }
 
 static bool sts_sizes_ok(int N, int gamma, int G, int bins) {

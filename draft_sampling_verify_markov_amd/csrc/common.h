@@ -695,13 +695,16 @@ struct RnnHead {
   double* gates;       // workspace [3][R][r]: u, candidate input part, g * s
 };
 
+// Parts of dspark_verify: the target-row stream (independent of the draft)
+// and the rest.
+enum { VERIFY_ALL = 0, VERIFY_STREAM = 1, VERIFY_FINISH = 2 };
+
 struct WsLayout {
   size_t err;      // int32 error word
   size_t trec;     // float4 [R][nt][2]     draft tile records (see select.h)
   size_t rowstat;  // double2[R][gamma+1]   target row (max, sum) or (max, argmax)
   size_t rej;      // int32  [R]            first rejected position (NO_REJECT if none)
   size_t vpart;    // float2 [R][gamma+1][nvt] target 1024-column tile partials
-  size_t tx;       // float  [R][gamma]     target logit at the drafted token
   size_t tp;       // float  [R][gamma]     p_k(x_k) of evaluated positions
   size_t rrec;     // float4 [R][nt][2]     residual tile records
   size_t tvpart;   // float  [R*gamma][nt]  acceptance-label tile sums
@@ -720,7 +723,6 @@ __host__ __device__ inline WsLayout ws_layout(int R, int gamma, int V) {
   L.rowstat = o;  o = ws_align(o + (size_t)R * (gamma + 1) * 16);
   L.rej = o;      o = ws_align(o + (size_t)R * 4);
   L.vpart = o;    o = ws_align(o + (size_t)R * (gamma + 1) * nvt * 8);
-  L.tx = o;       o = ws_align(o + (size_t)R * gamma * 4);
   L.tp = o;       o = ws_align(o + (size_t)R * gamma * 4);
   L.rrec = o;     o = ws_align(o + (size_t)R * nt * 32);
   L.tvpart = o;   o = ws_align(o + (size_t)R * gamma * nt * 4);

@@ -50,7 +50,6 @@ struct VerifyArgs {
   double2* rowstat;
   int32_t* rej;
   float2* vpart;
-  float* tx;
   float* tp;
   float4* rrec;
   float* tvpart;  // [R*gamma][V/256] per-tile sums of max(0, p - q) (acceptance labels)
@@ -100,12 +99,6 @@ __global__ __launch_bounds__(256) void k_verify_stream(VerifyArgs<WT> P) {
   const size_t rowj = (size_t)row * (P.gamma + 1) + jpos;
   const float* trow = P.target + rowj * P.V;
   const bool t_one = (P.T == 1.0f);
-
-  if (tid == 0 && jpos < L) {
-    const int x = P.dtok[(size_t)row * P.gamma + jpos];
-    const int xc = (x < 0 || x >= P.V) ? 0 : x;
-    if (xc / VSEG == seg) P.tx[(size_t)row * P.gamma + jpos] = trow[xc];
-  }
 
   const int tt = seg * 4 + wave, col0 = tt * VTILE;
   if (col0 >= P.V) return;
@@ -195,8 +188,10 @@ __global__ __launch_bounds__(256) void k_verify_decide(VerifyArgs<WT> P) {
       if (lane == 0) {
         P.rowstat[rowj] = make_double2((double)M, Z);
         if (j < L) {
-          checked_token(P.dtok[ev], P.V, P.err);
-          const double p = exp(((double)P.tx[ev] - (double)M) * invTd) / Z;
+          // target logit at the drafted token, read here so that the row
+          // stream does not depend on the draft
+          const int x = checked_token(P.dtok[ev], P.V, P.err);
+          const double p = exp(((double)P.target[rowj * P.V + x] - (double)M) * invTd) / Z;
           const float q = P.dprob[ev];
           bool ok;
           if (!(q > 0.f)) {
@@ -603,8 +598,10 @@ static int launch_accept_rates(const VerifyArgs<WT>& P, float* out, hipStream_t 
   return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
 }
 
+// Target rows 0..L_r of every request: per-1024-column partials.  Reads only
+// target and the verify lengths, so it can run before the draft is known.
 template <typename WT>
-static int launch_verify(const VerifyArgs<WT>& P, hipStream_t stream) {
+static void launch_verify_stream(const VerifyArgs<WT>& P, hipStream_t stream) {
   const int nseg = ceil_div(P.V, VSEG);
   const long long nblk = (long long)(P.gamma + 1) * P.R * nseg;
   const bool greedy = (P.T == 0.f);
@@ -616,6 +613,12 @@ static int launch_verify(const VerifyArgs<WT>& P, hipStream_t stream) {
       hipLaunchKernelGGL((k_verify_stream<WT, false>), dim3((unsigned)nblk), dim3(256), 0, stream, P);
   }
   prof_after(DSPARK_KID_VERIFY_STREAM, stream);
+}
+
+// Accept tests, residual and emission from the stream's partials.
+template <typename WT>
+static int launch_verify_finish(const VerifyArgs<WT>& P, hipStream_t stream) {
+  const bool greedy = (P.T == 0.f);
   prof_before(DSPARK_KID_VERIFY_DECIDE, stream);
   for (int rep = prof_repeat(DSPARK_KID_VERIFY_DECIDE); rep > 0; rep--) {
     if (greedy)
@@ -645,11 +648,19 @@ static int launch_verify(const VerifyArgs<WT>& P, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
 }
 
+template <typename WT>
+static int launch_verify(const VerifyArgs<WT>& P, hipStream_t stream, int part) {
+  if (part != VERIFY_FINISH) launch_verify_stream(P, stream);
+  if (part == VERIFY_STREAM) return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
+  return launch_verify_finish(P, stream);
+}
+
 int verify_impl(const float* target, const float* base, const void* W1, const void* W2,
                 dspark_wtype w_type, const int32_t* anchor, const int32_t* dtok, const float* dprob,
                 const float* dstats, const int32_t* vlen, const float* u_acc, const float* u_fin,
                 int R, int gamma, int V, int r, float T, int32_t* out_tokens, int32_t* accept_len,
-                float* target_probs, void* ws, hipStream_t stream, bool dense_rows = false) {
+                float* target_probs, void* ws, hipStream_t stream, bool dense_rows = false,
+                int part = VERIFY_ALL) {
   const WsLayout Lw = ws_layout(R, gamma, V);
   auto fill = [&](auto& P) {
     P.dense = dense_rows;
@@ -663,7 +674,6 @@ int verify_impl(const float* target, const float* base, const void* W1, const vo
     P.rowstat = ws_ptr<double2>(ws, Lw.rowstat);
     P.rej = ws_ptr<int32_t>(ws, Lw.rej);
     P.vpart = ws_ptr<float2>(ws, Lw.vpart);
-    P.tx = ws_ptr<float>(ws, Lw.tx);
     P.tp = ws_ptr<float>(ws, Lw.tp);
     P.rrec = ws_ptr<float4>(ws, Lw.rrec);
     P.tvpart = ws_ptr<float>(ws, Lw.tvpart);
@@ -674,13 +684,13 @@ int verify_impl(const float* target, const float* base, const void* W1, const vo
     fill(P);
     P.W1 = static_cast<const uint16_t*>(W1);
     P.W2 = static_cast<const uint16_t*>(W2);
-    return launch_verify(P, stream);
+    return launch_verify(P, stream, part);
   }
   VerifyArgs<float> P;
   fill(P);
   P.W1 = static_cast<const float*>(W1);
   P.W2 = static_cast<const float*>(W2);
-  return launch_verify(P, stream);
+  return launch_verify(P, stream, part);
 }
 
 int accept_rates_impl(const float* target, const float* base, const void* W1, const void* W2,
@@ -697,7 +707,6 @@ int accept_rates_impl(const float* target, const float* base, const void* W1, co
     P.T = T; P.invT = 1.0f / T;
     P.rowstat = ws_ptr<double2>(ws, Lw.rowstat);
     P.vpart = ws_ptr<float2>(ws, Lw.vpart);
-    P.tx = ws_ptr<float>(ws, Lw.tx);
     P.tvpart = ws_ptr<float>(ws, Lw.tvpart);
     P.err = ws_ptr<int32_t>(ws, Lw.err);
   };

@@ -46,7 +46,9 @@
  *   - The workspace is caller-allocated device memory of at least
  *     dspark_workspace_size(R, gamma, V, r) bytes, 256-byte aligned, cleared
  *     once with dspark_workspace_init.  Calls on one workspace must be ordered
- *     on one stream; concurrent calls need distinct workspaces.
+ *     on one stream; concurrent calls need distinct workspaces.  One exception:
+ *     dspark_verify_stream may run concurrently with dspark_draft or
+ *     dspark_draft_rnn on the same workspace (they touch disjoint parts of it).
  *
  * Limits (the sizes the kernels are built for): 1 <= gamma <= 16,
  * 16 <= r <= 256 with r % 16 == 0, 8 <= V <= 262144 with V % 8 == 0
@@ -289,6 +291,29 @@ int dspark_profile_arm(int kid, hipEvent_t* starts, hipEvent_t* stops, int n, in
 int dspark_profile_disarm(void);
 
 /*
+ * dspark_verify in two parts, so that the target-row stream can overlap the
+ * draft (it reads only target and the verify lengths).
+ *
+ * dspark_verify_stream: for every request, target rows 0..L_r (L_r from
+ * verify_len, or gamma if NULL) are reduced to per-1024-column softmax (or,
+ * at temperature 0, arg-max) partials kept in the workspace.
+ * dspark_verify_finish: the rest of dspark_verify (row statistics, ordered
+ * accept tests, residual or bonus emission), same arguments and outputs as
+ * dspark_verify.  It must follow a dspark_verify_stream on the same workspace
+ * with the same target, verify_len and temperature, with no other call on
+ * that workspace in between except dspark_draft / dspark_draft_rnn.
+ * dspark_verify = dspark_verify_stream + dspark_verify_finish.
+ */
+int dspark_verify_stream(const float* target, const int32_t* verify_len, int R, int gamma, int V,
+                         float temperature, void* workspace, size_t workspace_bytes, hipStream_t stream);
+int dspark_verify_finish(const float* target, const float* base, const void* W1, const void* W2,
+                         dspark_wtype w_type, const int32_t* anchor, const int32_t* draft_tokens,
+                         const float* draft_probs, const float* draft_stats, const int32_t* verify_len,
+                         const float* u_accept, const float* u_final, int R, int gamma, int V, int r,
+                         float temperature, int32_t* out_tokens, int32_t* accept_len, float* target_probs,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * dspark_draft_rnn - drafting with the RNN head instead of the Markov head
  * ("DSpark: Aceleração da inferência de LLM com speculative decoding",
  * pt.news.hada.io, section "Arquitetura", Semi-Autoregressive Generation, RNN
@@ -330,6 +355,14 @@ int dspark_verify_rnn(const float* target, const float* base, const void* states
                       const float* u_final, int R, int gamma, int V, int r, float temperature,
                       int32_t* out_tokens, int32_t* accept_len, float* target_probs, void* workspace,
                       size_t workspace_bytes, hipStream_t stream);
+/* The second part of dspark_verify_rnn, after dspark_verify_stream (as for
+ * dspark_verify_finish). */
+int dspark_verify_rnn_finish(const float* target, const float* base, const void* states, const void* W2,
+                             dspark_wtype w_type, const int32_t* draft_tokens, const float* draft_probs,
+                             const float* draft_stats, const int32_t* verify_len, const float* u_accept,
+                             const float* u_final, int R, int gamma, int V, int r, float temperature,
+                             int32_t* out_tokens, int32_t* accept_len, float* target_probs, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
 
 /*
  * dspark_sts_fit - sequential temperature scaling of the confidence head

@@ -146,6 +146,22 @@ def test_rnn_entry_points_reject_bad_arguments(lib):
     assert v(*bad) == ENOSPC
 
 
+def test_split_verify_rejects_bad_arguments(lib):
+    need = lib.dspark_workspace_size(4, 4, 512, 16)
+    f = lib.dspark_verify_stream
+    good = [16, None, 4, 4, 512, 1.0, 256, need, None]
+    for i, v in ((0, None), (0, 18), (2, 0), (3, 17), (4, 500), (5, -1.0), (5, float("inf")), (6, None),
+                 (6, 128)):
+        bad = list(good); bad[i] = v
+        assert f(*bad) == EINVAL, i
+    bad = list(good); bad[7] = need - 1
+    assert f(*bad) == ENOSPC
+    assert lib.dspark_verify_finish(None, 16, 16, 16, 0, 16, 16, 16, 16, None, 16, 16, 4, 4, 512, 16, 1.0, 16, 16,
+                                    None, 256, need, None) == EINVAL
+    assert lib.dspark_verify_rnn_finish(16, 16, None, 16, 0, 16, 16, 16, None, 16, 16, 4, 4, 512, 16, 1.0, 16, 16,
+                                        None, 256, need, None) == EINVAL
+
+
 def test_sts_workspace_and_argument_checks(lib):
     sz = lib.dspark_sts_workspace_size
     assert sz(65536, 7, 256, 15) >= 256 + 2 * 8 * 65536 + 7 * 256 * 8 + 64 * 256 * 15 * 8

@@ -412,3 +412,36 @@ def test_graph_replay_matches_eager():
         D.run_round(dd, 1.0, ws, ws_sched=ws_sched)
         torch.cuda.synchronize()
     assert D.device_error(ws) == 0 and D.device_error(ws_sched) == 0
+
+
+@pytest.mark.parametrize("T", [1.0, 0.0])
+def test_split_verify_equals_one_call(T):
+    """dspark_verify_stream + dspark_verify_finish (the overlapped round) give
+    the same bits as dspark_verify, for both heads."""
+    from gen.rnn import make_rnn_weights
+    d = config(1, R=40, gamma=6, V=3000, r=32, w_dtype="bf16")
+    inp = make_inputs(d, seed=12)
+    w = make_rnn_weights(32, "bf16", seed=3)
+    inp.update(Wx=w["Wx"], Ws=w["Ws"], rnn_bias=w["bias"])
+    dd = to_dev(inp)
+    dev = dd["base"].device
+    L = torch.from_numpy(np.random.default_rng(5).integers(0, 7, 40).astype(np.int32)).to(dev)
+    ws = D.new_workspace(40, 6, 3000, 32, dev)
+    tok, prob, st = D.draft(dd["base"], dd["W1"], dd["W2"], dd["anchor"], dd["u_draft"], T, ws)
+    args = (dd["target"], dd["base"], dd["W1"], dd["W2"], dd["anchor"], tok, prob, st, L, dd["u_accept"],
+            dd["u_final"], T, ws)
+    one = [x.clone() for x in D.verify(*args)]
+    D.verify_stream(dd["target"], L, T, ws)
+    two = D.verify(*args, finish_only=True)
+    for a, b in zip(one, two):
+        assert torch.equal(a, b)
+    tok, prob, st, states = D.draft_rnn(dd["base"], dd["W1"], dd["W2"], dd["Wx"], dd["Ws"], dd["rnn_bias"],
+                                        dd["anchor"], dd["u_draft"], T, ws)
+    rargs = (dd["target"], dd["base"], states, dd["W2"], tok, prob, st, L, dd["u_accept"], dd["u_final"], T, ws)
+    one = [x.clone() for x in D.verify_rnn(*rargs)]
+    D.verify_stream(dd["target"], L, T, ws)
+    two = D.verify_rnn(*rargs, finish_only=True)
+    for a, b in zip(one, two):
+        assert torch.equal(a, b)
+    torch.cuda.synchronize()
+    assert D.device_error(ws) == 0

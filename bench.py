@@ -9,8 +9,9 @@ rank r = 256, bf16 factors, fp32 logits, scheduler on, temperature 1.
 The round is captured once into a HIP graph and replayed; W untimed replays,
 then K timed replays between device synchronisations (ms_per_step).  A second
 timed pass of K rounds launches eagerly with the library's launch hook armed:
-HIP events recorded around every launch of the dominant kernel (the per-step
-bias GEMM + softmax partials) on its stream give its average duration.
+HIP events recorded around every launch of the dominant kernel (the one-launch
+draft, or the per-step bias GEMM + softmax partials where that path is taken)
+on its stream give its average duration.
 
 Prints ONE JSON line.  The CPU baseline is the float64 oracle, run in a child
 process on a bounded sample (whole rounds until --cpu-seconds elapse).
@@ -31,9 +32,22 @@ sys.path.insert(0, ROOT)
 METRIC = "draft+verify tokens/s at R=128,γ=7,V=131k; % of MI355X HBM roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
-PROFILE_KERNEL = "k_draft_partials"
-KID_DRAFT_PARTIALS = 1   # dspark_kernel_id of the dominant kernel
-K1_REPEAT = 8            # back-to-back launches per timed event pair
+# Dominant kernel of the draft, by the path dspark_draft takes: the one-launch
+# draft (all gamma steps, W2 read once) where it applies, else the per-step
+# bias GEMM + softmax partials.  dspark_kernel_id values and back-to-back
+# launches per timed event pair.
+KERNELS = {
+    "one-launch": dict(name="k_draft_fused", kid=8, repeat=2,
+                       sources=("draft_sampling_verify_markov_amd/csrc/draft_fused.hip",
+                                "draft_sampling_verify_markov_amd/csrc/common.h",
+                                "draft_sampling_verify_markov_amd/csrc/select.h",
+                                "include/dspark.h")),
+    "per-step": dict(name="k_draft_partials", kid=1, repeat=8,
+                     sources=("draft_sampling_verify_markov_amd/csrc/draft.hip",
+                              "draft_sampling_verify_markov_amd/csrc/common.h",
+                              "draft_sampling_verify_markov_amd/csrc/select.h",
+                              "include/dspark.h")),
+}
 
 
 def parse():
@@ -70,25 +84,17 @@ def cfg_key(s):
     return int(s) if s.isdigit() else s
 
 
-# Sources the draft partials kernel is compiled from (its translation unit and
-# the headers it includes).
-DRAFT_KERNEL_SOURCES = ("draft_sampling_verify_markov_amd/csrc/draft.hip",
-                        "draft_sampling_verify_markov_amd/csrc/common.h",
-                        "draft_sampling_verify_markov_amd/csrc/select.h",
-                        "include/dspark.h")
-
-
-def source_digest():
-    """sha256 of the draft kernel's sources: ties stored counter readings to
-    the kernel they were taken on."""
+def source_digest(sources):
+    """sha256 of a kernel's sources (its translation unit and the headers it
+    includes): ties stored counter readings to the kernel they were taken on."""
     h = hashlib.sha256()
-    for f in DRAFT_KERNEL_SOURCES:
+    for f in sources:
         h.update(f.encode())
         h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic(kernel, workload):
+def stored_traffic(kernel, sources, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None.
 
     The summary is used only if it was taken on the current kernel sources.
@@ -101,7 +107,7 @@ def stored_traffic(kernel, workload):
         if ":" in line and line.strip().startswith("- "):
             k, v = line.strip()[2:].split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_digest") != source_digest():
+    if vals.get("source_digest") != source_digest(sources):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -254,6 +260,23 @@ def gpu_bench(a):
     ref = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in ref.items()}
 
     lib = D.load_library()
+    # which draft path dspark_draft takes on this workload: arm the one-launch
+    # kernel's hook for one eager round and see whether it fired
+    ev_probe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    with torch.cuda.stream(stream):
+        for e in ev_probe:
+            e.record()
+    torch.cuda.synchronize()
+    P1 = ctypes.c_void_p * 1
+    assert lib.dspark_profile_arm(KERNELS["one-launch"]["kid"], P1(ev_probe[0].cuda_event),
+                                  P1(ev_probe[1].cuda_event), 1, 1) == 0
+    with torch.cuda.stream(stream):
+        D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta, head=a.head)
+    torch.cuda.synchronize()
+    path = "one-launch" if lib.dspark_profile_disarm() == 1 else "per-step"
+    K = KERNELS[path]
+    launches_per_round = 1 if path == "one-launch" else g
+
     use_graph = not a.eager
     graph = None
     if use_graph:
@@ -297,11 +320,11 @@ def gpu_bench(a):
         ms_eager = timed(lambda: D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta, head=a.head), a.steps)
 
     # Dominant-kernel duration: HIP events recorded by the library's launch
-    # hook on the kernel's stream, each pair around K1_REPEAT back-to-back
-    # launches of the same draft step (the kernel is idempotent), so the
+    # hook on the kernel's stream, each pair around K["repeat"] back-to-back
+    # launches of the same call (the kernels are idempotent), so the
     # per-launch figure excludes most of the event and dispatch latency.
     n_rounds = min(a.steps, 10)
-    n_prof = g * n_rounds
+    n_prof = launches_per_round * n_rounds
     ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(n_prof)]
     ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(n_prof)]
     with torch.cuda.stream(stream):
@@ -311,14 +334,15 @@ def gpu_bench(a):
     ArrT = ctypes.c_void_p * n_prof
     starts = ArrT(*[e.cuda_event for e in ev_s])
     stops = ArrT(*[e.cuda_event for e in ev_e])
-    status = lib.dspark_profile_arm(KID_DRAFT_PARTIALS, starts, stops, n_prof, K1_REPEAT)
+    status = lib.dspark_profile_arm(K["kid"], starts, stops, n_prof, K["repeat"])
     assert status == 0, f"dspark_profile_arm failed ({status})"
     with torch.cuda.stream(stream):
         for _ in range(n_rounds):
             D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta, head=a.head)
     torch.cuda.synchronize()
     used = lib.dspark_profile_disarm()
-    k1_ms = sum(s.elapsed_time(e) for s, e in zip(ev_s[:used], ev_e[:used])) / max(used, 1) / K1_REPEAT
+    assert used > 0, "the launch hook recorded no launch of the dominant kernel"
+    k1_ms = sum(s.elapsed_time(e) for s, e in zip(ev_s[:used], ev_e[:used])) / used / K["repeat"]
 
     labels = None
     if a.labels and T > 0:
@@ -355,15 +379,20 @@ def gpu_bench(a):
     tokens = int((A + 1).sum())
     b_min, b_sched = algorithmic_bytes(d, tokens, int((L + 1).sum()))
     wb = 2 if d["w_dtype"] == "bf16" else 4
-    k1_bytes = 4 * R * V + wb * r * V          # base slice + W2, one draft step
-    k1_flops = 2 * R * r * V
-    traffic = stored_traffic(PROFILE_KERNEL, f"R{R}_g{g}_V{V}_r{r}")
+    if path == "one-launch":
+        # every base row, W2 once, the gathered W1 rows
+        k1_bytes = 4 * R * g * V + wb * r * V + wb * R * g * r
+        k1_flops = 2 * R * r * V * g
+    else:
+        k1_bytes = 4 * R * V + wb * r * V          # base slice + W2, one draft step
+        k1_flops = 2 * R * r * V
+    traffic = stored_traffic(K["name"], K["sources"], f"R{R}_g{g}_V{V}_r{r}")
     return dict(
         ms=ms, tokens=tokens, A=A, L=L, n_admitted=(int(ref["n_admitted"].cpu()[0])
                                                     if ref["n_admitted"] is not None else None),
         b_min=b_min, b_sched=b_sched, k1_ms=k1_ms, k1_bytes=k1_bytes, k1_flops=k1_flops,
-        traffic=traffic, graph=use_graph, cfg=d, ms_eager=ms_eager, n_k1=used * K1_REPEAT, theta=theta,
-        labels=labels, sts=sts)
+        traffic=traffic, graph=use_graph, cfg=d, ms_eager=ms_eager, n_k1=used * K["repeat"], theta=theta,
+        labels=labels, sts=sts, path=path, kernel=K["name"])
 
 
 # VALU instructions per (sample, candidate) evaluation in the inner loop of
@@ -436,7 +465,7 @@ def main():
                    "R": d["R"], "gamma": d["gamma"], "V": d["V"], "r": d["r"],
                    "temperature": a.temperature, "scheduler": a.scheduler, "head": a.head,
                    **({"theta": gb["theta"]} if gb["theta"] is not None else {}),
-                   "launch": "hip graph" if gb["graph"] else "eager"},
+                   "launch": "hip graph" if gb["graph"] else "eager", "draft_kernel": gb["path"]},
         "ms_per_step_eager": gb["ms_eager"],
         "rounds_per_s": 1e3 / ms,
         "tokens_per_round": gb["tokens"],
@@ -450,13 +479,13 @@ def main():
             "frac_scheduled": gb["b_sched"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         },
         "roofline": {
-            "bound": "hbm", "kernel": PROFILE_KERNEL, "achieved": achieved, "peak": HBM_PEAK_GBS,
+            "bound": "hbm", "kernel": gb["kernel"], "achieved": achieved, "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
             "traffic": gb["traffic"], "launch_us": gb["k1_ms"] * 1e3, "launches_timed": gb["n_k1"],
             "algorithmic_bytes_per_launch": gb["k1_bytes"],
         },
         "mfma": {
-            "kernel": PROFILE_KERNEL,
+            "kernel": gb["kernel"],
             "achieved": gb["k1_flops"] / (gb["k1_ms"] * 1e-3) / 1e12,
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": gb["k1_flops"] / (gb["k1_ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,

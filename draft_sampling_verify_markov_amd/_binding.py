@@ -400,10 +400,12 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
               head="markov"):
     """draft -> schedule -> verify on a dict of device tensors.
 
-    The scheduler reads only confidences and the cost table, and verify's
-    target-row stream only the target and the verify lengths, so both run on
-    a side stream concurrently with the draft (forked from and joined back to
-    the current stream; capturable into a HIP graph); verify then finishes
+    The scheduler reads only confidences and the cost table; it runs first,
+    on the current stream (a single-workgroup kernel that cannot share a
+    compute unit with the one-launch draft).  Verify's target-row stream
+    reads only the target and the verify lengths, so it runs on a side stream
+    concurrently with the draft (forked after the scheduler and joined back
+    to the current stream; capturable into a HIP graph); verify then finishes
     on the current stream.  The scheduler uses its own small workspace
     ``ws_sched`` (allocated here if not given).  ``scheduler`` is
     "early" (dspark_schedule), "async" (dspark_schedule_async with the
@@ -425,18 +427,18 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
     sched = use_scheduler and d.get("conf") is not None
     if sched and ws_sched is None:
         ws_sched = torch.zeros(256, dtype=torch.uint8, device=dev)
-    # side stream: the scheduler, then the target-row stream of verify (it
-    # needs only the verify lengths), both overlapping the draft
+    if sched:
+        if scheduler == "async":
+            L, n, _ = schedule_async(d["conf"], d["conf_lag"], d["sps"], ws_sched, with_cum=False)
+        elif scheduler == "threshold":
+            L, n, _ = schedule_threshold(d["conf"], theta, ws_sched, with_cum=False)
+        else:
+            L, n, _ = schedule(d["conf"], d["sps"], ws_sched, with_cum=False)
+    # side stream: the target-row stream of verify (it needs only the verify
+    # lengths), overlapping the draft
     side = _side_stream(dev)
     side.wait_stream(cur)
     with torch.cuda.stream(side):
-        if sched:
-            if scheduler == "async":
-                L, n, _ = schedule_async(d["conf"], d["conf_lag"], d["sps"], ws_sched, with_cum=False)
-            elif scheduler == "threshold":
-                L, n, _ = schedule_threshold(d["conf"], theta, ws_sched, with_cum=False)
-            else:
-                L, n, _ = schedule(d["conf"], d["sps"], ws_sched, with_cum=False)
         verify_stream(d["target"], L, temperature, ws)
     states = None
     if head == "rnn":

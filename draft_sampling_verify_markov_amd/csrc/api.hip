@@ -92,8 +92,10 @@ size_t dspark_workspace_size(int R, int gamma, int V, int r) {
 
 int dspark_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!workspace || workspace_bytes < 256) return DSPARK_EINVAL;
-  hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, stream, static_cast<int32_t*>(workspace), 64,
-                     0);
+  // error word, counters and the fused draft's sync words
+  const int n = (int)((workspace_bytes < WS_INIT_BYTES ? workspace_bytes : WS_INIT_BYTES) / 4);
+  hipLaunchKernelGGL(k_fill_i32, dim3(ceil_div(n, 256)), dim3(256), 0, stream,
+                     static_cast<int32_t*>(workspace), n, 0);
   return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
 }
 
@@ -112,7 +114,7 @@ int dspark_device_error(void* workspace, size_t workspace_bytes, int32_t* host_b
 }
 
 int dspark_profile_arm(int kid, hipEvent_t* starts, hipEvent_t* stops, int n, int repeat) {
-  if (kid < DSPARK_KID_DRAFT_PARTIALS || kid > DSPARK_KID_VERIFY_FINALIZE || !starts || !stops ||
+  if (kid < DSPARK_KID_DRAFT_PARTIALS || kid > DSPARK_KID_DRAFT_FUSED || !starts || !stops ||
       n < 1 || repeat < 1 || repeat > 1000)
     return DSPARK_EINVAL;
   prof.kid = kid;

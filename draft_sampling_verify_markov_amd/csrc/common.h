@@ -150,6 +150,10 @@ constexpr int AUX_NT = 2;
 // W2 is re-read every draft step: plain (temporal) loads let it stay in the
 // memory-side cache while the streamed logit rows go non-temporal.
 constexpr int AUX_W2 = 0;
+// sc1: device-coherent access.  Stores write through to memory and loads do
+// not hit a copy another XCD's L2 may hold; used for every word that one
+// workgroup writes and another reads within the same launch.
+constexpr int AUX_DEV = 16;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, size_t bytes) {
   const uint32_t n = bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes;
@@ -699,8 +703,23 @@ struct RnnHead {
 // and the rest.
 enum { VERIFY_ALL = 0, VERIFY_STREAM = 1, VERIFY_FINISH = 2 };
 
+// Sync region of the fused draft (at a fixed offset, cleared by
+// dspark_workspace_init): epoch and done counter, one step flag per
+// workgroup, one tagged token word per request.
+constexpr int FUSED_MAX_G = 1024;
+constexpr size_t SYNC_EPOCH = 0;
+constexpr size_t SYNC_DONE = 4;
+constexpr size_t SYNC_FLAGS = 256;
+constexpr size_t SYNC_TOKW = SYNC_FLAGS + 4 * FUSED_MAX_G;
+constexpr size_t SYNC_BYTES = SYNC_TOKW + 8 * 1024;
+// Bytes at the start of a workspace that dspark_workspace_init clears.
+constexpr size_t WS_INIT_BYTES = 256 + SYNC_BYTES;
+// Real-time limit of one fused-draft wait (s_memrealtime runs at 100 MHz).
+constexpr uint64_t FUSED_SPIN_TICKS = 50000000ull;
+
 struct WsLayout {
   size_t err;      // int32 error word
+  size_t sync;     // fused-draft sync words (SYNC_* offsets)
   size_t trec;     // float4 [R][nt][2]     draft tile records (see select.h)
   size_t rowstat;  // double2[R][gamma+1]   target row (max, sum) or (max, argmax)
   size_t rej;      // int32  [R]            first rejected position (NO_REJECT if none)
@@ -719,6 +738,7 @@ __host__ __device__ inline WsLayout ws_layout(int R, int gamma, int V) {
   const size_t nt = (size_t)ceil_div(V, TILE), nvt = (size_t)ceil_div(V, VTILE);
   size_t o = 0;
   L.err = o;      o = ws_align(o + 256);
+  L.sync = o;     o = ws_align(o + SYNC_BYTES);
   L.trec = o;     o = ws_align(o + (size_t)R * nt * 32);
   L.rowstat = o;  o = ws_align(o + (size_t)R * (gamma + 1) * 16);
   L.rej = o;      o = ws_align(o + (size_t)R * 4);

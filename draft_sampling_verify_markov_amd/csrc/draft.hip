@@ -22,6 +22,9 @@
 //        64-column chunk holding u * Z, recomputes that chunk's logits with the
 //        same MFMA instruction sequence and does the in-chunk inverse-CDF
 //        search.
+#include <stdlib.h>
+#include <string.h>
+
 #include <type_traits>
 
 #include "rnn.h"
@@ -315,11 +318,27 @@ __global__ __launch_bounds__(256) void k_draft_select(DraftStep<WT> P) {
   }
 }
 
+bool draft_fused_supported(int R, int gamma, int V, int r, float T);
+int draft_fused_launch(const float* base, const void* W1, const void* W2, const int32_t* anchor,
+                       const float* u_draft, int R, int gamma, int V, int r, float T, int32_t* tokens,
+                       float* probs, float* stats, void* ws, hipStream_t stream);
+
+// DSPARK_DRAFT_KERNEL=stepwise selects the per-step kernels below even where
+// the one-launch draft (draft_fused.hip) applies; both compute the same draw.
+static bool stepwise_requested() {
+  const char* e = getenv("DSPARK_DRAFT_KERNEL");
+  return e != nullptr && strcmp(e, "stepwise") == 0;
+}
+
 template <typename WT>
 static int launch_draft(const float* base, const void* W1, const void* W2, const int32_t* anchor,
                         const float* u_draft, int R, int gamma, int V, int r, float T,
                         int32_t* tokens, float* probs, float* stats, void* ws, hipStream_t stream,
                         const RnnHead* rnn = nullptr) {
+  if (std::is_same<WT, uint16_t>::value && rnn == nullptr && !stepwise_requested() &&
+      draft_fused_supported(R, gamma, V, r, T))
+    return draft_fused_launch(base, W1, W2, anchor, u_draft, R, gamma, V, r, T, tokens, probs, stats, ws,
+                              stream);
   const WsLayout L = ws_layout(R, gamma, V);
   DraftStep<WT> P;
   P.base = base;

@@ -1,0 +1,480 @@
+// Markov-head sequential drafting, all gamma steps in one persistent launch.
+//
+// Source: "DSpark: Aceleração da inferência de LLM com speculative decoding"
+// (pt.news.hada.io), section "Arquitetura": Semi-Autoregressive Generation
+// and the Markov head (the bias of position k is W1[x_{k-1}] . W2, added to the
+// base logits, then x_k is sampled; positions are sequential, requests and
+// vocabulary columns are data-parallel).  Same arithmetic as the per-step
+// kernels in draft.hip; this file changes where the data lives:
+//
+//   * one workgroup per compute unit (all resident at once), each owning the
+//     256-column tiles b and b + G of the vocabulary;
+//   * the W2 fragments of those tiles are loaded into registers once and stay
+//     there for all gamma steps (W2 is read from HBM once per call instead of
+//     once per step);
+//   * per step: bias MFMA + base add + softmax tile records for every request
+//     (as k_draft_partials), then the records are published; the workgroups
+//     b, b + G, ... < R each draw request b's token (as k_draft_select) and
+//     publish it; every workgroup gathers the new tokens' W1 rows and goes on.
+//   * the next step's first base rows are loaded while the draws run.
+//
+// Cross-workgroup exchange.  The eight XCDs of the chip have separate L2
+// caches, so every word another workgroup reads is written and read with the
+// device-coherent cache policy (sc1: written through to memory, read past a
+// possibly stale L2 copy): tile records, the per-workgroup step flags and the
+// tagged token words.  A workgroup stores its flag only after its record
+// stores have completed (s_waitcnt vmcnt(0)), so a reader that sees the flag
+// sees the records.  No fences (an L2 writeback and invalidate per fence) are
+// used.  Tags are epoch + step with a per-workspace epoch that the last
+// workgroup to finish advances by gamma, so nothing needs clearing between
+// calls.  Every wait is bounded by a real-time limit; on expiry the kernel
+// sets DSPARK_DERR_SYNC and all workgroups still run to completion.
+#include "select.h"
+
+namespace dspark {
+
+// Largest request count of the fused launch (tokens of a step held in LDS).
+constexpr int FUSED_MAX_R = 1024;
+
+struct FusedArgs {
+  const float* base;
+  const uint16_t* W1;
+  const uint16_t* W2;
+  const int32_t* anchor;
+  const float* u_draft;
+  int R, gamma, V, r;
+  float T, invT;
+  int32_t* tokens;
+  float* probs;
+  float* stats;
+  float4* trec;  // [R][nt][2] tile records
+  int32_t* err;
+  uint32_t* epoch;
+  uint32_t* done;
+  uint32_t* flags;  // [G]
+  uint64_t* tokw;   // [R] (tag << 32) | token
+  uint64_t spin_ticks;
+};
+
+__device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev64(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_dev64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ bool reached(uint32_t have, uint32_t want) { return (int32_t)(have - want) >= 0; }
+
+// Bias block of one 32-request row block against the wave's 64 columns on a
+// resident operand-form W2 fragment (r == 16 KS): the B operands are read
+// from LDS eight k steps at a time, which keeps the register footprint below
+// what a co-running kernel's wave needs.
+template <int KS>
+__device__ __forceinline__ void mma_resident(const typename BiasBlock<uint16_t>::template Frag<KS>& F,
+                                             const uint16_t* A_rows, int a_stride, f32x16 (&acc)[2]) {
+  constexpr int BATCH = KS < 8 ? KS : 8;
+  const int lane = threadIdx.x & 63, j = lane & 31, h = lane >> 5;
+  const uint16_t* ap = A_rows + j * a_stride + 8 * h;
+#pragma unroll
+  for (int k0 = 0; k0 < KS; k0 += BATCH) {
+    u32x4 bb[BATCH];
+#pragma unroll
+    for (int i = 0; i < BATCH; i++) bb[i] = *reinterpret_cast<const u32x4*>(ap + (k0 + i) * 16);
+#pragma unroll
+    for (int i = 0; i < BATCH; i++) asm volatile("" : "+v"(bb[i]));
+#pragma unroll
+    for (int i = 0; i < BATCH; i++) {
+      const int ks = k0 + i;
+      const bf16x8 b = __builtin_bit_cast(bf16x8, bb[i]);
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, u32x4{F.w[ks][0], F.w[ks][1], F.w[ks][2], F.w[ks][3]});
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, u32x4{F.w[ks][4], F.w[ks][5], F.w[ks][6], F.w[ks][7]});
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b, acc[1], 0, 0, 0);
+    }
+  }
+}
+
+// 480 of the 512 registers per lane: a 32-register wave of a kernel on another
+// stream (verify's target-row stream) still fits beside every wave of this one.
+template <int KS, bool GREEDY>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdgpu_num_vgpr(240))) void k_draft_fused(FusedArgs P) {
+  using WT = uint16_t;
+  using BB = BiasBlock<WT>;
+  constexpr int APAD = BB::APAD;
+  constexpr int CH = RCH;
+  constexpr int GPER = CH * (KS * 16 / 8) / 256;
+  __shared__ __align__(16) WT A_lds[CH * (DSPARK_MAX_RANK + APAD)];
+  __shared__ __align__(16) float X[2][32 * BSTRIDE];
+  __shared__ float red_m[4][CH];
+  __shared__ float red_s[4][CH];
+  __shared__ int red_i[4][CH];
+  __shared__ int s_tok[FUSED_MAX_R];
+  __shared__ BlockSelectSmem sm;
+  __shared__ float w1s[DSPARK_MAX_RANK];
+  __shared__ float part[16][WCOLS];
+  __shared__ float gm[4];
+  __shared__ int gi[4];
+  __shared__ uint32_t s_E;
+  __shared__ int s_ok;
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int j = lane & 31, h = lane >> 5;
+  const int G = gridDim.x, b = blockIdx.x;
+  const int nt = ceil_div(P.V, TILE);
+  const int ntl = (b < nt ? 1 : 0) + (b + G < nt ? 1 : 0);
+  const bool t_one = (P.T == 1.0f);
+  const uint32_t row_bytes = (uint32_t)(P.gamma * P.V) * 4u;
+  const int a_stride = P.r + APAD;
+  const int nch = ceil_div(P.R, CH);
+  const int last_rows = P.R - (nch - 1) * CH;
+  const int nrb_last = ceil_div(last_rows, 32);
+  const int ups = ntl * ((nch - 1) * (CH / 32) + nrb_last);  // units per step
+  const int total = ups * P.gamma;
+  const uint64_t deadline = __builtin_amdgcn_s_memrealtime() + P.spin_ticks;
+
+  if (tid == 0) {
+    s_E = ld_dev(P.epoch);
+    s_ok = 1;
+  }
+  for (int q = tid; q < P.R; q += 256) s_tok[q] = checked_token(P.anchor[q], P.V, P.err);
+
+  // unit q of a step -> (chunk, tile slot, row block)
+  auto decode = [&](int q, int& c, int& ti, int& rb) {
+    const int full = (nch - 1) * ntl * (CH / 32);
+    if (q < full) {
+      c = q / (ntl * (CH / 32));
+      const int rem = q - c * ntl * (CH / 32);
+      ti = rem / (CH / 32);
+      rb = rem - ti * (CH / 32);
+    } else {
+      c = nch - 1;
+      const int rem = q - full;
+      ti = rem / nrb_last;
+      rb = rem - ti * nrb_last;
+    }
+  };
+  // base rows of global unit g (step g / ups) into X[g & 1]
+  auto issue = [&](int g) {
+    if (g >= total) return;
+    const int k = g / ups + 1;
+    int c, ti, rb;
+    decode(g - (k - 1) * ups, c, ti, rb);
+    const int c0 = c * CH, nrows = min(CH, P.R - c0);
+    const size_t first = (size_t)c0 * P.gamma + (k - 1);
+    const rsrc_t brs = make_rsrc(P.base + first * P.V, ((size_t)P.R * P.gamma - first) * P.V * 4);
+    stage_dma(brs, row_bytes, rb, nrows, (b + ti * G) * TILE, X[g & 1]);
+  };
+
+  // resident W2 fragments of this workgroup's tiles, loaded once
+  typename BB::template Frag<KS> F0, F1;
+  if (ntl > 0) BB::template load<KS>(F0, P.W2, P.V, P.r, b * TILE + wave * WCOLS);
+  if (ntl > 1) BB::template load<KS>(F1, P.W2, P.V, P.r, (b + G) * TILE + wave * WCOLS);
+  issue(0);
+  issue(1);
+  if (ntl > 0) BB::template to_operands<KS>(F0);
+  if (ntl > 1) BB::template to_operands<KS>(F1);
+  __syncthreads();
+  const uint32_t E = s_E;
+
+  const float sc = t_one ? LOG2E_F : LOG2E_F * P.invT;
+  const double invTd = t_one ? 1.0 : 1.0 / (double)P.T;
+  const rsrc_t rec_rs = make_rsrc(P.trec, (size_t)P.R * nt * 32);
+  bool ok = true;
+
+  for (int k = 1; k <= P.gamma && ok; k++) {
+    int g = (k - 1) * ups;
+    for (int c = 0; c < nch; c++) {
+      const int c0 = c * CH, nrows = min(CH, P.R - c0), nrb = ceil_div(nrows, 32);
+      __syncthreads();  // the previous chunk is done with A_lds and red_*
+      if (ntl > 0) {
+        W1Gather<WT, GPER> wg;
+        wg.load(P.W1, P.V, P.r, nrows, CH, a_stride, [&](int i) { return s_tok[c0 + i]; });
+        wg.store(A_lds);
+      }
+      for (int ti = 0; ti < ntl; ti++) {
+        const int tile = b + ti * G;
+        const int cbase = tile * TILE + wave * WCOLS;
+        for (int rb = 0; rb < nrb; rb++, g++) {
+          // the next unit's rows were issued during the previous unit unless
+          // this is the chunk's first unit (the W1 gather came after them) or
+          // the step's last unit (nothing of the next step is issued yet)
+          const bool first = (ti == 0 && rb == 0);
+          const bool next_in_step = (g + 1) < k * ups;
+          if (!first && next_in_step)
+            wait_vmcnt<8>();
+          else
+            wait_vmcnt<0>();
+          lds_barrier();
+
+          f32x16 acc[2];
+#pragma unroll
+          for (int p = 0; p < 2; p++)
+#pragma unroll
+            for (int t = 0; t < 16; t++) acc[p][t] = 0.f;
+          if (ti == 0)
+            mma_resident<KS>(F0, A_lds + rb * 32 * a_stride, a_stride, acc);
+          else
+            mma_resident<KS>(F1, A_lds + rb * 32 * a_stride, a_stride, acc);
+
+          const int rl = rb * 32 + j;
+          float bv2[2][16];
+          if ((tile + 1) * TILE <= P.V)
+            stage_read_full(X[g & 1], wave * WCOLS, bv2);
+          else
+            stage_read(X[g & 1], true, P.V, cbase, wave * WCOLS, bv2);
+          if (GREEDY) {
+            float bv = -INFINITY;
+            int bi = 0x7fffffff;
+            bool bad = false;
+#pragma unroll
+            for (int t = 0; t < 16; t++)
+#pragma unroll
+              for (int p = 0; p < 2; p++) {
+                const float z = bv2[p][t] + acc[p][t];
+                bad |= (z != z);
+                if (z > bv) { bv = z; bi = cbase + elem_col(p, t, h); }
+              }
+            if (bad) raise_err(P.err, DSPARK_DERR_NONFINITE);
+            argmax_merge(bv, bi, __shfl_xor(bv, 32), __shfl_xor(bi, 32));
+            if (h == 0) { red_m[wave][rl] = bv; red_i[wave][rl] = bi; }
+          } else {
+            float ml = -INFINITY;
+#pragma unroll
+            for (int p = 0; p < 2; p++)
+#pragma unroll
+              for (int t = 0; t < 16; t++) ml = fmaxf(ml, bv2[p][t] + acc[p][t]);
+            const float mw = fmaxf(ml, __shfl_xor(ml, 32));
+            const float mref = (mw == -INFINITY) ? 0.f : mw;
+            float e[2][16];
+#pragma unroll
+            for (int p = 0; p < 2; p++)
+#pragma unroll
+              for (int t = 0; t < 16; t++) e[p][t] = exp2_scaled((bv2[p][t] - mref) + acc[p][t], sc);
+            const float sl = tree_sum32(e);
+            const float sw = sl + __shfl_xor(sl, 32);
+            if (h == 0) { red_m[wave][rl] = mw; red_s[wave][rl] = sw; }
+          }
+          lds_barrier();  // X[g & 1] is free again; red_* of this unit complete
+          if (g + 2 < k * ups) issue(g + 2);
+        }
+        // tile records of this chunk, one thread per request, device-coherent stores
+        if (tid < nrows) {
+          const int q = tid;
+          const uint32_t roff = (uint32_t)(((size_t)(c0 + q) * nt + tile) * 32);
+          u32x4 w0, w1;
+          if (GREEDY) {
+            float v = red_m[0][q];
+            int i = red_i[0][q];
+#pragma unroll
+            for (int w = 1; w < 4; w++) argmax_merge(v, i, red_m[w][q], red_i[w][q]);
+            w0 = u32x4{__float_as_uint(v), (uint32_t)i, 0u, 0u};
+            w1 = u32x4{0u, 0u, 0u, 0u};
+          } else {
+            const float m0 = red_m[0][q], m1 = red_m[1][q], m2 = red_m[2][q], m3 = red_m[3][q];
+            const float mt = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+            auto rescale = [&](float swv, float mwv) {
+              const float d = t_one ? (mwv - mt) : (mwv - mt) * P.invT;
+              return (mwv == -INFINITY) ? 0.f : swv * exp_acc(d);
+            };
+            const float s0 = rescale(red_s[0][q], m0), s1 = rescale(red_s[1][q], m1);
+            const float s2 = rescale(red_s[2][q], m2), s3 = rescale(red_s[3][q], m3);
+            const float st = (s0 + s1) + (s2 + s3);
+            w0 = u32x4{__float_as_uint(mt), __float_as_uint(st), __float_as_uint(s0), __float_as_uint(s1)};
+            w1 = u32x4{__float_as_uint(s2), __float_as_uint(s3), 0u, 0u};
+            if (is_bad(st) || !(mt == mt) || mt == INFINITY) raise_err(P.err, DSPARK_DERR_NONFINITE);
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(w0, rec_rs, (int)roff, 0, AUX_DEV);
+          __builtin_amdgcn_raw_buffer_store_b128(w1, rec_rs, (int)roff + 16, 0, AUX_DEV);
+        }
+      }
+    }
+
+    // publish: this workgroup's records of step k are in memory
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (tid == 0) st_dev(P.flags + b, E + (uint32_t)k);
+    if (k < P.gamma) {
+      issue(k * ups);
+      issue(k * ups + 1);
+    }
+
+    // draws of the requests this workgroup serves
+    for (int row = b; row < P.R && ok; row += G) {
+      if (row == b) {
+        if (wave == 0) {
+          const uint32_t want = E + (uint32_t)k;
+          bool timed_out = false;
+          while (true) {
+            bool have = true;
+            for (int i = lane; i < G; i += 64) have &= reached(ld_dev(P.flags + i), want);
+            if (__all(have)) break;
+            if (__builtin_amdgcn_s_memrealtime() > deadline) { timed_out = true; break; }
+          }
+          if (timed_out && lane == 0) {
+            s_ok = 0;
+            raise_err(P.err, DSPARK_DERR_SYNC);
+          }
+        }
+        __syncthreads();
+        ok = s_ok != 0;
+        if (!ok) break;
+      }
+      const size_t ev = (size_t)row * P.gamma + (k - 1);
+      const int prev = s_tok[row];
+      const rsrc_t rrs = make_rsrc(P.trec + (size_t)row * nt * 2, (size_t)nt * 32);
+      auto ld_rec = [&](int i) {
+        return __builtin_bit_cast(float4, buf_u32x4<AUX_DEV>(rrs, (uint32_t)i * 16u, 0u));
+      };
+      int x;
+      if (GREEDY) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+        for (int t = tid; t < nt; t += 256) {
+          const float4 r0 = ld_rec(2 * t);
+          argmax_merge(bv, bi, r0.x, __float_as_int(r0.y));
+        }
+        wave_argmax(bv, bi);
+        if (lane == 0) { gm[wave] = bv; gi[wave] = bi; }
+        __syncthreads();
+        if (tid == 0) {
+          for (int w = 1; w < 4; w++) argmax_merge(bv, bi, gm[w], gi[w]);
+          x = bi;
+          if (x < 0 || x >= P.V) x = 0;  // only with non-finite logits (flagged)
+          P.tokens[ev] = x;
+          P.probs[ev] = 1.0f;
+          P.stats[2 * ev] = bv;
+          P.stats[2 * ev + 1] = 1.0f;
+          st_dev64(P.tokw + row, ((uint64_t)(E + (uint32_t)k) << 32) | (uint32_t)x);
+        }
+      } else {
+        for (int i = tid; i < P.r; i += 256) w1s[i] = to_f32(P.W1[(size_t)prev * P.r + i]);
+        const float u = checked_uniform(P.u_draft[ev], P.err);
+        const TilePick S = block_select_tile_ld(ld_rec, nt, true, invTd, (double)u, sm);
+        const int cb = S.t * TILE + S.w * WCOLS;
+        const int col = cb + lane;
+        float bval = 0.f;
+        if (wave == 0) bval = (col < P.V) ? P.base[ev * P.V + col] : -INFINITY;
+        const float bias = chunk_bias<WT, KS>(P.W2, P.V, P.r, cb, w1s, part);
+        if (wave == 0) {
+          const float ec = exp2_scaled((bval - S.mt) + bias, sc);
+          const int cpos = wave_pick64(ec, S.scale, S.rem);
+          const float ex = __shfl(ec, cpos);
+          if (lane == 0) {
+            x = min(cb + cpos, P.V - 1);
+            P.tokens[ev] = x;
+            P.probs[ev] = (float)((double)ex * S.scale / S.Z);
+            P.stats[2 * ev] = S.M;
+            P.stats[2 * ev + 1] = (float)S.Z;
+            if (!(S.Z > 0.0) || is_bad(S.M)) raise_err(P.err, DSPARK_DERR_NONFINITE);
+            st_dev64(P.tokw + row, ((uint64_t)(E + (uint32_t)k) << 32) | (uint32_t)x);
+          }
+        }
+      }
+      __syncthreads();  // select scratch is reused by the next request
+    }
+
+    // tokens x_k of every request, for the next step's W1 gather
+    if (k < P.gamma && ok) {
+      const uint32_t want = E + (uint32_t)k;
+      bool timed_out = false;
+      for (int q = tid; q < P.R; q += 256) {
+        uint64_t v;
+        while (true) {
+          v = ld_dev64(P.tokw + q);
+          if ((uint32_t)(v >> 32) == want) break;
+          if (__builtin_amdgcn_s_memrealtime() > deadline) { timed_out = true; break; }
+        }
+        if (timed_out) break;
+        s_tok[q] = checked_token((int)(uint32_t)v, P.V, P.err);
+      }
+      if (timed_out) {
+        s_ok = 0;
+        raise_err(P.err, DSPARK_DERR_SYNC);
+      }
+      __syncthreads();
+      ok = s_ok != 0;
+    }
+  }
+
+  // no direct-to-LDS load may outlive the workgroup
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t ticket = __hip_atomic_fetch_add(P.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (ticket == (uint32_t)G - 1) {
+      // every workgroup has read the epoch and finished: advance it for the next call
+      st_dev(P.done, 0u);
+      st_dev(P.epoch, E + (uint32_t)P.gamma);
+    }
+  }
+}
+
+// Occupancy check, once per process and device: the fused launch needs one
+// resident workgroup on every compute unit.
+template <int KS, bool GREEDY>
+static bool fused_fits() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_draft_fused<KS, GREEDY>, 256, 0) != hipSuccess)
+    return false;
+  return n >= 1;
+}
+
+template <int KS>
+static bool fused_fits_t(float T) {
+  static const bool f_samp = fused_fits<KS, false>();
+  static const bool f_greedy = fused_fits<KS, true>();
+  return T == 0.f ? f_greedy : f_samp;
+}
+
+bool draft_fused_supported(int R, int gamma, int V, int r, float T) {
+  (void)gamma;
+  const int G = device_cu_count();
+  if (G > FUSED_MAX_G || R > FUSED_MAX_R) return false;
+  if (r != 16 * ks_bucket(r)) return false;  // rank 16, 32, 64, 128 or 256
+  if (ceil_div(V, TILE) > 2 * G) return false;
+  bool fits = false;
+  DSPARK_DISPATCH_KS(r, { fits = fused_fits_t<KS>(T); });
+  return fits;
+}
+
+int draft_fused_launch(const float* base, const void* W1, const void* W2, const int32_t* anchor,
+                       const float* u_draft, int R, int gamma, int V, int r, float T, int32_t* tokens,
+                       float* probs, float* stats, void* ws, hipStream_t stream) {
+  const WsLayout L = ws_layout(R, gamma, V);
+  FusedArgs A;
+  A.base = base;
+  A.W1 = static_cast<const uint16_t*>(W1);
+  A.W2 = static_cast<const uint16_t*>(W2);
+  A.anchor = anchor;
+  A.u_draft = u_draft;
+  A.R = R; A.gamma = gamma; A.V = V; A.r = r;
+  A.T = T;
+  A.invT = (T > 0.f) ? 1.0f / T : 0.f;
+  A.tokens = tokens; A.probs = probs; A.stats = stats;
+  A.trec = ws_ptr<float4>(ws, L.trec);
+  A.err = ws_ptr<int32_t>(ws, L.err);
+  A.epoch = ws_ptr<uint32_t>(ws, L.sync + SYNC_EPOCH);
+  A.done = ws_ptr<uint32_t>(ws, L.sync + SYNC_DONE);
+  A.flags = ws_ptr<uint32_t>(ws, L.sync + SYNC_FLAGS);
+  A.tokw = ws_ptr<uint64_t>(ws, L.sync + SYNC_TOKW);
+  A.spin_ticks = FUSED_SPIN_TICKS;
+  const int G = device_cu_count();
+  prof_before(DSPARK_KID_DRAFT_FUSED, stream);
+  for (int rep = prof_repeat(DSPARK_KID_DRAFT_FUSED); rep > 0; rep--) {
+    DSPARK_DISPATCH_KS(r, {
+      if (T == 0.f)
+        hipLaunchKernelGGL((k_draft_fused<KS, true>), dim3(G), dim3(256), 0, stream, A);
+      else
+        hipLaunchKernelGGL((k_draft_fused<KS, false>), dim3(G), dim3(256), 0, stream, A);
+    });
+  }
+  prof_after(DSPARK_KID_DRAFT_FUSED, stream);
+  return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
+}
+
+}  // namespace dspark

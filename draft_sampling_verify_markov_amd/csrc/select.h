@@ -175,9 +175,11 @@ struct BlockSelectSmem {
   float4 csw;
 };
 
-__device__ __forceinline__ TilePick block_select_tile(const float4* __restrict__ recs, int nt,
-                                                      bool use_shift, double invTd, double u,
-                                                      BlockSelectSmem& sm) {
+// ld(i) returns float4 i of the row's records (2 per tile); the overload
+// below reads them with plain loads.
+template <typename Ld>
+__device__ __forceinline__ TilePick block_select_tile_ld(Ld ld, int nt, bool use_shift, double invTd,
+                                                         double u, BlockSelectSmem& sm) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int per = ceil_div(nt, 256);
   const int t0 = min(nt, tid * per), t1 = min(nt, t0 + per);
@@ -194,7 +196,7 @@ __device__ __forceinline__ TilePick block_select_tile(const float4* __restrict__
     const int t = t0 + i;
     const bool ok = (i < per) && (t < t1);
     const int tc = ok ? t : 0;
-    const float4 r0 = recs[2 * tc], r1 = recs[2 * tc + 1];
+    const float4 r0 = ld(2 * tc), r1 = ld(2 * tc + 1);
     m[i] = ok ? r0.x : -INFINITY;
     s[i] = ok ? r0.y : 0.f;
     sw[i] = ok ? make_float4(r0.z, r0.w, r1.x, r1.y) : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -305,6 +307,12 @@ __device__ __forceinline__ TilePick block_select_tile(const float4* __restrict__
   P.w = wstar;
   P.rem = remw;
   return P;
+}
+
+__device__ __forceinline__ TilePick block_select_tile(const float4* __restrict__ recs, int nt,
+                                                      bool use_shift, double invTd, double u,
+                                                      BlockSelectSmem& sm) {
+  return block_select_tile_ld([&](int i) { return recs[i]; }, nt, use_shift, invTd, u, sm);
 }
 
 // Bias of one 64-column chunk for one request: bias[c] = sum_k w1[k] *

@@ -88,6 +88,9 @@ typedef enum {
                                    label outside [0, 1] (clamped, NaN -> 0) or a
                                    temperature that is not finite and > 0 (never
                                    chosen; dspark_sts_apply leaves c unchanged)  */
+#define DSPARK_DERR_SYNC 128    /* the one-launch draft waited past its time limit
+                                   for another workgroup (not all resident, or
+                                   the GPU shared); its outputs are invalid     */
 
 #define DSPARK_MAX_GAMMA 16
 #define DSPARK_MAX_RANK 256
@@ -284,7 +287,8 @@ typedef enum {
   DSPARK_KID_VERIFY_STREAM = 4,   /* target-row stream (softmax partials)   */
   DSPARK_KID_VERIFY_DECIDE = 5,   /* row statistics + ordered accept tests  */
   DSPARK_KID_RESIDUAL = 6,        /* residual max(0, p - q) partials        */
-  DSPARK_KID_VERIFY_FINALIZE = 7  /* residual / bonus sample and outputs    */
+  DSPARK_KID_VERIFY_FINALIZE = 7, /* residual / bonus sample and outputs    */
+  DSPARK_KID_DRAFT_FUSED = 8      /* all draft steps in one launch          */
 } dspark_kernel_id;
 
 int dspark_profile_arm(int kid, hipEvent_t* starts, hipEvent_t* stops, int n, int repeat);

@@ -71,27 +71,118 @@ __device__ __forceinline__ bool is_bad(float x) { return !(x == x) || __builtin_
 // ---------------------------------------------------------------------------
 // cross-lane helpers (wave64)
 
+// Lane exchange without the LDS unit (a __shfl is a ds_bpermute, with an LDS
+// round trip per call): DPP moves within 16-lane rows and the gfx950
+// permlane swaps between rows.  A butterfly combine takes, in every lane, op
+// of the lane's value and its partner's: quad xor 1, quad xor 2, the mirror
+// lane within 8 and within 16, then the other row of the row pair (xor 16)
+// and the other half of the wave (xor 32).  Both operands of every op are
+// the same two values in both partner lanes, so a commutative op leaves the
+// same bits in all 64 lanes.
+constexpr int DPP_QUAD_XOR1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_SHR = 0x110;    // + n: lane i of a row reads lane i - n
+constexpr int DPP_WAVE_SHR1 = 0x138;  // lane i reads lane i - 1
+constexpr int DPP_ROW_MIRROR = 0x140;
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_BCAST15 = 0x142;  // lane 15 of each row into the next row
+constexpr int DPP_ROW_BCAST31 = 0x143;  // lane 31 into rows 2 and 3
+
+// v of the DPP source lane; lanes without a source (or outside ROW_MASK) get old.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t old, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(0u, __float_as_uint(v)));
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ double dpp_f64(double v) {  // 0.0 where there is no source
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = dpp_u32<CTRL, ROW_MASK>(0u, (uint32_t)b);
+  const uint32_t hi = dpp_u32<CTRL, ROW_MASK>(0u, (uint32_t)(b >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// The values of a lane and of its partner lane ^ 16 (swap16) or ^ 32 (swap32),
+// in an order that depends only on the pair (row-pair low row first).
+struct LanePair {
+  uint32_t a, b;
+};
+__device__ __forceinline__ LanePair swap16(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return LanePair{r[0], r[1]};
+}
+__device__ __forceinline__ LanePair swap32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return LanePair{r[0], r[1]};
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const LanePair p = swap32(__float_as_uint(v));
+  return fmaxf(__uint_as_float(p.a), __uint_as_float(p.b));
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const LanePair p = swap32(__float_as_uint(v));
+  return __uint_as_float(p.a) + __uint_as_float(p.b);
+}
+
+// Commutative butterfly reduction of a float over the wave (all lanes get it).
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = op(v, dpp_f32<DPP_QUAD_XOR1>(v));
+  v = op(v, dpp_f32<DPP_QUAD_XOR2>(v));
+  v = op(v, dpp_f32<DPP_ROW_HALF_MIRROR>(v));
+  v = op(v, dpp_f32<DPP_ROW_MIRROR>(v));
+  const LanePair p = swap16(__float_as_uint(v));
+  v = op(__uint_as_float(p.a), __uint_as_float(p.b));
+  const LanePair q = swap32(__float_as_uint(v));
+  return op(__uint_as_float(q.a), __uint_as_float(q.b));
+}
+template <typename Op>
+__device__ __forceinline__ int wave_reduce_i(int v, Op op) {
+  v = op(v, (int)dpp_u32<DPP_QUAD_XOR1>(0u, (uint32_t)v));
+  v = op(v, (int)dpp_u32<DPP_QUAD_XOR2>(0u, (uint32_t)v));
+  v = op(v, (int)dpp_u32<DPP_ROW_HALF_MIRROR>(0u, (uint32_t)v));
+  v = op(v, (int)dpp_u32<DPP_ROW_MIRROR>(0u, (uint32_t)v));
+  const LanePair p = swap16((uint32_t)v);
+  v = op((int)p.a, (int)p.b);
+  const LanePair q = swap32((uint32_t)v);
+  return op((int)q.a, (int)q.b);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return wave_reduce(v, [](float a, float b) { return a + b; });
 }
 // (value, index) maximum with the lowest index on ties.
 __device__ __forceinline__ void argmax_merge(float& v, int& i, float v2, int i2) {
   if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
 }
+template <int CTRL>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+  const float v2 = dpp_f32<CTRL>(v);
+  const int i2 = (int)dpp_u32<CTRL>(0u, (uint32_t)i);
+  argmax_merge(v, i, v2, i2);
+}
+__device__ __forceinline__ void argmax_pair(float& v, int& i, LanePair pv, LanePair pi) {
+  v = __uint_as_float(pv.a);
+  i = (int)pi.a;
+  argmax_merge(v, i, __uint_as_float(pv.b), (int)pi.b);
+}
+// Lane 0 (and every lane whose values are not NaN) gets the wave's argmax.
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    float v2 = __shfl_xor(v, o);
-    int i2 = __shfl_xor(i, o);
-    argmax_merge(v, i, v2, i2);
-  }
+  argmax_step<DPP_QUAD_XOR1>(v, i);
+  argmax_step<DPP_QUAD_XOR2>(v, i);
+  argmax_step<DPP_ROW_HALF_MIRROR>(v, i);
+  argmax_step<DPP_ROW_MIRROR>(v, i);
+  argmax_pair(v, i, swap16(__float_as_uint(v)), swap16((uint32_t)i));
+  argmax_pair(v, i, swap32(__float_as_uint(v)), swap32((uint32_t)i));
+}
+// argmax with the partner lane ^ 32 only
+__device__ __forceinline__ void argmax_xor32(float& v, int& i) {
+  argmax_pair(v, i, swap32(__float_as_uint(v)), swap32((uint32_t)i));
 }
 
 // Block-wide exclusive scan of one value per thread (blockDim.x == 256):

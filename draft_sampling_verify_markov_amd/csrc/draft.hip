@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             if (z > bv) { bv = z; bi = cbase + elem_col(p, t, h); }
           }
         if (bad) raise_err(P.err, DSPARK_DERR_NONFINITE);
-        argmax_merge(bv, bi, __shfl_xor(bv, 32), __shfl_xor(bi, 32));
+        argmax_xor32(bv, bi);
         if (h == 0) { red_m[wave][rl] = bv; red_i[wave][rl] = bi; }
       } else {
         float ml = -INFINITY;
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int p = 0; p < 2; p++)
 #pragma unroll
           for (int t = 0; t < 16; t++) ml = fmaxf(ml, b[p][t] + acc[p][t]);
-        const float mw = fmaxf(ml, __shfl_xor(ml, 32));
+        const float mw = max_xor32(ml);
         // a wave whose columns are all past V (or all -inf) has mass 0
         const float mref = (mw == -INFINITY) ? 0.f : mw;
         float e[2][16];
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
           for (int t = 0; t < 16; t++) e[p][t] = exp2_scaled((b[p][t] - mref) + acc[p][t], sc);
         const float sl = tree_sum32(e);
-        const float sw = sl + __shfl_xor(sl, 32);
+        const float sw = sum_xor32(sl);
         if (h == 0) { red_m[wave][rl] = mw; red_s[wave][rl] = sw; }
       }
       lds_barrier();  // X[u & 1] is free again; red_* of this unit complete

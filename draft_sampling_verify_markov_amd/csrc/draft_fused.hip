@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
     int g = (k - 1) * ups;
     for (int c = 0; c < nch; c++) {
       const int c0 = c * CH, nrows = min(CH, P.R - c0), nrb = ceil_div(nrows, 32);
-      __syncthreads();  // the previous chunk is done with A_lds and red_*
+      lds_barrier();  // the previous chunk is done with A_lds and red_*
       if (ntl > 0) {
         W1Gather<WT, GPER> wg;
         wg.load(P.W1, P.V, P.r, nrows, CH, a_stride, [&](int i) { return s_tok[c0 + i]; });
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
                 if (z > bv) { bv = z; bi = cbase + elem_col(p, t, h); }
               }
             if (bad) raise_err(P.err, DSPARK_DERR_NONFINITE);
-            argmax_merge(bv, bi, __shfl_xor(bv, 32), __shfl_xor(bi, 32));
+            argmax_xor32(bv, bi);
             if (h == 0) { red_m[wave][rl] = bv; red_i[wave][rl] = bi; }
           } else {
             float ml = -INFINITY;
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
             for (int p = 0; p < 2; p++)
 #pragma unroll
               for (int t = 0; t < 16; t++) ml = fmaxf(ml, bv2[p][t] + acc[p][t]);
-            const float mw = fmaxf(ml, __shfl_xor(ml, 32));
+            const float mw = max_xor32(ml);
             const float mref = (mw == -INFINITY) ? 0.f : mw;
             float e[2][16];
 #pragma unroll
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
 #pragma unroll
               for (int t = 0; t < 16; t++) e[p][t] = exp2_scaled((bv2[p][t] - mref) + acc[p][t], sc);
             const float sl = tree_sum32(e);
-            const float sw = sl + __shfl_xor(sl, 32);
+            const float sw = sum_xor32(sl);
             if (h == 0) { red_m[wave][rl] = mw; red_s[wave][rl] = sw; }
           }
           lds_barrier();  // X[g & 1] is free again; red_* of this unit complete
@@ -298,10 +298,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
     wait_vmcnt<0>();
     __syncthreads();
     if (tid == 0) st_dev(P.flags + b, E + (uint32_t)k);
-    if (k < P.gamma) {
-      issue(k * ups);
-      issue(k * ups + 1);
-    }
 
     // draws of the requests this workgroup serves
     for (int row = b; row < P.R && ok; row += G) {
@@ -378,6 +374,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
       __syncthreads();  // select scratch is reused by the next request
     }
 
+    // the next step's first base rows, issued after the draws: a load that
+    // returns to registers waits for every earlier load of its wave,
+    // direct-to-LDS ones included, and the draws' loads are on the critical
+    // path (the token polls below wait for the slowest draw anyway)
+    if (k < P.gamma) {
+      issue(k * ups);
+      issue(k * ups + 1);
+    }
+
     // tokens x_k of every request, for the next step's W1 gather
     if (k < P.gamma && ok) {
       const uint32_t want = E + (uint32_t)k;
@@ -396,7 +401,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
         s_ok = 0;
         raise_err(P.err, DSPARK_DERR_SYNC);
       }
-      __syncthreads();
+      lds_barrier();
       ok = s_ok != 0;
     }
   }

@@ -29,27 +29,25 @@ struct TilePick {
 };
 
 __device__ __forceinline__ double wave_excl_scan_d(double v, double* incl_out) {
-  const int lane = threadIdx.x & 63;
+  // inclusive scan within 16-lane rows (lanes past a row's start add 0.0),
+  // then rows 1 and 3 add the last lane of rows 0 and 2, rows 2 and 3 add
+  // lane 31; the exclusive value is the inclusive one of the lane before
   double incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  incl += dpp_f64<DPP_ROW_SHR + 1>(incl);
+  incl += dpp_f64<DPP_ROW_SHR + 2>(incl);
+  incl += dpp_f64<DPP_ROW_SHR + 4>(incl);
+  incl += dpp_f64<DPP_ROW_SHR + 8>(incl);
+  incl += dpp_f64<DPP_ROW_BCAST15, 0xA>(incl);
+  incl += dpp_f64<DPP_ROW_BCAST31, 0xC>(incl);
   *incl_out = incl;
-  const double ex = __shfl_up(incl, 1);
-  return lane == 0 ? 0.0 : ex;
+  return dpp_f64<DPP_WAVE_SHR1>(incl);
 }
 
 __device__ __forceinline__ int wave_min_i(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o));
-  return v;
+  return wave_reduce_i(v, [](int a, int b) { return min(a, b); });
 }
 __device__ __forceinline__ int wave_max_i(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o));
-  return v;
+  return wave_reduce_i(v, [](int a, int b) { return max(a, b); });
 }
 
 // recs: the row's records (2 float4 per tile).  use_shift: weights are
@@ -205,7 +203,7 @@ __device__ __forceinline__ TilePick block_select_tile_ld(Ld ld, int nt, bool use
   float M = 0.f;
   const float wm = wave_max(mloc);
   if (lane == 0) sm.wmax[wave] = wm;
-  __syncthreads();
+  lds_barrier();
   if (use_shift) M = fmaxf(fmaxf(sm.wmax[0], sm.wmax[1]), fmaxf(sm.wmax[2], sm.wmax[3]));
   double w[BTPL];
   double loc = 0.0;
@@ -219,7 +217,7 @@ __device__ __forceinline__ TilePick block_select_tile_ld(Ld ld, int nt, bool use
   double incl;
   const double ex = wave_excl_scan_d(loc, &incl);
   if (lane == 63) sm.wsum[wave] = incl;
-  __syncthreads();
+  lds_barrier();
   double base = 0.0;
   for (int q = 0; q < wave; q++) base += sm.wsum[q];
   base += ex;
@@ -227,7 +225,7 @@ __device__ __forceinline__ TilePick block_select_tile_ld(Ld ld, int nt, bool use
   // lands on a tile
   const int owner_last = (nt - 1) / per;
   if (tid == owner_last) sm.Z = base + loc;
-  __syncthreads();
+  lds_barrier();
   const double Z = sm.Z;
   const double target = u * Z;
 
@@ -259,7 +257,7 @@ __device__ __forceinline__ TilePick block_select_tile_ld(Ld ld, int nt, bool use
     sm.found[wave] = fw;
     sm.last[wave] = lw;
   }
-  __syncthreads();
+  lds_barrier();
   const int tmin = min(min(sm.found[0], sm.found[1]), min(sm.found[2], sm.found[3]));
   const int tl = max(max(max(sm.last[0], sm.last[1]), max(sm.last[2], sm.last[3])), 0);
   TilePick P;
@@ -280,7 +278,7 @@ __device__ __forceinline__ TilePick block_select_tile_ld(Ld ld, int nt, bool use
       sm.csw = lsw;
     }
   }
-  __syncthreads();
+  lds_barrier();
   P.rem = sm.rem;
   P.mt = sm.mt;
   const float4 csw = sm.csw;
@@ -354,7 +352,7 @@ __device__ __forceinline__ float chunk_bias(const WT* __restrict__ W2, int V, in
   }
 #pragma unroll
   for (int c = 0; c < CPT; c++) part[q][CPT * cg + c] = acc[c];
-  __syncthreads();
+  lds_barrier();
   if ((tid >> 6) != 0) return 0.f;
   const int lane = tid & 63;
   float bias = part[0][lane];

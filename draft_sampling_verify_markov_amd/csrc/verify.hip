@@ -378,7 +378,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
           for (int i = 0; i < 16; i++) d[p][i] = residual_elem(t[p][i], b[p][i], acc[p][i], Mt, iZt, mq, iZq, sc);
         const float sl = tree_sum32(d);
-        const float sw = sl + __shfl_xor(sl, 32);
+        const float sw = sum_xor32(sl);
         if ((lane >> 5) == 0) red_s[wave][q] = sw;
         lds_barrier();  // Xb / Xt free; red_s of this unit complete
         issue(u + 1);

@@ -31,9 +31,9 @@ int sts_fit_impl(const float* conf, const float* labels, const float* grid, int 
 int sts_apply_impl(const float* conf, const float* tau, int R, int gamma, float* out, void* ws,
                    hipStream_t stream);
 
-__global__ void k_fill_i32(int32_t* p, int n, int32_t v) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = v;
+__global__ void k_fill_i32(int32_t* p, size_t n, int32_t v) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = v;
 }
 
 // Largest element count any kernel indexes with 32-bit products.
@@ -92,9 +92,12 @@ size_t dspark_workspace_size(int R, int gamma, int V, int r) {
 
 int dspark_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!workspace || workspace_bytes < 256) return DSPARK_EINVAL;
-  // error word, counters and the fused draft's sync words
-  const int n = (int)((workspace_bytes < WS_INIT_BYTES ? workspace_bytes : WS_INIT_BYTES) / 4);
-  hipLaunchKernelGGL(k_fill_i32, dim3(ceil_div(n, 256)), dim3(256), 0, stream,
+  // all of it: besides the error word, counters and sync words, the fused
+  // draft's sealed records must not hold seals left by an earlier use of the
+  // memory (a new workspace starts its epoch from zero again)
+  const size_t n = workspace_bytes / 4;
+  const size_t nb = (n + 255) / 256;
+  hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)(nb < 65536 ? nb : 65536)), dim3(256), 0, stream,
                      static_cast<int32_t*>(workspace), n, 0);
   return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
 }
@@ -107,7 +110,7 @@ int dspark_device_error(void* workspace, size_t workspace_bytes, int32_t* host_b
     return DSPARK_EHIP;
   if (hipStreamSynchronize(stream) != hipSuccess) return DSPARK_EHIP;
   *host_bits = v;
-  hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, stream, static_cast<int32_t*>(workspace), 1,
+  hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(64), 0, stream, static_cast<int32_t*>(workspace), (size_t)1,
                      0);
   if (hipGetLastError() != hipSuccess) return DSPARK_EHIP;
   return hipStreamSynchronize(stream) == hipSuccess ? DSPARK_OK : DSPARK_EHIP;

@@ -794,17 +794,15 @@ struct RnnHead {
 // and the rest.
 enum { VERIFY_ALL = 0, VERIFY_STREAM = 1, VERIFY_FINISH = 2 };
 
-// Sync region of the fused draft (at a fixed offset, cleared by
-// dspark_workspace_init): epoch and done counter, one step flag per
-// workgroup, one tagged token word per request.
-constexpr int FUSED_MAX_G = 1024;
+// Sync region of the fused draft (at a fixed offset): epoch and done
+// counter, then one tagged token word per request (up to 1024 requests).
 constexpr size_t SYNC_EPOCH = 0;
 constexpr size_t SYNC_DONE = 4;
-constexpr size_t SYNC_FLAGS = 256;
-constexpr size_t SYNC_TOKW = SYNC_FLAGS + 4 * FUSED_MAX_G;
+constexpr size_t SYNC_TOKW = 256;
 constexpr size_t SYNC_BYTES = SYNC_TOKW + 8 * 1024;
-// Bytes at the start of a workspace that dspark_workspace_init clears.
-constexpr size_t WS_INIT_BYTES = 256 + SYNC_BYTES;
+// Bytes of one sealed tile record of the fused draft: two 16-byte words of
+// three payload dwords and a seal.
+constexpr size_t FREC_BYTES = 32;
 // Real-time limit of one fused-draft wait (s_memrealtime runs at 100 MHz).
 constexpr uint64_t FUSED_SPIN_TICKS = 50000000ull;
 
@@ -819,6 +817,7 @@ struct WsLayout {
   size_t rrec;     // float4 [R][nt][2]     residual tile records
   size_t tvpart;   // float  [R*gamma][nt]  acceptance-label tile sums
   size_t rnn;      // double [3][R][256]   RNN head gate outputs (update, candidate input part, reset * state)
+  size_t frec;     // [R][nt] x FREC_BYTES   sealed tile records of the fused draft
   size_t total;
 };
 
@@ -838,6 +837,7 @@ __host__ __device__ inline WsLayout ws_layout(int R, int gamma, int V) {
   L.rrec = o;     o = ws_align(o + (size_t)R * nt * 32);
   L.tvpart = o;   o = ws_align(o + (size_t)R * gamma * nt * 4);
   L.rnn = o;      o = ws_align(o + (size_t)3 * R * DSPARK_MAX_RANK * 8);
+  L.frec = o;     o = ws_align(o + (size_t)R * nt * FREC_BYTES);
   L.total = o;
   return L;
 }

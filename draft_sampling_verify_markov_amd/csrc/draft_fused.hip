@@ -13,28 +13,35 @@
 //     there for all gamma steps (W2 is read from HBM once per call instead of
 //     once per step);
 //   * per step: bias MFMA + base add + softmax tile records for every request
-//     (as k_draft_partials), then the records are published; the workgroups
-//     b, b + G, ... < R each draw request b's token (as k_draft_select) and
-//     publish it; every workgroup gathers the new tokens' W1 rows and goes on.
-//   * the next step's first base rows are loaded while the draws run.
+//     (as k_draft_partials); the workgroups b, b + G, ... < R each draw
+//     request b's token (as k_draft_select) and publish it; every workgroup
+//     gathers the new tokens' W1 rows and goes on;
+//   * the next step's first base rows are loaded while the token words are
+//     awaited.
 //
 // Cross-workgroup exchange.  The eight XCDs of the chip have separate L2
 // caches, so every word another workgroup reads is written and read with the
 // device-coherent cache policy (sc1: written through to memory, read past a
-// possibly stale L2 copy): tile records, the per-workgroup step flags and the
-// tagged token words.  A workgroup stores its flag only after its record
-// stores have completed (s_waitcnt vmcnt(0)), so a reader that sees the flag
-// sees the records.  No fences (an L2 writeback and invalidate per fence) are
-// used.  Tags are epoch + step with a per-workspace epoch that the last
-// workgroup to finish advances by gamma, so nothing needs clearing between
-// calls.  Every wait is bounded by a real-time limit; on expiry the kernel
-// sets DSPARK_DERR_SYNC and all workgroups still run to completion.
+// possibly stale L2 copy): the tile records and the token words.  Each
+// 16-byte record word carries a seal (the tag epoch + step mixed with its
+// payload) and a token word is (tag << 32) | token, so a reader polls the
+// words themselves until they carry the tag it needs: no flag, no fence (an
+// L2 writeback and invalidate) and no wait for store completion.  The
+// per-workspace epoch is advanced by gamma by the last workgroup to finish,
+// so the tags of one call never match another's and nothing needs clearing
+// between calls (the workspace is cleared once, at init).  Every wait is
+// bounded by a real-time limit; on expiry the kernel sets DSPARK_DERR_SYNC
+// and all workgroups still run to completion.
 #include "select.h"
 
 namespace dspark {
 
 // Largest request count of the fused launch (tokens of a step held in LDS).
 constexpr int FUSED_MAX_R = 1024;
+// Largest tile count (vocabulary <= 512 * 256 columns): a drawing thread
+// polls the records of at most two tiles.
+constexpr int FUSED_MAX_NT = 512;
+constexpr int FUSED_TPL = FUSED_MAX_NT / 256;
 
 struct FusedArgs {
   const float* base;
@@ -47,11 +54,10 @@ struct FusedArgs {
   int32_t* tokens;
   float* probs;
   float* stats;
-  float4* trec;  // [R][nt][2] tile records
+  uint32_t* frec;  // [R][nt] sealed tile records, FREC_BYTES each
   int32_t* err;
   uint32_t* epoch;
   uint32_t* done;
-  uint32_t* flags;  // [G]
   uint64_t* tokw;   // [R] (tag << 32) | token
   uint64_t spin_ticks;
 };
@@ -68,7 +74,16 @@ __device__ __forceinline__ uint64_t ld_dev64(const uint64_t* p) {
 __device__ __forceinline__ void st_dev64(uint64_t* p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ bool reached(uint32_t have, uint32_t want) { return (int32_t)(have - want) >= 0; }
+// Seal of a 16-byte record word: the tag (epoch + step) mixed with the
+// word's three payload dwords.  A reader accepts a word when its fourth dword
+// equals seal(want, payload): a word of another step fails on the tag, and a
+// word read torn between two writes fails on the payload (a false accept needs
+// a 32-bit collision).
+__device__ __forceinline__ uint32_t seal(uint32_t tag, uint32_t a, uint32_t b, uint32_t c) {
+  const uint32_t h = a * 0x9E3779B1u + __builtin_rotateleft32(b, 11) * 0x85EBCA77u +
+                     __builtin_rotateleft32(c, 23) * 0xC2B2AE3Du;
+  return tag ^ h ^ (h >> 15);
+}
 
 // Bias block of one 32-request row block against the wave's 64 columns on a
 // resident operand-form W2 fragment (r == 16 KS): the B operands are read
@@ -183,7 +198,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
 
   const float sc = t_one ? LOG2E_F : LOG2E_F * P.invT;
   const double invTd = t_one ? 1.0 : 1.0 / (double)P.T;
-  const rsrc_t rec_rs = make_rsrc(P.trec, (size_t)P.R * nt * 32);
+  const rsrc_t rec_rs = make_rsrc(P.frec, (size_t)P.R * nt * FREC_BYTES);
   bool ok = true;
 
   for (int k = 1; k <= P.gamma && ok; k++) {
@@ -262,18 +277,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
           lds_barrier();  // X[g & 1] is free again; red_* of this unit complete
           if (g + 2 < k * ups) issue(g + 2);
         }
-        // tile records of this chunk, one thread per request, device-coherent stores
+        // tile records of this chunk, one thread per request: two sealed
+        // 16-byte words, stored device-coherent (written through to memory)
         if (tid < nrows) {
           const int q = tid;
-          const uint32_t roff = (uint32_t)(((size_t)(c0 + q) * nt + tile) * 32);
-          u32x4 w0, w1;
+          const uint32_t tag = E + (uint32_t)k;
+          const uint32_t roff = (uint32_t)(((size_t)(c0 + q) * nt + tile) * FREC_BYTES);
+          uint32_t x0, x1, x2, y0 = 0u, y1 = 0u, y2 = 0u;
           if (GREEDY) {
             float v = red_m[0][q];
             int i = red_i[0][q];
 #pragma unroll
             for (int w = 1; w < 4; w++) argmax_merge(v, i, red_m[w][q], red_i[w][q]);
-            w0 = u32x4{__float_as_uint(v), (uint32_t)i, 0u, 0u};
-            w1 = u32x4{0u, 0u, 0u, 0u};
+            x0 = __float_as_uint(v);
+            x1 = (uint32_t)i;
+            x2 = 0u;
           } else {
             const float m0 = red_m[0][q], m1 = red_m[1][q], m2 = red_m[2][q], m3 = red_m[3][q];
             const float mt = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
@@ -284,56 +302,85 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
             const float s0 = rescale(red_s[0][q], m0), s1 = rescale(red_s[1][q], m1);
             const float s2 = rescale(red_s[2][q], m2), s3 = rescale(red_s[3][q], m3);
             const float st = (s0 + s1) + (s2 + s3);
-            w0 = u32x4{__float_as_uint(mt), __float_as_uint(st), __float_as_uint(s0), __float_as_uint(s1)};
-            w1 = u32x4{__float_as_uint(s2), __float_as_uint(s3), 0u, 0u};
+            x0 = __float_as_uint(mt);
+            x1 = __float_as_uint(st);
+            x2 = __float_as_uint(s0);
+            y0 = __float_as_uint(s1);
+            y1 = __float_as_uint(s2);
+            y2 = __float_as_uint(s3);
             if (is_bad(st) || !(mt == mt) || mt == INFINITY) raise_err(P.err, DSPARK_DERR_NONFINITE);
           }
-          __builtin_amdgcn_raw_buffer_store_b128(w0, rec_rs, (int)roff, 0, AUX_DEV);
-          __builtin_amdgcn_raw_buffer_store_b128(w1, rec_rs, (int)roff + 16, 0, AUX_DEV);
+          __builtin_amdgcn_raw_buffer_store_b128(u32x4{x0, x1, x2, seal(tag, x0, x1, x2)}, rec_rs, (int)roff, 0,
+                                                 AUX_DEV);
+          if (!GREEDY)
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{y0, y1, y2, seal(tag, y0, y1, y2)}, rec_rs,
+                                                   (int)roff + 16, 0, AUX_DEV);
         }
       }
     }
 
-    // publish: this workgroup's records of step k are in memory
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (tid == 0) st_dev(P.flags + b, E + (uint32_t)k);
-
-    // draws of the requests this workgroup serves
+    // draws of the requests this workgroup serves: the request's records from
+    // every workgroup, polled until every word carries this step's seal
     for (int row = b; row < P.R && ok; row += G) {
-      if (row == b) {
-        if (wave == 0) {
-          const uint32_t want = E + (uint32_t)k;
-          bool timed_out = false;
-          while (true) {
-            bool have = true;
-            for (int i = lane; i < G; i += 64) have &= reached(ld_dev(P.flags + i), want);
-            if (__all(have)) break;
-            if (__builtin_amdgcn_s_memrealtime() > deadline) { timed_out = true; break; }
-          }
-          if (timed_out && lane == 0) {
-            s_ok = 0;
-            raise_err(P.err, DSPARK_DERR_SYNC);
-          }
-        }
-        __syncthreads();
-        ok = s_ok != 0;
-        if (!ok) break;
-      }
       const size_t ev = (size_t)row * P.gamma + (k - 1);
       const int prev = s_tok[row];
-      const rsrc_t rrs = make_rsrc(P.trec + (size_t)row * nt * 2, (size_t)nt * 32);
-      auto ld_rec = [&](int i) {
-        return __builtin_bit_cast(float4, buf_u32x4<AUX_DEV>(rrs, (uint32_t)i * 16u, 0u));
-      };
+      const uint32_t want = E + (uint32_t)k;
+      const rsrc_t rrs = make_rsrc(P.frec + (size_t)row * nt * (FREC_BYTES / 4), (size_t)nt * FREC_BYTES);
+      float u = 0.f;
+      if (!GREEDY) {  // independent of the records: in flight with them
+        for (int i = tid; i < P.r; i += 256) w1s[i] = to_f32(P.W1[(size_t)prev * P.r + i]);
+        u = checked_uniform(P.u_draft[ev], P.err);
+      }
+      int t0, t1;
+      block_tile_range(nt, t0, t1);
+      // all words of the thread's tiles are loaded before any is checked (one
+      // memory round trip per poll); a poll that finds a stale word loads
+      // them all again
+      u32x4 wa[FUSED_TPL], wb[FUSED_TPL];
+      bool timed_out = false;
+      while (true) {
+#pragma unroll
+        for (int i = 0; i < FUSED_TPL; i++) {
+          const uint32_t off = (uint32_t)min(t0 + i, nt - 1) * (uint32_t)FREC_BYTES;
+          wa[i] = buf_u32x4<AUX_DEV>(rrs, off, 0u);
+          if (!GREEDY) wb[i] = buf_u32x4<AUX_DEV>(rrs, off + 16u, 0u);
+        }
+        bool have = true;
+#pragma unroll
+        for (int i = 0; i < FUSED_TPL; i++) {
+          if (t0 + i < t1) {
+            have = have && wa[i][3] == seal(want, wa[i][0], wa[i][1], wa[i][2]);
+            if (!GREEDY) have = have && wb[i][3] == seal(want, wb[i][0], wb[i][1], wb[i][2]);
+          }
+        }
+        if (have) break;
+        if (__builtin_amdgcn_s_memrealtime() > deadline) { timed_out = true; break; }
+      }
+      if (timed_out) {
+        s_ok = 0;
+        raise_err(P.err, DSPARK_DERR_SYNC);
+      }
+      float m[FUSED_TPL], s[FUSED_TPL];
+      float4 sw[FUSED_TPL];
+#pragma unroll
+      for (int i = 0; i < FUSED_TPL; i++) {
+        const bool mine = t0 + i < t1;
+        m[i] = mine ? __uint_as_float(wa[i][0]) : -INFINITY;
+        s[i] = mine ? (GREEDY ? __int_as_float((int)wa[i][1]) : __uint_as_float(wa[i][1])) : 0.f;
+        sw[i] = (mine && !GREEDY) ? make_float4(__uint_as_float(wa[i][2]), __uint_as_float(wb[i][0]),
+                                                __uint_as_float(wb[i][1]), __uint_as_float(wb[i][2]))
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+      lds_barrier();  // w1s, s_ok
+      ok = s_ok != 0;
+      if (!ok) break;
       int x;
       if (GREEDY) {
         float bv = -INFINITY;
         int bi = 0x7fffffff;
-        for (int t = tid; t < nt; t += 256) {
-          const float4 r0 = ld_rec(2 * t);
-          argmax_merge(bv, bi, r0.x, __float_as_int(r0.y));
-        }
+#pragma unroll
+        for (int i = 0; i < FUSED_TPL; i++)
+          if (t0 + i < t1) argmax_merge(bv, bi, m[i], __float_as_int(s[i]));
         wave_argmax(bv, bi);
         if (lane == 0) { gm[wave] = bv; gi[wave] = bi; }
         __syncthreads();
@@ -348,9 +395,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
           st_dev64(P.tokw + row, ((uint64_t)(E + (uint32_t)k) << 32) | (uint32_t)x);
         }
       } else {
-        for (int i = tid; i < P.r; i += 256) w1s[i] = to_f32(P.W1[(size_t)prev * P.r + i]);
-        const float u = checked_uniform(P.u_draft[ev], P.err);
-        const TilePick S = block_select_tile_ld(ld_rec, nt, true, invTd, (double)u, sm);
+        const TilePick S = block_select_tile_vals<FUSED_TPL>(m, s, sw, nt, true, invTd, (double)u, sm);
         const int cb = S.t * TILE + S.w * WCOLS;
         const int col = cb + lane;
         float bval = 0.f;
@@ -439,9 +484,9 @@ static bool fused_fits_t(float T) {
 bool draft_fused_supported(int R, int gamma, int V, int r, float T) {
   (void)gamma;
   const int G = device_cu_count();
-  if (G > FUSED_MAX_G || R > FUSED_MAX_R) return false;
+  if (R > FUSED_MAX_R) return false;
   if (r != 16 * ks_bucket(r)) return false;  // rank 16, 32, 64, 128 or 256
-  if (ceil_div(V, TILE) > 2 * G) return false;
+  if (ceil_div(V, TILE) > 2 * G || ceil_div(V, TILE) > FUSED_MAX_NT) return false;
   bool fits = false;
   DSPARK_DISPATCH_KS(r, { fits = fused_fits_t<KS>(T); });
   return fits;
@@ -461,11 +506,10 @@ int draft_fused_launch(const float* base, const void* W1, const void* W2, const 
   A.T = T;
   A.invT = (T > 0.f) ? 1.0f / T : 0.f;
   A.tokens = tokens; A.probs = probs; A.stats = stats;
-  A.trec = ws_ptr<float4>(ws, L.trec);
+  A.frec = ws_ptr<uint32_t>(ws, L.frec);
   A.err = ws_ptr<int32_t>(ws, L.err);
   A.epoch = ws_ptr<uint32_t>(ws, L.sync + SYNC_EPOCH);
   A.done = ws_ptr<uint32_t>(ws, L.sync + SYNC_DONE);
-  A.flags = ws_ptr<uint32_t>(ws, L.sync + SYNC_FLAGS);
   A.tokw = ws_ptr<uint64_t>(ws, L.sync + SYNC_TOKW);
   A.spin_ticks = FUSED_SPIN_TICKS;
   const int G = device_cu_count();

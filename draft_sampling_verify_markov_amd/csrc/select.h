@@ -173,42 +173,41 @@ struct BlockSelectSmem {
   float4 csw;
 };
 
-// ld(i) returns float4 i of the row's records (2 per tile); the overload
-// below reads them with plain loads.
-template <typename Ld>
-__device__ __forceinline__ TilePick block_select_tile_ld(Ld ld, int nt, bool use_shift, double invTd,
-                                                         double u, BlockSelectSmem& sm) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+// Tiles [t0, t1) of thread tid: tid * per, ... with per = ceil(nt / 256).
+__device__ __forceinline__ void block_tile_range(int nt, int& t0, int& t1) {
   const int per = ceil_div(nt, 256);
-  const int t0 = min(nt, tid * per), t1 = min(nt, t0 + per);
+  t0 = min(nt, (int)threadIdx.x * per);
+  t1 = min(nt, t0 + per);
+}
+
+// Selection on records already held by the threads: m[i], s[i] and the four
+// 64-column sums sw[i] of tile t0 + i (t0, t1 from block_tile_range, TPL at
+// least the tiles per thread; entries at or past t1 hold m = -inf, s = 0,
+// sw = 0).  All 256 threads call it.
+template <int TPL>
+__device__ __forceinline__ TilePick block_select_tile_vals(const float (&m)[TPL], const float (&s)[TPL],
+                                                           const float4 (&sw)[TPL], int nt, bool use_shift,
+                                                           double invTd, double u, BlockSelectSmem& sm) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int t0, t1;
+  block_tile_range(nt, t0, t1);
   if (tid == 0) {  // defaults when no tile carries mass (Z = 0, reported by the caller)
     sm.rem = INFINITY;
     sm.mt = 0.f;
     sm.csw = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  float m[BTPL], s[BTPL];
-  float4 sw[BTPL];
   float mloc = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < BTPL; i++) {
-    const int t = t0 + i;
-    const bool ok = (i < per) && (t < t1);
-    const int tc = ok ? t : 0;
-    const float4 r0 = ld(2 * tc), r1 = ld(2 * tc + 1);
-    m[i] = ok ? r0.x : -INFINITY;
-    s[i] = ok ? r0.y : 0.f;
-    sw[i] = ok ? make_float4(r0.z, r0.w, r1.x, r1.y) : make_float4(0.f, 0.f, 0.f, 0.f);
-    mloc = fmaxf(mloc, m[i]);
-  }
+  for (int i = 0; i < TPL; i++) mloc = fmaxf(mloc, m[i]);
   float M = 0.f;
   const float wm = wave_max(mloc);
   if (lane == 0) sm.wmax[wave] = wm;
   lds_barrier();
   if (use_shift) M = fmaxf(fmaxf(sm.wmax[0], sm.wmax[1]), fmaxf(sm.wmax[2], sm.wmax[3]));
-  double w[BTPL];
+  double w[TPL];
   double loc = 0.0;
 #pragma unroll
-  for (int i = 0; i < BTPL; i++) {
+  for (int i = 0; i < TPL; i++) {
     w[i] = 0.0;
     if (t0 + i < t1)
       w[i] = use_shift ? (double)s[i] * (double)exp_acc((m[i] - M) * (float)invTd) : (double)s[i];
@@ -223,7 +222,7 @@ __device__ __forceinline__ TilePick block_select_tile_ld(Ld ld, int nt, bool use
   base += ex;
   // Z is the inclusive prefix at the last tile, so a draw below Z always
   // lands on a tile
-  const int owner_last = (nt - 1) / per;
+  const int owner_last = (nt - 1) / ceil_div(nt, 256);
   if (tid == owner_last) sm.Z = base + loc;
   lds_barrier();
   const double Z = sm.Z;
@@ -234,7 +233,7 @@ __device__ __forceinline__ TilePick block_select_tile_ld(Ld ld, int nt, bool use
   float fm = 0.f, lm = 0.f;
   float4 fsw = make_float4(0.f, 0.f, 0.f, 0.f), lsw = fsw;
 #pragma unroll
-  for (int i = 0; i < BTPL; i++) {
+  for (int i = 0; i < TPL; i++) {
     const int t = t0 + i;
     if (t < t1) {
       const double pp = cum;
@@ -305,6 +304,28 @@ __device__ __forceinline__ TilePick block_select_tile_ld(Ld ld, int nt, bool use
   P.w = wstar;
   P.rem = remw;
   return P;
+}
+
+// ld(i) returns float4 i of the row's records (2 per tile); the overload
+// below reads them with plain loads.
+template <typename Ld>
+__device__ __forceinline__ TilePick block_select_tile_ld(Ld ld, int nt, bool use_shift, double invTd,
+                                                         double u, BlockSelectSmem& sm) {
+  int t0, t1;
+  block_tile_range(nt, t0, t1);
+  float m[BTPL], s[BTPL];
+  float4 sw[BTPL];
+#pragma unroll
+  for (int i = 0; i < BTPL; i++) {
+    const int t = t0 + i;
+    const bool ok = t < t1;
+    const int tc = ok ? t : 0;
+    const float4 r0 = ld(2 * tc), r1 = ld(2 * tc + 1);
+    m[i] = ok ? r0.x : -INFINITY;
+    s[i] = ok ? r0.y : 0.f;
+    sw[i] = ok ? make_float4(r0.z, r0.w, r1.x, r1.y) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  return block_select_tile_vals<BTPL>(m, s, sw, nt, use_shift, invTd, u, sm);
 }
 
 __device__ __forceinline__ TilePick block_select_tile(const float4* __restrict__ recs, int nt,

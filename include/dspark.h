@@ -103,7 +103,9 @@ typedef enum {
  * Returns 0 for sizes outside the limits above. */
 size_t dspark_workspace_size(int R, int gamma, int V, int r);
 
-/* Clear the workspace error word and counters (asynchronous on stream). */
+/* Clear the whole workspace (error word, counters, the one-launch draft's sync
+ * words and sealed records; asynchronous on stream).  Required once before
+ * first use: the one-launch draft's tags are unique only from that clear on. */
 int dspark_workspace_init(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Copy the workspace error word to *host_bits (host pointer), then clear it.

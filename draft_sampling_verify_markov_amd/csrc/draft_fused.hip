@@ -242,6 +242,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
             stage_read_full(X[g & 1], wave * WCOLS, bv2);
           else
             stage_read(X[g & 1], true, P.V, cbase, wave * WCOLS, bv2);
+          // every wave has its base values out of X[g & 1]: refill it with the
+          // rows of unit g + 2 while the MFMA chain runs (the epilogue below
+          // is the first use of acc)
+          lds_barrier();
+          if (g + 2 < k * ups) issue(g + 2);
           if (GREEDY) {
             float bv = -INFINITY;
             int bi = 0x7fffffff;
@@ -274,9 +279,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
             const float sw = sum_xor32(sl);
             if (h == 0) { red_m[wave][rl] = mw; red_s[wave][rl] = sw; }
           }
-          lds_barrier();  // X[g & 1] is free again; red_* of this unit complete
-          if (g + 2 < k * ups) issue(g + 2);
         }
+        lds_barrier();  // red_* of the tile's units complete
         // tile records of this chunk, one thread per request: two sealed
         // 16-byte words, stored device-coherent (written through to memory)
         if (tid < nrows) {

@@ -82,6 +82,7 @@ __device__ __forceinline__ bool is_bad(float x) { return !(x == x) || __builtin_
 constexpr int DPP_QUAD_XOR1 = 0xB1;   // quad_perm [1,0,3,2]
 constexpr int DPP_QUAD_XOR2 = 0x4E;   // quad_perm [2,3,0,1]
 constexpr int DPP_ROW_SHR = 0x110;    // + n: lane i of a row reads lane i - n
+constexpr int DPP_ROW_ROR = 0x120;    // + n: lane i of a row reads lane (i - n) mod 16
 constexpr int DPP_WAVE_SHR1 = 0x138;  // lane i reads lane i - 1
 constexpr int DPP_ROW_MIRROR = 0x140;
 constexpr int DPP_ROW_HALF_MIRROR = 0x141;
@@ -179,6 +180,32 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   argmax_step<DPP_ROW_MIRROR>(v, i);
   argmax_pair(v, i, swap16(__float_as_uint(v)), swap16((uint32_t)i));
   argmax_pair(v, i, swap32(__float_as_uint(v)), swap32((uint32_t)i));
+}
+// Value of lane ^ D for D in {1, 2, 4, 8, 16, 32}.
+template <int D>
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t v) {
+  static_assert(D == 1 || D == 2 || D == 4 || D == 8 || D == 16 || D == 32, "lane distance");
+  const int lane = threadIdx.x & 63;
+  if constexpr (D == 1) {
+    return dpp_u32<DPP_QUAD_XOR1>(0u, v);
+  } else if constexpr (D == 2) {
+    return dpp_u32<DPP_QUAD_XOR2>(0u, v);
+  } else if constexpr (D == 4) {
+    const uint32_t down = dpp_u32<DPP_ROW_ROR + 4>(0u, v), up = dpp_u32<DPP_ROW_ROR + 12>(0u, v);
+    return (lane & 4) ? down : up;
+  } else if constexpr (D == 8) {
+    return dpp_u32<DPP_ROW_ROR + 8>(0u, v);
+  } else if constexpr (D == 16) {
+    const LanePair p = swap16(v);
+    return ((lane >> 4) & 1) ? p.a : p.b;
+  } else {
+    const LanePair p = swap32(v);
+    return (lane >> 5) ? p.a : p.b;
+  }
+}
+template <int D>
+__device__ __forceinline__ uint64_t lane_xor_u64(uint64_t v) {
+  return ((uint64_t)lane_xor_u32<D>((uint32_t)(v >> 32)) << 32) | lane_xor_u32<D>((uint32_t)v);
 }
 // argmax with the partner lane ^ 32 only
 __device__ __forceinline__ void argmax_xor32(float& v, int& i) {

@@ -38,10 +38,6 @@ namespace dspark {
 constexpr int SCHED_THREADS = 1024;
 constexpr int FIX_SHIFT = 36;
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  const uint32_t lo = __shfl_xor((uint32_t)v, m), hi = __shfl_xor((uint32_t)(v >> 32), m);
-  return ((uint64_t)hi << 32) | lo;
-}
 __device__ __forceinline__ long long shfl_up_i64(long long v, int d) {
   const uint64_t u = (uint64_t)v;
   const uint32_t lo = __shfl_up((uint32_t)u, d), hi = __shfl_up((uint32_t)(u >> 32), d);
@@ -58,6 +54,21 @@ struct SchedSmem {
   int wmin[SCHED_THREADS / 64];
   int s_n;
 };
+
+// One bitonic stage at partner distance D < 64 (lane ^ D, DPP and permlane
+// moves) of the merge of size kk; no stage when D >= kk.
+template <int D, int KPT>
+__device__ __forceinline__ void sort_wave_stage(uint64_t (&k)[KPT], int kk) {
+  if (kk <= D) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+#pragma unroll
+  for (int m = 0; m < KPT; m++) {
+    const int i = tid + SCHED_THREADS * m;
+    const uint64_t y = lane_xor_u64<D>(k[m]);
+    const bool up = (i & kk) == 0, lower = (lane & D) == 0;
+    k[m] = (lower == up) ? (k[m] < y ? k[m] : y) : (k[m] > y ? k[m] : y);
+  }
+}
 
 // Steps 1-2 for one confidence array: running products (written to cum_conf
 // when non-NULL), 64-bit keys, bitonic sort.  On return slot t + 1024 m of
@@ -97,7 +108,7 @@ __device__ __forceinline__ void pool_sort(const float* __restrict__ conf, int R,
 
   int nb = 1;  // next exchange buffer (bufs[0] is still being read above)
   for (int kk = 2; kk <= NS; kk <<= 1) {
-    for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+    for (int jj = kk >> 1; jj >= 64; jj >>= 1) {
       if (jj >= NT) {
         const int mj = jj / NT;
 #pragma unroll
@@ -125,16 +136,15 @@ __device__ __forceinline__ void pool_sort(const float* __restrict__ conf, int R,
           const bool up = (i & kk) == 0, lower = i < pi;
           k[m] = (lower == up) ? (k[m] < y ? k[m] : y) : (k[m] > y ? k[m] : y);
         }
-      } else {
-#pragma unroll
-        for (int m = 0; m < KPT; m++) {
-          const int i = tid + NT * m;
-          const uint64_t y = shfl_xor_u64(k[m], jj);
-          const bool up = (i & kk) == 0, lower = (lane & jj) == 0;
-          k[m] = (lower == up) ? (k[m] < y ? k[m] : y) : (k[m] > y ? k[m] : y);
-        }
       }
     }
+    // distances below 64: partners in the same wave
+    sort_wave_stage<32>(k, kk);
+    sort_wave_stage<16>(k, kk);
+    sort_wave_stage<8>(k, kk);
+    sort_wave_stage<4>(k, kk);
+    sort_wave_stage<2>(k, kk);
+    sort_wave_stage<1>(k, kk);
   }
 }
 

@@ -114,6 +114,28 @@ def test_repeated_calls_on_one_workspace(monkeypatch):
             assert np.array_equal(a[key], b[key]), f"call {i}: {key}"
 
 
+def test_new_workspace_over_a_used_one(monkeypatch):
+    """A workspace allocated where an earlier one lived starts its epoch at
+    zero again, so the earlier call's sealed records carry tags the new calls
+    will look for: dspark_workspace_init must clear them.  Two workspaces at
+    the same address, different inputs: each call gives the per-step result."""
+    cfg = config(1, R=64, gamma=3, V=16384, r=128, w_dtype="bf16", table="linear")
+    ptrs = []
+    for i in range(3):
+        ws = D.new_workspace(64, 3, 16384, 128, dev())
+        ptrs.append(ws.data_ptr())
+        inp = make_inputs(cfg, seed=300 + i, seed_u=i)
+        say(f"[reuse {i}] workspace at {ws.data_ptr():#x}")
+        a = _draft(inp, 1.0, "fused", monkeypatch, ws=ws)
+        assert a["fused"] and a["err"] == 0
+        b = _draft(inp, 1.0, "stepwise", monkeypatch)
+        for key in ("tokens", "probs", "stats"):
+            assert np.array_equal(a[key], b[key]), f"workspace {i}: {key}"
+        del ws
+        torch.cuda.synchronize()
+    say(f"[reuse] distinct workspace addresses: {len(set(ptrs))} of {len(ptrs)}")
+
+
 def test_one_launch_draft_in_a_graph(monkeypatch):
     """Captured once, replayed several times with eager work in between: every
     replay gives the eager result."""

@@ -136,6 +136,15 @@ const char* dspark_status_string(int status);
  *   draft_probs   out [R, gamma] fp32  q_k(x_k) (1 for greedy)
  *   draft_stats   out [R, gamma, 2] fp32 (m, Z): m = max_v z_k[v],
  *                 Z = sum_v exp((z_k[v] - m) / T); greedy writes (m, 1)
+ *
+ * Kernels: with bf16 factors, r in {16, 32, 64, 128, 256}, R <= 1024 and
+ * ceil(V / 256) <= min(512, 2 x the compute units), all gamma steps run in one
+ * persistent launch of one workgroup per compute unit; its workgroups wait
+ * for each other's results through the workspace, so every one of them must
+ * be resident at once (checked on the host; a wait that exceeds its time
+ * limit sets DSPARK_DERR_SYNC).  Otherwise, or with the environment variable
+ * DSPARK_DRAFT_KERNEL=stepwise, two kernels per step run.  Both paths give
+ * identical outputs.
  */
 int dspark_draft(const float* base, const void* W1, const void* W2, dspark_wtype w_type,
                  const int32_t* anchor, const float* u_draft, int R, int gamma, int V, int r,

@@ -8,7 +8,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 DSPARK_W_BF16, DSPARK_W_F32 = 0, 1
 STATUS = {0: "DSPARK_OK", -1: "DSPARK_EINVAL", -2: "DSPARK_ENOSPC", -3: "DSPARK_EHIP"}
-DERR_BITS = {1: "NONFINITE", 2: "UNIFORM", 4: "CONF", 8: "TOKEN", 16: "PROB", 32: "LENGTH", 64: "CALIB"}
+DERR_BITS = {1: "NONFINITE", 2: "UNIFORM", 4: "CONF", 8: "TOKEN", 16: "PROB", 32: "LENGTH", 64: "CALIB", 128: "SYNC"}
 
 _lib = None
 

@@ -32,6 +32,8 @@
 // between calls (the workspace is cleared once, at init).  Every wait is
 // bounded by a real-time limit; on expiry the kernel sets DSPARK_DERR_SYNC
 // and all workgroups still run to completion.
+#include <cstdlib>
+
 #include "select.h"
 
 namespace dspark {
@@ -485,6 +487,17 @@ static bool fused_fits_t(float T) {
   return T == 0.f ? f_greedy : f_samp;
 }
 
+// Real-time limit of the kernel's waits: FUSED_SPIN_TICKS, or the value of
+// DSPARK_FUSED_SPIN_TICKS (read on every call; the tests of the time-out path
+// set it to 0, so that every wait that does not succeed at once gives up).
+static uint64_t fused_spin_ticks() {
+  const char* e = getenv("DSPARK_FUSED_SPIN_TICKS");
+  if (e == nullptr || *e == '\0') return FUSED_SPIN_TICKS;
+  char* end = nullptr;
+  const unsigned long long v = strtoull(e, &end, 10);
+  return (end != nullptr && *end == '\0') ? (uint64_t)v : FUSED_SPIN_TICKS;
+}
+
 bool draft_fused_supported(int R, int gamma, int V, int r, float T) {
   (void)gamma;
   const int G = device_cu_count();
@@ -515,7 +528,7 @@ int draft_fused_launch(const float* base, const void* W1, const void* W2, const 
   A.epoch = ws_ptr<uint32_t>(ws, L.sync + SYNC_EPOCH);
   A.done = ws_ptr<uint32_t>(ws, L.sync + SYNC_DONE);
   A.tokw = ws_ptr<uint64_t>(ws, L.sync + SYNC_TOKW);
-  A.spin_ticks = FUSED_SPIN_TICKS;
+  A.spin_ticks = fused_spin_ticks();
   const int G = device_cu_count();
   prof_before(DSPARK_KID_DRAFT_FUSED, stream);
   for (int rep = prof_repeat(DSPARK_KID_DRAFT_FUSED); rep > 0; rep--) {

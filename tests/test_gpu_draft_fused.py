@@ -136,6 +136,28 @@ def test_new_workspace_over_a_used_one(monkeypatch):
     say(f"[reuse] distinct workspace addresses: {len(set(ptrs))} of {len(ptrs)}")
 
 
+def test_wait_time_out_sets_sync_error(monkeypatch):
+    """With a time limit of 0 ticks (DSPARK_FUSED_SPIN_TICKS=0) every wait of
+    the one-launch draft that does not succeed at once gives up: the call must
+    still end, report DSPARK_DERR_SYNC, and leave the workspace usable (the
+    next call, with the normal limit, gives the per-step kernels' result)."""
+    cfg = config(1, R=64, gamma=4, V=65536, r=128, w_dtype="bf16", table="linear")
+    inp = make_inputs(cfg, seed=41)
+    ws = D.new_workspace(64, 4, 65536, 128, dev())
+    monkeypatch.setenv("DSPARK_FUSED_SPIN_TICKS", "0")
+    say("[time-out] draft with a zero time limit")
+    a = _draft(inp, 1.0, "fused", monkeypatch, ws=ws)
+    assert a["fused"]
+    assert a["err"] & 128, f"expected the SYNC error bit, got {a['err']}"
+    monkeypatch.delenv("DSPARK_FUSED_SPIN_TICKS")
+    say("[time-out] the same workspace with the normal limit")
+    a = _draft(inp, 1.0, "fused", monkeypatch, ws=ws)
+    assert a["fused"] and a["err"] == 0
+    b = _draft(inp, 1.0, "stepwise", monkeypatch)
+    for key in ("tokens", "probs", "stats"):
+        assert np.array_equal(a[key], b[key]), key
+
+
 def test_one_launch_draft_in_a_graph(monkeypatch):
     """Captured once, replayed several times with eager work in between: every
     replay gives the eager result."""

@@ -217,8 +217,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
         const int tile = b + ti * G;
         const int cbase = tile * TILE + wave * WCOLS;
         for (int rb = 0; rb < nrb; rb++, g++) {
-          // the next unit's rows were issued during the previous unit unless
-          // this is the chunk's first unit (the W1 gather came after them) or
+          // unit g's rows were issued two units earlier, so the next unit's 8
+          // loads may still be in flight behind them, unless this is the
+          // chunk's first unit (the W1 gather's loads came after its rows) or
           // the step's last unit (nothing of the next step is issued yet)
           const bool first = (ti == 0 && rb == 0);
           const bool next_in_step = (g + 1) < k * ups;
@@ -283,10 +284,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
           }
         }
         lds_barrier();  // red_* of the tile's units complete
-        // tile records of this chunk, one thread per request: two sealed
-        // 16-byte words, stored device-coherent (written through to memory)
-        if (tid < nrows) {
-          const int q = tid;
+        // tile records of this chunk: two sealed 16-byte words per request,
+        // stored device-coherent (written through to memory); the word w of
+        // request q is stored by thread q + 128 w (greedy: one word, by
+        // threads q < nrows), so the stores are spread over the four waves
+        const int nwords = GREEDY ? 1 : 2;
+        if (tid < nwords * CH && (tid & (CH - 1)) < nrows) {
+          const int q = tid & (CH - 1), word = tid / CH;
           const uint32_t tag = E + (uint32_t)k;
           const uint32_t roff = (uint32_t)(((size_t)(c0 + q) * nt + tile) * FREC_BYTES);
           uint32_t x0, x1, x2, y0 = 0u, y1 = 0u, y2 = 0u;
@@ -314,11 +318,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
             y0 = __float_as_uint(s1);
             y1 = __float_as_uint(s2);
             y2 = __float_as_uint(s3);
-            if (is_bad(st) || !(mt == mt) || mt == INFINITY) raise_err(P.err, DSPARK_DERR_NONFINITE);
+            if (word == 0 && (is_bad(st) || !(mt == mt) || mt == INFINITY)) raise_err(P.err, DSPARK_DERR_NONFINITE);
           }
-          __builtin_amdgcn_raw_buffer_store_b128(u32x4{x0, x1, x2, seal(tag, x0, x1, x2)}, rec_rs, (int)roff, 0,
-                                                 AUX_DEV);
-          if (!GREEDY)
+          if (word == 0)
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{x0, x1, x2, seal(tag, x0, x1, x2)}, rec_rs, (int)roff, 0,
+                                                   AUX_DEV);
+          else
             __builtin_amdgcn_raw_buffer_store_b128(u32x4{y0, y1, y2, seal(tag, y0, y1, y2)}, rec_rs,
                                                    (int)roff + 16, 0, AUX_DEV);
         }

@@ -76,6 +76,7 @@ SHAPES = [
     (300, 3, 4096, 128),    # more requests than compute units: two draws per workgroup
     (20, 3, 100000, 32),    # between one and two tiles per workgroup
     (64, 4, 131072, 256),   # two tiles on every workgroup
+    (1024, 2, 4096, 32),    # the largest request count: eight chunks, four draws per workgroup
 ]
 
 
@@ -96,6 +97,23 @@ def test_one_launch_draft_matches_stepwise_and_oracle(R, g, V, r, T, monkeypatch
     for key in ("tokens", "probs", "stats"):
         assert np.array_equal(a[key], b[key]), f"{label}: {key} differ between the two kernels"
     _oracle_check(inp, T, a, label)
+
+
+@pytest.mark.parametrize("R,g,V,r", [
+    (8, 2, 131328, 32),     # 513 tiles: more than the one-launch draft holds
+    (1025, 1, 1024, 32),    # more requests than it holds
+    (16, 3, 4096, 48),      # a rank it has no kernel for
+])
+def test_outside_the_one_launch_limits(R, g, V, r, monkeypatch):
+    """Outside its limits dspark_draft takes the per-step kernels by itself."""
+    cfg = config(1, R=R, gamma=g, V=V, r=r, w_dtype="bf16", table="linear")
+    inp = make_inputs(cfg, seed=500 + R, seed_u=g)
+    label = f"draft {R},{g},{V},{r}"
+    say(f"[{label}] default path")
+    a = _draft(inp, 1.0, "fused", monkeypatch)
+    assert not a["fused"], "the one-launch draft ran outside its limits"
+    assert a["err"] == 0
+    _oracle_check(inp, 1.0, a, label)
 
 
 def test_repeated_calls_on_one_workspace(monkeypatch):

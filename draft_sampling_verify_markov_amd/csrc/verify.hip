@@ -372,6 +372,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         const int qc = q < nrej ? q : 0;
         const float Mt = s_Mt[qc], iZt = s_iZt[qc], mq = s_mq[qc], iZq = s_iZq[qc];
+        // every wave has its rows out of Xb / Xt: the next unit's rows are
+        // loaded while this unit's residual is formed
+        lds_barrier();
+        issue(u + 1);
         float d[2][16];
 #pragma unroll
         for (int p = 0; p < 2; p++)
@@ -380,8 +384,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const float sl = tree_sum32(d);
         const float sw = sum_xor32(sl);
         if ((lane >> 5) == 0) red_s[wave][q] = sw;
-        lds_barrier();  // Xb / Xt free; red_s of this unit complete
-        issue(u + 1);
+        if (rb == nrb - 1) lds_barrier();  // red_s of the tile's units complete
         if (rb == nrb - 1 && tid < nrej) {
           const float s0 = red_s[0][tid], s1 = red_s[1][tid], s2 = red_s[2][tid], s3 = red_s[3][tid];
           if (TVM) {

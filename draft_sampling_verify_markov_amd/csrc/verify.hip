@@ -76,10 +76,20 @@ struct VerifyArgs {
   }
 };
 
+// fp64 butterfly sum over the wave without LDS shuffles (DPP row moves, then
+// the permlane swaps between rows); every lane gets the same bits.
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_f64<DPP_QUAD_XOR1>(v);
+  v += dpp_f64<DPP_QUAD_XOR2>(v);
+  v += dpp_f64<DPP_ROW_HALF_MIRROR>(v);
+  v += dpp_f64<DPP_ROW_MIRROR>(v);
+  auto join = [](uint32_t hi, uint32_t lo) { return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo); };
+  const uint64_t b1 = __builtin_bit_cast(uint64_t, v);
+  const LanePair h1 = swap16((uint32_t)(b1 >> 32)), l1 = swap16((uint32_t)b1);
+  v = join(h1.a, l1.a) + join(h1.b, l1.b);
+  const uint64_t b2 = __builtin_bit_cast(uint64_t, v);
+  const LanePair h2 = swap32((uint32_t)(b2 >> 32)), l2 = swap32((uint32_t)b2);
+  return join(h2.a, l2.a) + join(h2.b, l2.b);
 }
 
 // ---------------------------------------------------------------------------

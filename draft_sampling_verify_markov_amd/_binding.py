@@ -400,13 +400,14 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
               head="markov"):
     """draft -> schedule -> verify on a dict of device tensors.
 
-    The scheduler reads only confidences and the cost table; it runs first,
-    on the current stream (a single-workgroup kernel that cannot share a
-    compute unit with the one-launch draft).  Verify's target-row stream
-    reads only the target and the verify lengths, so it runs on a side stream
-    concurrently with the draft (forked after the scheduler and joined back
+    The scheduler reads only confidences and the cost table, and verify's
+    target-row stream reads only the target and the verify lengths: both run
+    on a side stream concurrently with the draft (forked from and joined back
     to the current stream; capturable into a HIP graph); verify then finishes
-    on the current stream.  The scheduler uses its own small workspace
+    on the current stream.  The early-stop scheduler on a pool of at most
+    1024 candidates is a workgroup small enough to share a compute unit with
+    the one-launch draft; the other schedulers run first on the current
+    stream.  The scheduler uses its own small workspace
     ``ws_sched`` (allocated here if not given).  ``scheduler`` is
     "early" (dspark_schedule), "async" (dspark_schedule_async with the
     lagged confidences ``conf_lag`` of the input dict) or "threshold"
@@ -427,7 +428,16 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
     sched = use_scheduler and d.get("conf") is not None
     if sched and ws_sched is None:
         ws_sched = torch.zeros(256, dtype=torch.uint8, device=dev)
-    if sched:
+    beside = sched and scheduler == "early" and d["conf"].numel() <= 1024
+    side = _side_stream(dev)
+    if beside:
+        # outputs allocated on the current stream, which reads them later
+        out = (torch.empty(d["conf"].shape[0], dtype=torch.int32, device=dev),
+               torch.empty(1, dtype=torch.int32, device=dev), None)
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            L, n, _ = schedule(d["conf"], d["sps"], ws_sched, out=out, with_cum=False)
+    elif sched:
         if scheduler == "async":
             L, n, _ = schedule_async(d["conf"], d["conf_lag"], d["sps"], ws_sched, with_cum=False)
         elif scheduler == "threshold":
@@ -436,7 +446,6 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
             L, n, _ = schedule(d["conf"], d["sps"], ws_sched, with_cum=False)
     # side stream: the target-row stream of verify (it needs only the verify
     # lengths), overlapping the draft
-    side = _side_stream(dev)
     side.wait_stream(cur)
     with torch.cuda.stream(side):
         verify_stream(d["target"], L, temperature, ws)

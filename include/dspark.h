@@ -169,6 +169,11 @@ int dspark_draft(const float* base, const void* W1, const void* W2, dspark_wtype
  *   verify_len   out [R] int32    L_r in [0, gamma]
  *   n_admitted   out [1] int32    n*
  *   cum_conf     out [R, gamma] fp32 a, or NULL
+ *
+ * A pool of at most 1024 candidates is handled by one 256-thread workgroup
+ * (at most 32 registers per lane, about 12 KiB of LDS), small enough to run on
+ * another stream beside a resident one-launch dspark_draft; larger pools by
+ * one 1024-thread workgroup.
  */
 int dspark_schedule(const float* conf, const float* sps, int R, int gamma, int n_table,
                     int32_t* verify_len, int32_t* n_admitted, float* cum_conf, void* workspace,

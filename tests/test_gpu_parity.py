@@ -139,6 +139,26 @@ def test_schedule_bit_exact(seed):
     assert np.array_equal(L, o["verify_len"])
 
 
+# pools of at most 1024 candidates take the 256-thread kernel, larger ones the
+# 1024-thread kernels: both sides of that boundary, with ties
+@pytest.mark.parametrize("R,g", [(1, 1), (93, 11), (64, 16), (128, 8), (205, 5), (1025, 1), (128, 16)])
+def test_schedule_pool_size_boundaries(R, g):
+    rng = np.random.default_rng(R * 31 + g)
+    conf = rng.beta(6, 2, (R, g)).astype(np.float32)
+    conf[rng.random((R, g)) < 0.2] = 1.0
+    conf[rng.random((R, g)) < 0.1] = 0.5
+    N = R * (g + 1) + 7
+    B = np.arange(1, N + 1)
+    sps = (1.0 / (1.0 + 3e-3 * np.ceil(B / 32))).astype(np.float32)
+    L, n, a, err = _gpu_schedule(conf, sps)
+    o = O.schedule(conf, sps)
+    say(f"pool {R}x{g}: n* = {n}")
+    assert err == 0
+    assert np.array_equal(a, o["cum_conf"])
+    assert n == o["n_admitted"]
+    assert np.array_equal(L, o["verify_len"])
+
+
 @pytest.mark.parametrize("cfg", [3, 5])
 def test_schedule_workload_tables(cfg):
     inp = make_inputs(cfg, rows=[0])

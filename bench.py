@@ -6,19 +6,26 @@ one batch of seeded synthetic inputs already resident in HBM.  Default
 workload: R = 128 requests, block gamma = 7, vocabulary V = 131072, Markov
 rank r = 256, bf16 factors, fp32 logits, scheduler on, temperature 1.
 
-The round is captured once into a HIP graph and replayed; W untimed replays,
-then K timed replays between device synchronisations.  K rounds are also timed
-launched eagerly (the kernels on their streams, no graph); ms_per_step is the
-faster of the two launch modes (config.launch names it, both are reported:
-the graph's replay does not always overlap verify's target-row stream with
-the draft as well as eager launches do).  A further timed pass of K rounds
-launches eagerly with the library's launch hook armed:
-HIP events recorded around every launch of the dominant kernel (the one-launch
-draft, or the per-step bias GEMM + softmax partials where that path is taken)
-on its stream give its average duration.
+The round is captured once into a HIP graph.  W untimed replays, then K timed
+replays between device synchronisations ("hot": inputs stay wherever the
+caches leave them); ms_per_step is their total time / K, and an event pair
+around each replay gives the median and the 10th/90th percentiles.  A second
+pass of K replays writes a 512 MiB scratch buffer before each one ("flushed":
+the last-level cache holds none of the round's inputs).  K rounds launched
+eagerly are timed as well.  After every timed block the device error words
+are read and the round's outputs are compared with the first eager round;
+any difference aborts the run.
+
+The dominant kernel (the one-launch draft, or the per-step bias GEMM +
+softmax partials where that path is taken) is timed by HIP events that the
+library's launch hook records around each of its launches, on its own stream,
+inside eager rounds with the scheduler and verify's target-row stream
+running beside it as in the timed rounds.
 
 Prints ONE JSON line.  The CPU baseline is the float64 oracle, run in a child
-process on a bounded sample (whole rounds until --cpu-seconds elapse).
+process on a bounded sample (whole rounds until --cpu-seconds elapse) on all
+host cores and again on one core; the all-core run's last round also gives
+the parity object (its outputs against the GPU round's, request by request).
 """
 
 import argparse
@@ -33,20 +40,25 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+
+def say(msg):
+    """Progress line on stderr (the JSON line alone goes to stdout)."""
+    print(msg, file=sys.stderr, flush=True)
+
 METRIC = "draft+verify tokens/s at R=128,γ=7,V=131k; % of MI355X HBM roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, vendor figure
 # Dominant kernel of the draft, by the path dspark_draft takes: the one-launch
 # draft (all gamma steps, W2 read once) where it applies, else the per-step
-# bias GEMM + softmax partials.  dspark_kernel_id values and back-to-back
-# launches per timed event pair.
+# bias GEMM + softmax partials.  dspark_kernel_id values and launches per
+# timed event pair (one: each launch is timed inside a real round).
 KERNELS = {
-    "one-launch": dict(name="k_draft_fused", kid=8, repeat=2,
+    "one-launch": dict(name="k_draft_fused", kid=8, repeat=1,
                        sources=("draft_sampling_verify_markov_amd/csrc/draft_fused.hip",
                                 "draft_sampling_verify_markov_amd/csrc/common.h",
                                 "draft_sampling_verify_markov_amd/csrc/select.h",
                                 "include/dspark.h")),
-    "per-step": dict(name="k_draft_partials", kid=1, repeat=8,
+    "per-step": dict(name="k_draft_partials", kid=1, repeat=1,
                      sources=("draft_sampling_verify_markov_amd/csrc/draft.hip",
                               "draft_sampling_verify_markov_amd/csrc/common.h",
                               "draft_sampling_verify_markov_amd/csrc/select.h",
@@ -57,8 +69,8 @@ KERNELS = {
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="3", help="workload key (default 3: R=128, gamma=7, V=131072)")
     ap.add_argument("--temperature", type=float, default=1.0)
     ap.add_argument("--scheduler", choices=("early", "async", "threshold"), default="early",
@@ -76,11 +88,18 @@ def parse():
                     help="also time the calibration fit (dspark_sts_fit) on a synthetic held-out set of "
                          "65536 blocks, 256 candidate temperatures, 15 ECE bins")
     ap.add_argument("--eager", action="store_true", help="launch kernels eagerly instead of a graph")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU time budget of the all-core oracle sample (whole rounds; at least one)")
+    ap.add_argument("--cpu-seconds-1core", type=float, default=15.0,
+                    help="CPU time budget of the one-core oracle sample")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="scratch buffer written before each replay of the flushed pass (0: no flushed pass)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after timing, run 3 device-to-device copies of this size (counter calibration)")
     ap.add_argument("--cpu-baseline-worker", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-rows", type=int, default=0, help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-dump", default="", help=argparse.SUPPRESS)
     return ap.parse_args()
 
 
@@ -137,7 +156,11 @@ def cpu_worker(a):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
         print(json.dumps(dict(seconds=dt, threads=threads)))
         return
-    inp = make_inputs(cfg_key(a.config))
+    rows = None
+    R = config(cfg_key(a.config))["R"]
+    if 0 < a.cpu_rows < R:
+        rows = list(range(a.cpu_rows))
+    inp = make_inputs(cfg_key(a.config), rows=rows)
     if a.head == "rnn":
         inp.update(rnn_weights(inp))
     theta = None
@@ -153,7 +176,13 @@ def cpu_worker(a):
             break
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    print(json.dumps(dict(rounds=n, seconds=dt, tokens=toks, threads=threads)))
+    if a.cpu_dump:
+        # the last round's outputs, for the parity object of the bench line
+        import numpy as np
+        np.savez(a.cpu_dump, rows=inp["rows"], draft_tokens=res["draft"]["tokens"],
+                 out_tokens=res["verify"]["out_tokens"], accept_len=res["verify"]["accept_len"],
+                 verify_len=res["verify_len"], flags=res["flags"])
+    print(json.dumps(dict(rounds=n, seconds=dt, tokens=toks, threads=threads, requests=len(inp["rows"]))))
 
 
 def rnn_weights(inp):
@@ -183,22 +212,49 @@ def cpu_sts_baseline(a):
                 sample="one whole fit of the same held-out set (65536 blocks, 256 candidates, 15 bins)")
 
 
-def cpu_baseline(a):
-    ncpu = len(os.sched_getaffinity(0))
+def cpu_baseline(a, one_core=False, dump=""):
+    """The oracle in a child process: all host cores in the affinity set, or
+    one core (BLAS pinned to one thread and the process to one CPU) on the
+    first quarter of the requests when there are 128 or more of them."""
+    cpus = sorted(os.sched_getaffinity(0))
+    ncpu = 1 if one_core else len(cpus)
     env = dict(os.environ)
     for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
-        env.setdefault(k, str(ncpu))
+        env[k] = str(ncpu)
+    R = __import__("gen").config(cfg_key(a.config))["R"]
+    rows = R // 4 if (one_core and R >= 128) else 0
     cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-worker", "--config", a.config,
-           "--cpu-seconds", str(a.cpu_seconds), "--temperature", str(a.temperature),
-           "--scheduler", a.scheduler, "--theta", a.theta, "--head", a.head]
-    out = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=600)
+           "--cpu-seconds", str(a.cpu_seconds_1core if one_core else a.cpu_seconds),
+           "--temperature", str(a.temperature), "--scheduler", a.scheduler, "--theta", a.theta,
+           "--head", a.head, "--cpu-rows", str(rows), "--cpu-dump", dump]
+    pre = (lambda: os.sched_setaffinity(0, {cpus[0]})) if one_core else None
+    out = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=900, preexec_fn=pre)
     if out.returncode != 0:
         return dict(error=out.stderr[-400:])
     r = json.loads(out.stdout.strip().splitlines()[-1])
-    return dict(value=r["tokens"] / r["seconds"], unit="tokens/s", cores=r["threads"], kind="oracle",
-                rounds_per_s=r["rounds"] / r["seconds"],
-                sample=f"{r['rounds']} whole round(s) of the same workload (all requests), "
-                       f"float64 NumPy oracle, {r['seconds']:.1f} s")
+    what = "all requests" if r["requests"] == R else f"the first {r['requests']} of {R} requests"
+    return dict(value=r["tokens"] / r["seconds"], unit="tokens/s", cores=1 if one_core else r["threads"],
+                kind="oracle", rounds_per_s=r["rounds"] / r["seconds"],
+                sample=f"{r['rounds']} round(s) of the same workload ({what}), float64 NumPy oracle, "
+                       f"{r['seconds']:.1f} s")
+
+
+def parity_counts(dump, ref):
+    """Request-by-request comparison of the oracle's round (the all-core CPU
+    baseline's last round) with the GPU round: exact equality of the drafted
+    tokens, verify lengths, accepted lengths and emitted tokens; requests with
+    an event within 1e-6 of a decision boundary are counted as flagged."""
+    import numpy as np
+    z = np.load(dump)
+    rows = z["rows"]
+    same = ((ref["draft_tokens"][rows] == z["draft_tokens"]).all(axis=1)
+            & (ref["out_tokens"][rows] == z["out_tokens"]).all(axis=1)
+            & (ref["accept_len"][rows] == z["accept_len"])
+            & (ref["verify_len"][rows] == z["verify_len"]))
+    fl = z["flags"]
+    return dict(rows=int(len(rows)), flagged=int(fl.sum()), flagged_mismatch=int((~same & fl).sum()),
+                unflagged_mismatch=int((~same & ~fl).sum()),
+                source="the all-core oracle round of cpu_baseline against the GPU round")
 
 
 # ---------------------------------------------------------------------------
@@ -283,51 +339,95 @@ def gpu_bench(a):
 
     use_graph = not a.eager
     graph = None
+    out = None
     if use_graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
             out = D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta, head=a.head)
         torch.cuda.synchronize()
+
+    out_keys = ("draft_tokens", "out_tokens", "accept_len", "verify_len", "n_admitted")
+
+    def check(res, what):
+        """Device error words clear and the round's outputs equal to the first
+        eager round's (the uniforms are fixed, so every round is the same)."""
+        torch.cuda.synchronize()
+        e1, e2 = D.device_error(ws), D.device_error(ws_sched)
+        if e1 != 0 or e2 != 0:
+            raise RuntimeError(f"device error bits after the {what}: workspace {e1:#x}, scheduler {e2:#x}")
+        for k in out_keys:
+            if ref[k] is not None and not torch.equal(res[k], ref[k]):
+                raise RuntimeError(f"the {what} changed {k}")
+
+    def eager_round():
+        return D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta, head=a.head)
+
+    if use_graph:
         # replays must reproduce the eager round exactly, replay after replay
         for _ in range(3):
             graph.replay()
-            torch.cuda.synchronize()
-            for k in ("draft_tokens", "out_tokens", "accept_len", "verify_len"):
-                if ref[k] is not None and not torch.equal(out[k], ref[k]):
-                    raise RuntimeError(f"graph replay differs from the eager round in {k}")
+            check(out, "graph replay")
 
     def one_round():
+        nonlocal out
         if use_graph:
             graph.replay()
         else:
-            D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta, head=a.head)
+            out = eager_round()
 
-    def timed(fn, n):
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
+    def timed(fn, n, flush=None):
+        """n rounds; an event pair around each.  Returns (total ms / n of the
+        back-to-back block, or None with a flush between rounds; per-round ms)."""
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
-            t0.record()
-            for _ in range(n):
+            for i in range(n):
+                if flush is not None:
+                    flush.add_(1)
+                ev[2 * i].record()
                 fn()
-            t1.record()
+                ev[2 * i + 1].record()
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / n
+        per = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n)]
+        total = None if flush is not None else ev[0].elapsed_time(ev[-1]) / n
+        return total, per
 
+    def stats(per):
+        q = np.percentile(np.asarray(per), [10, 50, 90])
+        return dict(n=len(per), median_ms=float(q[1]), p10_ms=float(q[0]), p90_ms=float(q[2]),
+                    mean_ms=float(np.mean(per)))
+
+    say(f"warm-up {a.warmup} + timed {a.steps} rounds ({'graph replays' if use_graph else 'eager'})")
     with torch.cuda.stream(stream):
         for _ in range(a.warmup):
             one_round()
-    ms = timed(one_round, a.steps)
+    ms, per_hot = timed(one_round, a.steps)
+    check(out, "timed rounds")
 
-    # Eager round time (no graph), for reference.
-    with torch.cuda.stream(stream):
-        ms_eager = timed(lambda: D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta, head=a.head), a.steps)
+    flushed = None
+    if a.flush_mib > 0:
+        # the same rounds with a scratch buffer larger than the last-level
+        # cache written before each (outside the event pair)
+        scratch = torch.zeros(a.flush_mib * (1 << 20) // 4, dtype=torch.float32, device=dev)
+        _, per_fl = timed(one_round, a.steps, flush=scratch)
+        check(out, "flushed rounds")
+        flushed = stats(per_fl)
+        del scratch
+
+    # eager launches (no graph), for reference
+    eout = {}
+
+    def eager_timed_round():
+        eout.update(eager_round())
+
+    ms_eager, per_eager = timed(eager_timed_round, a.steps)
+    check(eout, "eager rounds")
 
     # Dominant-kernel duration: HIP events recorded by the library's launch
-    # hook on the kernel's stream, each pair around K["repeat"] back-to-back
-    # launches of the same call (the kernels are idempotent), so the
-    # per-launch figure excludes most of the event and dispatch latency.
-    n_rounds = min(a.steps, 10)
+    # hook around each launch on the kernel's stream, inside eager rounds
+    # (the scheduler and verify's target-row stream run beside it as in the
+    # timed rounds).
+    n_rounds = min(a.steps, 50)
     n_prof = launches_per_round * n_rounds
     ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(n_prof)]
     ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(n_prof)]
@@ -342,11 +442,23 @@ def gpu_bench(a):
     assert status == 0, f"dspark_profile_arm failed ({status})"
     with torch.cuda.stream(stream):
         for _ in range(n_rounds):
-            D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta, head=a.head)
+            eout.update(eager_round())
     torch.cuda.synchronize()
     used = lib.dspark_profile_disarm()
     assert used > 0, "the launch hook recorded no launch of the dominant kernel"
-    k1_ms = sum(s.elapsed_time(e) for s, e in zip(ev_s[:used], ev_e[:used])) / used / K["repeat"]
+    check(eout, "profiled rounds")
+    k1_each = [s_.elapsed_time(e_) / K["repeat"] for s_, e_ in zip(ev_s[:used], ev_e[:used])]
+    k1_ms = sum(k1_each) / used
+
+    # device-to-device copy bandwidth (context for the vendor peak): read and
+    # write of a 1 GiB buffer
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    _, per_cp = timed(lambda: dst.copy_(src), 10)
+    d2d_GBs = 2 * nbytes / (float(np.median(per_cp)) * 1e-3) / 1e9
+    del src, dst
 
     labels = None
     if a.labels and T > 0:
@@ -355,7 +467,7 @@ def gpu_bench(a):
         with torch.cuda.stream(stream):
             D.accept_rates(dd["target"], dd["base"], dd["W1"], dd["W2"], dd["anchor"], ref["draft_tokens"],
                            ref["draft_stats"], T, ws, out=lab_out)
-            lab_ms = timed(lambda: D.accept_rates(dd["target"], dd["base"], dd["W1"], dd["W2"], dd["anchor"],
+            lab_ms, _ = timed(lambda: D.accept_rates(dd["target"], dd["base"], dd["W1"], dd["W2"], dd["anchor"],
                                                   ref["draft_tokens"], ref["draft_stats"], T, ws, out=lab_out),
                            max(a.steps // 2, 3))
         wb_ = 2 if d["w_dtype"] == "bf16" else 4
@@ -396,7 +508,9 @@ def gpu_bench(a):
                                                     if ref["n_admitted"] is not None else None),
         b_min=b_min, b_sched=b_sched, k1_ms=k1_ms, k1_bytes=k1_bytes, k1_flops=k1_flops,
         traffic=traffic, graph=use_graph, cfg=d, ms_eager=ms_eager, n_k1=used * K["repeat"], theta=theta,
-        labels=labels, sts=sts, path=path, kernel=K["name"])
+        labels=labels, sts=sts, path=path, kernel=K["name"], hot=stats(per_hot), flushed=flushed,
+        eager=stats(per_eager), k1=stats(k1_each), d2d_GBs=d2d_GBs,
+        ref={k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in ref.items()})
 
 
 # VALU instructions per (sample, candidate) evaluation in the inner loop of
@@ -418,7 +532,7 @@ def sts_bench(D, torch, dev, stream, timed, gamma, reps):
     ws = D.new_sts_workspace(N, gamma, G, bins, dev)
     with torch.cuda.stream(stream):
         out = D.sts_fit(c_t, l_t, g_t, bins, ws)
-        ms = timed(lambda: D.sts_fit(c_t, l_t, g_t, bins, ws, out=out), reps)
+        ms, _ = timed(lambda: D.sts_fit(c_t, l_t, g_t, bins, ws, out=out), reps)
     torch.cuda.synchronize()
     if D.device_error(ws) != 0:
         raise RuntimeError("device-side data error in the calibration inputs")
@@ -448,9 +562,7 @@ def main():
     rank = int(os.environ.get("RANK", "0"))
     gb = gpu_bench(a)
     d = gb["cfg"]
-    # the faster of the two launch modes (both time the same complete round)
-    ms = min(gb["ms"], gb["ms_eager"]) if gb["graph"] else gb["ms"]
-    launch = ("hip graph" if ms == gb["ms"] else "eager") if gb["graph"] else "eager"
+    ms = gb["ms"]
     achieved = gb["k1_bytes"] / (gb["k1_ms"] * 1e-3) / 1e9
     res = {
         "metric": METRIC,
@@ -471,8 +583,8 @@ def main():
                    "R": d["R"], "gamma": d["gamma"], "V": d["V"], "r": d["r"],
                    "temperature": a.temperature, "scheduler": a.scheduler, "head": a.head,
                    **({"theta": gb["theta"]} if gb["theta"] is not None else {}),
-                   "launch": launch, "draft_kernel": gb["path"]},
-        "ms_per_step_graph": gb["ms"] if gb["graph"] else None,
+                   "launch": "hip graph" if gb["graph"] else "eager", "draft_kernel": gb["path"]},
+        "replays": {"hot": gb["hot"], "flushed": gb["flushed"], "eager": gb["eager"]},
         "ms_per_step_eager": gb["ms_eager"],
         "rounds_per_s": 1e3 / ms,
         "tokens_per_round": gb["tokens"],
@@ -484,29 +596,44 @@ def main():
             "achieved_min_GBs": gb["b_min"] / (ms * 1e-3) / 1e9,
             "frac_min": gb["b_min"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "frac_scheduled": gb["b_sched"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "frac_min_of_d2d_copy": gb["b_min"] / (ms * 1e-3) / 1e9 / gb["d2d_GBs"],
         },
         "roofline": {
             "bound": "hbm", "kernel": gb["kernel"], "achieved": achieved, "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-            "traffic": gb["traffic"], "launch_us": gb["k1_ms"] * 1e3, "launches_timed": gb["n_k1"],
+            "traffic": gb["traffic"], "launch_us": gb["k1_ms"] * 1e3,
+            "launch_us_median": gb["k1"]["median_ms"] * 1e3, "launches_timed": gb["n_k1"],
             "algorithmic_bytes_per_launch": gb["k1_bytes"],
         },
+        "d2d_copy_GBs": gb["d2d_GBs"],
         "mfma": {
             "kernel": gb["kernel"],
             "achieved": gb["k1_flops"] / (gb["k1_ms"] * 1e-3) / 1e12,
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": gb["k1_flops"] / (gb["k1_ms"] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         },
+        "checks": {"device_errors_after_timing": 0, "outputs_equal_reference_round": True},
     }
     if gb["sts"] is not None:
         res["sts_fit"] = gb["sts"]
     if gb["labels"] is not None:
         res["accept_rates"] = gb["labels"]
     if not a.no_cpu_baseline and rank == 0:
-        res["cpu_baseline"] = cpu_baseline(a)
+        import tempfile
+        with tempfile.TemporaryDirectory() as tmp:
+            dump = os.path.join(tmp, "oracle_round.npz")
+            say("oracle on all host cores")
+            res["cpu_baseline"] = cpu_baseline(a, dump=dump)
+            if os.path.exists(dump):
+                res["parity"] = parity_counts(dump, gb["ref"])
+        say("oracle on one core")
+        res["cpu_baseline_1core"] = cpu_baseline(a, one_core=True)
         if gb["sts"] is not None:
             res["sts_fit"]["cpu_oracle"] = cpu_sts_baseline(a)
     print(json.dumps(res), flush=True)
+    if "parity" in res and res["parity"]["unflagged_mismatch"] != 0:
+        say(f"PARITY FAILURE: {res['parity']}")
+        return 1
     return 0
 
 

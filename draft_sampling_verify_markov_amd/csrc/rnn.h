@@ -10,7 +10,7 @@
 //   u = sigmoid(e Wx[0] + s Ws[0] + b[0]),  g = sigmoid(e Wx[1] + s Ws[1] + b[1])
 //   h = tanh(e Wx[2] + (g * s) Ws[2] + b[2]),  s_k = (1 - u) * s + u * h
 // and the transition bias at position k is s_k . W2.  s_k is stored in the
-// weights' type (fp32, then bf16 round-to-nearest-even for bf16 weights) and
+// weights' type, rounded once from fp64 (nearest, ties to even), and
 // feeds the same bias contraction as a gathered W1 row.  The gate arithmetic
 // is fp64: products of stored values are exact there, so the stored state is
 // reproducible to the last bit (6 r^2 multiply-adds per request and step).
@@ -34,11 +34,23 @@ template <>
 __device__ __forceinline__ float store_state<float>(double x) {
   return (float)x;
 }
+// One rounding from fp64 to bf16, nearest with ties to even: the fp64
+// significand is cut to bf16's 8 significant bits, then the value (now exact
+// in fp32) is narrowed.  Below 2^-126 (bf16 subnormals) the spacing is
+// 2^-133, so the value is rounded on that grid instead (exact scalings).
+// |x| <= 1 here, so nothing overflows.
 template <>
 __device__ __forceinline__ uint16_t store_state<uint16_t>(double x) {
-  uint32_t u = __float_as_uint((float)x);
-  u += 0x7FFFu + ((u >> 16) & 1u);  // |x| < 1: no overflow into the exponent's top
-  return (uint16_t)(u >> 16);
+  double q;
+  if (fabs(x) < 0x1p-126) {
+    q = rint(x * 0x1p133) * 0x1p-133;
+  } else {
+    uint64_t u = __builtin_bit_cast(uint64_t, x);
+    constexpr uint64_t DROP = (1ull << 45) - 1;  // 52 - 7 significand bits go
+    u += (DROP >> 1) + ((u >> 45) & 1ull);
+    q = __builtin_bit_cast(double, u & ~DROP);
+  }
+  return (uint16_t)(__float_as_uint((float)q) >> 16);
 }
 
 // Eight consecutive weights of one row of a gate matrix (one or two 16-byte

@@ -500,14 +500,15 @@ def sts_fit(conf, labels, grid, bins, follow=None):
 
 
 def to_storage(x, w_dtype):
-    """Round float64 values to fp32 (nearest, ties to even) and, for bf16
-    weights, on to bf16 (nearest, ties to even); returned as float64."""
-    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    """Round float64 values once to the storage type (nearest, ties to even)
+    and return them as float64: fp32, or bf16 (8 significant bits over the
+    exponent range of fp32; below 2^-126 the spacing stays 2^-133)."""
+    x = np.asarray(x, dtype=np.float64)
     if w_dtype != "bf16":
-        return f.astype(np.float64)
-    u = np.ascontiguousarray(f).view(np.uint32).astype(np.uint64)
-    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+        return x.astype(np.float32).astype(np.float64)
+    _, e = np.frexp(x)                        # x = m 2^e with 1/2 <= |m| < 1
+    e = np.maximum(e, -125)
+    return np.ldexp(np.rint(np.ldexp(x, 8 - e)), e - 8)
 
 
 def _sigmoid(x):

@@ -1,7 +1,13 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times: the whole round runs on the GPU, and the oracle recomputes a
-sample of request rows one by one (the scheduler is global, so the oracle runs
-it on all confidences).  Whole-workload properties are checked on every row.
+benchmark times: the whole round runs on the GPU, the oracle runs the same
+round on every request, and the two are compared request by request.
+
+Unflagged requests must match exactly (tokens, verify and accepted lengths);
+flagged requests (an event within 1e-6 of a decision boundary) are counted,
+and so are the flagged requests whose outcome differs.  Each of those must
+depart from the oracle at an event that is itself within 1e-6 of its
+boundary (in practice within 1e-7: the GPU's CDF error is far inside the
+window), and at most a few per cent of the flagged requests may differ.
 """
 
 import numpy as np
@@ -9,16 +15,17 @@ import pytest
 
 import oracle as O
 from gen import make_inputs, config
+from gen.rnn import make_rnn_weights
 
 from gpu_util import compare_rounds, gpu_round, say
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
-
-def _rows(R, n, seed):
-    rng = np.random.default_rng(seed)
-    pick = set(rng.choice(R, size=min(n, R), replace=False).tolist()) | {0, R - 1}
-    return sorted(pick)
+# Largest share of the flagged requests whose GPU outcome may differ, and the
+# largest boundary distance of the event where one departs from the oracle
+# (observed: 1.8e-8 at most, over these six workloads).
+MAX_FLAGGED_MISMATCH_FRAC = 0.05
+MAX_FLIP_MARGIN = 1e-7
 
 
 def _whole_round_properties(gpu, d):
@@ -41,19 +48,39 @@ def _whole_round_properties(gpu, d):
     assert ((tp[k <= lim[:, None]] >= 0) & (tp[k <= lim[:, None]] <= 1)).all()
 
 
-@pytest.mark.parametrize("cfg,T,nrows", [(3, 1.0, 40), (4, 1.0, 16), (4, 0.0, 16), (5, 1.0, 24)])
-def test_fullsize_sampled_rows(cfg, T, nrows):
+def _every_row(cfg, T, head="markov"):
     d = config(cfg)
-    say(f"[cfg {cfg} T={T}] generating R={d['R']} gamma={d['gamma']} V={d['V']}")
+    label = f"cfg {cfg} T={T} {head}"
+    say(f"[{label}] generating R={d['R']} gamma={d['gamma']} V={d['V']}")
     inp = make_inputs(cfg)
-    gpu = gpu_round(inp, T)
-    assert gpu["device_error"] == 0
+    if head == "rnn":
+        w = make_rnn_weights(inp["W1"].shape[1], inp["w_dtype"], seed=0)
+        inp.update(Wx=w["Wx"], Ws=w["Ws"], rnn_bias=w["bias"])
+    gpu = gpu_round(inp, T, head=head)
+    assert gpu["device_error"] == 0, f"device error bits {gpu['device_error']}"
     _whole_round_properties(gpu, d)
-    del inp
-    rows = _rows(d["R"], nrows, cfg)
-    sub = make_inputs(cfg, rows=rows)
-    orc = O.run_round(sub, T=T)
-    n_flag = compare_rounds(orc, gpu, rows=rows, label=f"cfg {cfg} T={T}")
+    say(f"[{label}] GPU round done; oracle on all {d['R']} requests")
+    orc = O.run_round(inp, T=T, head=head)
+    c = compare_rounds(orc, gpu, label=label).counts
+    if head == "rnn":
+        same = (gpu["draft_tokens"] == orc["draft"]["tokens"]).all(axis=1)
+        assert np.array_equal(gpu["states"][same].astype(np.float64), orc["draft"]["states"][same])
     A = gpu["accept_len"]
-    say(f"[cfg {cfg} T={T}] mean accepted {A.mean():.3f}, tokens/round {int((A + 1).sum())}, "
-        f"flagged {n_flag}/{len(rows)}")
+    say(f"[{label}] PARITY rows={c['rows']} flagged={c['flagged']} "
+        f"flagged_mismatch={c['flagged_mismatch']} unflagged_mismatch={c['unflagged_mismatch']} "
+        f"max_flip_margin={c['max_flip_margin']} "
+        f"mean_accepted={A.mean():.3f} tokens_per_round={int((A + 1).sum())}")
+    assert c["rows"] == d["R"] and c["unflagged_mismatch"] == 0
+    assert c["flagged_mismatch"] <= MAX_FLAGGED_MISMATCH_FRAC * max(c["flagged"], 1)
+    assert c["max_flip_margin"] is None or c["max_flip_margin"] < MAX_FLIP_MARGIN
+    return c
+
+
+@pytest.mark.parametrize("cfg,T", [(3, 1.0), ("3alt", 1.0), (4, 1.0), (4, 0.0), (5, 1.0)])
+def test_fullsize_every_request(cfg, T):
+    _every_row(cfg, T)
+
+
+def test_fullsize_rnn_head_every_request():
+    """The bench workload (R=128, gamma=7, V=131072, r=256) with the RNN head."""
+    _every_row(3, 1.0, head="rnn")

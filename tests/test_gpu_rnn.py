@@ -81,18 +81,44 @@ def test_rnn_bias_differs_from_the_markov_head():
     assert not np.array_equal(a["draft_stats"], b["draft_stats"])
 
 
-@pytest.mark.slow
-def test_rnn_fullsize_sampled_rows():
-    """The bench workload (R=128, gamma=7, V=131072, r=256) with the RNN head:
-    the whole round on the GPU, the oracle on sampled requests."""
-    inp = _with_rnn(make_inputs(3), 0)
+def _near_tie_biases(n, seed=0):
+    """fp32 values b whose float64 tanh lies just above a bf16 tie whose lower
+    neighbour is even: one rounding to bf16 goes up, an fp32 rounding first
+    would land on the tie and go down.  The distance above the tie is at least
+    2^-12 fp32 units in the last place, far above any fp64 tanh error."""
+    rng = np.random.default_rng(seed)
+    out = []
+    lo = np.float32(0.3).view(np.uint32)
+    while len(out) < n:
+        start = int(lo) + int(rng.integers(0, 1 << 22))
+        b = np.arange(start, start + (1 << 20), dtype=np.uint32).view(np.float32)
+        t = np.tanh(b.astype(np.float64))
+        m, e = np.frexp(t)
+        k = np.floor(m * 256.0)                     # bf16 lower neighbour, in units of 2^(e-8)
+        frac = m * 256.0 - k - 0.5                  # distance above the tie, bf16 units
+        ok = (frac > 2.0**-28) & (frac < 2.0**-18) & (k % 2 == 0)
+        out.extend(b[ok][: n - len(out)].tolist())
+    b = np.array(out, np.float32)
+    t = np.tanh(b.astype(np.float64))
+    assert (O.to_storage(t, "bf16") != O.to_storage(t.astype(np.float32), "bf16")).all()
+    return b
+
+
+def test_rnn_state_is_rounded_once_to_bf16():
+    """Open update gate (u = 1) and zero weights: s_1 = tanh(b_candidate), so
+    the stored state shows the kernel's rounding of a planted near-tie."""
+    from gen.inputs import bf16_bits_from_f32
+    r, V, R, g = 16, 512, 4, 2
+    inp = make_inputs(config(1, w_dtype="bf16", r=r, R=R, gamma=g), seed=3)
+    b = np.zeros((3, r), np.float32)
+    b[0] = 60.0                                     # sigmoid(60) == 1 in float64
+    sign = np.where(np.arange(r) % 2 == 0, 1.0, -1.0).astype(np.float32)
+    b[2] = _near_tie_biases(r) * sign
+    z = bf16_bits_from_f32(np.zeros((3, r, r), np.float32))
+    inp.update(Wx=z, Ws=z, rnn_bias=b)
     gpu = gpu_round(inp, 1.0, head="rnn")
     assert gpu["device_error"] == 0
-    del inp
-    rows = [0, 17, 64, 101, 127]
-    sub = _with_rnn(make_inputs(3, rows=rows), 0)
-    orc = O.run_round(sub, T=1.0, head="rnn")
-    compare_rounds(orc, gpu, rows=rows, label="rnn 131k")
-    _check_states(orc, gpu, rows)
-    A = gpu["accept_len"]
-    say(f"[rnn 131k] mean accepted {A.mean():.3f}, tokens/round {int((A + 1).sum())}")
+    want = O.to_storage(np.tanh(b[2].astype(np.float64)), "bf16")
+    got = gpu["states"][:, 0, :].astype(np.float64)
+    assert np.array_equal(got, np.broadcast_to(want, got.shape)), "state not rounded once from fp64"
+    say(f"  {R * r} planted near-tie states rounded once")

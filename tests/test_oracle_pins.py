@@ -417,6 +417,175 @@ def test_boundary_uniform_is_flagged():
 
 
 # ---------------------------------------------------------------------------
+# boundary flags: every clause of row_flags, planted against boundaries
+# computed here from scipy's softmax (zero Markov factors, so the draft
+# distribution at position k is softmax(base row k-1) and the target
+# distribution softmax(target row k-1))
+
+
+class _FlagCase:
+    """One request, gamma = 3, V = 12, zero factors; drafted tokens chosen by
+    putting u_draft in the middle of the chosen token's CDF interval."""
+
+    V, G = 12, 3
+
+    def __init__(self, seed=31, xs=(3, 2, 3)):
+        rng = np.random.default_rng(seed)
+        V, g = self.V, self.G
+        self.base = (rng.standard_normal((1, g, V)) * 0.6).astype(np.float32)
+        self.target = (rng.standard_normal((1, g + 1, V)) * 0.6).astype(np.float32)
+        self.W1 = np.zeros((V, 2), np.float32)
+        self.W2 = np.zeros((2, V), np.float32)
+        self.anchor = np.array([0], np.int32)
+        self.q = [_softmax(self.base[0, k]) for k in range(g)]          # draft distributions
+        self.p = [_softmax(self.target[0, k]) for k in range(g + 1)]    # target distributions
+        self.x = list(xs)
+        u = []
+        for k, xk in enumerate(xs):
+            F = np.cumsum(self.q[k])
+            lo = F[xk - 1] if xk > 0 else 0.0
+            u.append(0.5 * (lo + F[xk]))
+            assert F[xk] - lo > 1e-2           # the draft events sit far from every edge
+        self.u_draft = np.array([u], np.float64)
+        self.rho = [self.p[k][xs[k]] / self.q[k][xs[k]] for k in range(g)]
+
+    def run(self, L, u_accept, u_final, T=1.0, u_draft=None):
+        inp = dict(base=self.base, target=self.target, W1=self.W1, W2=self.W2, w_dtype="f32",
+                   anchor=self.anchor, u_draft=self.u_draft if u_draft is None else u_draft,
+                   u_accept=np.array([u_accept], np.float64), u_final=np.array([u_final], np.float64))
+        d = O.draft(inp["base"], self.W1, self.W2, "f32", self.anchor, inp["u_draft"], T)
+        v = O.verify(self.target, self.base, self.W1, self.W2, "f32", self.anchor, d["tokens"], d["probs"],
+                     np.array([L]), inp["u_accept"], inp["u_final"], T)
+        return d, v, bool(O.row_flags(d, v)[0])
+
+    def residual_cdf(self, k):
+        d = np.maximum(0.0, self.p[k - 1] - self.q[k - 1])
+        return np.cumsum(d) / d.sum(), d / d.sum()
+
+    @staticmethod
+    def mid_of_largest(w):
+        """Midpoint of the widest CDF interval of the weights w (far from every edge)."""
+        F = np.cumsum(w) / np.sum(w)
+        j = int(np.argmax(w))
+        return 0.5 * ((F[j - 1] if j > 0 else 0.0) + F[j])
+
+
+def _flag_case_with_rho_below_one():
+    c = _FlagCase()
+    assert 0.1 < c.rho[0] < 0.9 and 0.05 < c.rho[1]       # a real accept test at position 1
+    return c
+
+
+@pytest.mark.parametrize("delta,flagged", [(-3e-7, True), (3e-7, True), (-3e-6, False), (3e-6, False)])
+def test_accept_test_near_p_over_q_flags(delta, flagged):
+    """Accept events: |u - p/q| < 1e-6 flags the request, 3e-6 away does not."""
+    c = _flag_case_with_rho_below_one()
+    u = c.rho[0] + delta
+    accepted = delta < 0
+    # the final uniform sits mid-interval of whichever law it samples: the bonus
+    # row 1 after an accept (L = 1), the residual at position 1 after a reject
+    uf = c.mid_of_largest(c.p[1]) if accepted else c.mid_of_largest(c.residual_cdf(1)[1])
+    d, v, fl = c.run(1, [u, 0.5, 0.5], uf)
+    assert v["accept_len"][0] == (1 if accepted else 0)
+    assert (d["margin"][0] > 1e-3).all() and v["final_margin"][0] > 1e-3
+    assert fl == flagged
+
+
+def test_accept_tests_after_the_rejection_never_flag():
+    """Only the accept tests up to the first rejection are events: positions
+    after k*, and positions past the verify length, do not flag even with u
+    planted on p/q."""
+    c = _flag_case_with_rho_below_one()
+    u1 = min(0.999, c.rho[0] + 0.05)                      # reject at k* = 1
+    uf = c.mid_of_largest(c.residual_cdf(1)[1])
+    ua = [u1, min(c.rho[1], 0.999) - 1e-9, min(c.rho[2], 0.999) + 1e-9]
+    d, v, fl = c.run(3, ua, uf)
+    assert v["accept_len"][0] == 0 and not fl
+    # accepted at position 1 with L = 1: position 2 is not verified
+    d, v, fl = c.run(1, [0.0, min(c.rho[1], 0.999) - 1e-9, 0.5], c.mid_of_largest(c.p[1]))
+    assert v["accept_len"][0] == 1 and not fl
+
+
+@pytest.mark.parametrize("delta,flagged", [(-3e-7, True), (3e-7, True), (-3e-6, False), (3e-6, False)])
+def test_final_sample_near_a_residual_edge_flags(delta, flagged):
+    c = _flag_case_with_rho_below_one()
+    F, w = c.residual_cdf(1)
+    # an inner edge between two tokens that both carry residual mass
+    j = next(i for i in range(c.V - 1) if w[i] > 0.02 and w[i + 1] > 0.02)
+    d, v, fl = c.run(1, [0.999, 0.5, 0.5], F[j] + delta)
+    assert v["accept_len"][0] == 0
+    assert v["out_tokens"][0, 0] == (j if delta < 0 else j + 1)
+    assert (d["margin"][0] > 1e-3).all() and abs(0.999 - c.rho[0]) > 1e-3
+    assert fl == flagged
+
+
+@pytest.mark.parametrize("L", [0, 1])
+@pytest.mark.parametrize("delta,flagged", [(-3e-7, True), (3e-7, True), (-3e-6, False), (3e-6, False)])
+def test_final_sample_near_a_bonus_edge_flags(L, delta, flagged):
+    """The bonus sample from target row L (L = 0: a plain target step)."""
+    c = _flag_case_with_rho_below_one()
+    F = np.cumsum(c.p[L])
+    j = 4
+    d, v, fl = c.run(L, [0.0, 0.5, 0.5], F[j] + delta)
+    assert v["accept_len"][0] == L
+    assert v["out_tokens"][0, L] == (j if delta < 0 else j + 1)
+    assert fl == flagged
+
+
+def test_every_draft_event_flags_even_after_the_rejection():
+    """Draft events count at all gamma positions, verified or not."""
+    c = _flag_case_with_rho_below_one()
+    F = np.cumsum(c.q[2])
+    u_draft = c.u_draft.copy()
+    u_draft[0, 2] = F[c.x[2]] - 3e-7                       # position 3, near its upper edge
+    uf = c.mid_of_largest(c.residual_cdf(1)[1])
+    d, v, fl = c.run(1, [0.999, 0.5, 0.5], uf, u_draft=u_draft)
+    assert v["accept_len"][0] == 0 and d["tokens"][0, 2] == c.x[2]
+    assert fl
+    u_draft[0, 2] = F[c.x[2]] - 3e-6
+    assert not c.run(1, [0.999, 0.5, 0.5], uf, u_draft=u_draft)[2]
+
+
+def _greedy_case(gap_accept, gap_final, top=0.5):
+    """Greedy round, one request, gamma = 2, V = 8, zero factors.  Draft argmaxes
+    are tokens 3 and 6 (wide gaps); target row 0 has its maximum at token 3 and
+    a runner-up gap_accept below it; target row 1 (the bonus row at L = 1) has
+    its two largest values gap_final apart."""
+    V = 8
+    base = np.zeros((1, 2, V), np.float32)
+    base[0, 0, 3] = base[0, 1, 6] = 5.0
+    target = np.full((1, 3, V), top - 10.0, np.float32)
+    target[0, 0, 3] = top
+    target[0, 0, 1] = np.float32(top - gap_accept)
+    target[0, 1, 2] = top
+    target[0, 1, 5] = np.float32(top - gap_final)
+    W1 = np.zeros((V, 2), np.float32)
+    W2 = np.zeros((2, V), np.float32)
+    anchor = np.array([0], np.int32)
+    d = O.draft(base, W1, W2, "f32", anchor, np.zeros((1, 2)), 0.0)
+    v = O.verify(target, base, W1, W2, "f32", anchor, d["tokens"], d["probs"], np.array([1]),
+                 np.zeros((1, 2)), np.zeros(1), 0.0)
+    return d, v, bool(O.row_flags(d, v)[0]), target
+
+
+@pytest.mark.parametrize("top", [0.5, -3.0])
+def test_greedy_top2_gap_flags(top):
+    """Greedy events flag when the top-2 gap is below 1e-6 * max(1, |top1|):
+    in the verified target row (the accept test) and in the bonus row."""
+    scale = max(1.0, abs(top))
+    for ga, gf, want in ((5e-7 * scale, 1e-3, True), (1e-3, 5e-7 * scale, True),
+                         (5e-6 * scale, 1e-3, False), (1e-3, 5e-6 * scale, False)):
+        d, v, fl, target = _greedy_case(ga, gf, top)
+        # the stored fp32 gaps are what the rule sees
+        real_a = float(target[0, 0, 3]) - float(target[0, 0, 1])
+        real_f = float(target[0, 1, 2]) - float(target[0, 1, 5])
+        assert (real_a < 1e-6 * scale or real_f < 1e-6 * scale) == want
+        assert d["tokens"][0].tolist() == [3, 6] and v["accept_len"][0] == 1
+        assert v["out_tokens"][0].tolist() == [3, 2, -1]
+        assert fl == want
+
+
+# ---------------------------------------------------------------------------
 # scheduler
 
 
@@ -834,6 +1003,18 @@ def test_storage_rounding_ties_to_even():
     v = O.to_storage([1 + 2**-8, 1 + 3 * 2**-8, 1 + 2**-8 + 2**-20, -(1 + 2**-8), 0.0], "bf16")
     assert list(v) == [1.0, 1 + 2**-6, 1 + 2**-7, -1.0, 0.0]
     assert O.to_storage([1 + 2**-30, 1 + 2**-23], "f32").tolist() == [1.0, 1 + 2**-23]
+
+
+def test_storage_rounds_once_from_float64():
+    """The state is rounded once: just above a bf16 tie it goes up, although
+    an fp32 rounding first would land on the tie and go to the even
+    neighbour.  Subnormal bf16 values sit on the 2^-133 grid."""
+    x = [1 + 2**-8 + 2**-30, 0.5 + 2**-9 + 2**-40, -(0.75 + 2**-9 + 2**-33)]
+    assert O.to_storage(x, "bf16").tolist() == [1 + 2**-7, 0.5 + 2**-8, -(0.75 + 2**-8)]
+    twice = O.to_storage(np.asarray(x, np.float32).astype(np.float64), "bf16")
+    assert twice.tolist() == [1.0, 0.5, -0.75]
+    sub = [2**-133 * 5.5, 2**-133 * 4.5, 2**-133 * 4.5 + 2**-160, 2**-127 * (1 + 2**-9)]
+    assert O.to_storage(sub, "bf16").tolist() == [2**-133 * 6, 2**-133 * 4, 2**-133 * 5, 2**-127]
 
 
 def _rnn_case(r=16, V=64, R=3, g=5, seed=0):

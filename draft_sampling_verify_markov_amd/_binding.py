@@ -44,6 +44,8 @@ def load_library():
     lib.dspark_status_string.restype = ctypes.c_char_p
     lib.dspark_draft.argtypes = [P, P, P, I, P, P, I, I, I, I, F, P, P, P, P, Z, P]
     lib.dspark_draft.restype = I
+    lib.dspark_draft_noalloc.argtypes = [P, P, P, I, P, P, I, I, I, I, F, P, P, P, P, P]
+    lib.dspark_draft_noalloc.restype = I
     lib.dspark_schedule.argtypes = [P, P, I, I, I, P, P, P, P, Z, P]
     lib.dspark_schedule.restype = I
     lib.dspark_schedule_async.argtypes = [P, P, P, I, I, I, P, P, P, P, Z, P]
@@ -161,6 +163,30 @@ def draft(base, W1, W2, anchor, u_draft, temperature, ws, out=None):
             ws.data_ptr(), ws.numel(), _stream(dev))
     _check("dspark_draft", load_library().dspark_draft(*args))
     return tok, prob, stats
+
+
+def draft_noalloc(base, W1, W2, anchor, u_draft, temperature, device_error, out):
+    """dspark_draft_noalloc: dspark_draft without a workspace (static device
+    scratch).  ``out`` = (draft_tokens, draft_probs, draft_stats) preallocated
+    by the caller, ``device_error`` a 1-element int32 device tensor the error
+    bits are OR-ed into.  Allocates nothing.  Returns ``out``."""
+    R, g, V = base.shape
+    r = W1.shape[1]
+    dev = base.device
+    wt = _wtype(W1)
+    wdt = W1.dtype
+    tok, prob, stats = out
+    args = (_ptr(base, torch.float32, (R, g, V), "base", dev),
+            _ptr(W1, wdt, (V, r), "W1", dev), _ptr(W2, wdt, (r, V), "W2", dev), wt,
+            _ptr(anchor, torch.int32, (R,), "anchor", dev),
+            _ptr(u_draft, torch.float32, (R, g), "u_draft", dev),
+            R, g, V, r, float(temperature),
+            _ptr(tok, torch.int32, (R, g), "draft_tokens", dev),
+            _ptr(prob, torch.float32, (R, g), "draft_probs", dev),
+            _ptr(stats, torch.float32, (R, g, 2), "draft_stats", dev),
+            _ptr(device_error, torch.int32, (1,), "device_error", dev), _stream(dev))
+    _check("dspark_draft_noalloc", load_library().dspark_draft_noalloc(*args))
+    return out
 
 
 def schedule(conf, sps, ws, out=None, with_cum=True):

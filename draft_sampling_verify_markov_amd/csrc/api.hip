@@ -1,11 +1,13 @@
 // C ABI entry points: host-side argument checks, workspace queries and
 // dispatch to the draft / schedule / verify launchers.
+#include <mutex>
+
 #include "select.h"
 
 namespace dspark {
 int draft_impl(const float* base, const void* W1, const void* W2, dspark_wtype w_type,
                const int32_t* anchor, const float* u_draft, int R, int gamma, int V, int r, float T,
-               int32_t* tokens, float* probs, float* stats, void* ws, hipStream_t stream,
+               int32_t* tokens, float* probs, float* stats, const DraftWs& dw, hipStream_t stream,
                const RnnHead* rnn = nullptr);
 int schedule_impl(const float* conf, const float* sps, int R, int gamma, int n_table,
                   int32_t* verify_len, int32_t* n_admitted, float* cum_conf, void* ws,
@@ -77,6 +79,52 @@ static int check_ws(void* ws, size_t bytes, int R, int gamma, int V) {
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0) return DSPARK_EINVAL;
   if (bytes < ws_layout(R, gamma, V).total) return DSPARK_ENOSPC;
   return DSPARK_OK;
+}
+
+// ---------------------------------------------------------------------------
+// dspark_draft_noalloc: the draft's sync words and tile records live in this
+// file-scope device array instead of a caller workspace.  Layout: the sync
+// words (SYNC_* offsets) at 0, the record region (shared by the one-launch and
+// the per-step paths, one of which a call uses) at NOALLOC_REC.  Each device
+// the library runs on holds its own copy until the process ends.
+constexpr size_t NOALLOC_REC = (SYNC_BYTES + 255) & ~(size_t)255;
+static_assert(NOALLOC_REC < DSPARK_DRAFT_NOALLOC_SCRATCH_BYTES, "scratch holds the sync words");
+static __device__ __align__(256) unsigned char scratch[DSPARK_DRAFT_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on each device (the host-side name is only a
+// stand-in for the symbol), found once per device with that device current.
+constexpr int NOALLOC_MAX_DEVICES = 64;
+struct NoallocDevice {
+  std::once_flag once;
+  unsigned char* ptr = nullptr;
+  hipError_t status = hipSuccess;
+};
+static NoallocDevice noalloc_dev[NOALLOC_MAX_DEVICES];
+
+// Scratch bytes a draft of these sizes uses (sync words and records).
+static size_t noalloc_bytes(int R, int V) { return NOALLOC_REC + (size_t)R * ceil_div(V, TILE) * 32; }
+
+// Set-up on the first call on the current device: the symbol's address, then
+// the whole array cleared by a fill kernel on the caller's stream (ahead of
+// that call's draft).  The clear makes every later tag unique (the one-launch
+// draft's epoch restarts at zero with no sealed record left); a graph that
+// captured the first call repeats the clear on every replay, which keeps
+// that property.
+static unsigned char* noalloc_scratch(hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) return nullptr;
+  NoallocDevice& D = noalloc_dev[dev];
+  std::call_once(D.once, [&] {
+    void* p = nullptr;
+    D.status = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (D.status != hipSuccess || p == nullptr) return;
+    const size_t n = DSPARK_DRAFT_NOALLOC_SCRATCH_BYTES / 4;
+    hipLaunchKernelGGL(k_fill_i32, dim3((unsigned)((n + 255) / 256 < 65536 ? (n + 255) / 256 : 65536)), dim3(256),
+                       0, stream, static_cast<int32_t*>(p), n, 0);
+    D.status = hipGetLastError();
+    if (D.status == hipSuccess) D.ptr = static_cast<unsigned char*>(p);
+  });
+  return D.ptr;
 }
 
 }  // namespace dspark
@@ -158,7 +206,27 @@ int dspark_draft(const float* base, const void* W1, const void* W2, dspark_wtype
   const int wsr = check_ws(workspace, workspace_bytes, R, gamma, V);
   if (wsr != DSPARK_OK) return wsr;
   return draft_impl(base, W1, W2, w_type, anchor, u_draft, R, gamma, V, r, temperature,
-                    draft_tokens, draft_probs, draft_stats, workspace, stream);
+                    draft_tokens, draft_probs, draft_stats, draft_ws(workspace, R, gamma, V), stream);
+}
+
+int dspark_draft_noalloc(const float* base, const void* W1, const void* W2, dspark_wtype w_type,
+                         const int32_t* anchor, const float* u_draft, int R, int gamma, int V, int r,
+                         float temperature, int32_t* draft_tokens, float* draft_probs, float* draft_stats,
+                         int32_t* device_error, hipStream_t stream) {
+  if (!sizes_ok(R, gamma, V, r)) return DSPARK_EINVAL;
+  if (w_type != DSPARK_W_BF16 && w_type != DSPARK_W_F32) return DSPARK_EINVAL;
+  if (!base || !W1 || !W2 || !anchor || !u_draft || !draft_tokens || !draft_probs || !draft_stats ||
+      !device_error)
+    return DSPARK_EINVAL;
+  if (!aligned16(base) || !aligned16(W1) || !aligned16(W2)) return DSPARK_EINVAL;
+  if (!(temperature >= 0.f) || __builtin_isinf(temperature)) return DSPARK_EINVAL;
+  if (noalloc_bytes(R, V) > DSPARK_DRAFT_NOALLOC_SCRATCH_BYTES) return DSPARK_ENOSPC;
+  unsigned char* p = noalloc_scratch(stream);
+  if (p == nullptr) return DSPARK_EHIP;
+  const DraftWs dw{device_error, p, reinterpret_cast<uint32_t*>(p + NOALLOC_REC),
+                   reinterpret_cast<float4*>(p + NOALLOC_REC)};
+  return draft_impl(base, W1, W2, w_type, anchor, u_draft, R, gamma, V, r, temperature, draft_tokens,
+                    draft_probs, draft_stats, dw, stream);
 }
 
 int dspark_schedule(const float* conf, const float* sps, int R, int gamma, int n_table,
@@ -287,7 +355,7 @@ int dspark_draft_rnn(const float* base, const void* W1, const void* W2, const vo
   if (wsr != DSPARK_OK) return wsr;
   const RnnHead head{Wx, Ws, rnn_bias, states, ws_ptr<double>(workspace, ws_layout(R, gamma, V).rnn)};
   return draft_impl(base, W1, W2, w_type, anchor, u_draft, R, gamma, V, r, temperature, draft_tokens,
-                    draft_probs, draft_stats, workspace, stream, &head);
+                    draft_probs, draft_stats, draft_ws(workspace, R, gamma, V), stream, &head);
 }
 
 static int verify_rnn_checked(const float* target, const float* base, const void* states, const void* W2,

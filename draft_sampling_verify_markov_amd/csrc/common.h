@@ -885,4 +885,20 @@ __host__ __device__ inline T* ws_ptr(void* ws, size_t off) {
   return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off);
 }
 
+// The parts of a workspace the draft uses: the error word, the one-launch
+// draft's sync words (SYNC_* offsets) and sealed tile records, and the
+// per-step path's tile records (each R * ceil(V / 256) * 32 bytes; a call
+// uses one of the two record regions, so they may coincide).
+struct DraftWs {
+  int32_t* err;
+  uint8_t* sync;
+  uint32_t* frec;
+  float4* trec;
+};
+__host__ inline DraftWs draft_ws(void* ws, int R, int gamma, int V) {
+  const WsLayout L = ws_layout(R, gamma, V);
+  return DraftWs{ws_ptr<int32_t>(ws, L.err), ws_ptr<uint8_t>(ws, L.sync), ws_ptr<uint32_t>(ws, L.frec),
+                 ws_ptr<float4>(ws, L.trec)};
+}
+
 }  // namespace dspark

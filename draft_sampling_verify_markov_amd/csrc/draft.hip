@@ -321,7 +321,7 @@ __global__ __launch_bounds__(256) void k_draft_select(DraftStep<WT> P) {
 bool draft_fused_supported(int R, int gamma, int V, int r, float T);
 int draft_fused_launch(const float* base, const void* W1, const void* W2, const int32_t* anchor,
                        const float* u_draft, int R, int gamma, int V, int r, float T, int32_t* tokens,
-                       float* probs, float* stats, void* ws, hipStream_t stream);
+                       float* probs, float* stats, const DraftWs& dw, hipStream_t stream);
 
 // DSPARK_DRAFT_KERNEL=stepwise selects the per-step kernels below even where
 // the one-launch draft (draft_fused.hip) applies; both compute the same draw.
@@ -333,13 +333,12 @@ static bool stepwise_requested() {
 template <typename WT>
 static int launch_draft(const float* base, const void* W1, const void* W2, const int32_t* anchor,
                         const float* u_draft, int R, int gamma, int V, int r, float T,
-                        int32_t* tokens, float* probs, float* stats, void* ws, hipStream_t stream,
+                        int32_t* tokens, float* probs, float* stats, const DraftWs& dw, hipStream_t stream,
                         const RnnHead* rnn = nullptr) {
   if (std::is_same<WT, uint16_t>::value && rnn == nullptr && !stepwise_requested() &&
       draft_fused_supported(R, gamma, V, r, T))
-    return draft_fused_launch(base, W1, W2, anchor, u_draft, R, gamma, V, r, T, tokens, probs, stats, ws,
+    return draft_fused_launch(base, W1, W2, anchor, u_draft, R, gamma, V, r, T, tokens, probs, stats, dw,
                               stream);
-  const WsLayout L = ws_layout(R, gamma, V);
   DraftStep<WT> P;
   P.base = base;
   P.W1 = static_cast<const WT*>(rnn ? rnn->states : W1);
@@ -352,8 +351,8 @@ static int launch_draft(const float* base, const void* W1, const void* W2, const
   P.T = T;
   P.invT = (T > 0.f) ? 1.0f / T : 0.f;
   P.tokens = tokens; P.probs = probs; P.stats = stats;
-  P.trec = ws_ptr<float4>(ws, L.trec);
-  P.err = ws_ptr<int32_t>(ws, L.err);
+  P.trec = dw.trec;
+  P.err = dw.err;
   const int nt = ceil_div(V, TILE);
   const int grid1 = min(nt, device_cu_count());
   for (int k = 1; k <= gamma; k++) {
@@ -385,13 +384,13 @@ static int launch_draft(const float* base, const void* W1, const void* W2, const
 
 int draft_impl(const float* base, const void* W1, const void* W2, dspark_wtype w_type,
                const int32_t* anchor, const float* u_draft, int R, int gamma, int V, int r, float T,
-               int32_t* tokens, float* probs, float* stats, void* ws, hipStream_t stream,
+               int32_t* tokens, float* probs, float* stats, const DraftWs& dw, hipStream_t stream,
                const RnnHead* rnn = nullptr) {
   if (w_type == DSPARK_W_BF16)
     return launch_draft<uint16_t>(base, W1, W2, anchor, u_draft, R, gamma, V, r, T, tokens, probs,
-                                  stats, ws, stream, rnn);
+                                  stats, dw, stream, rnn);
   return launch_draft<float>(base, W1, W2, anchor, u_draft, R, gamma, V, r, T, tokens, probs, stats,
-                             ws, stream, rnn);
+                             dw, stream, rnn);
 }
 
 }  // namespace dspark

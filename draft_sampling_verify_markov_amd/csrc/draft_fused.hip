@@ -516,8 +516,7 @@ bool draft_fused_supported(int R, int gamma, int V, int r, float T) {
 
 int draft_fused_launch(const float* base, const void* W1, const void* W2, const int32_t* anchor,
                        const float* u_draft, int R, int gamma, int V, int r, float T, int32_t* tokens,
-                       float* probs, float* stats, void* ws, hipStream_t stream) {
-  const WsLayout L = ws_layout(R, gamma, V);
+                       float* probs, float* stats, const DraftWs& dw, hipStream_t stream) {
   FusedArgs A;
   A.base = base;
   A.W1 = static_cast<const uint16_t*>(W1);
@@ -528,11 +527,11 @@ int draft_fused_launch(const float* base, const void* W1, const void* W2, const 
   A.T = T;
   A.invT = (T > 0.f) ? 1.0f / T : 0.f;
   A.tokens = tokens; A.probs = probs; A.stats = stats;
-  A.frec = ws_ptr<uint32_t>(ws, L.frec);
-  A.err = ws_ptr<int32_t>(ws, L.err);
-  A.epoch = ws_ptr<uint32_t>(ws, L.sync + SYNC_EPOCH);
-  A.done = ws_ptr<uint32_t>(ws, L.sync + SYNC_DONE);
-  A.tokw = ws_ptr<uint64_t>(ws, L.sync + SYNC_TOKW);
+  A.frec = dw.frec;
+  A.err = dw.err;
+  A.epoch = reinterpret_cast<uint32_t*>(dw.sync + SYNC_EPOCH);
+  A.done = reinterpret_cast<uint32_t*>(dw.sync + SYNC_DONE);
+  A.tokw = reinterpret_cast<uint64_t*>(dw.sync + SYNC_TOKW);
   A.spin_ticks = fused_spin_ticks();
   const int G = device_cu_count();
   prof_before(DSPARK_KID_DRAFT_FUSED, stream);

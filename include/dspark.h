@@ -152,6 +152,33 @@ int dspark_draft(const float* base, const void* W1, const void* W2, dspark_wtype
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * dspark_draft_noalloc - dspark_draft for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, outputs, kernels and results as
+ * dspark_draft, without a workspace: the draft's sync words and tile records
+ * live in a static device array of DSPARK_DRAFT_NOALLOC_SCRATCH_BYTES that
+ * each GPU the library runs on holds until the process ends.  The call makes
+ * no hipMalloc / hipFree and no allocating library call.
+ *
+ *   device_error  in/out [1] int32 (device): DSPARK_DERR_* bits are OR-ed into
+ *                 it (including DSPARK_DERR_SYNC); the caller clears it.
+ *
+ * Limit: 8448 + 32 * R * ceil(V / 256) <= DSPARK_DRAFT_NOALLOC_SCRATCH_BYTES
+ * (R <= 1024 at V = 131072); larger sizes return DSPARK_ENOSPC and launch
+ * nothing.  The first call on a device clears the array with a kernel on
+ * `stream` ahead of its draft (if that call is captured into a graph, every
+ * replay repeats the clear, which is correct and a few microseconds slower).
+ * Every call on one GPU shares that GPU's array and leaves its contents for
+ * the next: calls that overlap on one GPU (other streams, other threads) race
+ * and must not be issued.
+ */
+#define DSPARK_DRAFT_NOALLOC_SCRATCH_BYTES ((16u << 20) + 8448u)
+int dspark_draft_noalloc(const float* base, const void* W1, const void* W2, dspark_wtype w_type,
+                         const int32_t* anchor, const float* u_draft, int R, int gamma, int V, int r,
+                         float temperature, int32_t* draft_tokens, float* draft_probs, float* draft_stats,
+                         int32_t* device_error, hipStream_t stream);
+
+/*
  * dspark_schedule - hardware-aware prefix scheduler.  Reads only confidences
  * and the cost table, never a drafted token (non-anticipation).
  *

@@ -231,3 +231,23 @@ def test_binding_checks_tensors():
     with pytest.raises(TypeError):
         D.draft(torch.zeros(2, 2, 8), torch.zeros(8, 16, dtype=torch.float64),
                 torch.zeros(16, 8, dtype=torch.float64), None, None, 1.0, None)
+
+
+def _draft_noalloc(lib, **kw):
+    a = dict(base=16, W1=16, W2=16, wt=0, anchor=16, u=16, R=4, g=4, V=512, r=16, T=1.0,
+             tok=16, prob=16, stats=16, err=16, stream=None)
+    a.update(kw)
+    return lib.dspark_draft_noalloc(a["base"], a["W1"], a["W2"], a["wt"], a["anchor"], a["u"], a["R"], a["g"],
+                                    a["V"], a["r"], a["T"], a["tok"], a["prob"], a["stats"], a["err"],
+                                    a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(base=None), EINVAL), (dict(err=None), EINVAL), (dict(V=500), EINVAL), (dict(g=17), EINVAL),
+    (dict(T=-1.0), EINVAL), (dict(wt=7), EINVAL), (dict(W1=18), EINVAL),
+    # the static scratch holds 8448 + 32 R ceil(V / 256) bytes at most
+    (dict(R=1025, V=131072), ENOSPC), (dict(R=4097, V=32768), ENOSPC),
+])
+def test_draft_noalloc_rejects_bad_arguments_and_oversized_calls(lib, kw, status):
+    """Checked on the host before the scratch array is touched."""
+    assert _draft_noalloc(lib, **kw) == status

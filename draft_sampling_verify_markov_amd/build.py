@@ -22,6 +22,13 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source extra flags.  The one-launch draft keeps its resident W2
+# fragments in the AGPRs, so its MFMAs write their results to VGPRs.
+EXTRA_FLAGS = {
+    "draft_fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
@@ -43,7 +50,7 @@ def build(jobs=None, verbose=False):
         for s in srcs:
             o = os.path.join(tmp, os.path.basename(s) + ".o")
             objs.append(o)
-            cmd = [cc, *HIPCC_FLAGS, "-c", s, "-o", o]
+            cmd = [cc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(os.path.basename(s), []), "-c", s, "-o", o]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((s, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

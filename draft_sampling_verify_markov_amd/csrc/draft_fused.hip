@@ -16,6 +16,10 @@
 //     (as k_draft_partials); the workgroups b, b + G, ... < R each draw
 //     request b's token (as k_draft_select) and publish it; every workgroup
 //     gathers the new tokens' W1 rows and goes on;
+//   * the units of a step are software-pipelined in every wave: the MFMA
+//     chain of the next unit is issued interleaved with the epilogue (max,
+//     exponentials, sums) of the current one and with the direct-to-LDS loads
+//     of the unit after next, so the matrix and vector units work at once;
 //   * the next step's first base rows are loaded while the token words are
 //     awaited.
 //
@@ -116,8 +120,153 @@ __device__ __forceinline__ void mma_resident(const typename BiasBlock<uint16_t>:
   }
 }
 
+// Direct-to-LDS loads of one unit's 32 base rows (as stage_dma), issued one
+// 1 KiB row piece per wave at a time; `on` (wave-uniform) is false when the
+// unit lies past the step, whose rows are issued after the draws.
+struct DmaPlan {
+  rsrc_t rs;
+  uint32_t row_bytes, coff;
+  int rb, nrows;
+  float* X;
+  bool on;
+};
+__device__ __forceinline__ void dma_row(const DmaPlan& d, int i) {
+  if (!d.on) return;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rl = d.rb * 32 + 4 * i + wave;
+  const uint32_t voff = (rl < d.nrows ? (uint32_t)rl * d.row_bytes : 0u) + d.coff;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      d.rs, (__attribute__((address_space(3))) void*)(d.X + (4 * i + wave) * BSTRIDE), 16, (int)voff, 0, 0, AUX_NT);
+}
+
+// Where a unit's per-wave reduction goes: row rl of this wave's slice of the
+// workgroup's LDS reduction arrays.
+struct UnitOut {
+  float (*m)[RCH];
+  float (*s)[RCH];
+  int (*i)[RCH];
+  int wave, rl;
+  int32_t* err;
+};
+
+// One pipelined unit step of a wave, in 8 parts fenced by sched_barrier:
+// part p issues the MFMAs of k steps [p KS / 8, (p + 1) KS / 8) of the NEXT
+// unit's bias block (rows A_next against the resident fragment F, into
+// accN), one eighth of the epilogue of the current unit (accC + base values
+// bv: the maximum, the exponentials and their fixed-order tree sum, the
+// cross-half reduction and the LDS write; greedy: the arg-max), and one of
+// the 8 direct-to-LDS row loads of a later unit.  The fences keep the VALU
+// work of the epilogue in the shadow of the MFMAs instead of after them; the
+// arithmetic and its order are those of the unpipelined loop, so the results
+// are bit-identical.  The B operands of part p + 1 are read from LDS during
+// part p.
+template <int KS, bool GREEDY, bool NEXT>
+__device__ __forceinline__ void unit_block(const typename BiasBlock<uint16_t>::template Frag<KS>& F,
+                                           const uint16_t* A_next, int a_stride, f32x16 (&accN)[2],
+                                           const f32x16 (&accC)[2], const float (&bv)[2][16], float sc, int cbase,
+                                           const DmaPlan& dma, const UnitOut& o) {
+  constexpr int NP = 8;
+  constexpr int KPP = (KS + NP - 1) / NP;  // k steps per part, at most
+  const int lane = threadIdx.x & 63, j = lane & 31, h = lane >> 5;
+  const uint16_t* ap = A_next + j * a_stride + 8 * h;
+  u32x4 bcur[KPP], bnext[KPP];
+  if (NEXT) {
+#pragma unroll
+    for (int p = 0; p < 2; p++)
+#pragma unroll
+      for (int t = 0; t < 16; t++) accN[p][t] = 0.f;
+#pragma unroll
+    for (int i = 0; i < KPP; i++)
+      if (i < KS / NP) bcur[i] = *reinterpret_cast<const u32x4*>(ap + i * 16);
+  }
+  float ml = -INFINITY, mw = 0.f, mref = 0.f;
+  float s[8];
+  float gv = -INFINITY;
+  int gi = 0x7fffffff;
+  bool bad = false;
+#pragma unroll
+  for (int p = 0; p < NP; p++) {
+    if (NEXT) {
+      const int k0 = p * KS / NP, k1 = (p + 1) * KS / NP;
+      if (p + 1 < NP) {
+        const int n0 = k1, n1 = (p + 2) * KS / NP;
+#pragma unroll
+        for (int i = 0; i < KPP; i++)
+          if (n0 + i < n1) bnext[i] = *reinterpret_cast<const u32x4*>(ap + (n0 + i) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < KPP; i++) {
+        if (k0 + i < k1) {
+          const int ks = k0 + i;
+          const bf16x8 bb = __builtin_bit_cast(bf16x8, bcur[i]);
+          const bf16x8 a0 = __builtin_bit_cast(bf16x8, u32x4{F.w[ks][0], F.w[ks][1], F.w[ks][2], F.w[ks][3]});
+          const bf16x8 a1 = __builtin_bit_cast(bf16x8, u32x4{F.w[ks][4], F.w[ks][5], F.w[ks][6], F.w[ks][7]});
+          accN[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bb, accN[0], 0, 0, 0);
+          accN[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bb, accN[1], 0, 0, 0);
+        }
+      }
+    }
+    if (GREEDY) {
+      if (p < 4) {
+#pragma unroll
+        for (int t = 4 * p; t < 4 * p + 4; t++)
+#pragma unroll
+          for (int q = 0; q < 2; q++) {
+            const float z = bv[q][t] + accC[q][t];
+            bad |= (z != z);
+            if (z > gv) { gv = z; gi = cbase + elem_col(q, t, h); }
+          }
+      } else if (p == 4) {
+        if (bad) raise_err(o.err, DSPARK_DERR_NONFINITE);
+        argmax_xor32(gv, gi);
+      } else if (p == 5) {
+        if (h == 0) { o.m[o.wave][o.rl] = gv; o.i[o.wave][o.rl] = gi; }
+      }
+    } else {
+      if (p < 2) {
+#pragma unroll
+        for (int t = 8 * p; t < 8 * p + 8; t++)
+#pragma unroll
+          for (int q = 0; q < 2; q++) ml = fmaxf(ml, bv[q][t] + accC[q][t]);
+        if (p == 1) {
+          mw = max_xor32(ml);
+          mref = (mw == -INFINITY) ? 0.f : mw;
+        }
+      } else if (p < 6) {
+        // pair sums s_t = e[0][t] + e[1][t], and the first level of the
+        // fixed tree (s_t + s_{t+8}) as soon as both terms exist
+#pragma unroll
+        for (int t = 4 * (p - 2); t < 4 * (p - 2) + 4; t++) {
+          const float st = exp2_scaled((bv[0][t] - mref) + accC[0][t], sc) +
+                           exp2_scaled((bv[1][t] - mref) + accC[1][t], sc);
+          if (t < 8)
+            s[t] = st;
+          else
+            s[t - 8] = s[t - 8] + st;
+        }
+      } else if (p == 6) {
+#pragma unroll
+        for (int w = 4; w >= 1; w >>= 1)
+#pragma unroll
+          for (int t = 0; t < w; t++) s[t] = s[t] + s[t + w];
+      } else {
+        const float sw = sum_xor32(s[0]);
+        if (h == 0) { o.m[o.wave][o.rl] = mw; o.s[o.wave][o.rl] = sw; }
+      }
+    }
+    dma_row(dma, p);
+    if (NEXT) {
+#pragma unroll
+      for (int i = 0; i < KPP; i++) bcur[i] = bnext[i];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // 480 of the 512 registers per lane: a 32-register wave of a kernel on another
 // stream (verify's target-row stream) still fits beside every wave of this one.
+// Built with MFMA results in VGPRs (-amdgpu-mfma-vgpr-form): the AGPRs hold
+// the resident W2 fragments.
 template <int KS, bool GREEDY>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdgpu_num_vgpr(240))) void k_draft_fused(FusedArgs P) {
   using WT = uint16_t;
@@ -187,7 +336,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
     stage_dma(brs, row_bytes, rb, nrows, (b + ti * G) * TILE, X[g & 1]);
   };
 
-  // resident W2 fragments of this workgroup's tiles, loaded once
+  // resident W2 fragments of this workgroup's tiles, loaded once.  Most of
+  // them live in the accumulation registers (AGPRs), which the MFMAs read
+  // their A operand from directly, so the VGPRs stay free for the unit
+  // pipeline; the register budget (480 of the 512 per lane, so that a
+  // 32-register wave of a kernel on another stream still fits beside every
+  // wave of this one) leaves the last two k steps in VGPRs.
   typename BB::template Frag<KS> F0, F1;
   if (ntl > 0) BB::template load<KS>(F0, P.W2, P.V, P.r, b * TILE + wave * WCOLS);
   if (ntl > 1) BB::template load<KS>(F1, P.W2, P.V, P.r, (b + G) * TILE + wave * WCOLS);
@@ -195,6 +349,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
   issue(1);
   if (ntl > 0) BB::template to_operands<KS>(F0);
   if (ntl > 1) BB::template to_operands<KS>(F1);
+#pragma unroll
+  for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+    for (int e = 0; e < 8; e++)
+      if (ks < 14) asm volatile("" : "+a"(F0.w[ks][e]), "+a"(F1.w[ks][e]));
   __syncthreads();
   const uint32_t E = s_E;
 
@@ -203,130 +362,156 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
   const rsrc_t rec_rs = make_rsrc(P.frec, (size_t)P.R * nt * FREC_BYTES);
   bool ok = true;
 
+  // One unit (tile slot ti, row block rb of chunk c) of step k at a time,
+  // software-pipelined: the MFMA chain of the next unit runs interleaved with
+  // the epilogue of the current one (unit_block); the base rows of a unit
+  // arrive by direct-to-LDS loads issued two units ahead.
+  auto records = [&](int k, int c0, int nrows, int tile) {
+    // tile records of this chunk: two sealed 16-byte words per request,
+    // stored device-coherent (written through to memory); the word w of
+    // request q is stored by thread q + 128 w (greedy: one word, by
+    // threads q < nrows), so the stores are spread over the four waves
+    const int nwords = GREEDY ? 1 : 2;
+    if (tid < nwords * CH && (tid & (CH - 1)) < nrows) {
+      const int q = tid & (CH - 1), word = tid / CH;
+      const uint32_t tag = E + (uint32_t)k;
+      const uint32_t roff = (uint32_t)(((size_t)(c0 + q) * nt + tile) * FREC_BYTES);
+      uint32_t x0, x1, x2, y0 = 0u, y1 = 0u, y2 = 0u;
+      if (GREEDY) {
+        float v = red_m[0][q];
+        int i = red_i[0][q];
+#pragma unroll
+        for (int w = 1; w < 4; w++) argmax_merge(v, i, red_m[w][q], red_i[w][q]);
+        x0 = __float_as_uint(v);
+        x1 = (uint32_t)i;
+        x2 = 0u;
+      } else {
+        const float m0 = red_m[0][q], m1 = red_m[1][q], m2 = red_m[2][q], m3 = red_m[3][q];
+        const float mt = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+        auto rescale = [&](float swv, float mwv) {
+          const float d = t_one ? (mwv - mt) : (mwv - mt) * P.invT;
+          return (mwv == -INFINITY) ? 0.f : swv * exp_acc(d);
+        };
+        const float s0 = rescale(red_s[0][q], m0), s1 = rescale(red_s[1][q], m1);
+        const float s2 = rescale(red_s[2][q], m2), s3 = rescale(red_s[3][q], m3);
+        const float st = (s0 + s1) + (s2 + s3);
+        x0 = __float_as_uint(mt);
+        x1 = __float_as_uint(st);
+        x2 = __float_as_uint(s0);
+        y0 = __float_as_uint(s1);
+        y1 = __float_as_uint(s2);
+        y2 = __float_as_uint(s3);
+        if (word == 0 && (is_bad(st) || !(mt == mt) || mt == INFINITY)) raise_err(P.err, DSPARK_DERR_NONFINITE);
+      }
+      if (word == 0)
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{x0, x1, x2, seal(tag, x0, x1, x2)}, rec_rs, (int)roff, 0,
+                                               AUX_DEV);
+      else
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{y0, y1, y2, seal(tag, y0, y1, y2)}, rec_rs,
+                                               (int)roff + 16, 0, AUX_DEV);
+    }
+  };
+  // direct-to-LDS rows of global unit g (into X[g & 1]), issued one row
+  // piece per part of a unit block; off when g is past the step
+  auto dma_plan = [&](int g, int step_end) {
+    DmaPlan d;
+    const bool on = g < step_end;
+    d.on = on;
+    const int gg = on ? g : 0;
+    const int k = gg / ups + 1;
+    int c, ti, rb;
+    decode(gg - (k - 1) * ups, c, ti, rb);
+    const int c0 = c * CH;
+    d.nrows = min(CH, P.R - c0);
+    d.rb = rb;
+    d.row_bytes = row_bytes;
+    const size_t first = (size_t)c0 * P.gamma + (k - 1);
+    d.rs = make_rsrc(P.base + first * P.V, ((size_t)P.R * P.gamma - first) * P.V * 4);
+    d.coff = (uint32_t)((b + ti * G) * TILE + 4 * lane) * 4u;
+    d.X = X[g & 1];
+    return d;
+  };
+
   for (int k = 1; k <= P.gamma && ok; k++) {
     int g = (k - 1) * ups;
-    for (int c = 0; c < nch; c++) {
+    const int step_end = k * ups;
+    for (int c = 0; c < nch && ntl > 0; c++) {
       const int c0 = c * CH, nrows = min(CH, P.R - c0), nrb = ceil_div(nrows, 32);
+      const int n_u = ntl * nrb;  // units of this chunk: tile-major, then row block
       lds_barrier();  // the previous chunk is done with A_lds and red_*
-      if (ntl > 0) {
-        W1Gather<WT, GPER> wg;
-        wg.load(P.W1, P.V, P.r, nrows, CH, a_stride, [&](int i) { return s_tok[c0 + i]; });
-        wg.store(A_lds);
+      {
+        // W1 rows of the chunk's tokens (r = 16 KS: 2 KS pieces of 16 bytes per
+        // row), recomputing every per-thread index here: an opaque thread id
+        // keeps them from living in registers across the whole step loop
+        constexpr int PIECES = 2 * KS;
+        int t = threadIdx.x;
+        asm volatile("" : "+v"(t));
+        const rsrc_t w1rs = make_rsrc(P.W1, (size_t)P.V * P.r * 2);
+        u32x4 wv[GPER];
+#pragma unroll
+        for (int i = 0; i < GPER; i++) {
+          const int idx = t + 256 * i, row = idx / PIECES, pc = idx % PIECES;
+          const int tk = (row < nrows) ? s_tok[c0 + row] : -1;
+          const u32x4 x = buf_u32x4<0>(w1rs, (uint32_t)(max(tk, 0) * P.r + pc * 8) * 2u, 0u);
+          wv[i] = (tk >= 0) ? x : u32x4{0u, 0u, 0u, 0u};
+        }
+        asm volatile("" : "+v"(t));
+#pragma unroll
+        for (int i = 0; i < GPER; i++) {
+          const int idx = t + 256 * i, row = idx / PIECES, pc = idx % PIECES;
+          *reinterpret_cast<u32x4*>(A_lds + row * a_stride + pc * 8) = wv[i];
+        }
       }
-      for (int ti = 0; ti < ntl; ti++) {
+      lds_barrier();  // A_lds complete
+      f32x16 accA[2], accB[2];
+      // the chunk's first MFMA chain (unit 0: tile slot 0, row block 0), alone
+#pragma unroll
+      for (int p = 0; p < 2; p++)
+#pragma unroll
+        for (int t = 0; t < 16; t++) accA[p][t] = 0.f;
+      mma_resident<KS>(F0, A_lds, a_stride, accA);
+      auto iter = [&](auto& accC, auto& accN, int u) {
+        const int ti = u / nrb, rb = u - ti * nrb;
         const int tile = b + ti * G;
         const int cbase = tile * TILE + wave * WCOLS;
-        for (int rb = 0; rb < nrb; rb++, g++) {
-          // unit g's rows were issued two units earlier, so the next unit's 8
-          // loads may still be in flight behind them, unless this is the
-          // chunk's first unit (the W1 gather's loads came after its rows) or
-          // the step's last unit (nothing of the next step is issued yet)
-          const bool first = (ti == 0 && rb == 0);
-          const bool next_in_step = (g + 1) < k * ups;
-          if (!first && next_in_step)
-            wait_vmcnt<8>();
+        // unit g's rows were issued two units earlier, so the next unit's 8
+        // loads may still be in flight behind them, unless the next unit is
+        // of the next step (issued after the draws)
+        if (g + 1 < step_end)
+          wait_vmcnt<8>();
+        else
+          wait_vmcnt<0>();
+        lds_barrier();
+        float bv2[2][16];
+        if ((tile + 1) * TILE <= P.V)
+          stage_read_full(X[g & 1], wave * WCOLS, bv2);
+        else
+          stage_read(X[g & 1], true, P.V, cbase, wave * WCOLS, bv2);
+        lds_barrier();  // every wave has its base values out of X[g & 1]
+        const DmaPlan dp = dma_plan(g + 2, step_end);
+        const int rl = rb * 32 + j;
+        const UnitOut o{red_m, red_s, red_i, wave, rl, P.err};
+        if (u + 1 < n_u) {
+          const int tn = (u + 1) / nrb, rbn = (u + 1) - tn * nrb;
+          if (tn == 0)
+            unit_block<KS, GREEDY, true>(F0, A_lds + rbn * 32 * a_stride, a_stride, accN, accC, bv2, sc, cbase,
+                                         dp, o);
           else
-            wait_vmcnt<0>();
-          lds_barrier();
-
-          f32x16 acc[2];
-#pragma unroll
-          for (int p = 0; p < 2; p++)
-#pragma unroll
-            for (int t = 0; t < 16; t++) acc[p][t] = 0.f;
-          if (ti == 0)
-            mma_resident<KS>(F0, A_lds + rb * 32 * a_stride, a_stride, acc);
-          else
-            mma_resident<KS>(F1, A_lds + rb * 32 * a_stride, a_stride, acc);
-
-          const int rl = rb * 32 + j;
-          float bv2[2][16];
-          if ((tile + 1) * TILE <= P.V)
-            stage_read_full(X[g & 1], wave * WCOLS, bv2);
-          else
-            stage_read(X[g & 1], true, P.V, cbase, wave * WCOLS, bv2);
-          // every wave has its base values out of X[g & 1]: refill it with the
-          // rows of unit g + 2 while the MFMA chain runs (the epilogue below
-          // is the first use of acc)
-          lds_barrier();
-          if (g + 2 < k * ups) issue(g + 2);
-          if (GREEDY) {
-            float bv = -INFINITY;
-            int bi = 0x7fffffff;
-            bool bad = false;
-#pragma unroll
-            for (int t = 0; t < 16; t++)
-#pragma unroll
-              for (int p = 0; p < 2; p++) {
-                const float z = bv2[p][t] + acc[p][t];
-                bad |= (z != z);
-                if (z > bv) { bv = z; bi = cbase + elem_col(p, t, h); }
-              }
-            if (bad) raise_err(P.err, DSPARK_DERR_NONFINITE);
-            argmax_xor32(bv, bi);
-            if (h == 0) { red_m[wave][rl] = bv; red_i[wave][rl] = bi; }
-          } else {
-            float ml = -INFINITY;
-#pragma unroll
-            for (int p = 0; p < 2; p++)
-#pragma unroll
-              for (int t = 0; t < 16; t++) ml = fmaxf(ml, bv2[p][t] + acc[p][t]);
-            const float mw = max_xor32(ml);
-            const float mref = (mw == -INFINITY) ? 0.f : mw;
-            float e[2][16];
-#pragma unroll
-            for (int p = 0; p < 2; p++)
-#pragma unroll
-              for (int t = 0; t < 16; t++) e[p][t] = exp2_scaled((bv2[p][t] - mref) + acc[p][t], sc);
-            const float sl = tree_sum32(e);
-            const float sw = sum_xor32(sl);
-            if (h == 0) { red_m[wave][rl] = mw; red_s[wave][rl] = sw; }
-          }
+            unit_block<KS, GREEDY, true>(F1, A_lds + rbn * 32 * a_stride, a_stride, accN, accC, bv2, sc, cbase,
+                                         dp, o);
+        } else {
+          unit_block<KS, GREEDY, false>(F0, A_lds, a_stride, accN, accC, bv2, sc, cbase, dp, o);
         }
-        lds_barrier();  // red_* of the tile's units complete
-        // tile records of this chunk: two sealed 16-byte words per request,
-        // stored device-coherent (written through to memory); the word w of
-        // request q is stored by thread q + 128 w (greedy: one word, by
-        // threads q < nrows), so the stores are spread over the four waves
-        const int nwords = GREEDY ? 1 : 2;
-        if (tid < nwords * CH && (tid & (CH - 1)) < nrows) {
-          const int q = tid & (CH - 1), word = tid / CH;
-          const uint32_t tag = E + (uint32_t)k;
-          const uint32_t roff = (uint32_t)(((size_t)(c0 + q) * nt + tile) * FREC_BYTES);
-          uint32_t x0, x1, x2, y0 = 0u, y1 = 0u, y2 = 0u;
-          if (GREEDY) {
-            float v = red_m[0][q];
-            int i = red_i[0][q];
-#pragma unroll
-            for (int w = 1; w < 4; w++) argmax_merge(v, i, red_m[w][q], red_i[w][q]);
-            x0 = __float_as_uint(v);
-            x1 = (uint32_t)i;
-            x2 = 0u;
-          } else {
-            const float m0 = red_m[0][q], m1 = red_m[1][q], m2 = red_m[2][q], m3 = red_m[3][q];
-            const float mt = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
-            auto rescale = [&](float swv, float mwv) {
-              const float d = t_one ? (mwv - mt) : (mwv - mt) * P.invT;
-              return (mwv == -INFINITY) ? 0.f : swv * exp_acc(d);
-            };
-            const float s0 = rescale(red_s[0][q], m0), s1 = rescale(red_s[1][q], m1);
-            const float s2 = rescale(red_s[2][q], m2), s3 = rescale(red_s[3][q], m3);
-            const float st = (s0 + s1) + (s2 + s3);
-            x0 = __float_as_uint(mt);
-            x1 = __float_as_uint(st);
-            x2 = __float_as_uint(s0);
-            y0 = __float_as_uint(s1);
-            y1 = __float_as_uint(s2);
-            y2 = __float_as_uint(s3);
-            if (word == 0 && (is_bad(st) || !(mt == mt) || mt == INFINITY)) raise_err(P.err, DSPARK_DERR_NONFINITE);
-          }
-          if (word == 0)
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4{x0, x1, x2, seal(tag, x0, x1, x2)}, rec_rs, (int)roff, 0,
-                                                   AUX_DEV);
-          else
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4{y0, y1, y2, seal(tag, y0, y1, y2)}, rec_rs,
-                                                   (int)roff + 16, 0, AUX_DEV);
+        if (rb == nrb - 1) {
+          lds_barrier();  // red_* of the tile's units complete
+          records(k, c0, nrows, tile);
         }
+        g++;
+      };
+      for (int u = 0; u < n_u;) {
+        iter(accA, accB, u++);
+        if (u >= n_u) break;
+        iter(accB, accA, u++);
       }
     }
 

@@ -247,10 +247,13 @@ def parity_counts(dump, ref):
     import numpy as np
     z = np.load(dump)
     rows = z["rows"]
+    vl = ref["verify_len"]
+    if vl is None:  # no scheduler: every request verifies its whole block
+        vl = np.full(ref["accept_len"].shape, ref["draft_tokens"].shape[1], np.int32)
     same = ((ref["draft_tokens"][rows] == z["draft_tokens"]).all(axis=1)
             & (ref["out_tokens"][rows] == z["out_tokens"]).all(axis=1)
             & (ref["accept_len"][rows] == z["accept_len"])
-            & (ref["verify_len"][rows] == z["verify_len"]))
+            & (vl[rows] == z["verify_len"]))
     fl = z["flags"]
     return dict(rows=int(len(rows)), flagged=int(fl.sum()), flagged_mismatch=int((~same & fl).sum()),
                 unflagged_mismatch=int((~same & ~fl).sum()),

@@ -423,7 +423,7 @@ def _side_stream(device):
 
 
 def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, scheduler="early", theta=None,
-              head="markov"):
+              head="markov", check=False):
     """draft -> schedule -> verify on a dict of device tensors.
 
     The scheduler reads only confidences and the cost table, and verify's
@@ -439,7 +439,11 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
     lagged confidences ``conf_lag`` of the input dict) or "threshold"
     (dspark_schedule_threshold with ``theta``).  ``head`` "rnn" drafts with
     dspark_draft_rnn (gate weights ``Wx``, ``Ws``, ``rnn_bias`` of the input
-    dict) and verifies with dspark_verify_rnn.
+    dict) and verifies with dspark_verify_rnn.  ``check``: synchronize, read
+    (and clear) the error words of ``ws`` and ``ws_sched`` and raise
+    DSparkError if any device-side error bit is set; a round with
+    DSPARK_DERR_SYNC (a wait of the one-launch draft that ran out of time) has
+    invalid outputs.  Not for graph capture, since it synchronizes.
     """
     if head not in ("markov", "rnn"):
         raise ValueError(f"head must be 'markov' or 'rnn', got {head!r}")
@@ -488,5 +492,10 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
     else:
         ot, al, tp = verify(d["target"], d["base"], d["W1"], d["W2"], d["anchor"], tok, prob, stats, L,
                             d["u_accept"], d["u_final"], temperature, ws, finish_only=True)
+    if check:
+        bits = device_error(ws) | (device_error(ws_sched) if ws_sched is not None else 0)
+        if bits:
+            names = ", ".join(v for k, v in DERR_BITS.items() if bits & k)
+            raise DSparkError(f"device-side error bits {bits:#x} ({names}) set by the round")
     return dict(draft_tokens=tok, draft_probs=prob, draft_stats=stats, verify_len=L, n_admitted=n,
                 out_tokens=ot, accept_len=al, target_probs=tp, ws_sched=ws_sched, states=states)

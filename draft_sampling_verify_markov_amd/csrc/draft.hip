@@ -19,9 +19,11 @@
 //        never written to memory.
 //   K2 draft_select    one workgroup per request.
 //        Combines the tile records in fp64, finds the tile and then the
-//        64-column chunk holding u * Z, recomputes that chunk's logits with the
-//        same MFMA instruction sequence and does the in-chunk inverse-CDF
-//        search.
+//        64-column chunk holding u * Z, recomputes that chunk's logits (the
+//        bias with vector FMAs over all 256 threads and a fixed-order sum of
+//        their partials, so its rounding differs from the MFMA sums behind
+//        the records by fp32 accumulation error only) and does the in-chunk
+//        inverse-CDF search.
 #include <stdlib.h>
 #include <string.h>
 

@@ -12,10 +12,12 @@
 //   stream    grid = (gamma+1) x R x ceil(V / 4096), position-major.  Streams
 //             target rows j = 0..L_r of request r in 4096-column segments
 //             (non-temporal loads) and writes per-1024-column softmax partials;
-//             the segment holding the drafted token x_{j+1} stores its logit.
+//             it reads no drafted token, so it can run before or beside the
+//             draft.
 //   decide    one workgroup per request, one wave per position: fp64 row
-//             statistics, p_{j+1}(x_{j+1}), the accept tests u < p/q, and the
-//             first rejected position.
+//             statistics, the target logit at the drafted token x_{j+1} and
+//             p_{j+1}(x_{j+1}), the accept tests u < p/q, and the first
+//             rejected position.
 //   residual  persistent, one workgroup per compute unit over the 256-column
 //             tiles (T > 0 only).  For requests that rejected at k*,
 //             recomputes the draft logits of position k* with the MFMA bias

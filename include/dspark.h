@@ -27,8 +27,16 @@
  *
  * Conventions (all calls)
  *   - Every pointer argument is a DEVICE pointer owned by the caller, except
- *     where a parameter says "host".  The library allocates nothing, keeps no
- *     global state and never modifies an input.
+ *     where a parameter says "host".  The library allocates no device memory
+ *     (dspark_draft_noalloc's static array aside) and never modifies an input.
+ *     Process-wide state: per device, whether the one-launch draft fits (an
+ *     occupancy query, cached on first use) and dspark_draft_noalloc's array;
+ *     per host thread, the optional launch-timing hook (dspark_profile_arm).
+ *     Two environment variables are read on every dspark_draft call:
+ *     DSPARK_DRAFT_KERNEL=stepwise selects the per-step kernels, and
+ *     DSPARK_FUSED_SPIN_TICKS overrides the one-launch draft's wait limit
+ *     (in 100 MHz ticks; 0 makes every wait that does not succeed at once
+ *     give up, which the tests of that path use).
  *   - Arrays are dense, row-major, with the last index contiguous.
  *   - W1/W2 are bf16 (bit patterns in uint16) or fp32 according to w_type.
  *   - No random numbers are drawn inside the library: every random choice is
@@ -141,10 +149,15 @@ const char* dspark_status_string(int status);
  * ceil(V / 256) <= min(512, 2 x the compute units), all gamma steps run in one
  * persistent launch of one workgroup per compute unit; its workgroups wait
  * for each other's results through the workspace, so every one of them must
- * be resident at once (checked on the host; a wait that exceeds its time
- * limit sets DSPARK_DERR_SYNC).  Otherwise, or with the environment variable
- * DSPARK_DRAFT_KERNEL=stepwise, two kernels per step run.  Both paths give
- * identical outputs.
+ * be resident at once.  The host checks that one workgroup fits on a compute
+ * unit (480 registers per lane, about 148 KiB of LDS), not that the compute
+ * units are free: kernels of other streams or processes that occupy them can
+ * keep part of the grid waiting.  Every wait is bounded (0.5 s); one that
+ * runs out sets DSPARK_DERR_SYNC, every workgroup still finishes, and the
+ * call's outputs are then INVALID: a caller that shares the GPU must read the
+ * error word (dspark_device_error) before using them.  Otherwise, or with the
+ * environment variable DSPARK_DRAFT_KERNEL=stepwise, two kernels per step
+ * run.  Both paths give identical outputs.
  */
 int dspark_draft(const float* base, const void* W1, const void* W2, dspark_wtype w_type,
                  const int32_t* anchor, const float* u_draft, int R, int gamma, int V, int r,

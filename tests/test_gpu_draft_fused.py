@@ -176,6 +176,27 @@ def test_wait_time_out_sets_sync_error(monkeypatch):
         assert np.array_equal(a[key], b[key]), key
 
 
+def test_checked_round_raises_on_sync_error(monkeypatch):
+    """run_round(check=True) reads both error words after the round: a round
+    whose one-launch draft gave up waiting (time limit 0) raises DSparkError
+    naming SYNC; the same round with the normal limit returns its outputs and
+    leaves both error words clear."""
+    monkeypatch.delenv("DSPARK_DRAFT_KERNEL", raising=False)
+    cfg = config(1, R=64, gamma=4, V=65536, r=128, w_dtype="bf16", table="linear")
+    inp = make_inputs(cfg, seed=43)
+    d = to_dev(inp)
+    ws = D.new_workspace(64, 4, 65536, 128, dev())
+    monkeypatch.setenv("DSPARK_FUSED_SPIN_TICKS", "0")
+    say("[checked] round with a zero time limit")
+    with pytest.raises(D.DSparkError, match="SYNC"):
+        D.run_round(d, 1.0, ws, check=True)
+    monkeypatch.delenv("DSPARK_FUSED_SPIN_TICKS")
+    say("[checked] round with the normal limit")
+    out = D.run_round(d, 1.0, ws, check=True)
+    assert D.device_error(ws) == 0 and D.device_error(out["ws_sched"]) == 0
+    assert (out["accept_len"] >= 0).all().item()
+
+
 def test_one_launch_draft_in_a_graph(monkeypatch):
     """Captured once, replayed several times with eager work in between: every
     replay gives the eager result."""

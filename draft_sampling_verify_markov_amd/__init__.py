@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     DSPARK_W_F32,
     DERR_BITS,
     DSparkError,
+    DSparkDeviceError,
     lib_path,
     load_library,
     workspace_size,
@@ -36,7 +37,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "DSPARK_W_BF16", "DSPARK_W_F32", "DERR_BITS", "DSparkError", "lib_path", "load_library",
+    "DSPARK_W_BF16", "DSPARK_W_F32", "DERR_BITS", "DSparkError", "DSparkDeviceError", "lib_path", "load_library",
     "workspace_size", "new_workspace", "workspace_init", "device_error", "draft", "draft_noalloc", "schedule", "schedule_async", "schedule_threshold", "accept_rates",
     "verify", "run_round", "draft_rnn", "verify_rnn", "verify_stream", "sts_workspace_size", "new_sts_workspace", "sts_fit", "sts_apply",
 ]

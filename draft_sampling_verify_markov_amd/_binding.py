@@ -19,6 +19,16 @@ class DSparkError(RuntimeError):
         self.status = status
 
 
+class DSparkDeviceError(DSparkError):
+    """Device-side error bits (DSPARK_DERR_*) found after a round."""
+
+    def __init__(self, bits):
+        names = ", ".join(v for k, v in DERR_BITS.items() if bits & k)
+        RuntimeError.__init__(self, f"device-side error bits {bits:#x} ({names}) set by the round")
+        self.status = None
+        self.bits = bits
+
+
 def lib_path():
     return os.environ.get("DSPARK_LIB", os.path.join(HERE, "libdspark.so"))
 
@@ -428,12 +438,13 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
 
     The scheduler reads only confidences and the cost table, and verify's
     target-row stream reads only the target and the verify lengths: both run
-    on a side stream concurrently with the draft (forked from and joined back
-    to the current stream; capturable into a HIP graph); verify then finishes
-    on the current stream.  The early-stop scheduler on a pool of at most
-    1024 candidates is a workgroup small enough to share a compute unit with
-    the one-launch draft; the other schedulers run first on the current
-    stream.  The scheduler uses its own small workspace
+    on the current stream while the draft runs on a side stream (forked from
+    and joined back to the current stream; capturable into a HIP graph);
+    verify then finishes on the current stream.  The draft is the longer of
+    the two branches, so the join waits on a kernel that has already ended
+    or is about to.  The early-stop scheduler on a pool of at most 1024
+    candidates is a workgroup small enough to share a compute unit with the
+    one-launch draft; the other schedulers run first, before the fork.  The scheduler uses its own small workspace
     ``ws_sched`` (allocated here if not given).  ``scheduler`` is
     "early" (dspark_schedule), "async" (dspark_schedule_async with the
     lagged confidences ``conf_lag`` of the input dict) or "threshold"
@@ -454,37 +465,40 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
     d = dev_inputs
     dev = d["base"].device
     cur = torch.cuda.current_stream(dev)
+    R, g, V = d["base"].shape
     L = n = None
     sched = use_scheduler and d.get("conf") is not None
     if sched and ws_sched is None:
         ws_sched = torch.zeros(256, dtype=torch.uint8, device=dev)
     beside = sched and scheduler == "early" and d["conf"].numel() <= 1024
-    side = _side_stream(dev)
-    if beside:
-        # outputs allocated on the current stream, which reads them later
-        out = (torch.empty(d["conf"].shape[0], dtype=torch.int32, device=dev),
-               torch.empty(1, dtype=torch.int32, device=dev), None)
-        side.wait_stream(cur)
-        with torch.cuda.stream(side):
-            L, n, _ = schedule(d["conf"], d["sps"], ws_sched, out=out, with_cum=False)
-    elif sched:
+    if sched and not beside:
         if scheduler == "async":
             L, n, _ = schedule_async(d["conf"], d["conf_lag"], d["sps"], ws_sched, with_cum=False)
         elif scheduler == "threshold":
             L, n, _ = schedule_threshold(d["conf"], theta, ws_sched, with_cum=False)
         else:
             L, n, _ = schedule(d["conf"], d["sps"], ws_sched, with_cum=False)
-    # side stream: the target-row stream of verify (it needs only the verify
-    # lengths), overlapping the draft
-    side.wait_stream(cur)
-    with torch.cuda.stream(side):
-        verify_stream(d["target"], L, temperature, ws)
+    # the draft's outputs are allocated on the current stream, which reads them
+    # after the join
+    tok = torch.empty((R, g), dtype=torch.int32, device=dev)
+    prob = torch.empty((R, g), dtype=torch.float32, device=dev)
+    stats = torch.empty((R, g, 2), dtype=torch.float32, device=dev)
     states = None
     if head == "rnn":
-        tok, prob, stats, states = draft_rnn(d["base"], d["W1"], d["W2"], d["Wx"], d["Ws"], d["rnn_bias"],
-                                             d["anchor"], d["u_draft"], temperature, ws)
-    else:
-        tok, prob, stats = draft(d["base"], d["W1"], d["W2"], d["anchor"], d["u_draft"], temperature, ws)
+        states = torch.empty((R, g, d["W1"].shape[1]), dtype=d["W1"].dtype, device=dev)
+    side = _side_stream(dev)
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        if head == "rnn":
+            draft_rnn(d["base"], d["W1"], d["W2"], d["Wx"], d["Ws"], d["rnn_bias"], d["anchor"], d["u_draft"],
+                      temperature, ws, out=(tok, prob, stats, states))
+        else:
+            draft(d["base"], d["W1"], d["W2"], d["anchor"], d["u_draft"], temperature, ws, out=(tok, prob, stats))
+    # current stream, beside the draft: the scheduler (when small) and the
+    # target-row stream of verify (it needs only the verify lengths)
+    if beside:
+        L, n, _ = schedule(d["conf"], d["sps"], ws_sched, with_cum=False)
+    verify_stream(d["target"], L, temperature, ws)
     cur.wait_stream(side)
     if head == "rnn":
         ot, al, tp = verify_rnn(d["target"], d["base"], states, d["W2"], tok, prob, stats, L, d["u_accept"],
@@ -495,7 +509,6 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
     if check:
         bits = device_error(ws) | (device_error(ws_sched) if ws_sched is not None else 0)
         if bits:
-            names = ", ".join(v for k, v in DERR_BITS.items() if bits & k)
-            raise DSparkError(f"device-side error bits {bits:#x} ({names}) set by the round")
+            raise DSparkDeviceError(bits)
     return dict(draft_tokens=tok, draft_probs=prob, draft_stats=stats, verify_len=L, n_admitted=n,
                 out_tokens=ot, accept_len=al, target_probs=tp, ws_sched=ws_sched, states=states)

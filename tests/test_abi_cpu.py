@@ -251,3 +251,9 @@ def _draft_noalloc(lib, **kw):
 def test_draft_noalloc_rejects_bad_arguments_and_oversized_calls(lib, kw, status):
     """Checked on the host before the scratch array is touched."""
     assert _draft_noalloc(lib, **kw) == status
+
+
+def test_device_error_names_its_bits():
+    e = D.DSparkDeviceError(128 | 8)
+    assert isinstance(e, D.DSparkError) and e.bits == 136
+    assert "SYNC" in str(e) and "TOKEN" in str(e) and "NONFINITE" not in str(e)

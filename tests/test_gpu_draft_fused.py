@@ -188,7 +188,7 @@ def test_checked_round_raises_on_sync_error(monkeypatch):
     ws = D.new_workspace(64, 4, 65536, 128, dev())
     monkeypatch.setenv("DSPARK_FUSED_SPIN_TICKS", "0")
     say("[checked] round with a zero time limit")
-    with pytest.raises(D.DSparkError, match="SYNC"):
+    with pytest.raises(D.DSparkDeviceError, match="SYNC"):
         D.run_round(d, 1.0, ws, check=True)
     monkeypatch.delenv("DSPARK_FUSED_SPIN_TICKS")
     say("[checked] round with the normal limit")

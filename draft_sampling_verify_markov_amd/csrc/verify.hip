@@ -162,29 +162,46 @@ __global__ __launch_bounds__(256) void k_verify_stream(VerifyArgs<WT> P) {
 // ---------------------------------------------------------------------------
 // accept tests: one workgroup per request, one wave per position
 
+// Waves per decide workgroup: one per target row j = 0..gamma, at most 16.
+__host__ __device__ constexpr int decide_waves(int gamma) { return gamma + 1 < 16 ? gamma + 1 : 16; }
+
+// Every load a position needs is issued before any result is used: the verify
+// length, the drafted token x_{j+1} and, as soon as it arrives, the target
+// logit at it, the row's tile partials, q and u.  Positions past L are
+// computed on whatever the buffers hold and discarded.
 template <typename WT, bool GREEDY>
-__global__ __launch_bounds__(256) void k_verify_decide(VerifyArgs<WT> P) {
+__global__ __launch_bounds__(1024) void k_verify_decide(VerifyArgs<WT> P) {
   __shared__ int s_ok[DSPARK_MAX_GAMMA + 1];
   const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int nw = decide_waves(P.gamma);
   const int nvt = ceil_div(P.V, VTILE);
   const int L = P.L_of(row, tid == 0);
   const bool t_one = (P.T == 1.0f);
   const double invTd = t_one ? 1.0 : 1.0 / (double)P.T;
 
-  for (int j = wave; j <= L; j += 4) {
+  for (int j = wave; j <= P.gamma; j += nw) {
     const size_t rowj = (size_t)row * (P.gamma + 1) + j;
     const float2* vp = P.vpart + rowj * nvt;
     const size_t ev = (size_t)row * P.gamma + j;
+    const bool drafted = j < P.gamma;
+    // lane 0: the drafted token and the target logit at it
+    int x = 0;
+    float tx = 0.f, q = 1.f, u = 0.f;
+    if (lane == 0 && drafted) {
+      x = P.dtok[ev];
+      q = P.dprob[ev];
+      if (!GREEDY) u = P.u_acc[ev];
+      if (!GREEDY && x >= 0 && x < P.V) tx = P.target[rowj * P.V + x];
+    }
     if (GREEDY) {
       float bv = -INFINITY;
       int bi = 0x7fffffff;
       for (int t = lane; t < nvt; t += 64) argmax_merge(bv, bi, vp[t].x, __float_as_int(vp[t].y));
       wave_argmax(bv, bi);
-      if (lane == 0) {
+      if (lane == 0 && j <= L) {
         P.rowstat[rowj] = make_double2((double)bv, (double)bi);
         if (j < L) {
-          const int x = checked_token(P.dtok[ev], P.V, P.err);
-          const bool ok = (x == bi);
+          const bool ok = (checked_token(x, P.V, P.err) == bi);
           P.tp[ev] = ok ? 1.0f : 0.0f;
           s_ok[j] = ok;
         }
@@ -197,21 +214,19 @@ __global__ __launch_bounds__(256) void k_verify_decide(VerifyArgs<WT> P) {
       for (int t = lane; t < nvt; t += 64)
         zl += (double)vp[t].y * (double)exp_acc((vp[t].x - M) * (float)invTd);
       const double Z = wave_sum_d(zl);
-      if (lane == 0) {
+      if (lane == 0 && j <= L) {
         P.rowstat[rowj] = make_double2((double)M, Z);
         if (j < L) {
-          // target logit at the drafted token, read here so that the row
-          // stream does not depend on the draft
-          const int x = checked_token(P.dtok[ev], P.V, P.err);
-          const double p = exp(((double)P.target[rowj * P.V + x] - (double)M) * invTd) / Z;
-          const float q = P.dprob[ev];
+          // the target logit at the drafted token is read here (not by the
+          // row stream), so the stream does not depend on the draft
+          checked_token(x, P.V, P.err);
+          const double p = exp(((double)tx - (double)M) * invTd) / Z;
           bool ok;
           if (!(q > 0.f)) {
             raise_err(P.err, DSPARK_DERR_PROB);
             ok = false;
           } else {
-            const float u = checked_uniform(P.u_acc[ev], P.err);
-            ok = (double)u < p / (double)q;
+            ok = (double)checked_uniform(u, P.err) < p / (double)q;
           }
           P.tp[ev] = (float)p;
           s_ok[j] = ok;
@@ -637,9 +652,9 @@ static int launch_verify_finish(const VerifyArgs<WT>& P, hipStream_t stream) {
   prof_before(DSPARK_KID_VERIFY_DECIDE, stream);
   for (int rep = prof_repeat(DSPARK_KID_VERIFY_DECIDE); rep > 0; rep--) {
     if (greedy)
-      hipLaunchKernelGGL((k_verify_decide<WT, true>), dim3(P.R), dim3(256), 0, stream, P);
+      hipLaunchKernelGGL((k_verify_decide<WT, true>), dim3(P.R), dim3(64 * decide_waves(P.gamma)), 0, stream, P);
     else
-      hipLaunchKernelGGL((k_verify_decide<WT, false>), dim3(P.R), dim3(256), 0, stream, P);
+      hipLaunchKernelGGL((k_verify_decide<WT, false>), dim3(P.R), dim3(64 * decide_waves(P.gamma)), 0, stream, P);
   }
   prof_after(DSPARK_KID_VERIFY_DECIDE, stream);
   if (!greedy) {

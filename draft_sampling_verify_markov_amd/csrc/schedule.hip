@@ -109,7 +109,10 @@ __device__ __forceinline__ void pool_sort(const float* __restrict__ conf, int R,
   for (int m = 0; m < KPT; m++) k[m] = sm.bufs[0][tid + NT * m];
 
   int nb = NB - 1;  // next exchange buffer (bufs[0] is still being read above)
+  // unrolled: every stage's distances and directions are constants
+#pragma unroll
   for (int kk = 2; kk <= NS; kk <<= 1) {
+#pragma unroll
     for (int jj = kk >> 1; jj >= 64; jj >>= 1) {
       if (jj >= NT) {
         const int mj = jj / NT;

@@ -22,10 +22,12 @@ HIPCC_FLAGS = [
 ]
 
 
-# Per-source extra flags.  The one-launch draft keeps its resident W2
-# fragments in the AGPRs, so its MFMAs write their results to VGPRs.
+# Per-source extra flags.  The one-launch draft and the resident-W2 residual
+# pass keep their W2 fragments in the AGPRs, so their MFMAs write their
+# results to VGPRs.
 EXTRA_FLAGS = {
     "draft_fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "verify.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

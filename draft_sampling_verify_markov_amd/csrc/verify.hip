@@ -27,6 +27,8 @@
 //   finalize  one workgroup per request: residual or bonus inverse-CDF sample
 //             (fp64 scan over tiles, recompute of one chunk or tile), emitted
 //             tokens and the p_k(x_k) output.
+#include <type_traits>
+
 #include "select.h"
 
 namespace dspark {
@@ -427,6 +429,249 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
+// Acceptance-label pass with bf16 factors and at most two tiles per
+// workgroup: the W2 fragments of both tiles stay in registers for the whole
+// launch, so W2 is read from memory once per call instead of once per chunk
+// of items (k_residual_partials reloads a tile's fragment for every chunk).
+// Chunks of 96 items (the LDS then holds two base-row buffers and one
+// target-row buffer); units are taken row block first, tile second.  A unit's
+// base rows arrive by direct-to-LDS loads two units ahead, its target rows
+// one unit ahead; a unit's records are written after the next unit's first
+// barrier.  Same per-element arithmetic and sums as k_residual_partials.  (For
+// the residual of dspark_verify, one chunk of at most 128 rejected requests,
+// loading both tiles' fragments up front measured slower than the per-tile
+// kernel.)
+template <int KS>
+__device__ __forceinline__ void mma_rows(const typename BiasBlock<uint16_t>::template Frag<KS>& F, int r,
+                                         const uint16_t* A_rows, int a_stride, f32x16 (&acc)[2]) {
+  const int lane = threadIdx.x & 63, j = lane & 31, h = lane >> 5;
+  const int nks = r / 16;
+  const uint16_t* ap = A_rows + j * a_stride + 8 * h;
+#pragma unroll
+  for (int ks = 0; ks < KS; ks++) {
+    if (ks < nks) {
+      const bf16x8 bb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(ap + ks * 16));
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, u32x4{F.w[ks][0], F.w[ks][1], F.w[ks][2], F.w[ks][3]});
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, u32x4{F.w[ks][4], F.w[ks][5], F.w[ks][6], F.w[ks][7]});
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bb, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bb, acc[1], 0, 0, 0);
+    }
+  }
+}
+
+template <int KS, bool TVM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_residual_resident(
+    VerifyArgs<uint16_t> P) {
+  using WT = uint16_t;
+  using BB = BiasBlock<WT>;
+  constexpr int APAD = BB::APAD;
+  constexpr int CH = 96;
+  __shared__ __align__(16) WT A_lds[CH * (DSPARK_MAX_RANK + APAD)];
+  __shared__ __align__(16) float Xb[2][32 * BSTRIDE];
+  __shared__ __align__(16) float Xt[32 * BSTRIDE];
+  __shared__ float red_s[2][4][32];
+  __shared__ int s_list[CH], s_tok[CH], s_cnt[2];
+  __shared__ uint32_t s_boff[CH], s_toff[CH];
+  __shared__ float s_Mt[CH], s_iZt[CH], s_mq[CH], s_iZq[CH];
+
+  const int a_stride = P.r + APAD;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int j = lane & 31, h = lane >> 5;
+  const int nt = ceil_div(P.V, TILE);
+  const int G = gridDim.x, b = blockIdx.x;
+  if (b >= nt) return;
+  const int ntl = (b + G < nt) ? 2 : 1;
+  const float sc = (P.T == 1.0f) ? LOG2E_F : LOG2E_F * P.invT;
+
+  // the fragments, in MFMA operand form, held in the accumulation registers
+  // (AGPRs, which the MFMAs read their A operand from); the MFMA results go to
+  // VGPRs (this file is built with -amdgpu-mfma-vgpr-form)
+  typename BB::template Frag<KS> F0, F1;
+  BB::template load<KS>(F0, P.W2, P.V, P.r, b * TILE + wave * WCOLS);
+  if (ntl > 1) BB::template load<KS>(F1, P.W2, P.V, P.r, (b + G) * TILE + wave * WCOLS);
+  BB::template to_operands<KS>(F0);
+  if (ntl > 1) BB::template to_operands<KS>(F1);
+#pragma unroll
+  for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+    for (int e = 0; e < 8; e++) asm volatile("" : "+a"(F0.w[ks][e]), "+a"(F1.w[ks][e]));
+
+  const int nitems = TVM ? P.R * P.gamma : P.R;
+  for (int c0 = 0; c0 < nitems; c0 += CH) {
+    const int r0 = TVM ? c0 / P.gamma : c0;
+    int nrej;
+    __syncthreads();  // the previous chunk is done with every LDS array
+    if (TVM) {
+      nrej = min(CH, nitems - c0);
+    } else {
+      // compaction of the chunk's rejected requests (order kept)
+      const int nrows = min(CH, P.R - c0);
+      bool mine = false;
+      if (tid < nrows) mine = P.rej[c0 + tid] <= P.L_of(c0 + tid);
+      const uint64_t bal = __ballot(mine);
+      if (tid < CH && lane == 0) s_cnt[wave] = __popcll(bal);
+      __syncthreads();
+      nrej = s_cnt[0] + s_cnt[1];
+      if (nrej == 0) continue;  // uniform
+      if (mine) {
+        const int pos = (wave == 1 ? s_cnt[0] : 0) + __popcll(bal & ((1ull << lane) - 1ull));
+        s_list[pos] = tid;
+      }
+      __syncthreads();
+    }
+    if (tid < nrej) {
+      int row, ks;  // request and 1-based position of the item
+      if (TVM) {
+        const int item = c0 + tid;
+        row = item / P.gamma;
+        ks = item - row * P.gamma + 1;
+        s_list[tid] = tid;
+      } else {
+        row = c0 + s_list[tid];
+        ks = P.rej[row];  // k*
+      }
+      const double2 rs = P.rowstat[(size_t)row * (P.gamma + 1) + ks - 1];
+      const size_t ev = (size_t)row * P.gamma + ks - 1;
+      s_Mt[tid] = (float)rs.x;
+      s_iZt[tid] = (float)(1.0 / rs.y);
+      s_mq[tid] = P.dstats[2 * ev];
+      s_iZq[tid] = (float)(1.0 / (double)P.dstats[2 * ev + 1]);
+      const uint32_t rl = (uint32_t)(row - r0);
+      s_boff[tid] = (rl * (uint32_t)P.gamma + (uint32_t)(ks - 1)) * (uint32_t)P.V * 4u;
+      s_toff[tid] = (rl * (uint32_t)(P.gamma + 1) + (uint32_t)(ks - 1)) * (uint32_t)P.V * 4u;
+      s_tok[tid] = P.prev_of(row, ks);
+    }
+    __syncthreads();
+
+    const int nrb = ceil_div(nrej, 32);
+    const int nunits = nrb * ntl;
+    const size_t R_left = (size_t)(P.R - r0);
+    const rsrc_t brs = make_rsrc(P.base + (size_t)r0 * P.gamma * P.V, R_left * P.gamma * P.V * 4);
+    const rsrc_t trs = make_rsrc(P.target + (size_t)r0 * (P.gamma + 1) * P.V, R_left * (P.gamma + 1) * P.V * 4);
+    // base rows of unit u: wave w loads compacted rows 4i + w of the block
+    // (8 loads per wave; rows past nrej re-read row 0)
+    auto issue_b = [&](int u) {
+      if (u >= nunits) return;
+      const int rb = u / ntl, ti = u - rb * ntl;
+      const int tile0 = (b + ti * G) * TILE;
+      const int w = __builtin_amdgcn_readfirstlane(wave);
+      const uint32_t coff = (uint32_t)(tile0 + 4 * lane) * 4u;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const int q = rb * 32 + 4 * i + w;
+        const int qc = q < nrej ? q : 0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            brs, (__attribute__((address_space(3))) void*)(Xb[u & 1] + (4 * i + w) * BSTRIDE), 16,
+            (int)(s_boff[qc] + coff), 0, 0, AUX_NT);
+      }
+    };
+    // target rows of unit u into Xt (one buffer: issued once the previous
+    // unit has read it)
+    auto issue_t = [&](int u) {
+      if (u >= nunits) return;
+      const int rb = u / ntl, ti = u - rb * ntl;
+      const int tile0 = (b + ti * G) * TILE;
+      const int w = __builtin_amdgcn_readfirstlane(wave);
+      const uint32_t coff = (uint32_t)(tile0 + 4 * lane) * 4u;
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const int q = rb * 32 + 4 * i + w;
+        const int qc = q < nrej ? q : 0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            trs, (__attribute__((address_space(3))) void*)(Xt + (4 * i + w) * BSTRIDE), 16,
+            (int)(s_toff[qc] + coff), 0, 0, AUX_NT);
+      }
+    };
+    // records of unit u (its 32 rows, its tile) from the four waves' sums
+    auto records = [&](int u) {
+      const int rb = u / ntl, ti = u - rb * ntl;
+      const int tile = b + ti * G;
+      const int q = rb * 32 + tid;
+      if (tid < 32 && q < nrej) {
+        const float s0 = red_s[u & 1][0][tid], s1 = red_s[u & 1][1][tid];
+        const float s2 = red_s[u & 1][2][tid], s3 = red_s[u & 1][3][tid];
+        if (TVM) {
+          P.tvpart[(size_t)(c0 + q) * nt + tile] = (s0 + s1) + (s2 + s3);
+        } else {
+          float4* rec = P.rrec + ((size_t)(c0 + s_list[q]) * nt + tile) * 2;
+          rec[0] = make_float4(0.f, (s0 + s1) + (s2 + s3), s0, s1);
+          rec[1] = make_float4(s2, s3, 0.f, 0.f);
+        }
+      }
+    };
+
+    // W1 rows of the chunk's items straight to LDS: one 16-byte piece per
+    // lane, one row per load (r / 8 lanes), wave w takes items w, w + 4, ...
+    {
+      const rsrc_t wrs = make_rsrc(P.W1, (size_t)P.a_rows * P.r * 2);
+      const int w = __builtin_amdgcn_readfirstlane(wave);
+      for (int i = w; i < nrej; i += 4) {
+        const int tk = __builtin_amdgcn_readfirstlane(s_tok[i]);
+        if (8 * lane < P.r)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              wrs, (__attribute__((address_space(3))) void*)(A_lds + i * a_stride), 16,
+              (int)((uint32_t)(tk * P.r + 8 * lane) * 2u), 0, 0, 0);
+      }
+    }
+    issue_b(0);
+    issue_t(0);
+    issue_b(1);
+    // the W1 rows (issued before unit 0's and unit 1's loads) have landed
+    if (nunits > 1)
+      wait_vmcnt<24>();
+    else
+      wait_vmcnt<16>();
+    lds_barrier();  // A_lds complete; unit 0's and unit 1's rows in flight
+
+    auto unit = [&](int u) {
+      const int rb = u / ntl, ti = u - rb * ntl;
+      const int tile = b + ti * G, cbase = tile * TILE + wave * WCOLS;
+      f32x16 acc[2];
+#pragma unroll
+      for (int p = 0; p < 2; p++)
+#pragma unroll
+        for (int t = 0; t < 16; t++) acc[p][t] = 0.f;
+      if (ti == 0)
+        mma_rows<KS>(F0, P.r, A_lds + rb * 32 * a_stride, a_stride, acc);
+      else
+        mma_rows<KS>(F1, P.r, A_lds + rb * 32 * a_stride, a_stride, acc);
+      // this unit's base rows and target values; the next unit's base rows
+      // (8 loads, issued after them) may stay in flight
+      if (u + 1 < nunits)
+        wait_vmcnt<8>();
+      else
+        wait_vmcnt<0>();
+      lds_barrier();
+      if (u > 0) records(u - 1);
+      float bv[2][16], tc[2][16];
+      if ((tile + 1) * TILE <= P.V) {
+        stage_read_full(Xb[u & 1], wave * WCOLS, bv);
+        stage_read_full(Xt, wave * WCOLS, tc);
+      } else {
+        stage_read(Xb[u & 1], true, P.V, cbase, wave * WCOLS, bv);
+        stage_read(Xt, true, P.V, cbase, wave * WCOLS, tc);
+      }
+      lds_barrier();  // every wave has its rows out of Xb[u & 1] and Xt
+      issue_t(u + 1);
+      issue_b(u + 2);
+      const int q = rb * 32 + j;
+      const int qc = q < nrej ? q : 0;
+      const float Mt = s_Mt[qc], iZt = s_iZt[qc], mq = s_mq[qc], iZq = s_iZq[qc];
+      // the residual in place of the target values
+#pragma unroll
+      for (int p = 0; p < 2; p++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) tc[p][i] = residual_elem(tc[p][i], bv[p][i], acc[p][i], Mt, iZt, mq, iZq, sc);
+      const float sl = tree_sum32(tc);
+      const float sw = sum_xor32(sl);
+      if (h == 0) red_s[u & 1][wave][j] = sw;
+    };
+    for (int u = 0; u < nunits; u++) unit(u);
+    lds_barrier();  // the last unit's sums
+    records(nunits - 1);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // finalize: one wave per request
 
@@ -615,15 +860,30 @@ __global__ __launch_bounds__(256) void k_accept_finalize(VerifyArgs<WT> P, float
   }
 }
 
+// Residual tile records: the per-tile kernel; for the acceptance labels with
+// bf16 factors and at most two tiles per workgroup, the resident-W2 kernel.
+template <typename WT, bool TVM>
+static void launch_residual(const VerifyArgs<WT>& P, hipStream_t stream) {
+  const int nt = ceil_div(P.V, TILE), G = device_cu_count();
+  const int grid_r = min(nt, G);
+  if constexpr (TVM && std::is_same<WT, uint16_t>::value) {
+    if (nt <= 2 * G) {
+      DSPARK_DISPATCH_KS(P.r, hipLaunchKernelGGL((k_residual_resident<KS, TVM>), dim3(grid_r), dim3(256), 0,
+                                                 stream, P));
+      return;
+    }
+  }
+  DSPARK_DISPATCH_KS(P.r, hipLaunchKernelGGL((k_residual_partials<WT, KS, TVM>), dim3(grid_r), dim3(256), 0,
+                                             stream, P));
+}
+
 template <typename WT>
 static int launch_accept_rates(const VerifyArgs<WT>& P, float* out, hipStream_t stream) {
   const int nseg = ceil_div(P.V, VSEG);
   const long long nblk = (long long)(P.gamma + 1) * P.R * nseg;
   hipLaunchKernelGGL((k_verify_stream<WT, false>), dim3((unsigned)nblk), dim3(256), 0, stream, P);
   hipLaunchKernelGGL((k_target_rowstats<WT>), dim3(P.R), dim3(256), 0, stream, P);
-  const int grid_r = min(ceil_div(P.V, TILE), device_cu_count());
-  DSPARK_DISPATCH_KS(P.r, hipLaunchKernelGGL((k_residual_partials<WT, KS, true>), dim3(grid_r), dim3(256), 0,
-                                             stream, P));
+  launch_residual<WT, true>(P, stream);
   hipLaunchKernelGGL((k_accept_finalize<WT>), dim3(ceil_div(P.R * P.gamma, 4)), dim3(256), 0, stream, P, out);
   return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
 }
@@ -646,6 +906,7 @@ static void launch_verify_stream(const VerifyArgs<WT>& P, hipStream_t stream) {
 }
 
 // Accept tests, residual and emission from the stream's partials.
+
 template <typename WT>
 static int launch_verify_finish(const VerifyArgs<WT>& P, hipStream_t stream) {
   const bool greedy = (P.T == 0.f);
@@ -660,9 +921,7 @@ static int launch_verify_finish(const VerifyArgs<WT>& P, hipStream_t stream) {
   if (!greedy) {
     prof_before(DSPARK_KID_RESIDUAL, stream);
     for (int rep = prof_repeat(DSPARK_KID_RESIDUAL); rep > 0; rep--) {
-      const int grid_r = min(ceil_div(P.V, TILE), device_cu_count());
-      DSPARK_DISPATCH_KS(P.r, hipLaunchKernelGGL((k_residual_partials<WT, KS, false>), dim3(grid_r), dim3(256),
-                                                 0, stream, P));
+      launch_residual<WT, false>(P, stream);
     }
     prof_after(DSPARK_KID_RESIDUAL, stream);
   }

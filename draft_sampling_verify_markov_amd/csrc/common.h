@@ -23,10 +23,12 @@ constexpr int TILE = 256;
 constexpr int WCOLS = 64;
 // Rows of the gathered W1 block held in LDS per pass (4 MFMA row blocks of 32).
 constexpr int RCH = 128;
-// Column tile of the target-row partials (one wave, 16 floats per lane) and
-// the column segment one verify-stream workgroup covers (4 such tiles).
+// Column tile of the target-row partials (16 floats per lane of a wave) and
+// the column segment one verify-stream workgroup covers: two such tiles per
+// wave (8 per workgroup), one per wave for the greedy arg-max.
 constexpr int VTILE = 1024;
-constexpr int VSEG = 4 * VTILE;
+__host__ __device__ constexpr int stream_seg(bool greedy) { return (greedy ? 4 : 8) * VTILE; }
+constexpr int VSEG = 4 * VTILE;  // the smaller segment (grid-size checks)
 // Sentinel "no rejection" position in the per-request rejection slot.
 constexpr int NO_REJECT = 1 << 30;
 

@@ -263,12 +263,13 @@ __device__ __forceinline__ void unit_block(const typename BiasBlock<uint16_t>::t
   }
 }
 
-// 480 of the 512 registers per lane: a 32-register wave of a kernel on another
-// stream (verify's target-row stream) still fits beside every wave of this one.
+// 472 of the 512 registers per lane: a 40-register wave of a kernel on another
+// stream (verify's target-row stream, the scheduler) still fits beside every
+// wave of this one.
 // Built with MFMA results in VGPRs (-amdgpu-mfma-vgpr-form): the AGPRs hold
 // the resident W2 fragments.
 template <int KS, bool GREEDY>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdgpu_num_vgpr(240))) void k_draft_fused(FusedArgs P) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdgpu_num_vgpr(236))) void k_draft_fused(FusedArgs P) {
   using WT = uint16_t;
   using BB = BiasBlock<WT>;
   constexpr int APAD = BB::APAD;
@@ -339,8 +340,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
   // resident W2 fragments of this workgroup's tiles, loaded once.  Most of
   // them live in the accumulation registers (AGPRs), which the MFMAs read
   // their A operand from directly, so the VGPRs stay free for the unit
-  // pipeline; the register budget (480 of the 512 per lane, so that a
-  // 32-register wave of a kernel on another stream still fits beside every
+  // pipeline; the register budget (472 of the 512 per lane, so that a
+  // 40-register wave of a kernel on another stream still fits beside every
   // wave of this one) leaves the last two k steps in VGPRs.
   typename BB::template Frag<KS> F0, F1;
   if (ntl > 0) BB::template load<KS>(F0, P.W2, P.V, P.r, b * TILE + wave * WCOLS);

@@ -9,8 +9,8 @@
 // the output is statistically identical to the target model's.
 //
 // Kernels, in stream order (no kernel waits on another workgroup):
-//   stream    grid = (gamma+1) x R x ceil(V / 4096), position-major.  Streams
-//             target rows j = 0..L_r of request r in 4096-column segments
+//   stream    grid = (gamma+1) x R x ceil(V / 8192) (greedy: 4096),
+//             position-major.  Streams target rows j = 0..L_r of request r
 //             (non-temporal loads) and writes per-1024-column softmax partials;
 //             it reads no drafted token, so it can run before or beside the
 //             draft.
@@ -99,31 +99,14 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 // ---------------------------------------------------------------------------
 // target-row stream
 
+// One 1024-column tile of a target row already in registers: lane l holds
+// columns col0 + f*256 + 4l + e (f, e < 4) in v[4f + e], -inf past V.  Writes
+// the tile's partial (max, sum of exp((x - max)/T)) or (max, arg-max).
 template <typename WT, bool GREEDY>
-__global__ __launch_bounds__(256) void k_verify_stream(VerifyArgs<WT> P) {
-  const int nseg = ceil_div(P.V, VSEG), nvt = ceil_div(P.V, VTILE);
-  const int b = blockIdx.x;
-  const int jpos = b / (P.R * nseg);
-  const int rem = b - jpos * P.R * nseg;
-  const int row = rem / nseg, seg = rem - row * nseg;
-  const int L = P.L_of(row);
-  if (jpos > L) return;
-
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const size_t rowj = (size_t)row * (P.gamma + 1) + jpos;
-  const float* trow = P.target + rowj * P.V;
-  const bool t_one = (P.T == 1.0f);
-
-  const int tt = seg * 4 + wave, col0 = tt * VTILE;
-  if (col0 >= P.V) return;
-  float v[16];
-#pragma unroll
-  for (int f = 0; f < 4; f++) {
-    const int c = col0 + f * 256 + lane * 4;
-    f32x4 x = (c < P.V) ? ld_stream4(trow + c) : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-    for (int e = 0; e < 4; e++) v[4 * f + e] = x[e];
-  }
+__device__ __forceinline__ void stream_tile(const VerifyArgs<WT>& P, size_t rowj, int nvt, int tt,
+                                            const float (&v)[16]) {
+  const int lane = threadIdx.x & 63;
+  const int col0 = tt * VTILE;
   bool bad = false;
   if (GREEDY) {
     float bv = -INFINITY;
@@ -139,26 +122,75 @@ __global__ __launch_bounds__(256) void k_verify_stream(VerifyArgs<WT> P) {
     wave_argmax(bv, bi);
     if (lane == 0) P.vpart[rowj * nvt + tt] = make_float2(bv, __int_as_float(bi));
   } else {
+    const bool t_one = (P.T == 1.0f);
     float m = v[0];
 #pragma unroll
     for (int i = 1; i < 16; i++) m = fmaxf(m, v[i]);
     m = wave_max(m);
-    float s[8];
+    // pair sums exp(v_i) + exp(v_{i+8}), the fixed tree's first level folded
+    // in as soon as both terms exist
+    float s[4];
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       const float d0 = t_one ? (v[i] - m) : (v[i] - m) * P.invT;
       const float d1 = t_one ? (v[i + 8] - m) : (v[i + 8] - m) * P.invT;
-      s[i] = exp_acc(d0) + exp_acc(d1);
+      const float pr = exp_acc(d0) + exp_acc(d1);
+      if (i < 4) s[i] = pr; else s[i - 4] = s[i - 4] + pr;
     }
-#pragma unroll
-    for (int w = 4; w >= 1; w >>= 1)
-#pragma unroll
-      for (int i = 0; i < w; i++) s[i] += s[i + w];
-    const float sum = wave_sum(s[0]);
+    s[0] = s[0] + s[2];
+    s[1] = s[1] + s[3];
+    const float sum = wave_sum(s[0] + s[1]);
     bad = is_bad(sum) || is_bad(m);
     if (lane == 0) P.vpart[rowj * nvt + tt] = make_float2(m, sum);
   }
   if (bad) raise_err(P.err, DSPARK_DERR_NONFINITE);
+}
+
+// Target rows 0..L_r in 8192-column segments (greedy: 4096), one workgroup
+// per (row j, request, segment), position-major.  Every wave loads two
+// adjacent 1024-column tiles before reducing either (two tiles in flight per
+// wave), in 40 registers per lane: beside a resident one-launch draft
+// workgroup (472 registers per lane) the stream gets one wave per SIMD.  The
+// greedy arg-max needs more registers, so there a wave takes one tile (25
+// registers).
+template <typename WT, bool GREEDY>
+__global__ __launch_bounds__(256) void k_verify_stream(VerifyArgs<WT> P) {
+  constexpr int TPW = GREEDY ? 1 : 2;  // tiles per wave
+  const int nseg = ceil_div(P.V, stream_seg(GREEDY)), nvt = ceil_div(P.V, VTILE);
+  const int b = blockIdx.x;
+  const int jpos = b / (P.R * nseg);
+  const int rem = b - jpos * P.R * nseg;
+  const int row = rem / nseg, seg = rem - row * nseg;
+  const int L = P.L_of(row);
+  if (jpos > L) return;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const size_t rowj = (size_t)row * (P.gamma + 1) + jpos;
+  const int tt = (seg * 4 + wave) * TPW;
+  if (tt * VTILE >= P.V) return;
+  // the row from tile tt on; loads past V read 0 and are replaced by -inf
+  const int col0 = tt * VTILE;
+  const rsrc_t rs = make_rsrc(P.target + rowj * P.V + col0, (size_t)(P.V - col0) * 4);
+  const uint32_t voff = (uint32_t)lane * 16u;
+  f32x4 x[TPW][4];
+#pragma unroll
+  for (int q = 0; q < TPW; q++)
+#pragma unroll
+    for (int f = 0; f < 4; f++)
+      x[q][f] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff, q * 4096 + f * 1024, AUX_NT));
+#pragma unroll
+  for (int q = 0; q < TPW; q++) {
+    if (tt + q < nvt) {
+      float v[16];
+#pragma unroll
+      for (int f = 0; f < 4; f++)
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+          v[4 * f + e] = (col0 + q * VTILE + f * 256 + lane * 4 + e < P.V) ? x[q][f][e] : -INFINITY;
+      stream_tile<WT, GREEDY>(P, rowj, nvt, tt + q, v);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -879,7 +911,7 @@ static void launch_residual(const VerifyArgs<WT>& P, hipStream_t stream) {
 
 template <typename WT>
 static int launch_accept_rates(const VerifyArgs<WT>& P, float* out, hipStream_t stream) {
-  const int nseg = ceil_div(P.V, VSEG);
+  const int nseg = ceil_div(P.V, stream_seg(false));
   const long long nblk = (long long)(P.gamma + 1) * P.R * nseg;
   hipLaunchKernelGGL((k_verify_stream<WT, false>), dim3((unsigned)nblk), dim3(256), 0, stream, P);
   hipLaunchKernelGGL((k_target_rowstats<WT>), dim3(P.R), dim3(256), 0, stream, P);
@@ -892,9 +924,9 @@ static int launch_accept_rates(const VerifyArgs<WT>& P, float* out, hipStream_t 
 // target and the verify lengths, so it can run before the draft is known.
 template <typename WT>
 static void launch_verify_stream(const VerifyArgs<WT>& P, hipStream_t stream) {
-  const int nseg = ceil_div(P.V, VSEG);
-  const long long nblk = (long long)(P.gamma + 1) * P.R * nseg;
   const bool greedy = (P.T == 0.f);
+  const int nseg = ceil_div(P.V, stream_seg(greedy));
+  const long long nblk = (long long)(P.gamma + 1) * P.R * nseg;
   prof_before(DSPARK_KID_VERIFY_STREAM, stream);
   for (int rep = prof_repeat(DSPARK_KID_VERIFY_STREAM); rep > 0; rep--) {
     if (greedy)

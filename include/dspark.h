@@ -150,7 +150,7 @@ const char* dspark_status_string(int status);
  * persistent launch of one workgroup per compute unit; its workgroups wait
  * for each other's results through the workspace, so every one of them must
  * be resident at once.  The host checks that one workgroup fits on a compute
- * unit (480 registers per lane, about 148 KiB of LDS), not that the compute
+ * unit (472 registers per lane, about 148 KiB of LDS), not that the compute
  * units are free: kernels of other streams or processes that occupy them can
  * keep part of the grid waiting.  Every wait is bounded (0.5 s); one that
  * runs out sets DSPARK_DERR_SYNC, every workgroup still finishes, and the

@@ -513,7 +513,8 @@ def gpu_bench(a):
         traffic=traffic, graph=use_graph, cfg=d, ms_eager=ms_eager, n_k1=used * K["repeat"], theta=theta,
         labels=labels, sts=sts, path=path, kernel=K["name"], hot=stats(per_hot), flushed=flushed,
         eager=stats(per_eager), k1=stats(k1_each), d2d_GBs=d2d_GBs,
-        ref={k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in ref.items()})
+        ref={k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in ref.items()
+             if not (isinstance(v, torch.Tensor) and v.dtype == torch.bfloat16)})
 
 
 # VALU instructions per (sample, candidate) evaluation in the inner loop of

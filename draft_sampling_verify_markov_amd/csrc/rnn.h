@@ -16,8 +16,8 @@
 // reproducible to the last bit (6 r^2 multiply-adds per request and step).
 //
 // Per draft step two launches, each tiled over (16 requests x 8 state units)
-// with the tile's weight columns and input rows staged in LDS: k_rnn_gates
-// (update and reset gates, the candidate's input part, g * s) and
+// with the tile's weight columns and input rows staged in LDS as fp64:
+// k_rnn_gates (update and reset gates, the candidate's input part, g * s) and
 // k_rnn_update (the candidate's recurrent part, which needs g * s of every
 // unit, and the new state).
 #pragma once
@@ -70,20 +70,21 @@ __device__ __forceinline__ void load8(const float* __restrict__ p, float (&w)[8]
   w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
 }
 
-__device__ __forceinline__ double shfl_xor_f64(double v, int m) {
-  const uint64_t u = (uint64_t)__double_as_longlong(v);
-  const uint32_t lo = __shfl_xor((uint32_t)u, m), hi = __shfl_xor((uint32_t)(u >> 32), m);
-  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
-
-// Tiling of the per-step gate products: a workgroup takes RNN_RB requests and
-// RNN_UB consecutive state units; thread t = (request t / 16, input lane
-// t % 16) sums the inputs i = 16 m + lane, and the 16 lanes of a request are
-// combined by a fixed xor butterfly (deterministic; the 16 lanes of a request
-// are consecutive lanes of one wave).
+// Tiling of the per-step gate products: a workgroup of RNN_W waves takes
+// RNN_RB requests and RNN_UB consecutive state units, with the tile's weight
+// columns and its requests' input rows staged in LDS as fp64 (exact
+// widenings, converted once).  Wave w sums the inputs [w r / RNN_W,
+// (w + 1) r / RNN_W) in order; lane l owns unit l % 8 and requests 2 (l / 8),
+// 2 (l / 8) + 1: ten fp64 sums in the gates kernel (five gate products, two
+// requests), two in the update kernel.  The waves' partial sums are then
+// added in a fixed pairwise order, ((w0 + w1) + (w2 + w3)) + ((w4 + w5) +
+// (w6 + w7)): deterministic, and no lane shuffles.  Two waves per SIMD and
+// an unrolled input loop keep LDS reads in flight behind the fp64 FMAs.
 constexpr int RNN_RB = 16;
 constexpr int RNN_UB = 8;
-constexpr int RNN_LANES = 16;
+constexpr int RNN_W = 8;
+constexpr int RNN_T = 64 * RNN_W;
+constexpr int RNN_XPAD = 2;  // row padding of the staged inputs (conflict-free reads)
 
 template <typename WT>
 struct RnnStep {
@@ -99,119 +100,191 @@ struct RnnStep {
   int32_t* err;
 };
 
+// Staging of a request block's input rows into LDS as fp64, in pieces of 8
+// consecutive values: piece p = thread + RNN_T m is row p / (r / 8), values
+// [8 (p % (r / 8)), + 8).  Every global load of a thread is issued before the
+// first LDS store, so the staging costs one memory latency, not one per value.
+constexpr int RNN_PIECES = RNN_RB * DSPARK_MAX_RANK / 8 / RNN_T;  // per thread, at most
+__device__ __forceinline__ void piece_of(int m, int r, int& q, int& c) {
+  const int idx = threadIdx.x + RNN_T * m, per_row = r / 8;
+  q = idx / per_row;
+  c = idx - q * per_row;
+}
+
+// Sum of the RNN_W partial sums x[w * stride], w = 0..7, in the fixed order.
+__device__ __forceinline__ double wave_sum8(const double* x, int stride) {
+  return ((x[0] + x[stride]) + (x[2 * stride] + x[3 * stride])) +
+         ((x[4 * stride] + x[5 * stride]) + (x[6 * stride] + x[7 * stride]));
+}
+
 // Update gate, reset gate and the candidate's input part for a tile of
 // (requests, units); writes u, e.Wx[2] and g * s to the gate buffer.
 template <typename WT>
-__global__ __launch_bounds__(256) void k_rnn_gates(RnnStep<WT> P) {
-  __shared__ float s_w[5][DSPARK_MAX_RANK][RNN_UB];           // Wx[0..2], Ws[0..1] columns of the tile
-  // rows padded by 16 floats: the four requests of a wave read distinct banks
-  __shared__ float s_e[RNN_RB][DSPARK_MAX_RANK + 16], s_s[RNN_RB][DSPARK_MAX_RANK + 16];
-  const int t = threadIdx.x, rl = t / RNN_LANES, ln = t % RNN_LANES;
+__global__ __launch_bounds__(RNN_T) void k_rnn_gates(RnnStep<WT> P) {
+  __shared__ double s_w[5][DSPARK_MAX_RANK][RNN_UB];  // Wx[0..2], Ws[0..1] columns of the tile
+  // e rows, then s rows; after the products the partial sums reuse this space
+  __shared__ double s_x[2][RNN_RB][DSPARK_MAX_RANK + RNN_XPAD];
+  const int t = threadIdx.x;
   const int u0 = blockIdx.x * RNN_UB, row0 = blockIdx.y * RNN_RB;
   const int r = P.r;
   const size_t rr = (size_t)r * r;
-#pragma unroll
-  for (int g = 0; g < 5; g++) {
-    const WT* src = (g < 3 ? P.Wx + g * rr : P.Ws + (g - 3) * rr) + u0;
-    for (int i = t; i < r; i += 256) {
-      float w[8];
-      load8(src + (size_t)i * r, w);
-#pragma unroll
-      for (int e = 0; e < 8; e++) s_w[g][i][e] = w[e];
-    }
-  }
   {
-    // request q = t / 16 of the tile, r / 16 consecutive input units per thread
-    const int q = t / RNN_LANES, per = r / RNN_LANES, i0 = (t % RNN_LANES) * per, row = row0 + q;
-    const bool ok = row < P.R;
-    int prev = 0;
-    if (ok) prev = checked_token((P.k == 1) ? P.anchor[row] : P.tokens[(size_t)row * P.gamma + P.k - 2], P.V, P.err);
-    const WT* erow = P.W1 + (size_t)prev * r + i0;
-    const WT* srow = P.S + ((size_t)row * P.gamma + P.k - 2) * r + i0;
-    for (int e = 0; e < per; e++) {
-      s_e[q][i0 + e] = ok ? to_f32(erow[e]) : 0.f;
-      s_s[q][i0 + e] = (ok && P.k > 1) ? to_f32(srow[e]) : 0.f;
+    // every global load first: weight pieces of input row t % 256 (gates 0-2
+    // by the first 256 threads, 3-4 by the others), the previous tokens of
+    // this thread's input pieces, then their W1 and state rows
+    const int wi = t & 255, g0 = t < 256 ? 0 : 3, ng = t < 256 ? 3 : 2;
+    float w[3][8];
+    if (wi < r)
+#pragma unroll
+      for (int gg = 0; gg < 3; gg++)
+        if (gg < ng) {
+          const int g = g0 + gg;
+          load8((g < 3 ? P.Wx + g * rr : P.Ws + (g - 3) * rr) + u0 + (size_t)wi * r, w[gg]);
+        }
+    int prev[RNN_PIECES];
+#pragma unroll
+    for (int m = 0; m < RNN_PIECES; m++) {
+      int q, c;
+      piece_of(m, r, q, c);
+      const int row = row0 + q;
+      prev[m] = -1;
+      if (q < RNN_RB && row < P.R)
+        prev[m] = (P.k == 1) ? P.anchor[row] : P.tokens[(size_t)row * P.gamma + P.k - 2];
+    }
+    float ev[RNN_PIECES][8], sv8[RNN_PIECES][8];
+#pragma unroll
+    for (int m = 0; m < RNN_PIECES; m++) {
+      int q, c;
+      piece_of(m, r, q, c);
+      const bool ok = prev[m] >= 0;
+      const int tok = ok ? checked_token(prev[m], P.V, P.err) : 0;
+#pragma unroll
+      for (int e = 0; e < 8; e++) ev[m][e] = sv8[m][e] = 0.f;
+      if (ok) load8(P.W1 + (size_t)tok * r + 8 * c, ev[m]);
+      if (ok && P.k > 1) load8(P.S + ((size_t)(row0 + q) * P.gamma + P.k - 2) * r + 8 * c, sv8[m]);
+    }
+    if (wi < r)
+#pragma unroll
+      for (int gg = 0; gg < 3; gg++)
+        if (gg < ng)
+#pragma unroll
+          for (int e = 0; e < 8; e++) s_w[g0 + gg][wi][e] = (double)w[gg][e];
+#pragma unroll
+    for (int m = 0; m < RNN_PIECES; m++) {
+      int q, c;
+      piece_of(m, r, q, c);
+      if (q < RNN_RB)
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          s_x[0][q][8 * c + e] = (double)ev[m][e];
+          s_x[1][q][8 * c + e] = (double)sv8[m][e];
+        }
     }
   }
   __syncthreads();
-  double acc[5][RNN_UB];
+  const int wave = t >> 6, l = t & 63, n = l & 7, mq = l >> 3;
+  const int qa = 2 * mq, qb = qa + 1;
+  double acc[5][2];
+#pragma unroll
+  for (int g = 0; g < 5; g++) acc[g][0] = acc[g][1] = 0.0;
+  const int kw = r / RNN_W, i1 = (wave + 1) * kw;
+#pragma unroll 4
+  for (int i = wave * kw; i < i1; i++) {
+    const double ea = s_x[0][qa][i], eb = s_x[0][qb][i];
+    const double sa = s_x[1][qa][i], sb = s_x[1][qb][i];
+#pragma unroll
+    for (int g = 0; g < 5; g++) {
+      const double w = s_w[g][i][n];
+      acc[g][0] = fma(g < 3 ? ea : sa, w, acc[g][0]);  // the products are exact in fp64
+      acc[g][1] = fma(g < 3 ? eb : sb, w, acc[g][1]);
+    }
+  }
+  // output thread t < 128: request t / 8, unit u0 + t % 8; its s value is read
+  // before the partial sums overwrite the staged rows
+  const int oq = t >> 3, on = t & 7, j = u0 + on;
+  const double sv = (t < RNN_RB * RNN_UB) ? s_x[1][oq][j] : 0.0;
+  __syncthreads();
+  double* red = &s_x[0][0][0];  // [wave][gate][request parity][lane]
 #pragma unroll
   for (int g = 0; g < 5; g++)
 #pragma unroll
-    for (int e = 0; e < RNN_UB; e++) acc[g][e] = 0.0;
-  for (int i = ln; i < r; i += RNN_LANES) {
-    const double ev = s_e[rl][i], sv = s_s[rl][i];
-#pragma unroll
-    for (int g = 0; g < 5; g++) {
-      const double x = g < 3 ? ev : sv;
-#pragma unroll
-      for (int e = 0; e < RNN_UB; e++) acc[g][e] += x * (double)s_w[g][i][e];
-    }
-  }
-#pragma unroll
-  for (int m = RNN_LANES / 2; m >= 1; m >>= 1)
-#pragma unroll
-    for (int g = 0; g < 5; g++)
-#pragma unroll
-      for (int e = 0; e < RNN_UB; e++) acc[g][e] += shfl_xor_f64(acc[g][e], m);
-  // lane ln < 8 finishes unit u0 + ln of its request
-  const int row = row0 + rl, j = u0 + ln;
-  if (ln < RNN_UB && row < P.R) {
+    for (int q = 0; q < 2; q++) red[((wave * 5 + g) * 2 + q) * 64 + l] = acc[g][q];
+  __syncthreads();
+  const int row = row0 + oq;
+  if (t < RNN_RB * RNN_UB && row < P.R) {
+    const int ol = (oq >> 1) * 8 + on, op = oq & 1;
     double p[5];
 #pragma unroll
-    for (int g = 0; g < 5; g++) {
-      double v = acc[g][0];
-#pragma unroll
-      for (int e = 1; e < RNN_UB; e++) v = (ln == e) ? acc[g][e] : v;
-      p[g] = v;
-    }
+    for (int g = 0; g < 5; g++) p[g] = wave_sum8(red + (g * 2 + op) * 64 + ol, 5 * 2 * 64);
     const double u = 1.0 / (1.0 + exp(-((p[0] + p[3]) + (double)P.bias[j])));
     const double gr = 1.0 / (1.0 + exp(-((p[1] + p[4]) + (double)P.bias[r + j])));
     const size_t o = (size_t)row * r + j, plane = (size_t)P.R * r;
     P.gates[o] = u;
     P.gates[plane + o] = p[2];
-    P.gates[2 * plane + o] = gr * (double)s_s[rl][j];
+    P.gates[2 * plane + o] = gr * sv;
   }
 }
 
 // Candidate h = tanh(e.Wx[2] + (g * s).Ws[2] + b[2]) and the new state.
 template <typename WT>
-__global__ __launch_bounds__(256) void k_rnn_update(RnnStep<WT> P) {
-  __shared__ float s_w[DSPARK_MAX_RANK][RNN_UB];
-  __shared__ double s_gs[RNN_RB][DSPARK_MAX_RANK];
-  const int t = threadIdx.x, rl = t / RNN_LANES, ln = t % RNN_LANES;
+__global__ __launch_bounds__(RNN_T) void k_rnn_update(RnnStep<WT> P) {
+  __shared__ double s_w[DSPARK_MAX_RANK][RNN_UB];
+  __shared__ double s_gs[RNN_RB][DSPARK_MAX_RANK + RNN_XPAD];
+  __shared__ double red[RNN_W][2][64];
+  const int t = threadIdx.x;
   const int u0 = blockIdx.x * RNN_UB, row0 = blockIdx.y * RNN_RB;
   const int r = P.r;
   const size_t rr = (size_t)r * r, plane = (size_t)P.R * r;
-  for (int i = t; i < r; i += 256) {
-    float w[8];
-    load8(P.Ws + 2 * rr + (size_t)i * r + u0, w);
-#pragma unroll
-    for (int e = 0; e < 8; e++) s_w[i][e] = w[e];
-  }
   {
-    const int q = t / RNN_LANES, per = r / RNN_LANES, i0 = (t % RNN_LANES) * per, row = row0 + q;
-    const double* src = P.gates + 2 * plane + (size_t)row * r + i0;
-    for (int e = 0; e < per; e++) s_gs[q][i0 + e] = (row < P.R) ? src[e] : 0.0;
+    // every global load first (weight piece of input row t, the g * s pieces)
+    float w[8];
+    if (t < r) load8(P.Ws + 2 * rr + (size_t)t * r + u0, w);
+    double gv[RNN_PIECES][8];
+#pragma unroll
+    for (int m = 0; m < RNN_PIECES; m++) {
+      int q, c;
+      piece_of(m, r, q, c);
+      const int row = row0 + q;
+      const bool ok = q < RNN_RB && row < P.R;
+      double4 a{0.0, 0.0, 0.0, 0.0}, b{0.0, 0.0, 0.0, 0.0};
+      if (ok) {
+        const double4* src = reinterpret_cast<const double4*>(P.gates + 2 * plane + (size_t)row * r + 8 * c);
+        a = src[0];
+        b = src[1];
+      }
+      gv[m][0] = a.x; gv[m][1] = a.y; gv[m][2] = a.z; gv[m][3] = a.w;
+      gv[m][4] = b.x; gv[m][5] = b.y; gv[m][6] = b.z; gv[m][7] = b.w;
+    }
+    if (t < r)
+#pragma unroll
+      for (int e = 0; e < 8; e++) s_w[t][e] = (double)w[e];
+#pragma unroll
+    for (int m = 0; m < RNN_PIECES; m++) {
+      int q, c;
+      piece_of(m, r, q, c);
+      if (q < RNN_RB)
+#pragma unroll
+        for (int e = 0; e < 8; e++) s_gs[q][8 * c + e] = gv[m][e];
+    }
   }
   __syncthreads();
-  double acc[RNN_UB];
-#pragma unroll
-  for (int e = 0; e < RNN_UB; e++) acc[e] = 0.0;
-  for (int i = ln; i < r; i += RNN_LANES) {
-    const double gv = s_gs[rl][i];
-#pragma unroll
-    for (int e = 0; e < RNN_UB; e++) acc[e] += gv * (double)s_w[i][e];
+  const int wave = t >> 6, l = t & 63, n = l & 7, mq = l >> 3;
+  const int qa = 2 * mq, qb = qa + 1;
+  double acc0 = 0.0, acc1 = 0.0;
+  const int kw = r / RNN_W, i1 = (wave + 1) * kw;
+#pragma unroll 4
+  for (int i = wave * kw; i < i1; i++) {
+    const double w = s_w[i][n];
+    acc0 = fma(s_gs[qa][i], w, acc0);
+    acc1 = fma(s_gs[qb][i], w, acc1);
   }
-#pragma unroll
-  for (int m = RNN_LANES / 2; m >= 1; m >>= 1)
-#pragma unroll
-    for (int e = 0; e < RNN_UB; e++) acc[e] += shfl_xor_f64(acc[e], m);
-  const int row = row0 + rl, j = u0 + ln;
-  if (ln < RNN_UB && row < P.R) {
-    double hs = acc[0];
-#pragma unroll
-    for (int e = 1; e < RNN_UB; e++) hs = (ln == e) ? acc[e] : hs;
+  red[wave][0][l] = acc0;
+  red[wave][1][l] = acc1;
+  __syncthreads();
+  const int oq = t >> 3, on = t & 7, row = row0 + oq, j = u0 + on;
+  if (t < RNN_RB * RNN_UB && row < P.R) {
+    const int ol = (oq >> 1) * 8 + on, op = oq & 1;
+    const double hs = wave_sum8(&red[0][op][ol], 2 * 64);
     const size_t o = (size_t)row * r + j;
     const double u = P.gates[o];
     const double h = tanh((P.gates[plane + o] + hs) + (double)P.bias[2 * r + j]);
@@ -235,8 +308,8 @@ inline void launch_rnn_state(const RnnHead& h, const WT* W1, const int32_t* anch
   P.R = R; P.gamma = gamma; P.V = V; P.r = r; P.k = k;
   P.err = err;
   const dim3 grid((unsigned)(r / RNN_UB), (unsigned)ceil_div(R, RNN_RB));
-  hipLaunchKernelGGL(k_rnn_gates<WT>, grid, dim3(256), 0, stream, P);
-  hipLaunchKernelGGL(k_rnn_update<WT>, grid, dim3(256), 0, stream, P);
+  hipLaunchKernelGGL(k_rnn_gates<WT>, grid, dim3(RNN_T), 0, stream, P);
+  hipLaunchKernelGGL(k_rnn_update<WT>, grid, dim3(RNN_T), 0, stream, P);
 }
 
 }  // namespace dspark

@@ -289,6 +289,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1), amdg
   __shared__ uint32_t s_E;
   __shared__ int s_ok;
 
+  // the waves of a kernel beside this one (verify's target-row stream) share
+  // every SIMD: let this kernel's wave issue first when both are ready
+  __builtin_amdgcn_s_setprio(3);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int j = lane & 31, h = lane >> 5;
   const int G = gridDim.x, b = blockIdx.x;

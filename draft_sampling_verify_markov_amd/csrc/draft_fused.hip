@@ -149,13 +149,13 @@ struct UnitOut {
   int32_t* err;
 };
 
-// One pipelined unit step of a wave, in 8 parts fenced by sched_barrier:
-// part p issues the MFMAs of k steps [p KS / 8, (p + 1) KS / 8) of the NEXT
-// unit's bias block (rows A_next against the resident fragment F, into
-// accN), one eighth of the epilogue of the current unit (accC + base values
-// bv: the maximum, the exponentials and their fixed-order tree sum, the
-// cross-half reduction and the LDS write; greedy: the arg-max), and one of
-// the 8 direct-to-LDS row loads of a later unit.  The fences keep the VALU
+// One pipelined unit step of a wave: the 8 direct-to-LDS row loads of a later
+// unit first, then 8 parts fenced by sched_barrier: part p issues the MFMAs
+// of k steps [p KS / 8, (p + 1) KS / 8) of the NEXT unit's bias block (rows
+// A_next against the resident fragment F, into accN) and one eighth of the
+// epilogue of the current unit (accC + base values bv: the maximum, the
+// exponentials and their fixed-order tree sum, the cross-half reduction and
+// the LDS write; greedy: the arg-max).  The fences keep the VALU
 // work of the epilogue in the shadow of the MFMAs instead of after them; the
 // arithmetic and its order are those of the unpipelined loop, so the results
 // are bit-identical.  The B operands of part p + 1 are read from LDS during
@@ -179,6 +179,10 @@ __device__ __forceinline__ void unit_block(const typename BiasBlock<uint16_t>::t
     for (int i = 0; i < KPP; i++)
       if (i < KS / NP) bcur[i] = *reinterpret_cast<const u32x4*>(ap + i * 16);
   }
+  // the later unit's row loads, all at once: issued while the memory
+  // pipeline has room (one per part stalled the wave at each part instead)
+#pragma unroll
+  for (int q = 0; q < NP; q++) dma_row(dma, q);
   float ml = -INFINITY, mw = 0.f, mref = 0.f;
   float s[8];
   float gv = -INFINITY;
@@ -254,7 +258,6 @@ __device__ __forceinline__ void unit_block(const typename BiasBlock<uint16_t>::t
         if (h == 0) { o.m[o.wave][o.rl] = mw; o.s[o.wave][o.rl] = sw; }
       }
     }
-    dma_row(dma, p);
     if (NEXT) {
 #pragma unroll
       for (int i = 0; i < KPP; i++) bcur[i] = bnext[i];

@@ -442,9 +442,11 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
     and joined back to the current stream; capturable into a HIP graph);
     verify then finishes on the current stream.  The draft is the longer of
     the two branches, so the join waits on a kernel that has already ended
-    or is about to.  The early-stop scheduler on a pool of at most 1024
-    candidates is a workgroup small enough to share a compute unit with the
-    one-launch draft; the other schedulers run first, before the fork.  The scheduler uses its own small workspace
+    or is about to.  The early-stop and asynchronous schedulers on a pool of
+    at most 1024 candidates, and the static-threshold scheduler, are
+    workgroups small enough to share a compute unit with the one-launch draft
+    and run beside it; larger pools are scheduled first, before the fork.
+    The scheduler uses its own small workspace
     ``ws_sched`` (allocated here if not given).  ``scheduler`` is
     "early" (dspark_schedule), "async" (dspark_schedule_async with the
     lagged confidences ``conf_lag`` of the input dict) or "threshold"
@@ -470,14 +472,17 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
     sched = use_scheduler and d.get("conf") is not None
     if sched and ws_sched is None:
         ws_sched = torch.zeros(256, dtype=torch.uint8, device=dev)
-    beside = sched and scheduler == "early" and d["conf"].numel() <= 1024
-    if sched and not beside:
+    beside = sched and (scheduler == "threshold" or d["conf"].numel() <= 1024)
+
+    def run_scheduler():
         if scheduler == "async":
-            L, n, _ = schedule_async(d["conf"], d["conf_lag"], d["sps"], ws_sched, with_cum=False)
-        elif scheduler == "threshold":
-            L, n, _ = schedule_threshold(d["conf"], theta, ws_sched, with_cum=False)
-        else:
-            L, n, _ = schedule(d["conf"], d["sps"], ws_sched, with_cum=False)
+            return schedule_async(d["conf"], d["conf_lag"], d["sps"], ws_sched, with_cum=False)
+        if scheduler == "threshold":
+            return schedule_threshold(d["conf"], theta, ws_sched, with_cum=False)
+        return schedule(d["conf"], d["sps"], ws_sched, with_cum=False)
+
+    if sched and not beside:
+        L, n, _ = run_scheduler()
     # the draft's outputs are allocated on the current stream, which reads them
     # after the join
     tok = torch.empty((R, g), dtype=torch.int32, device=dev)
@@ -497,7 +502,7 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
     # current stream, beside the draft: the scheduler (when small) and the
     # target-row stream of verify (it needs only the verify lengths)
     if beside:
-        L, n, _ = schedule(d["conf"], d["sps"], ws_sched, with_cum=False)
+        L, n, _ = run_scheduler()
     verify_stream(d["target"], L, temperature, ws)
     cur.wait_stream(side)
     if head == "rnn":

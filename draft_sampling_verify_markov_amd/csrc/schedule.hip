@@ -38,6 +38,9 @@ namespace dspark {
 
 constexpr int SCHED_THREADS = 1024;
 constexpr int FIX_SHIFT = 36;
+// The lean shape: pools of at most 1024 candidates in 256 threads.
+constexpr int SCHED_LEAN_THREADS = 256;
+constexpr int SCHED_LEAN_KPT = 4;
 
 // LDS of the scheduler kernels: NB exchange buffers of NS = NT * KPT keys
 // (also the per-request counters), the confidence staging (the second buffer,
@@ -208,7 +211,9 @@ __device__ __forceinline__ void pool_scan_lds(int n, int R, SchedSmem<NT, KPT, N
   if (lane == 63) sm.wsum[wave] = (long long)incl_d;
   __syncthreads();
   long long Tn = ((long long)R << FIX_SHIFT) + (long long)excl_d;
-  for (int w = 0; w < wave; w++) Tn += sm.wsum[w];
+#pragma unroll
+  for (int w = 0; w < NT / 64; w++)
+    if (w < wave) Tn += sm.wsum[w];
 #pragma unroll 1
   for (int q = 0; q < KPT; q++) {
     const int i = tid * KPT + q;
@@ -296,8 +301,6 @@ __global__ __launch_bounds__(SCHED_THREADS) void k_schedule(const float* __restr
 // enough to share a compute unit with the one-launch draft (one wave per SIMD,
 // at most 32 registers per lane, one 8 KiB exchange buffer), so that it can
 // run beside the draft instead of ahead of it.
-constexpr int SCHED_LEAN_THREADS = 256;
-constexpr int SCHED_LEAN_KPT = 4;
 __global__ __launch_bounds__(SCHED_LEAN_THREADS) __attribute__((amdgpu_num_vgpr(32))) void k_schedule_lean(
     const float* __restrict__ conf, const float* __restrict__ sps, int R, int gamma, int n_table,
     int32_t* __restrict__ verify_len, int32_t* __restrict__ n_admitted, float* __restrict__ cum_conf,
@@ -308,26 +311,37 @@ __global__ __launch_bounds__(SCHED_LEAN_THREADS) __attribute__((amdgpu_num_vgpr(
 
 // Asynchronous production variant: K = the first maximiser of Theta over the
 // lagged pool (no early stop), then the current pool's top K are admitted.
-template <int KPT>
-__global__ __launch_bounds__(SCHED_THREADS) void k_schedule_async(const float* __restrict__ conf,
-                                                                 const float* __restrict__ conf_lag,
-                                                                 const float* __restrict__ sps, int R,
-                                                                 int gamma, int n_table,
-                                                                 int32_t* __restrict__ verify_len,
-                                                                 int32_t* __restrict__ n_admitted,
-                                                                 float* __restrict__ cum_conf,
-                                                                 int32_t* err) {
-  constexpr int NT = SCHED_THREADS;
-  __shared__ SchedSmem<NT, KPT, 2> sm;
+template <int NT, int KPT, int NB>
+__device__ __forceinline__ void schedule_async_body(const float* __restrict__ conf,
+                                                    const float* __restrict__ conf_lag,
+                                                    const float* __restrict__ sps, int R, int gamma, int n_table,
+                                                    int32_t* __restrict__ verify_len,
+                                                    int32_t* __restrict__ n_admitted, float* __restrict__ cum_conf,
+                                                    int32_t* err) {
+  __shared__ SchedSmem<NT, KPT, NB> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = R * gamma;
   uint64_t k[KPT];
-  pool_sort<NT, KPT, 2>(conf_lag, R, gamma, nullptr, err, sm, k);
-  auto key = [&](int m) { return k[m]; };
+  // with one buffer the sorted keys go back to LDS (fewer live registers)
+  auto to_lds = [&]() {
+    if (NB == 1) {
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < KPT; m++) sm.bufs[0][tid + NT * m] = k[m];
+      __syncthreads();
+    }
+  };
+  auto key = [&](int m) { return NB == 1 ? sm.bufs[0][tid + NT * m] : k[m]; };
+  auto scan = [&](auto f) {
+    if (NB == 1) pool_scan_lds<NT, KPT, NB>(n, R, sm, f);
+    else pool_scan<NT, KPT, NB>(key, n, R, sm, f);
+  };
+  pool_sort<NT, KPT, NB>(conf_lag, R, gamma, nullptr, err, sm, k);
+  to_lds();
   // Theta_0 (no draft admitted) belongs to thread 0; slot i gives Theta_{i+1}
   const double theta0 = (double)((long long)R << FIX_SHIFT) * sps_at(sps, n_table, R);
   double best = (tid == 0) ? theta0 : -1.0;
-  pool_scan<NT, KPT, 2>(key, n, R, sm, [&](int i, long long Tn, long long v) {
+  scan([&](int i, long long Tn, long long v) {
     best = fmax(best, (double)(Tn + v) * sps_at(sps, n_table, R + i + 1));
   });
   // block arg-max: largest Theta, then the smallest n holding it
@@ -337,9 +351,9 @@ __global__ __launch_bounds__(SCHED_THREADS) void k_schedule_async(const float* _
   __syncthreads();
   double bmax = sm.wmax[0];
 #pragma unroll
-  for (int w = 1; w < SCHED_THREADS / 64; w++) bmax = fmax(bmax, sm.wmax[w]);
+  for (int w = 1; w < NT / 64; w++) bmax = fmax(bmax, sm.wmax[w]);
   int cand = 0x7fffffff;
-  pool_scan<NT, KPT, 2>(key, n, R, sm, [&](int i, long long Tn, long long v) {
+  scan([&](int i, long long Tn, long long v) {
     const double th = (double)(Tn + v) * sps_at(sps, n_table, R + i + 1);
     if (th == bmax) cand = min(cand, i + 1);
   });
@@ -350,25 +364,50 @@ __global__ __launch_bounds__(SCHED_THREADS) void k_schedule_async(const float* _
   __syncthreads();
   int K = sm.wmin[0];
 #pragma unroll
-  for (int w = 1; w < SCHED_THREADS / 64; w++) K = min(K, sm.wmin[w]);
+  for (int w = 1; w < NT / 64; w++) K = min(K, sm.wmin[w]);
 
-  pool_sort<NT, KPT, 2>(conf, R, gamma, cum_conf, err, sm, k);
-  pool_admit<NT, KPT, 2>(key, K, R, gamma, sm, verify_len);
+  pool_sort<NT, KPT, NB>(conf, R, gamma, cum_conf, err, sm, k);
+  to_lds();
+  pool_admit<NT, KPT, NB>(key, K, R, gamma, sm, verify_len);
   if (tid == 0) *n_admitted = K;
 }
 
-// Static-threshold baseline: L_r = #{j : a_{r,j} >= theta}.  One workgroup;
-// thread t handles requests t, t + 1024, ...; the admitted total is summed in
-// a fixed order through LDS.
-__global__ __launch_bounds__(SCHED_THREADS) void k_schedule_threshold(const float* __restrict__ conf,
-                                                                     float theta, int R, int gamma,
-                                                                     int32_t* __restrict__ verify_len,
-                                                                     int32_t* __restrict__ n_admitted,
-                                                                     float* __restrict__ cum_conf, int32_t* err) {
-  __shared__ int wsum[SCHED_THREADS / 64];
+template <int KPT>
+__global__ __launch_bounds__(SCHED_THREADS) void k_schedule_async(const float* __restrict__ conf,
+                                                                 const float* __restrict__ conf_lag,
+                                                                 const float* __restrict__ sps, int R,
+                                                                 int gamma, int n_table,
+                                                                 int32_t* __restrict__ verify_len,
+                                                                 int32_t* __restrict__ n_admitted,
+                                                                 float* __restrict__ cum_conf,
+                                                                 int32_t* err) {
+  schedule_async_body<SCHED_THREADS, KPT, 2>(conf, conf_lag, sps, R, gamma, n_table, verify_len, n_admitted,
+                                             cum_conf, err);
+}
+
+// The asynchronous variant for pools of at most 1024 candidates, in the lean
+// scheduler's shape (256 threads, at most 32 registers per lane, one 8 KiB
+// exchange buffer): it shares a compute unit with the one-launch draft.
+__global__ __launch_bounds__(SCHED_LEAN_THREADS) __attribute__((amdgpu_num_vgpr(32))) void k_schedule_async_lean(
+    const float* __restrict__ conf, const float* __restrict__ conf_lag, const float* __restrict__ sps, int R,
+    int gamma, int n_table, int32_t* __restrict__ verify_len, int32_t* __restrict__ n_admitted,
+    float* __restrict__ cum_conf, int32_t* err) {
+  schedule_async_body<SCHED_LEAN_THREADS, SCHED_LEAN_KPT, 1>(conf, conf_lag, sps, R, gamma, n_table, verify_len,
+                                                             n_admitted, cum_conf, err);
+}
+
+// Static-threshold baseline: L_r = #{j : a_{r,j} >= theta}.  One workgroup
+// of 256 threads in at most 32 registers per lane (it shares a compute unit
+// with the one-launch draft); thread t handles requests t, t + 256, ...; the
+// admitted total is summed in a fixed order through LDS.
+constexpr int SCHED_TH_THREADS = 256;
+__global__ __launch_bounds__(SCHED_TH_THREADS) __attribute__((amdgpu_num_vgpr(32))) void k_schedule_threshold(
+    const float* __restrict__ conf, float theta, int R, int gamma, int32_t* __restrict__ verify_len,
+    int32_t* __restrict__ n_admitted, float* __restrict__ cum_conf, int32_t* err) {
+  __shared__ int wsum[SCHED_TH_THREADS / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int tot = 0;
-  for (int r = tid; r < R; r += SCHED_THREADS) {
+  for (int r = tid; r < R; r += SCHED_TH_THREADS) {
     float a = 1.0f;
     int L = 0;
     for (int j = 0; j < gamma; j++) {
@@ -391,7 +430,7 @@ __global__ __launch_bounds__(SCHED_THREADS) void k_schedule_threshold(const floa
   __syncthreads();
   if (tid == 0) {
     int n = 0;
-    for (int w = 0; w < SCHED_THREADS / 64; w++) n += wsum[w];
+    for (int w = 0; w < SCHED_TH_THREADS / 64; w++) n += wsum[w];
     *n_admitted = n;
   }
 }
@@ -401,7 +440,7 @@ int schedule_threshold_impl(const float* conf, float theta, int R, int gamma, in
   const WsLayout L = ws_layout(R, gamma, 8);
   prof_before(DSPARK_KID_SCHEDULE, stream);
   for (int rep = prof_repeat(DSPARK_KID_SCHEDULE); rep > 0; rep--)
-    hipLaunchKernelGGL(k_schedule_threshold, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, theta, R, gamma,
+    hipLaunchKernelGGL(k_schedule_threshold, dim3(1), dim3(SCHED_TH_THREADS), 0, stream, conf, theta, R, gamma,
                        verify_len, n_admitted, cum_conf, ws_ptr<int32_t>(ws, L.err));
   prof_after(DSPARK_KID_SCHEDULE, stream);
   return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
@@ -415,9 +454,9 @@ int schedule_async_impl(const float* conf, const float* conf_lag, const float* s
   int32_t* err = ws_ptr<int32_t>(ws, L.err);
   prof_before(DSPARK_KID_SCHEDULE, stream);
   for (int rep = prof_repeat(DSPARK_KID_SCHEDULE); rep > 0; rep--) {
-    if (n <= SCHED_THREADS)
-      hipLaunchKernelGGL(k_schedule_async<1>, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, conf_lag, sps, R,
-                         gamma, n_table, verify_len, n_admitted, cum_conf, err);
+    if (n <= SCHED_LEAN_THREADS * SCHED_LEAN_KPT)
+      hipLaunchKernelGGL(k_schedule_async_lean, dim3(1), dim3(SCHED_LEAN_THREADS), 0, stream, conf, conf_lag, sps,
+                         R, gamma, n_table, verify_len, n_admitted, cum_conf, err);
     else if (n <= 2 * SCHED_THREADS)
       hipLaunchKernelGGL(k_schedule_async<2>, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, conf_lag, sps, R,
                          gamma, n_table, verify_len, n_admitted, cum_conf, err);

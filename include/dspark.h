@@ -211,7 +211,7 @@ int dspark_draft_noalloc(const float* base, const void* W1, const void* W2, dspa
  *   cum_conf     out [R, gamma] fp32 a, or NULL
  *
  * A pool of at most 1024 candidates is handled by one 256-thread workgroup
- * (at most 32 registers per lane, about 12 KiB of LDS), small enough to run on
+ * (at most 40 registers per lane, about 12 KiB of LDS), small enough to run on
  * another stream beside a resident one-launch dspark_draft; larger pools by
  * one 1024-thread workgroup.
  */
@@ -242,6 +242,9 @@ int dspark_schedule(const float* conf, const float* sps, int R, int gamma, int n
  *   n_admitted   out [1] int32    K
  *   cum_conf     out [R, gamma] fp32 a of conf, or NULL
  * Same checks and status codes as dspark_schedule (conf_lag must be non-NULL).
+ * Like dspark_schedule, a pool of at most 1024 candidates is handled by one
+ * 256-thread workgroup (at most 40 registers per lane, about 12 KiB of LDS)
+ * that can run beside a resident one-launch dspark_draft.
  */
 int dspark_schedule_async(const float* conf, const float* conf_lag, const float* sps, int R, int gamma,
                           int n_table, int32_t* verify_len, int32_t* n_admitted, float* cum_conf,
@@ -257,6 +260,9 @@ int dspark_schedule_async(const float* conf, const float* conf_lag, const float*
  *                   since a is non-increasing); n_admitted = sum of them
  *
  *   conf, cum_conf  as for dspark_schedule; theta: host scalar (not NaN)
+ *
+ * One 256-thread workgroup of at most 16 registers per lane (any R): it can
+ * run beside a resident one-launch dspark_draft.
  */
 int dspark_schedule_threshold(const float* conf, float theta, int R, int gamma, int32_t* verify_len,
                               int32_t* n_admitted, float* cum_conf, void* workspace, size_t workspace_bytes,

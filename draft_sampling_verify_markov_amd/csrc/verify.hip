@@ -469,10 +469,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // target-row buffer); units are taken row block first, tile second.  A unit's
 // base rows arrive by direct-to-LDS loads two units ahead, its target rows
 // one unit ahead; a unit's records are written after the next unit's first
-// barrier.  Same per-element arithmetic and sums as k_residual_partials.  (For
-// the residual of dspark_verify, one chunk of at most 128 rejected requests,
-// loading both tiles' fragments up front measured slower than the per-tile
-// kernel.)
+// barrier.  Same per-element arithmetic and sums as k_residual_partials.  Also
+// verify's residual when more than 128 requests would make the per-tile kernel
+// reload W2 for each chunk (R = 512, gamma = 16, V = 131072: 1.573 -> 1.558 ms
+// per round); for a single chunk of at most 128 requests, loading both tiles'
+// fragments up front measured slower than the per-tile kernel.
 template <int KS>
 __device__ __forceinline__ void mma_rows(const typename BiasBlock<uint16_t>::template Frag<KS>& F, int r,
                                          const uint16_t* A_rows, int a_stride, f32x16 (&acc)[2]) {
@@ -892,14 +893,16 @@ __global__ __launch_bounds__(256) void k_accept_finalize(VerifyArgs<WT> P, float
   }
 }
 
-// Residual tile records: the per-tile kernel; for the acceptance labels with
-// bf16 factors and at most two tiles per workgroup, the resident-W2 kernel.
+// Residual tile records: the per-tile kernel, which reads a tile's W2
+// fragment once per chunk of 128 requests; with bf16 factors and at most two
+// tiles per workgroup, the resident-W2 kernel (W2 read once per call) for the
+// acceptance labels and for verify's residual over more than 128 requests.
 template <typename WT, bool TVM>
 static void launch_residual(const VerifyArgs<WT>& P, hipStream_t stream) {
   const int nt = ceil_div(P.V, TILE), G = device_cu_count();
   const int grid_r = min(nt, G);
-  if constexpr (TVM && std::is_same<WT, uint16_t>::value) {
-    if (nt <= 2 * G) {
+  if constexpr (std::is_same<WT, uint16_t>::value) {
+    if (nt <= 2 * G && (TVM || P.R > 128)) {
       DSPARK_DISPATCH_KS(P.r, hipLaunchKernelGGL((k_residual_resident<KS, TVM>), dim3(grid_r), dim3(256), 0,
                                                  stream, P));
       return;

@@ -58,9 +58,9 @@ struct SchedSmem {
 // One bitonic stage at partner distance D < 64 (lane ^ D, DPP and permlane
 // moves) of the merge of size kk; no stage when D >= kk.
 template <int D, int NT, int KPT>
-__device__ __forceinline__ void sort_wave_stage(uint64_t (&k)[KPT], int kk) {
+__device__ __forceinline__ void sort_wave_stage(uint64_t (&k)[KPT], int kk, int tid) {
   if (kk <= D) return;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int lane = tid & 63;
   const int tk = tid & kk;  // slot i = tid + NT m: i & kk = tk | (NT m & kk)
 #pragma unroll
   for (int m = 0; m < KPT; m++) {
@@ -73,13 +73,10 @@ __device__ __forceinline__ void sort_wave_stage(uint64_t (&k)[KPT], int kk) {
   }
 }
 
-// Steps 1-2 for one confidence array: running products (written to cum_conf
-// when non-NULL), 64-bit keys, bitonic sort.  On return slot t + NT m of the
-// sorted pool is k[m] of thread t.  Every thread must call it.  With NB = 2
-// the LDS stages alternate between two buffers (one barrier each); with one
-// buffer a stage also waits before it overwrites the buffer.
+// Step 1 and the keys: on return slot t + NT m (flat index order) of the
+// unsorted pool is k[m] of thread t, slots past R * gamma hold ~0.
 template <int NT, int KPT, int NB>
-__device__ __forceinline__ void pool_sort(const float* __restrict__ conf, int R, int gamma,
+__device__ __forceinline__ void pool_keys(const float* __restrict__ conf, int R, int gamma,
                                           float* __restrict__ cum_conf, int32_t* err, SchedSmem<NT, KPT, NB>& sm,
                                           uint64_t (&k)[KPT]) {
   constexpr int NS = NT * KPT;
@@ -110,8 +107,19 @@ __device__ __forceinline__ void pool_sort(const float* __restrict__ conf, int R,
   __syncthreads();
 #pragma unroll
   for (int m = 0; m < KPT; m++) k[m] = sm.bufs[0][tid + NT * m];
+}
 
-  int nb = NB - 1;  // next exchange buffer (bufs[0] is still being read above)
+// Bitonic sort, ascending, of the NT * KS keys in registers (slot t + NT m is
+// k[m] of thread t; tid is threadIdx.x, passed in so that a caller in a loop
+// can keep the per-stage partner indices from being hoisted out of it).  Distances of NT and up stay inside a thread, 64..NT/2
+// go through the LDS exchange buffers of sm, below 64 through DPP and
+// permlane moves.  The first LDS stage writes bufs[NB - 1], so bufs[0] may
+// still be read by other threads when this starts (with NB = 2).
+template <int NT, int KS, int NB, typename SM>
+__device__ __forceinline__ void pool_bitonic(SM& sm, uint64_t (&k)[KS], int tid) {
+  constexpr int NS = NT * KS;
+  constexpr int KPT = KS;
+  int nb = NB - 1;  // next exchange buffer
   // unrolled: every stage's distances and directions are constants
 #pragma unroll
   for (int kk = 2; kk <= NS; kk <<= 1) {
@@ -148,21 +156,35 @@ __device__ __forceinline__ void pool_sort(const float* __restrict__ conf, int R,
       }
     }
     // distances below 64: partners in the same wave
-    sort_wave_stage<32, NT>(k, kk);
-    sort_wave_stage<16, NT>(k, kk);
-    sort_wave_stage<8, NT>(k, kk);
-    sort_wave_stage<4, NT>(k, kk);
-    sort_wave_stage<2, NT>(k, kk);
-    sort_wave_stage<1, NT>(k, kk);
+    sort_wave_stage<32, NT>(k, kk, tid);
+    sort_wave_stage<16, NT>(k, kk, tid);
+    sort_wave_stage<8, NT>(k, kk, tid);
+    sort_wave_stage<4, NT>(k, kk, tid);
+    sort_wave_stage<2, NT>(k, kk, tid);
+    sort_wave_stage<1, NT>(k, kk, tid);
   }
 }
 
+// Steps 1-2 for one confidence array: running products (written to cum_conf
+// when non-NULL), 64-bit keys, bitonic sort.  On return slot t + NT m of the
+// sorted pool is k[m] of thread t.  Every thread must call it.  With NB = 2
+// the LDS stages alternate between two buffers (one barrier each); with one
+// buffer a stage also waits before it overwrites the buffer.
+template <int NT, int KPT, int NB>
+__device__ __forceinline__ void pool_sort(const float* __restrict__ conf, int R, int gamma,
+                                          float* __restrict__ cum_conf, int32_t* err, SchedSmem<NT, KPT, NB>& sm,
+                                          uint64_t (&k)[KPT]) {
+  pool_keys<NT, KPT, NB>(conf, R, gamma, cum_conf, err, sm, k);
+  pool_bitonic<NT, KPT, NB>(sm, k, (int)threadIdx.x);
+}
+
 // Step 3: exact fixed-point prefix in slot order.  Calls f(i, Tn, v) for every
-// slot i < n of the thread, with Tn = R * 2^36 + (sum of the first i values)
-// and v = floor(a_i * 2^36).  Every thread must call it.
+// slot i < n of the thread, with Tn = T0 + (sum of the first i values) and
+// v = floor(a_i * 2^36); returns the sum of all n values.  T0 = R * 2^36 for
+// a whole pool.  Every thread must call it.
 // key(m) gives the thread's slot tid + NT m.
-template <int NT, int KPT, int NB, typename Key, typename Fn>
-__device__ __forceinline__ void pool_scan(Key key, int n, int R, SchedSmem<NT, KPT, NB>& sm, Fn f) {
+template <int NT, int KPT, typename SM, typename Key, typename Fn>
+__device__ __forceinline__ long long pool_scan(Key key, int n, long long T0, SM& sm, Fn f) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   long long carry = 0;
 #pragma unroll
@@ -184,10 +206,11 @@ __device__ __forceinline__ void pool_scan(Key key, int n, int R, SchedSmem<NT, K
       if (w < wave) before += x;
       total += x;
     }
-    if (i < n) f(i, ((long long)R << FIX_SHIFT) + carry + before + (incl - vm), vm);
+    if (i < n) f(i, T0 + carry + before + (incl - vm), vm);
     carry += total;
     __syncthreads();  // wsum is rewritten for the next m
   }
+  return carry;
 }
 
 // Step 3 with the sorted keys in LDS (bufs[0], slot order): thread t takes
@@ -276,7 +299,7 @@ __device__ __forceinline__ void schedule_body(const float* __restrict__ conf, co
     if (th1 < th0) drop = min(drop, i);
   };
   if (NB == 1) pool_scan_lds<NT, KPT, NB>(n, R, sm, walk);
-  else pool_scan<NT, KPT, NB>(key, n, R, sm, walk);
+  else pool_scan<NT, KPT>(key, n, (long long)R << FIX_SHIFT, sm, walk);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) drop = min(drop, __shfl_xor(drop, o));
   if (lane == 0 && drop < n) atomicMin(&sm.s_n, drop);
@@ -284,6 +307,210 @@ __device__ __forceinline__ void schedule_body(const float* __restrict__ conf, co
   const int nstar = sm.s_n;
   pool_admit<NT, KPT, NB>(key, nstar, R, gamma, sm, verify_len);
   if (tid == 0) *n_admitted = nstar;
+}
+
+// The (rank + 1)-th smallest of the 32-bit values hv(m) over the slots with
+// cand(m) (rank below their count): four 8-bit digit passes, most significant
+// first, each an LDS histogram of the candidates whose higher digits match the
+// ones chosen so far.  Returns w with #{h < w} <= rank < #{h <= w}.  Every
+// thread must call it.
+template <int NT, int KPT, typename Cand, typename HV>
+__device__ __forceinline__ uint32_t select_rank(Cand cand, HV hv, int rank, uint32_t* hist, int* sel) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  uint32_t prefix = 0u, pmask = 0u;
+  int r = rank;
+#pragma unroll 1
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int b = tid; b < 256; b += NT) hist[b] = 0u;
+    __syncthreads();
+#pragma unroll 1
+    for (int m = 0; m < KPT; m++) {
+      const uint32_t h = hv(m);
+      if (cand(m) && (h & pmask) == prefix) atomicAdd(&hist[(h >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l holds bins 4l .. 4l + 3; exactly one lane holds rank r
+      const int c0 = (int)hist[4 * lane], c1 = (int)hist[4 * lane + 1];
+      const int c2 = (int)hist[4 * lane + 2], c3 = (int)hist[4 * lane + 3];
+      const int tot = c0 + c1 + c2 + c3;
+      double incl;
+      const int q = r - (int)wave_excl_scan_d((double)tot, &incl);
+      if (q >= 0 && q < tot) {
+        int bin = 4 * lane, rr = q;
+        if (rr >= c0) {
+          rr -= c0;
+          bin++;
+          if (rr >= c1) {
+            rr -= c1;
+            bin++;
+            if (rr >= c2) {
+              rr -= c2;
+              bin++;
+            }
+          }
+        }
+        sel[0] = bin;
+        sel[1] = rr;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sel[0] << shift;
+    pmask |= 255u << shift;
+    r = sel[1];
+    __syncthreads();  // hist and sel are rewritten by the next pass
+  }
+  return prefix;
+}
+
+// The early-stop walk needs the sorted pool only up to its first drop, so
+// pools of more than 2048 candidates are sorted a chunk at a time.  The next
+// chunk is every remaining candidate whose key lies below the (2048 + 1)-th
+// smallest remaining key, found on the high word (the survival probability)
+// by select_rank and, when a group of equal high words larger than a chunk
+// leaves that empty, refined on the low word (the flat index) within the
+// group: at most 2048 candidates, all of them below every candidate still
+// left.  It is gathered into LDS, sorted, and walked with the prefix carried
+// over from the chunks before; the walk ends at the first drop.  A chunk thus
+// holds exactly the next slots of the whole sorted pool, and n*, T_n and the
+// admitted set are those of the whole-pool sort.  The admitted candidates are
+// the keys below the first one not admitted.
+constexpr int SCHED_CHUNK = 2 * SCHED_THREADS;
+
+// Two exchange buffers of a chunk sort carved out of a larger LDS array.
+struct ChunkBufs {
+  uint64_t* bufs[2];
+};
+
+template <int KPT>
+__device__ __forceinline__ void schedule_chunked_body(const float* __restrict__ conf,
+                                                      const float* __restrict__ sps, int R, int gamma,
+                                                      int n_table, int32_t* __restrict__ verify_len,
+                                                      int32_t* __restrict__ n_admitted,
+                                                      float* __restrict__ cum_conf, int32_t* err) {
+  constexpr int NT = SCHED_THREADS, NB = 2, CK = SCHED_CHUNK / NT;
+  __shared__ SchedSmem<NT, KPT, NB> sm;
+  __shared__ uint32_t hist[256];
+  __shared__ int sel[2];
+  __shared__ int s_cnt, s_drop;
+  __shared__ uint64_t s_cut;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int n = R * gamma;
+  {
+    uint64_t unused[KPT];
+    pool_keys<NT, KPT, NB>(conf, R, gamma, cum_conf, err, sm, unused);
+  }
+  // the pool stays in LDS in flat index order (bufs[0]); bufs[1] holds the
+  // chunk (its first 2048 slots, then the sort's second exchange buffer)
+  const uint64_t* K = sm.bufs[0];
+  uint64_t* C = sm.bufs[1];
+  ChunkBufs cb;
+  cb.bufs[0] = C;
+  cb.bufs[1] = C + SCHED_CHUNK;
+
+  int base = 0;                               // pool slots already walked
+  long long Tb = (long long)R << FIX_SHIFT;   // T at slot base
+  uint64_t klo = 0ull;                        // remaining candidates: keys >= klo
+  uint64_t cut = ~0ull;                       // admitted: keys below cut
+  int nstar = n;
+  auto cand = [&](int m) { return tid + NT * m < n && K[tid + NT * m] >= klo; };
+  // gathers the candidates below khi into C; returns their count
+  auto gather = [&](uint64_t khi) {
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+#pragma unroll 1
+    for (int m = 0; m < KPT; m++) {
+      const uint64_t x = K[tid + NT * m];
+      if (tid + NT * m < n && x >= klo && x < khi) C[atomicAdd(&s_cnt, 1)] = x;
+    }
+    __syncthreads();
+    return s_cnt;
+  };
+#pragma unroll 1
+  while (base < n) {
+    uint64_t khi = ~0ull;  // every real key is below it
+    if (n - base > SCHED_CHUNK) {
+      const uint32_t w = select_rank<NT, KPT>(cand, [&](int m) { return (uint32_t)(K[tid + NT * m] >> 32); },
+                                              SCHED_CHUNK, hist, sel);
+      khi = (uint64_t)w << 32;
+    }
+    int cs = gather(khi);
+    if (cs == 0) {  // uniform: more than a chunk of keys share the high word w
+      const uint32_t w = (uint32_t)(khi >> 32);
+      const uint32_t w2 = select_rank<NT, KPT>(
+          [&](int m) { return cand(m) && (uint32_t)(K[tid + NT * m] >> 32) == w; },
+          [&](int m) { return (uint32_t)K[tid + NT * m]; }, SCHED_CHUNK, hist, sel);
+      khi |= w2;
+      __syncthreads();  // every thread has read s_cnt
+      cs = gather(khi);
+      // exactly a chunk by construction; the guard keeps the loop finite
+      if (cs == 0) {
+        nstar = base;
+        cut = klo;
+        break;
+      }
+    }
+    for (int i = cs + tid; i < SCHED_CHUNK; i += NT) C[i] = ~0ull;
+    __syncthreads();
+    uint64_t c[CK];
+#pragma unroll
+    for (int m = 0; m < CK; m++) c[m] = C[tid + NT * m];
+    // the first exchange stage writes cb.bufs[1], beyond the chunk's slots;
+    // an opaque thread id keeps the stages' partner indices inside the loop
+    int otid = tid;
+    asm volatile("" : "+v"(otid));
+    pool_bitonic<NT, CK, NB>(cb, c, otid);
+    if (tid == 0) s_drop = cs;
+    int drop = cs;
+    auto walk = [&](int i, long long Tn, long long v) {
+      const double th0 = (double)Tn * sps_at(sps, n_table, R + base + i);
+      const double th1 = (double)(Tn + v) * sps_at(sps, n_table, R + base + i + 1);
+      if (th1 < th0) drop = min(drop, i);
+    };
+    const long long tot = pool_scan<NT, CK>([&](int m) { return c[m]; }, cs, Tb, sm, walk);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) drop = min(drop, __shfl_xor(drop, o));
+    if (lane == 0 && drop < cs) atomicMin(&s_drop, drop);
+    __syncthreads();
+    const int d = s_drop;
+    if (d < cs) {  // uniform: the first drop is in this chunk, at sorted slot d
+#pragma unroll
+      for (int m = 0; m < CK; m++)
+        if (tid + NT * m == d) s_cut = c[m];
+      __syncthreads();
+      cut = s_cut;
+      nstar = base + d;
+      break;
+    }
+    base += cs;
+    Tb += tot;
+    klo = khi;
+    __syncthreads();  // the chunk buffer and the exchange buffers are reused
+  }
+
+  // Step 5 on the pool in index order: the admitted keys are those below cut
+  int* cnt = reinterpret_cast<int*>(C);
+  __syncthreads();
+  for (int r = tid; r < R; r += NT) cnt[r] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < KPT; m++) {
+    const uint64_t x = K[tid + NT * m];
+    if (tid + NT * m < n && x < cut) atomicAdd(&cnt[(uint32_t)x / gamma], 1);
+  }
+  __syncthreads();
+  for (int r = tid; r < R; r += NT) verify_len[r] = cnt[r];
+  if (tid == 0) *n_admitted = nstar;
+}
+
+template <int KPT>
+__global__ __launch_bounds__(SCHED_THREADS) void k_schedule_chunked(const float* __restrict__ conf,
+                                                                   const float* __restrict__ sps, int R,
+                                                                   int gamma, int n_table,
+                                                                   int32_t* __restrict__ verify_len,
+                                                                   int32_t* __restrict__ n_admitted,
+                                                                   float* __restrict__ cum_conf, int32_t* err) {
+  schedule_chunked_body<KPT>(conf, sps, R, gamma, n_table, verify_len, n_admitted, cum_conf, err);
 }
 
 template <int KPT>
@@ -334,7 +561,7 @@ __device__ __forceinline__ void schedule_async_body(const float* __restrict__ co
   auto key = [&](int m) { return NB == 1 ? sm.bufs[0][tid + NT * m] : k[m]; };
   auto scan = [&](auto f) {
     if (NB == 1) pool_scan_lds<NT, KPT, NB>(n, R, sm, f);
-    else pool_scan<NT, KPT, NB>(key, n, R, sm, f);
+    else pool_scan<NT, KPT>(key, n, (long long)R << FIX_SHIFT, sm, f);
   };
   pool_sort<NT, KPT, NB>(conf_lag, R, gamma, nullptr, err, sm, k);
   to_lds();
@@ -486,11 +713,11 @@ int schedule_impl(const float* conf, const float* sps, int R, int gamma, int n_t
       hipLaunchKernelGGL(k_schedule<2>, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, sps, R, gamma, n_table,
                          verify_len, n_admitted, cum_conf, err);
     else if (n <= 4 * SCHED_THREADS)
-      hipLaunchKernelGGL(k_schedule<4>, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, sps, R, gamma, n_table,
-                         verify_len, n_admitted, cum_conf, err);
+      hipLaunchKernelGGL(k_schedule_chunked<4>, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, sps, R, gamma,
+                         n_table, verify_len, n_admitted, cum_conf, err);
     else
-      hipLaunchKernelGGL(k_schedule<8>, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, sps, R, gamma, n_table,
-                         verify_len, n_admitted, cum_conf, err);
+      hipLaunchKernelGGL(k_schedule_chunked<8>, dim3(1), dim3(SCHED_THREADS), 0, stream, conf, sps, R, gamma,
+                         n_table, verify_len, n_admitted, cum_conf, err);
   }
   prof_after(DSPARK_KID_SCHEDULE, stream);
   return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;

@@ -178,6 +178,47 @@ def test_schedule_edge_tables():
         assert np.array_equal(L, O.schedule(conf, sps)["verify_len"])
 
 
+# pools of more than 2048 candidates are walked a sorted chunk of 2048 at a
+# time: first drops in the first, second and third chunk, no drop at all, and
+# groups of equal survival probabilities larger than a chunk (split on the
+# flat index); table: "flat", a slope c of 1 / (1 + c B), or a cliff (SPS
+# halves past B = R + 3000)
+@pytest.mark.parametrize("R,g,mode,table,expect", [
+    (512, 16, "beta", 3e-3, 485),       # 8192 candidates, drop in the first chunk
+    (1266, 4, "half", 1e-4, 3641),      # drop in the second chunk
+    (672, 11, "ties", 3e-4, 3058),      # drop in the second chunk, ties
+    (512, 16, "beta", 3e-5, 4755),      # drop in the third chunk
+    (2342, 2, "half", "flat", 4684),    # no drop: every chunk walked
+    (2619, 3, "ones", "cliff", 3000),   # 7857 equal keys, drop in the second chunk
+    (482, 15, "ones", "flat", 7230),    # 7230 equal keys, no drop
+])
+def test_schedule_chunked_walks(R, g, mode, table, expect):
+    rng = np.random.default_rng(R + 7 * g)
+    conf = rng.beta(6, 2, (R, g)).astype(np.float32)
+    if mode == "half":
+        conf[rng.random((R, g)) < 0.5] = 0.5
+    elif mode == "ones":
+        conf[:] = 1.0
+    elif mode == "ties":
+        conf[rng.random((R, g)) < 0.3] = 1.0
+    N = R * (g + 1) + 11
+    B = np.arange(1, N + 1)
+    if table == "flat":
+        sps = np.ones(N, np.float32)
+    elif table == "cliff":
+        sps = np.where(B <= R + 3000, 1.0, 0.5).astype(np.float32)
+    else:
+        sps = (1.0 / (1.0 + table * B)).astype(np.float32)
+    L, n, a, err = _gpu_schedule(conf, sps)
+    o = O.schedule(conf, sps)
+    say(f"pool {R}x{g} {mode}/{table}: n* = {n} (oracle {o['n_admitted']})")
+    assert o["n_admitted"] == expect  # the case exercises the chunk it names
+    assert err == 0
+    assert np.array_equal(a, o["cum_conf"])
+    assert n == o["n_admitted"]
+    assert np.array_equal(L, o["verify_len"])
+
+
 def _gpu_schedule_async(conf, conf_lag, sps):
     dv = dev()
     c = torch.from_numpy(np.ascontiguousarray(conf)).to(dv)

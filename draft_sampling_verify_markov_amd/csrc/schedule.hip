@@ -312,10 +312,12 @@ __device__ __forceinline__ void schedule_body(const float* __restrict__ conf, co
 // The (rank + 1)-th smallest of the 32-bit values hv(m) over the slots with
 // cand(m) (rank below their count): four 8-bit digit passes, most significant
 // first, each an LDS histogram of the candidates whose higher digits match the
-// ones chosen so far.  Returns w with #{h < w} <= rank < #{h <= w}.  Every
-// thread must call it.
+// ones chosen so far.  Returns w with #{h < w} <= rank < #{h <= w}, and in
+// *rank_in_group the rank among the candidates equal to w.  Every thread must
+// call it.
 template <int NT, int KPT, typename Cand, typename HV>
-__device__ __forceinline__ uint32_t select_rank(Cand cand, HV hv, int rank, uint32_t* hist, int* sel) {
+__device__ __forceinline__ uint32_t select_rank(Cand cand, HV hv, int rank, uint32_t* hist, int* sel,
+                                                int* rank_in_group = nullptr) {
   const int tid = threadIdx.x, lane = tid & 63;
   uint32_t prefix = 0u, pmask = 0u;
   int r = rank;
@@ -360,6 +362,7 @@ __device__ __forceinline__ uint32_t select_rank(Cand cand, HV hv, int rank, uint
     r = sel[1];
     __syncthreads();  // hist and sel are rewritten by the next pass
   }
+  if (rank_in_group) *rank_in_group = r;  // #{h < w} = rank - r
   return prefix;
 }
 
@@ -593,9 +596,35 @@ __device__ __forceinline__ void schedule_async_body(const float* __restrict__ co
 #pragma unroll
   for (int w = 1; w < NT / 64; w++) K = min(K, sm.wmin[w]);
 
-  pool_sort<NT, KPT, NB>(conf, R, gamma, cum_conf, err, sm, k);
-  to_lds();
-  pool_admit<NT, KPT, NB>(key, K, R, gamma, sm, verify_len);
+  // the current pool's first K candidates are its K smallest keys: no second
+  // sort, only the (K + 1)-th smallest key, selected on the high word and,
+  // inside a group of equal high words, on the low word (the flat index)
+  pool_keys<NT, KPT, NB>(conf, R, gamma, cum_conf, err, sm, k);
+  // the keys in flat index order: LDS with one buffer, registers with two
+  auto ckey = [&](int m) { return NB == 1 ? sm.bufs[0][tid + NT * m] : k[m]; };
+  auto live = [&](int m) { return tid + NT * m < n; };
+  uint32_t* hist = NB == 1 ? reinterpret_cast<uint32_t*>(sm.cstage) : reinterpret_cast<uint32_t*>(&sm.bufs[1][0]);
+  uint64_t cut = ~0ull;  // admitted: keys below cut
+  if (K < n) {
+    int r;
+    const uint32_t w = select_rank<NT, KPT>(live, [&](int m) { return (uint32_t)(ckey(m) >> 32); }, K, hist,
+                                            sm.wmin, &r);
+    cut = (uint64_t)w << 32;
+    if (r > 0)  // uniform: the cut falls inside the group of keys equal to w
+      cut |= select_rank<NT, KPT>([&](int m) { return live(m) && (uint32_t)(ckey(m) >> 32) == w; },
+                                  [&](int m) { return (uint32_t)ckey(m); }, r, hist, sm.wmin);
+  }
+  int* cnt = NB == 1 ? reinterpret_cast<int*>(sm.cstage) : reinterpret_cast<int*>(&sm.bufs[0][0]);
+  __syncthreads();
+  for (int r = tid; r < R; r += NT) cnt[r] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < KPT; m++) {
+    const uint64_t x = ckey(m);
+    if (live(m) && x < cut) atomicAdd(&cnt[(uint32_t)x / gamma], 1);
+  }
+  __syncthreads();
+  for (int r = tid; r < R; r += NT) verify_len[r] = cnt[r];
   if (tid == 0) *n_admitted = K;
 }
 

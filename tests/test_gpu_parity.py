@@ -284,6 +284,27 @@ def test_schedule_async_edge_tables():
         assert err == 0 and n == o["n_admitted"] and np.array_equal(L, o["verify_len"])
 
 
+# the current pool's first K candidates are found by selection, not a second
+# sort: equal confidences in every row make each position a group of R equal
+# keys, so the cut K (from the lagged pool) falls inside a group and the
+# selection has to split it on the flat index
+@pytest.mark.parametrize("R,g", [(128, 7), (250, 8), (500, 8), (512, 16)])
+def test_schedule_async_cut_inside_tie_group(R, g):
+    rng = np.random.default_rng(R + g)
+    conf = np.full((R, g), 0.9, np.float32)
+    conf_lag = rng.beta(6, 2, (R, g)).astype(np.float32)
+    N = R * (g + 1) + 5
+    B = np.arange(1, N + 1)
+    sps = (1.0 / (1.0 + 3e-4 * B)).astype(np.float32)
+    L, n, a, err = _gpu_schedule_async(conf, conf_lag, sps)
+    o = O.schedule_async(conf, conf_lag, sps)
+    say(f"async ties {R}x{g}: K={n} (oracle {o['n_admitted']}), K mod R = {n % R}")
+    assert 0 < o["n_admitted"] < R * g and o["n_admitted"] % R != 0  # the cut splits a group
+    assert err == 0
+    assert n == o["n_admitted"]
+    assert np.array_equal(L, o["verify_len"])
+
+
 # ---------------------------------------------------------------------------
 # stage parity: verify fed with the oracle's draft outputs
 

@@ -21,7 +21,9 @@
 //   residual  persistent, one workgroup per compute unit over the 256-column
 //             tiles (T > 0 only).  For requests that rejected at k*,
 //             recomputes the draft logits of position k* with the MFMA bias
-//             block and writes tile records of max(0, p - pi).
+//             block and writes tile records of max(0, p - pi).  Over more
+//             than 128 requests with bf16 factors the workgroup keeps its
+//             tiles' W2 fragments in registers for the whole call.
 //   (dspark_accept_rates reuses the stream and the residual pipeline over
 //   every request and position to form c*_k = 1 - |q_k - p_k|_1 / 2.)
 //   finalize  one workgroup per request: residual or bonus inverse-CDF sample

@@ -438,12 +438,15 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
 
     The scheduler reads only confidences and the cost table, and verify's
     target-row stream reads only the target and the verify lengths: both run
-    on the current stream while the draft runs on a side stream (forked from
-    and joined back to the current stream; capturable into a HIP graph);
-    verify then finishes on the current stream.  The draft is the longer of
-    the two branches, so the join waits on a kernel that has already ended
-    or is about to.  The early-stop and asynchronous schedulers on a pool of
-    at most 1024 candidates, and the static-threshold scheduler, are
+    on a side stream (forked from and joined back to the current stream;
+    capturable into a HIP graph) while the draft runs on the current stream;
+    verify then finishes on the current stream.  The draft is enqueued first,
+    on the stream that needs no event wait, so its workgroups are resident
+    before the side stream's kernels take the free slots (with the draft
+    behind the event wait instead, eager rounds lost up to 130 microseconds
+    to target-row blocks that filled the compute units before the one-launch
+    draft could start).  The early-stop and asynchronous schedulers on a pool
+    of at most 1024 candidates, and the static-threshold scheduler, are
     workgroups small enough to share a compute unit with the one-launch draft
     and run beside it; larger pools are scheduled first, before the fork.
     The scheduler uses its own small workspace
@@ -474,17 +477,22 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
         ws_sched = torch.zeros(256, dtype=torch.uint8, device=dev)
     beside = sched and (scheduler == "threshold" or d["conf"].numel() <= 1024)
 
+    # every output is allocated on the current stream, which reads them after
+    # the join (on the side stream the scheduler only writes into its own)
+    sched_out = None
+    if sched:
+        sched_out = (torch.empty(R, dtype=torch.int32, device=dev), torch.empty(1, dtype=torch.int32, device=dev),
+                     None)
+
     def run_scheduler():
         if scheduler == "async":
-            return schedule_async(d["conf"], d["conf_lag"], d["sps"], ws_sched, with_cum=False)
+            return schedule_async(d["conf"], d["conf_lag"], d["sps"], ws_sched, out=sched_out)
         if scheduler == "threshold":
-            return schedule_threshold(d["conf"], theta, ws_sched, with_cum=False)
-        return schedule(d["conf"], d["sps"], ws_sched, with_cum=False)
+            return schedule_threshold(d["conf"], theta, ws_sched, out=sched_out)
+        return schedule(d["conf"], d["sps"], ws_sched, out=sched_out)
 
     if sched and not beside:
         L, n, _ = run_scheduler()
-    # the draft's outputs are allocated on the current stream, which reads them
-    # after the join
     tok = torch.empty((R, g), dtype=torch.int32, device=dev)
     prob = torch.empty((R, g), dtype=torch.float32, device=dev)
     stats = torch.empty((R, g, 2), dtype=torch.float32, device=dev)
@@ -493,17 +501,17 @@ def run_round(dev_inputs, temperature, ws, use_scheduler=True, ws_sched=None, sc
         states = torch.empty((R, g, d["W1"].shape[1]), dtype=d["W1"].dtype, device=dev)
     side = _side_stream(dev)
     side.wait_stream(cur)
-    with torch.cuda.stream(side):
-        if head == "rnn":
-            draft_rnn(d["base"], d["W1"], d["W2"], d["Wx"], d["Ws"], d["rnn_bias"], d["anchor"], d["u_draft"],
-                      temperature, ws, out=(tok, prob, stats, states))
-        else:
-            draft(d["base"], d["W1"], d["W2"], d["anchor"], d["u_draft"], temperature, ws, out=(tok, prob, stats))
-    # current stream, beside the draft: the scheduler (when small) and the
+    if head == "rnn":
+        draft_rnn(d["base"], d["W1"], d["W2"], d["Wx"], d["Ws"], d["rnn_bias"], d["anchor"], d["u_draft"],
+                  temperature, ws, out=(tok, prob, stats, states))
+    else:
+        draft(d["base"], d["W1"], d["W2"], d["anchor"], d["u_draft"], temperature, ws, out=(tok, prob, stats))
+    # side stream, beside the draft: the scheduler (when small) and the
     # target-row stream of verify (it needs only the verify lengths)
-    if beside:
-        L, n, _ = run_scheduler()
-    verify_stream(d["target"], L, temperature, ws)
+    with torch.cuda.stream(side):
+        if beside:
+            L, n, _ = run_scheduler()
+        verify_stream(d["target"], L, temperature, ws)
     cur.wait_stream(side)
     if head == "rnn":
         ot, al, tp = verify_rnn(d["target"], d["base"], states, d["W2"], tok, prob, stats, L, d["u_accept"],

@@ -58,6 +58,11 @@ KERNELS = {
                                 "draft_sampling_verify_markov_amd/csrc/common.h",
                                 "draft_sampling_verify_markov_amd/csrc/select.h",
                                 "include/dspark.h")),
+    "rows": dict(name="k_draft_rows", kid=9, repeat=1,
+                 sources=("draft_sampling_verify_markov_amd/csrc/draft.hip",
+                          "draft_sampling_verify_markov_amd/csrc/common.h",
+                          "draft_sampling_verify_markov_amd/csrc/select.h",
+                          "include/dspark.h")),
     "per-step": dict(name="k_draft_partials", kid=1, repeat=1,
                      sources=("draft_sampling_verify_markov_amd/csrc/draft.hip",
                               "draft_sampling_verify_markov_amd/csrc/common.h",
@@ -323,7 +328,7 @@ def gpu_bench(a):
     ref = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in ref.items()}
 
     lib = D.load_library()
-    # which draft path dspark_draft takes on this workload: arm the one-launch
+    # which draft path dspark_draft takes on this workload: arm a one-launch
     # kernel's hook for one eager round and see whether it fired
     ev_probe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     with torch.cuda.stream(stream):
@@ -331,14 +336,17 @@ def gpu_bench(a):
             e.record()
     torch.cuda.synchronize()
     P1 = ctypes.c_void_p * 1
-    assert lib.dspark_profile_arm(KERNELS["one-launch"]["kid"], P1(ev_probe[0].cuda_event),
-                                  P1(ev_probe[1].cuda_event), 1, 1) == 0
-    with torch.cuda.stream(stream):
-        D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta, head=a.head)
-    torch.cuda.synchronize()
-    path = "one-launch" if lib.dspark_profile_disarm() == 1 else "per-step"
+
+    def fires(kid):
+        assert lib.dspark_profile_arm(kid, P1(ev_probe[0].cuda_event), P1(ev_probe[1].cuda_event), 1, 1) == 0
+        with torch.cuda.stream(stream):
+            D.run_round(dd, T, ws, ws_sched=ws_sched, scheduler=a.scheduler, theta=theta, head=a.head)
+        torch.cuda.synchronize()
+        return lib.dspark_profile_disarm() == 1
+
+    path = next((p for p in ("one-launch", "rows") if fires(KERNELS[p]["kid"])), "per-step")
     K = KERNELS[path]
-    launches_per_round = 1 if path == "one-launch" else g
+    launches_per_round = g if path == "per-step" else 1
 
     use_graph = not a.eager
     graph = None
@@ -498,7 +506,7 @@ def gpu_bench(a):
     tokens = int((A + 1).sum())
     b_min, b_sched = algorithmic_bytes(d, tokens, int((L + 1).sum()))
     wb = 2 if d["w_dtype"] == "bf16" else 4
-    if path == "one-launch":
+    if path != "per-step":
         # every base row, W2 once, the gathered W1 rows
         k1_bytes = 4 * R * g * V + wb * r * V + wb * R * g * r
         k1_flops = 2 * R * r * V * g

@@ -165,7 +165,7 @@ int dspark_device_error(void* workspace, size_t workspace_bytes, int32_t* host_b
 }
 
 int dspark_profile_arm(int kid, hipEvent_t* starts, hipEvent_t* stops, int n, int repeat) {
-  if (kid < DSPARK_KID_DRAFT_PARTIALS || kid > DSPARK_KID_DRAFT_FUSED || !starts || !stops ||
+  if (kid < DSPARK_KID_DRAFT_PARTIALS || kid > DSPARK_KID_DRAFT_ROWS || !starts || !stops ||
       n < 1 || repeat < 1 || repeat > 1000)
     return DSPARK_EINVAL;
   prof.kid = kid;

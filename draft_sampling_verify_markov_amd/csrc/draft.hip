@@ -320,6 +320,238 @@ __global__ __launch_bounds__(256) void k_draft_select(DraftStep<WT> P) {
   }
 }
 
+// Small problems: one workgroup per request runs all gamma steps.  A
+// request's draw depends only on its own previous token, so no workgroup
+// waits on another.  Per step and tile the workgroup computes the bias block
+// of its single request with the arithmetic of k_draft_partials: bf16 factors
+// through the same fragment and MFMA chain (the request's W1 row read by all
+// 32 block rows, a zero row stride), fp32 factors through the same fmaf chain
+// per column, one column per thread; then the same epilogue on block row 0.
+// It keeps the tile records in LDS and draws with the selection of
+// k_draft_select, so its outputs are bit-identical to the per-step kernels'.  The step's base row
+// sits in LDS (the next step's is loaded during the current one); with fp32
+// factors W2 is staged in LDS once, with bf16 factors every workgroup reads
+// W2 once per step, which bounds the sizes this path takes (draft_rows_fits).
+constexpr int ROWS_MAX_TILES = 16;
+constexpr int ROWS_MAX_V = ROWS_MAX_TILES * TILE;
+constexpr int ROWS_W2_LDS_FLOATS = 16384;                // fp32 factors: r * V at most
+constexpr size_t ROWS_MAX_W2_BYTES = size_t(32) << 20;  // bf16: R * gamma * r * V * 2 at most
+
+template <typename WT>
+static bool draft_rows_fits(int R, int gamma, int V, int r) {
+  if (ceil_div(V, TILE) > ROWS_MAX_TILES) return false;
+  if (std::is_same<WT, float>::value) return (size_t)r * (size_t)V <= (size_t)ROWS_W2_LDS_FLOATS;
+  return (size_t)R * (size_t)gamma * (size_t)r * (size_t)V * sizeof(WT) <= ROWS_MAX_W2_BYTES;
+}
+
+template <typename WT, bool GREEDY, int KS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_draft_rows(DraftStep<WT> P) {
+  constexpr int APAD = BiasBlock<WT>::APAD;
+  constexpr bool W2_LDS = std::is_same<WT, float>::value;
+  constexpr int PF = ROWS_MAX_V / 256;  // base values per thread of a prefetched row
+  __shared__ __align__(16) WT A_row[DSPARK_MAX_RANK + APAD];
+  // block rows of the tile's base values: row 0 the request's; with fp32
+  // factors row 1 holds its bias (read as block row 0 from X + BSTRIDE); the
+  // rest zero
+  __shared__ __align__(16) float X[33 * BSTRIDE];
+  __shared__ __align__(16) float Bs[2][ROWS_MAX_V];
+  __shared__ __align__(16) WT W2s[W2_LDS ? ROWS_W2_LDS_FLOATS : 1];
+  __shared__ float red_m[4], red_s[4];
+  __shared__ int red_i[4];
+  __shared__ __align__(16) float4 recs[2 * ROWS_MAX_TILES];
+  __shared__ BlockSelectSmem sm;
+  __shared__ float w1s[DSPARK_MAX_RANK];
+  __shared__ float part[32 / sizeof(WT)][WCOLS];
+  __shared__ float gm[4];
+  __shared__ int gi[4];
+  __shared__ int s_x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, h = lane >> 5;
+  const int row = blockIdx.x;
+  const int nt = ceil_div(P.V, TILE);
+  const bool t_one = (P.T == 1.0f);
+  const float sc = t_one ? LOG2E_F : LOG2E_F * P.invT;
+  const double invTd = t_one ? 1.0 : 1.0 / (double)P.T;
+  const WT* W2 = W2_LDS ? W2s : P.W2;
+
+  auto load_base = [&](int k, float (&v)[PF]) {  // base row of step k, in registers
+    const float* brow = P.base + ((size_t)row * P.gamma + (k - 1)) * P.V;
+#pragma unroll
+    for (int i = 0; i < PF; i++) {
+      const int c = tid + 256 * i;
+      v[i] = (c < P.V) ? brow[c] : 0.f;
+    }
+  };
+  auto store_base = [&](float* dst, const float (&v)[PF]) {
+#pragma unroll
+    for (int i = 0; i < PF; i++) dst[tid + 256 * i] = v[i];
+  };
+  {
+    float v[PF];
+    load_base(1, v);
+    if (W2_LDS)
+      for (int i = tid; i < P.r * P.V; i += 256) W2s[i] = P.W2[i];
+    for (int i = tid; i < 33 * BSTRIDE; i += 256) X[i] = 0.f;
+    if (tid == 0) s_x = checked_token(P.anchor[row], P.V, P.err);
+    store_base(Bs[0], v);
+  }
+  __syncthreads();
+
+  for (int k = 1; k <= P.gamma; k++) {
+    const int prev = s_x;
+    const size_t ev = (size_t)row * P.gamma + (k - 1);
+    const float* bl = Bs[(k - 1) & 1];
+    float nxt[PF];
+    if (k < P.gamma) load_base(k + 1, nxt);
+    // the previous token's W1 row (the MMA operand of every block row) and,
+    // widened, the chunk recompute's copy
+    for (int e = tid; e < P.r; e += 256) {
+      const WT w = P.W1[(size_t)prev * P.r + e];
+      A_row[e] = w;
+      w1s[e] = to_f32(w);
+    }
+    if (W2_LDS) __syncthreads();  // A_row complete before the per-column sums read it
+    for (int t = 0; t < nt; t++) {
+      const int cbase = t * TILE + wave * WCOLS;
+      f32x16 acc[2];
+      X[tid] = bl[t * TILE + tid];  // block row 0 (past V: 0, masked by the reader)
+      if constexpr (W2_LDS) {
+        // fp32 factors: the request's bias at column t TILE + tid, the fmaf
+        // chain of the block's MMA (ascending k from 0); columns past V have
+        // W2 = 0 there
+        const int c = t * TILE + tid;
+        float a = 0.f;
+        for (int kk = 0; kk < P.r; kk++)
+          a = fmaf(to_f32(A_row[kk]), (c < P.V) ? to_f32(W2s[(size_t)kk * P.V + c]) : 0.f, a);
+        X[BSTRIDE + tid] = a;
+        __syncthreads();
+        float av[2][16];
+        stage_read_full(X + BSTRIDE, wave * WCOLS, av);
+#pragma unroll
+        for (int p = 0; p < 2; p++)
+#pragma unroll
+          for (int q = 0; q < 16; q++) acc[p][q] = av[p][q];
+      } else {
+        typename BiasBlock<WT>::template Frag<KS> F;
+        BiasBlock<WT>::template load<KS>(F, W2, P.V, P.r, t * TILE + wave * WCOLS);
+        __syncthreads();
+        BiasBlock<WT>::template to_operands<KS>(F);
+#pragma unroll
+        for (int p = 0; p < 2; p++)
+#pragma unroll
+          for (int q = 0; q < 16; q++) acc[p][q] = 0.f;
+        BiasBlock<WT>::template mma_rb_op<KS>(F, P.r, A_row, 0, acc);
+      }
+      float b[2][16];
+      if ((t + 1) * TILE <= P.V)
+        stage_read_full(X, wave * WCOLS, b);
+      else
+        stage_read(X, true, P.V, cbase, wave * WCOLS, b);
+      if (GREEDY) {
+        float bv = -INFINITY;
+        int bi = 0x7fffffff;
+        bool bad = false;
+#pragma unroll
+        for (int q = 0; q < 16; q++)
+#pragma unroll
+          for (int p = 0; p < 2; p++) {
+            const float z = b[p][q] + acc[p][q];
+            bad |= (z != z);
+            if (z > bv) { bv = z; bi = cbase + elem_col(p, q, h); }
+          }
+        if (bad) raise_err(P.err, DSPARK_DERR_NONFINITE);
+        argmax_xor32(bv, bi);
+        if (lane == 0) { red_m[wave] = bv; red_i[wave] = bi; }
+      } else {
+        float ml = -INFINITY;
+#pragma unroll
+        for (int p = 0; p < 2; p++)
+#pragma unroll
+          for (int q = 0; q < 16; q++) ml = fmaxf(ml, b[p][q] + acc[p][q]);
+        const float mw = max_xor32(ml);
+        const float mref = (mw == -INFINITY) ? 0.f : mw;
+        float e[2][16];
+#pragma unroll
+        for (int p = 0; p < 2; p++)
+#pragma unroll
+          for (int q = 0; q < 16; q++) e[p][q] = exp2_scaled((b[p][q] - mref) + acc[p][q], sc);
+        const float sl = tree_sum32(e);
+        const float sw = sum_xor32(sl);
+        if (lane == 0) { red_m[wave] = mw; red_s[wave] = sw; }
+      }
+      __syncthreads();
+      if (tid == 0) {
+        if (GREEDY) {
+          float v = red_m[0];
+          int i = red_i[0];
+#pragma unroll
+          for (int w = 1; w < 4; w++) argmax_merge(v, i, red_m[w], red_i[w]);
+          recs[2 * t] = make_float4(v, __int_as_float(i), 0.f, 0.f);
+        } else {
+          const float m0 = red_m[0], m1 = red_m[1], m2 = red_m[2], m3 = red_m[3];
+          const float mt = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+          auto rescale = [&](float swv, float mwv) {
+            const float d = t_one ? (mwv - mt) : (mwv - mt) * P.invT;
+            return (mwv == -INFINITY) ? 0.f : swv * exp_acc(d);
+          };
+          const float s0 = rescale(red_s[0], m0), s1 = rescale(red_s[1], m1);
+          const float s2 = rescale(red_s[2], m2), s3 = rescale(red_s[3], m3);
+          const float st = (s0 + s1) + (s2 + s3);
+          recs[2 * t] = make_float4(mt, st, s0, s1);
+          recs[2 * t + 1] = make_float4(s2, s3, 0.f, 0.f);
+          if (is_bad(st) || !(mt == mt) || mt == INFINITY) raise_err(P.err, DSPARK_DERR_NONFINITE);
+        }
+      }
+      __syncthreads();  // X and red_* are rewritten by the next tile; recs complete
+    }
+
+    // the draw from the records (k_draft_select's selection)
+    if (GREEDY) {
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int t = tid; t < nt; t += 256) {
+        const float4 r0 = recs[2 * t];
+        argmax_merge(bv, bi, r0.x, __float_as_int(r0.y));
+      }
+      wave_argmax(bv, bi);
+      if (lane == 0) { gm[wave] = bv; gi[wave] = bi; }
+      __syncthreads();
+      if (tid == 0) {
+        for (int w = 1; w < 4; w++) argmax_merge(bv, bi, gm[w], gi[w]);
+        int x = bi;
+        if (x < 0 || x >= P.V) x = 0;  // only with non-finite logits (flagged)
+        P.tokens[ev] = x;
+        P.probs[ev] = 1.0f;
+        P.stats[2 * ev] = bv;
+        P.stats[2 * ev + 1] = 1.0f;
+        s_x = x;
+      }
+    } else {
+      const float u = checked_uniform(P.u_draft[ev], P.err);
+      const TilePick S = block_select_tile(recs, nt, true, invTd, (double)u, sm);
+      const int cb = S.t * TILE + S.w * WCOLS;
+      const int col = cb + lane;
+      const float bval = (wave == 0 && col < P.V) ? bl[col] : -INFINITY;
+      const float bias = chunk_bias<WT, KS>(W2, P.V, P.r, cb, w1s, part);
+      if (wave == 0) {
+        const float ec = exp2_scaled((bval - S.mt) + bias, sc);
+        const int c = wave_pick64(ec, S.scale, S.rem);
+        const float ex = __shfl(ec, c);
+        if (lane == 0) {
+          const int x = min(cb + c, P.V - 1);
+          P.tokens[ev] = x;
+          P.probs[ev] = (float)((double)ex * S.scale / S.Z);
+          P.stats[2 * ev] = S.M;
+          P.stats[2 * ev + 1] = (float)S.Z;
+          if (!(S.Z > 0.0) || is_bad(S.M)) raise_err(P.err, DSPARK_DERR_NONFINITE);
+          s_x = x;
+        }
+      }
+    }
+    if (k < P.gamma) store_base(Bs[k & 1], nxt);
+    __syncthreads();  // s_x, the next base row, w1s, A_row and the selection's LDS are reused by the next step
+  }
+}
+
 bool draft_fused_supported(int R, int gamma, int V, int r, float T);
 int draft_fused_launch(const float* base, const void* W1, const void* W2, const int32_t* anchor,
                        const float* u_draft, int R, int gamma, int V, int r, float T, int32_t* tokens,
@@ -341,6 +573,7 @@ static int launch_draft(const float* base, const void* W1, const void* W2, const
       draft_fused_supported(R, gamma, V, r, T))
     return draft_fused_launch(base, W1, W2, anchor, u_draft, R, gamma, V, r, T, tokens, probs, stats, dw,
                               stream);
+  const bool rows = rnn == nullptr && !stepwise_requested() && draft_rows_fits<WT>(R, gamma, V, r);
   DraftStep<WT> P;
   P.base = base;
   P.W1 = static_cast<const WT*>(rnn ? rnn->states : W1);
@@ -355,6 +588,20 @@ static int launch_draft(const float* base, const void* W1, const void* W2, const
   P.tokens = tokens; P.probs = probs; P.stats = stats;
   P.trec = dw.trec;
   P.err = dw.err;
+  if (rows) {
+    P.k = 1;
+    prof_before(DSPARK_KID_DRAFT_ROWS, stream);
+    for (int rep = prof_repeat(DSPARK_KID_DRAFT_ROWS); rep > 0; rep--) {
+      DSPARK_DISPATCH_KS(r, {
+        if (T == 0.f)
+          hipLaunchKernelGGL((k_draft_rows<WT, true, KS>), dim3(R), dim3(256), 0, stream, P);
+        else
+          hipLaunchKernelGGL((k_draft_rows<WT, false, KS>), dim3(R), dim3(256), 0, stream, P);
+      });
+    }
+    prof_after(DSPARK_KID_DRAFT_ROWS, stream);
+    return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
+  }
   const int nt = ceil_div(V, TILE);
   const int grid1 = min(nt, device_cu_count());
   for (int k = 1; k <= gamma; k++) {

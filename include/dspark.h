@@ -155,9 +155,12 @@ const char* dspark_status_string(int status);
  * keep part of the grid waiting.  Every wait is bounded (0.5 s); one that
  * runs out sets DSPARK_DERR_SYNC, every workgroup still finishes, and the
  * call's outputs are then INVALID: a caller that shares the GPU must read the
- * error word (dspark_device_error) before using them.  Otherwise, or with the
- * environment variable DSPARK_DRAFT_KERNEL=stepwise, two kernels per step
- * run.  Both paths give identical outputs.
+ * error word (dspark_device_error) before using them.  Otherwise, small
+ * problems (at most 16 column tiles, V <= 4096, and R * gamma * r * V times
+ * the factor size at most 32 MiB) run all steps in one launch of one
+ * workgroup per request, which waits on no other workgroup; the rest run two
+ * kernels per step, as does every call with the environment variable
+ * DSPARK_DRAFT_KERNEL=stepwise.  All paths give identical outputs.
  */
 int dspark_draft(const float* base, const void* W1, const void* W2, dspark_wtype w_type,
                  const int32_t* anchor, const float* u_draft, int R, int gamma, int V, int r,
@@ -350,7 +353,8 @@ typedef enum {
   DSPARK_KID_VERIFY_DECIDE = 5,   /* row statistics + ordered accept tests  */
   DSPARK_KID_RESIDUAL = 6,        /* residual max(0, p - q) partials        */
   DSPARK_KID_VERIFY_FINALIZE = 7, /* residual / bonus sample and outputs    */
-  DSPARK_KID_DRAFT_FUSED = 8      /* all draft steps in one launch          */
+  DSPARK_KID_DRAFT_FUSED = 8,     /* all draft steps in one launch          */
+  DSPARK_KID_DRAFT_ROWS = 9       /* small problems: one workgroup/request  */
 } dspark_kernel_id;
 
 int dspark_profile_arm(int kid, hipEvent_t* starts, hipEvent_t* stops, int n, int repeat);

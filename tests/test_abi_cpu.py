@@ -208,8 +208,10 @@ def test_profile_hook_arguments(lib):
     arr = (ctypes.c_void_p * 4)(1, 2, 3, 4)
     EINVAL = -1
     assert lib.dspark_profile_arm(0, arr, arr, 4, 1) == EINVAL          # unknown kernel id
-    assert lib.dspark_profile_arm(9, arr, arr, 4, 1) == EINVAL
+    assert lib.dspark_profile_arm(10, arr, arr, 4, 1) == EINVAL
     assert lib.dspark_profile_arm(8, arr, arr, 4, 1) == 0              # one-launch draft
+    assert lib.dspark_profile_disarm() == 0
+    assert lib.dspark_profile_arm(9, arr, arr, 4, 1) == 0              # one workgroup per request
     assert lib.dspark_profile_disarm() == 0
     assert lib.dspark_profile_arm(1, None, arr, 4, 1) == EINVAL         # NULL arrays
     assert lib.dspark_profile_arm(1, arr, None, 4, 1) == EINVAL

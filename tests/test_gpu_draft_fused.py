@@ -23,9 +23,10 @@ from gpu_util import ATOL, RTOL, dev, say, to_dev
 pytestmark = pytest.mark.gpu
 
 KID_DRAFT_FUSED = 8
+KID_DRAFT_ROWS = 9
 
 
-def _draft(inp, T, kernel, monkeypatch, ws=None, d=None):
+def _draft(inp, T, kernel, monkeypatch, ws=None, d=None, kid=KID_DRAFT_FUSED):
     if kernel == "stepwise":
         monkeypatch.setenv("DSPARK_DRAFT_KERNEL", "stepwise")
     else:
@@ -41,7 +42,7 @@ def _draft(inp, T, kernel, monkeypatch, ws=None, d=None):
     torch.cuda.synchronize()
     arr_s = (ctypes.c_void_p * 1)(ev[0].cuda_event)
     arr_e = (ctypes.c_void_p * 1)(ev[1].cuda_event)
-    assert lib.dspark_profile_arm(KID_DRAFT_FUSED, arr_s, arr_e, 1, 1) == 0
+    assert lib.dspark_profile_arm(kid, arr_s, arr_e, 1, 1) == 0
     try:
         tok, prob, stats = D.draft(d["base"], d["W1"], d["W2"], d["anchor"], d["u_draft"], T, ws)
         torch.cuda.synchronize()
@@ -105,7 +106,8 @@ def test_one_launch_draft_matches_stepwise_and_oracle(R, g, V, r, T, monkeypatch
     (16, 3, 4096, 48),      # a rank it has no kernel for
 ])
 def test_outside_the_one_launch_limits(R, g, V, r, monkeypatch):
-    """Outside its limits dspark_draft takes the per-step kernels by itself."""
+    """Outside its limits dspark_draft takes another path by itself (the
+    per-request kernel for small problems, else the per-step kernels)."""
     cfg = config(1, R=R, gamma=g, V=V, r=r, w_dtype="bf16", table="linear")
     inp = make_inputs(cfg, seed=500 + R, seed_u=g)
     label = f"draft {R},{g},{V},{r}"
@@ -114,6 +116,33 @@ def test_outside_the_one_launch_limits(R, g, V, r, monkeypatch):
     assert not a["fused"], "the one-launch draft ran outside its limits"
     assert a["err"] == 0
     _oracle_check(inp, 1.0, a, label)
+
+
+# Small problems the one-launch draft does not take (fp32 factors, ranks it
+# has no kernel for) run in one launch of one workgroup per request: the same
+# per-row arithmetic as the per-step kernels, so bit-identical outputs.
+@pytest.mark.parametrize("T", [1.0, 0.0, 0.7])
+@pytest.mark.parametrize("R,g,V,r,w", [
+    (4, 4, 512, 16, "f32"),      # the tiny workload's shape
+    (5, 3, 1000, 16, "f32"),     # ragged vocabulary tail
+    (33, 5, 264, 48, "f32"),     # more requests than a 32-row block, rank 48
+    (3, 16, 1024, 16, "f32"),    # four tiles, the longest block
+    (16, 3, 4096, 48, "bf16"),   # sixteen tiles, a rank the one-launch draft has no kernel for
+])
+def test_per_request_draft_matches_stepwise_and_oracle(R, g, V, r, w, T, monkeypatch):
+    cfg = config(1, R=R, gamma=g, V=V, r=r, w_dtype=w, table="linear")
+    inp = make_inputs(cfg, seed=2000 + R + g, seed_u=R + 1)
+    label = f"per-request draft {R},{g},{V},{r},{w} T={T}"
+    say(f"[{label}] default path")
+    a = _draft(inp, T, "default", monkeypatch, kid=KID_DRAFT_ROWS)
+    assert a["fused"], "the per-request draft did not run"
+    assert a["err"] == 0, f"device error bits {a['err']}"
+    b = _draft(inp, T, "stepwise", monkeypatch, kid=KID_DRAFT_ROWS)
+    assert not b["fused"]
+    assert b["err"] == 0
+    for key in ("tokens", "probs", "stats"):
+        assert np.array_equal(a[key], b[key]), f"{label}: {key} differ from the per-step kernels"
+    _oracle_check(inp, T, a, label)
 
 
 def test_repeated_calls_on_one_workspace(monkeypatch):

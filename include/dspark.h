@@ -156,11 +156,12 @@ const char* dspark_status_string(int status);
  * runs out sets DSPARK_DERR_SYNC, every workgroup still finishes, and the
  * call's outputs are then INVALID: a caller that shares the GPU must read the
  * error word (dspark_device_error) before using them.  Otherwise, small
- * problems (at most 16 column tiles, V <= 4096, and R * gamma * r * V times
- * the factor size at most 32 MiB) run all steps in one launch of one
- * workgroup per request, which waits on no other workgroup; the rest run two
- * kernels per step, as does every call with the environment variable
- * DSPARK_DRAFT_KERNEL=stepwise.  All paths give identical outputs.
+ * problems (at most 16 column tiles, V <= 4096, and with fp32 factors
+ * r * V <= 16384, with bf16 factors R * gamma * r * V * 2 bytes <= 32 MiB)
+ * run all steps in one launch of one workgroup per request, which waits on
+ * no other workgroup; the rest run two kernels per step, as does every call
+ * with the environment variable DSPARK_DRAFT_KERNEL=stepwise.  All paths
+ * give identical outputs.
  */
 int dspark_draft(const float* base, const void* W1, const void* W2, dspark_wtype w_type,
                  const int32_t* anchor, const float* u_draft, int R, int gamma, int V, int r,

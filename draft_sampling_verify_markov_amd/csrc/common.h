@@ -519,25 +519,30 @@ struct BiasBlock<float> {
     F.V = V;
     F.cbase = cbase;
   }
+  // Row k of W2 at the lane's columns c0 + 2 q + p -> w[g][p][q], c0 = cbase
+  // + 16 g + 8 h: two 16-byte loads per group.  c0 and V are multiples of 8,
+  // so a group's eight columns lie all below V or all past it (then 0).
   template <int KS>
   __device__ static __forceinline__ void w2_at(const Frag<KS>& F, int k, float (&w)[4][2][4]) {
     const int h = (threadIdx.x & 63) >> 5;
 #pragma unroll
     for (int g = 0; g < 4; g++) {
       const int c0 = F.cbase + 16 * g + 8 * h;
-#pragma unroll
-      for (int q = 0; q < 4; q++)
-#pragma unroll
-        for (int p = 0; p < 2; p++) {
-          const int c = c0 + 2 * q + p;
-          w[g][p][q] = (c < F.V) ? F.W2[(size_t)k * F.V + c] : 0.f;
-        }
+      float4 lo = make_float4(0.f, 0.f, 0.f, 0.f), hi = lo;
+      if (c0 < F.V) {
+        const float4* src = reinterpret_cast<const float4*>(F.W2 + (size_t)k * F.V + c0);
+        lo = src[0];
+        hi = src[1];
+      }
+      w[g][0][0] = lo.x; w[g][1][0] = lo.y; w[g][0][1] = lo.z; w[g][1][1] = lo.w;
+      w[g][0][2] = hi.x; w[g][1][2] = hi.y; w[g][0][3] = hi.z; w[g][1][3] = hi.w;
     }
   }
   template <int KS>
   __device__ static inline void mma(const Frag<KS>& F, int r, const float* A_lds, int a_stride,
                                     int nrb, f32x16 (&acc)[4][2]) {
     const int j = (threadIdx.x & 63) & 31;
+#pragma unroll 4
     for (int k = 0; k < r; k++) {
       float w[4][2][4];
       w2_at(F, k, w);
@@ -566,6 +571,7 @@ struct BiasBlock<float> {
   __device__ static inline void mma_rb(const Frag<KS>& F, int r, const float* A_rows, int a_stride,
                                        f32x16 (&acc)[2]) {
     const int j = (threadIdx.x & 63) & 31;
+#pragma unroll 4
     for (int k = 0; k < r; k++) {
       float w[4][2][4];
       w2_at(F, k, w);
@@ -590,6 +596,7 @@ struct BiasBlock<float> {
   template <int KS>
   __device__ static inline void mma_row(const Frag<KS>& F, int r, const Row<KS>& B,
                                         f32x16 (&acc)[2]) {
+#pragma unroll 4
     for (int k = 0; k < r; k++) {
       float w[4][2][4];
       w2_at(F, k, w);

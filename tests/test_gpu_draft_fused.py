@@ -1,10 +1,11 @@
-"""GPU parity of the one-launch draft (all gamma steps in one persistent kernel).
+"""GPU parity of the one-launch drafts (all gamma steps in one kernel).
 
-dspark_draft runs the one-launch kernel where it applies (bf16 factors, rank
-16/32/64/128/256, at most two 256-column tiles per compute unit, R <= 1024);
-DSPARK_DRAFT_KERNEL=stepwise selects the per-step kernels instead.  Both do the
-same arithmetic in the same order, so their outputs must be bit-identical;
-both must match the float64 oracle on every request whose draws are not within
+dspark_draft runs the persistent one-launch kernel where it applies (bf16
+factors, rank 16/32/64/128/256, at most two 256-column tiles per compute unit,
+R <= 1024), else, for small problems, one launch of one workgroup per request;
+DSPARK_DRAFT_KERNEL=stepwise selects the per-step kernels instead.  All do the
+same arithmetic in the same order, so their outputs must be bit-identical; all
+must match the float64 oracle on every request whose draws are not within
 1e-6 of a CDF boundary.  The launch hook tells which kernel ran.
 """
 

@@ -29,6 +29,9 @@
 //   finalize  one workgroup per request: residual or bonus inverse-CDF sample
 //             (fp64 scan over tiles, recompute of one chunk or tile), emitted
 //             tokens and the p_k(x_k) output.
+#include <stdlib.h>
+#include <string.h>
+
 #include <type_traits>
 
 #include "select.h"
@@ -792,13 +795,22 @@ __device__ __forceinline__ int wave_sample_target_row(const VerifyArgs<WT>& P, s
 // and chunk from the residual records, recompute that chunk's draft bias with
 // vector FMAs (chunk_bias), and wave 0 does the in-chunk search.  Bonus sample
 // (or a residual with no mass): wave 0 samples the target row.
+template <typename WT>
+struct FinalizeSmem {
+  BlockSelectSmem sm;
+  float w1s[DSPARK_MAX_RANK];
+  float part[32 / sizeof(WT)][WCOLS];
+};
+
+// The finalize of one request (one workgroup), from its residual tile records
+// `rrec` (global, or LDS in the small-problem kernel).
 template <typename WT, bool GREEDY, int KS>
-__global__ __launch_bounds__(256) void k_verify_finalize(VerifyArgs<WT> P) {
-  __shared__ BlockSelectSmem sm;
-  __shared__ float w1s[DSPARK_MAX_RANK];
-  __shared__ float part[32 / sizeof(WT)][WCOLS];
+__device__ __forceinline__ void finalize_request(const VerifyArgs<WT>& P, int row, const float4* rrec,
+                                                 FinalizeSmem<WT>& fs) {
+  BlockSelectSmem& sm = fs.sm;
+  float* w1s = fs.w1s;
+  auto& part = fs.part;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int row = blockIdx.x;
   const int L = P.L_of(row);
   const int ks = P.rej[row];
   const bool rejected = ks <= L;
@@ -817,7 +829,7 @@ __global__ __launch_bounds__(256) void k_verify_finalize(VerifyArgs<WT> P) {
       const int prev = P.prev_of(row, ks);
       for (int k = tid; k < P.r; k += 256) w1s[k] = to_f32(P.W1[(size_t)prev * P.r + k]);
       const int nt = ceil_div(P.V, TILE);
-      const TilePick S = block_select_tile(P.rrec + (size_t)row * nt * 2, nt, false, 1.0, u, sm);
+      const TilePick S = block_select_tile(rrec, nt, false, 1.0, u, sm);
       if (!(S.Z > 0.0)) {
         use_p = true;  // no residual mass: sample p itself
       } else {
@@ -853,6 +865,110 @@ __global__ __launch_bounds__(256) void k_verify_finalize(VerifyArgs<WT> P) {
       P.target_probs[(size_t)row * P.gamma + k - 1] =
           (k <= lim) ? P.tp[(size_t)row * P.gamma + k - 1] : -1.0f;
   }
+}
+
+template <typename WT, bool GREEDY, int KS>
+__global__ __launch_bounds__(256) void k_verify_finalize(VerifyArgs<WT> P) {
+  __shared__ FinalizeSmem<WT> fs;
+  const int row = blockIdx.x;
+  finalize_request<WT, GREEDY, KS>(P, row, P.rrec + (size_t)row * ceil_div(P.V, TILE) * 2, fs);
+}
+
+// Small problems (at most 16 column tiles): verify's residual and finalize in
+// one workgroup per request.  A rejected request's residual tile records are
+// formed in LDS with the arithmetic of k_residual_partials on block row 0 (bf16
+// factors through the same fragment and MFMA chain with the request's bias row
+// read by all 32 block rows, fp32 factors through the same fmaf chain per
+// column, one column per thread; the base and target values of block rows
+// 1..31 are zero and go unused), then the request is finalized from them as
+// k_verify_finalize would: the outputs are bit-identical to the two kernels'.
+constexpr int VROWS_MAX_TILES = 16;
+constexpr size_t VROWS_MAX_W2_BYTES = size_t(32) << 20;  // R * r * V * sizeof(WT), W2 read per request
+
+template <typename WT, int KS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_verify_tail_rows(
+    VerifyArgs<WT> P) {
+  constexpr int APAD = BiasBlock<WT>::APAD;
+  constexpr bool FP32 = std::is_same<WT, float>::value;
+  __shared__ __align__(16) WT A_row[DSPARK_MAX_RANK + APAD];
+  __shared__ __align__(16) float Xb[33 * BSTRIDE];  // row 0 base values, row 1 (fp32) the bias, rest 0
+  __shared__ __align__(16) float Xt[32 * BSTRIDE];  // row 0 target values, rest 0
+  __shared__ float red_s[4];
+  __shared__ __align__(16) float4 recs[2 * VROWS_MAX_TILES];
+  __shared__ FinalizeSmem<WT> fs;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int row = blockIdx.x;
+  const int nt = ceil_div(P.V, TILE);
+  const int L = P.L_of(row);
+  const int ks = P.rej[row];
+  if (ks <= L) {  // uniform
+    for (int i = tid; i < 33 * BSTRIDE; i += 256) Xb[i] = 0.f;
+    for (int i = tid; i < 32 * BSTRIDE; i += 256) Xt[i] = 0.f;
+    const float sc = (P.T == 1.0f) ? LOG2E_F : LOG2E_F * P.invT;
+    const double2 rs = P.rowstat[(size_t)row * (P.gamma + 1) + ks - 1];
+    const size_t ev = (size_t)row * P.gamma + ks - 1;
+    const float Mt = (float)rs.x, iZt = (float)(1.0 / rs.y);
+    const float mq = P.dstats[2 * ev], iZq = (float)(1.0 / (double)P.dstats[2 * ev + 1]);
+    const int prev = P.prev_of(row, ks);
+    for (int e = tid; e < P.r; e += 256) A_row[e] = P.W1[(size_t)prev * P.r + e];
+    const float* brow = P.base + ev * P.V;
+    const float* trow = P.target + ((size_t)row * (P.gamma + 1) + ks - 1) * P.V;
+    __syncthreads();
+    for (int t = 0; t < nt; t++) {
+      const int cbase = t * TILE + wave * WCOLS;
+      const int c = t * TILE + tid;
+      Xb[tid] = (c < P.V) ? brow[c] : 0.f;
+      Xt[tid] = (c < P.V) ? trow[c] : 0.f;
+      f32x16 acc[2];
+      if constexpr (FP32) {
+        float a = 0.f;
+        for (int kk = 0; kk < P.r; kk++)
+          a = fmaf(to_f32(A_row[kk]), (c < P.V) ? to_f32(P.W2[(size_t)kk * P.V + c]) : 0.f, a);
+        Xb[BSTRIDE + tid] = a;
+        __syncthreads();
+        float av[2][16];
+        stage_read_full(Xb + BSTRIDE, wave * WCOLS, av);
+#pragma unroll
+        for (int p = 0; p < 2; p++)
+#pragma unroll
+          for (int q = 0; q < 16; q++) acc[p][q] = av[p][q];
+      } else {
+        typename BiasBlock<WT>::template Frag<KS> F;
+        BiasBlock<WT>::template load<KS>(F, P.W2, P.V, P.r, cbase);
+        __syncthreads();
+        BiasBlock<WT>::template to_operands<KS>(F);
+#pragma unroll
+        for (int p = 0; p < 2; p++)
+#pragma unroll
+          for (int q = 0; q < 16; q++) acc[p][q] = 0.f;
+        BiasBlock<WT>::template mma_rb_op<KS>(F, P.r, A_row, 0, acc);
+      }
+      float b[2][16], tv[2][16];
+      if ((t + 1) * TILE <= P.V) {
+        stage_read_full(Xb, wave * WCOLS, b);
+        stage_read_full(Xt, wave * WCOLS, tv);
+      } else {
+        stage_read(Xb, true, P.V, cbase, wave * WCOLS, b);
+        stage_read(Xt, true, P.V, cbase, wave * WCOLS, tv);
+      }
+      float d[2][16];
+#pragma unroll
+      for (int p = 0; p < 2; p++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) d[p][i] = residual_elem(tv[p][i], b[p][i], acc[p][i], Mt, iZt, mq, iZq, sc);
+      const float sl = tree_sum32(d);
+      const float sw = sum_xor32(sl);
+      if (lane == 0) red_s[wave] = sw;
+      __syncthreads();
+      if (tid == 0) {
+        const float s0 = red_s[0], s1 = red_s[1], s2 = red_s[2], s3 = red_s[3];
+        recs[2 * t] = make_float4(0.f, (s0 + s1) + (s2 + s3), s0, s1);
+        recs[2 * t + 1] = make_float4(s2, s3, 0.f, 0.f);
+      }
+      __syncthreads();  // Xb, Xt and red_s are rewritten by the next tile; recs complete
+    }
+  }
+  finalize_request<WT, false, KS>(P, row, recs, fs);
 }
 
 // ---------------------------------------------------------------------------
@@ -944,6 +1060,19 @@ static void launch_verify_stream(const VerifyArgs<WT>& P, hipStream_t stream) {
 
 // Accept tests, residual and emission from the stream's partials.
 
+// DSPARK_VERIFY_KERNEL=split keeps the residual and finalize kernels apart
+// even where the small-problem kernel applies; both compute the same outputs.
+static bool split_requested() {
+  const char* e = getenv("DSPARK_VERIFY_KERNEL");
+  return e != nullptr && strcmp(e, "split") == 0;
+}
+
+template <typename WT>
+static bool verify_rows_fits(const VerifyArgs<WT>& P) {
+  return !split_requested() && ceil_div(P.V, TILE) <= VROWS_MAX_TILES &&
+         (size_t)P.R * (size_t)P.r * (size_t)P.V * sizeof(WT) <= VROWS_MAX_W2_BYTES;
+}
+
 template <typename WT>
 static int launch_verify_finish(const VerifyArgs<WT>& P, hipStream_t stream) {
   const bool greedy = (P.T == 0.f);
@@ -955,6 +1084,13 @@ static int launch_verify_finish(const VerifyArgs<WT>& P, hipStream_t stream) {
       hipLaunchKernelGGL((k_verify_decide<WT, false>), dim3(P.R), dim3(64 * decide_waves(P.gamma)), 0, stream, P);
   }
   prof_after(DSPARK_KID_VERIFY_DECIDE, stream);
+  if (!greedy && verify_rows_fits(P)) {
+    prof_before(DSPARK_KID_VERIFY_FINALIZE, stream);
+    for (int rep = prof_repeat(DSPARK_KID_VERIFY_FINALIZE); rep > 0; rep--)
+      DSPARK_DISPATCH_KS(P.r, hipLaunchKernelGGL((k_verify_tail_rows<WT, KS>), dim3(P.R), dim3(256), 0, stream, P));
+    prof_after(DSPARK_KID_VERIFY_FINALIZE, stream);
+    return hipGetLastError() == hipSuccess ? DSPARK_OK : DSPARK_EHIP;
+  }
   if (!greedy) {
     prof_before(DSPARK_KID_RESIDUAL, stream);
     for (int rep = prof_repeat(DSPARK_KID_RESIDUAL); rep > 0; rep--) {

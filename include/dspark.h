@@ -36,7 +36,10 @@
  *     DSPARK_DRAFT_KERNEL=stepwise selects the per-step kernels, and
  *     DSPARK_FUSED_SPIN_TICKS overrides the one-launch draft's wait limit
  *     (in 100 MHz ticks; 0 makes every wait that does not succeed at once
- *     give up, which the tests of that path use).
+ *     give up, which the tests of that path use).  Every verify call reads
+ *     DSPARK_VERIFY_KERNEL: "split" keeps the residual and finalize kernels
+ *     apart for small problems (at most 16 column tiles), where one kernel
+ *     per request otherwise does both; the outputs are the same.
  *   - Arrays are dense, row-major, with the last index contiguous.
  *   - W1/W2 are bf16 (bit patterns in uint16) or fp32 according to w_type.
  *   - No random numbers are drawn inside the library: every random choice is

@@ -559,3 +559,49 @@ def test_split_verify_equals_one_call(T):
         assert torch.equal(a, b)
     torch.cuda.synchronize()
     assert D.device_error(ws) == 0
+
+
+# Small problems (at most 16 column tiles) run verify's residual and finalize
+# as one kernel per request; DSPARK_VERIFY_KERNEL=split keeps the two kernels.
+# Same draft outputs and verify lengths: the outputs must be bit-identical.
+@pytest.mark.parametrize("T", [1.0, 0.7])
+@pytest.mark.parametrize("R,g,V,r,w", [
+    (4, 4, 512, 16, "f32"),       # the tiny workload's shape
+    (33, 5, 1000, 48, "f32"),     # ragged vocabulary tail
+    (40, 6, 3000, 32, "bf16"),    # twelve tiles, bf16 factors
+    (7, 16, 4096, 256, "bf16"),   # sixteen tiles, full rank, the longest block
+])
+def test_small_verify_tail_equals_split_kernels(R, g, V, r, w, T, monkeypatch):
+    from gen.rnn import make_rnn_weights
+    d = config(1, R=R, gamma=g, V=V, r=r, w_dtype=w)
+    inp = make_inputs(d, seed=31 + R)
+    wr = make_rnn_weights(r, w, seed=4)
+    inp.update(Wx=wr["Wx"], Ws=wr["Ws"], rnn_bias=wr["bias"])
+    dd = to_dev(inp)
+    dv = dd["base"].device
+    L = torch.from_numpy(np.random.default_rng(R).integers(0, g + 1, R).astype(np.int32)).to(dv)
+    ws = D.new_workspace(R, g, V, r, dv)
+    tok, prob, st = D.draft(dd["base"], dd["W1"], dd["W2"], dd["anchor"], dd["u_draft"], T, ws)
+    args = (dd["target"], dd["base"], dd["W1"], dd["W2"], dd["anchor"], tok, prob, st, L, dd["u_accept"],
+            dd["u_final"], T, ws)
+    monkeypatch.delenv("DSPARK_VERIFY_KERNEL", raising=False)
+    one = [x.clone() for x in D.verify(*args)]
+    monkeypatch.setenv("DSPARK_VERIFY_KERNEL", "split")
+    two = [x.clone() for x in D.verify(*args)]
+    rejected = int((one[1] < L).sum())
+    say(f"small verify {R},{g},{V},{r},{w} T={T}: {rejected} rejected requests")
+    assert rejected > 0
+    for a, b in zip(one, two):
+        assert torch.equal(a, b)
+    # the RNN head's verify (dense bias rows) takes the same kernel
+    tok, prob, st, states = D.draft_rnn(dd["base"], dd["W1"], dd["W2"], dd["Wx"], dd["Ws"], dd["rnn_bias"],
+                                        dd["anchor"], dd["u_draft"], T, ws)
+    rargs = (dd["target"], dd["base"], states, dd["W2"], tok, prob, st, L, dd["u_accept"], dd["u_final"], T, ws)
+    monkeypatch.delenv("DSPARK_VERIFY_KERNEL", raising=False)
+    one = [x.clone() for x in D.verify_rnn(*rargs)]
+    monkeypatch.setenv("DSPARK_VERIFY_KERNEL", "split")
+    two = [x.clone() for x in D.verify_rnn(*rargs)]
+    for a, b in zip(one, two):
+        assert torch.equal(a, b)
+    torch.cuda.synchronize()
+    assert D.device_error(ws) == 0

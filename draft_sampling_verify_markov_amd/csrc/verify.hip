@@ -383,7 +383,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const rsrc_t brs = make_rsrc(P.base + (size_t)r0 * P.gamma * P.V, R_left * P.gamma * P.V * 4);
     const rsrc_t trs = make_rsrc(P.target + (size_t)r0 * (P.gamma + 1) * P.V, R_left * (P.gamma + 1) * P.V * 4);
     // unit u's rows: wave w loads compacted rows 4i + w of the block (8 base,
-    // 8 target loads per wave; rows past nrej re-read row 0)
+    // 8 target loads per wave).  Rows past nrej are not loaded: their staged
+    // values are stale, and the sums formed from them are never read.
     auto issue = [&](int u) {
       if (u >= nunits) return;
       const int ti = u / nrb, rb = u - ti * nrb;
@@ -393,13 +394,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
       for (int i = 0; i < 8; i++) {
         const int q = rb * 32 + 4 * i + w;
-        const int qc = q < nrej ? q : 0;
+        if (q >= nrej) break;  // wave-uniform; the waits below are for all loads
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             brs, (__attribute__((address_space(3))) void*)(Xb + (4 * i + w) * BSTRIDE), 16,
-            (int)(s_boff[qc] + coff), 0, 0, AUX_NT);
+            (int)(s_boff[q] + coff), 0, 0, AUX_NT);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             trs, (__attribute__((address_space(3))) void*)(Xt + (4 * i + w) * BSTRIDE), 16,
-            (int)(s_toff[qc] + coff), 0, 0, AUX_NT);
+            (int)(s_toff[q] + coff), 0, 0, AUX_NT);
       }
     };
 

@@ -818,6 +818,14 @@ __device__ __forceinline__ void finalize_request(const VerifyArgs<WT>& P, int ro
   const int A = rejected ? ks - 1 : L;
   const size_t rowA = (size_t)row * (P.gamma + 1) + A;
   int y = 0;
+  // the outputs' accepted tokens and probabilities, loaded before the sample
+  // is drawn so that the final stores wait on no load
+  int dt = -1;
+  float tpv = -1.0f;
+  if (wave == 0 && lane < P.gamma) {
+    if (lane < A) dt = P.dtok[(size_t)row * P.gamma + lane];
+    if (P.target_probs && lane + 1 <= min(L, A + 1)) tpv = P.tp[(size_t)row * P.gamma + lane];
+  }
 
   if (GREEDY) {
     if (wave != 0) return;
@@ -829,6 +837,11 @@ __device__ __forceinline__ void finalize_request(const VerifyArgs<WT>& P, int ro
     if (rejected) {  // uniform over the workgroup
       const int prev = P.prev_of(row, ks);
       for (int k = tid; k < P.r; k += 256) w1s[k] = to_f32(P.W1[(size_t)prev * P.r + k]);
+      // position k*'s target row statistics and draft normaliser, loaded
+      // before the tile and chunk picks that precede their use
+      const size_t ev = (size_t)row * P.gamma + ks - 1;
+      const double2 rs = P.rowstat[(size_t)row * (P.gamma + 1) + ks - 1];
+      const float dq_m = P.dstats[2 * ev], dq_z = P.dstats[2 * ev + 1];
       const int nt = ceil_div(P.V, TILE);
       const TilePick S = block_select_tile(rrec, nt, false, 1.0, u, sm);
       if (!(S.Z > 0.0)) {
@@ -836,7 +849,6 @@ __device__ __forceinline__ void finalize_request(const VerifyArgs<WT>& P, int ro
       } else {
         const int cb = S.t * TILE + S.w * WCOLS;
         const int col = cb + lane;
-        const size_t ev = (size_t)row * P.gamma + ks - 1;
         float b = -INFINITY, t = -INFINITY;
         if (wave == 0 && col < P.V) {
           b = P.base[ev * P.V + col];
@@ -844,10 +856,9 @@ __device__ __forceinline__ void finalize_request(const VerifyArgs<WT>& P, int ro
         }
         const float bias = chunk_bias<WT, KS>(P.W2, P.V, P.r, cb, w1s, part);
         if (wave != 0) return;
-        const double2 rs = P.rowstat[(size_t)row * (P.gamma + 1) + ks - 1];
         const float sc = (P.T == 1.0f) ? LOG2E_F : LOG2E_F * P.invT;
-        const float d = residual_elem(t, b, bias, (float)rs.x, (float)(1.0 / rs.y), P.dstats[2 * ev],
-                                      (float)(1.0 / (double)P.dstats[2 * ev + 1]), sc);
+        const float d = residual_elem(t, b, bias, (float)rs.x, (float)(1.0 / rs.y), dq_m,
+                                      (float)(1.0 / (double)dq_z), sc);
         y = min(cb + wave_pick64(d, 1.0, S.rem), P.V - 1);
       }
     }
@@ -857,15 +868,9 @@ __device__ __forceinline__ void finalize_request(const VerifyArgs<WT>& P, int ro
 
   // outputs (wave 0): lane i writes slot i
   int32_t* out = P.out_tokens + (size_t)row * (P.gamma + 1);
-  for (int i = lane; i <= P.gamma; i += 64)
-    out[i] = (i < A) ? P.dtok[(size_t)row * P.gamma + i] : ((i == A) ? y : -1);
+  if (lane <= P.gamma) out[lane] = (lane < A) ? dt : ((lane == A) ? y : -1);
   if (lane == 0) P.accept_len[row] = A;
-  if (P.target_probs) {
-    const int lim = min(L, A + 1);
-    for (int k = lane + 1; k <= P.gamma; k += 64)
-      P.target_probs[(size_t)row * P.gamma + k - 1] =
-          (k <= lim) ? P.tp[(size_t)row * P.gamma + k - 1] : -1.0f;
-  }
+  if (P.target_probs && lane < P.gamma) P.target_probs[(size_t)row * P.gamma + lane] = tpv;
 }
 
 template <typename WT, bool GREEDY, int KS>
